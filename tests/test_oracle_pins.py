@@ -1,0 +1,337 @@
+"""Pins for the CPU oracle: every check compares it with something other than
+itself -- hand-worked golden files, closed forms, integer arithmetic, brute
+force on tiny inputs, textbook special cases and invariants of the method."""
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle as O
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ----------------------------------------------------------------------------
+# test-side helpers, written independently of the oracle
+# ----------------------------------------------------------------------------
+def pack_codes_loop(codes):
+    """Pack codes [rows, K] (ints 0..15) into uint32 words, first code lowest."""
+    rows, K = codes.shape
+    out = np.zeros((rows, K // 8), dtype=np.uint32)
+    for r in range(rows):
+        for c in range(K):
+            out[r, c // 8] |= np.uint32(int(codes[r, c]) << (4 * (c % 8)))
+    return out
+
+
+def bf16(v):
+    return synth.to_bf16_bits(np.asarray(v, dtype=np.float32))
+
+
+def integer_qtensor(codes):
+    """Weights with scale 1 and bias -8, so W = q - 8 exactly."""
+    rows, K = codes.shape
+    G = K // 64
+    return (pack_codes_loop(codes), bf16(np.ones((rows, G))), bf16(np.full((rows, G), -8.0)))
+
+
+# ----------------------------------------------------------------------------
+# Q: packing and dequantization
+# ----------------------------------------------------------------------------
+def test_nibble_order_golden():
+    with open(os.path.join(GOLDEN, "nibble_order.txt")) as f:
+        rows = [l.split() for l in f if l.strip() and not l.startswith("#")]
+    words = np.array([int(r[0], 16) for r in rows], dtype=np.uint32)
+    expect = np.array([[int(v) for v in r[1:]] for r in rows], dtype=np.uint8)
+    got = O.unpack_codes(words.reshape(-1, 1))
+    np.testing.assert_array_equal(got, expect)
+
+
+def test_pack_unpack_roundtrip():
+    rng = np.random.default_rng(11)
+    codes = rng.integers(0, 16, size=(5, 128))
+    np.testing.assert_array_equal(O.unpack_codes(pack_codes_loop(codes)), codes)
+
+
+def test_dequant_group_structure():
+    # all codes 1, bias 0, scale of group g = g + 1  ->  W[c] = c // 64 + 1
+    K = 256
+    codes = np.ones((3, K), dtype=np.int64)
+    w = pack_codes_loop(codes)
+    s = bf16(np.tile(np.arange(1, K // 64 + 1), (3, 1)))
+    b = bf16(np.zeros((3, K // 64)))
+    W = O.dequantize(w, s, b)
+    expect = np.tile(np.arange(K) // 64 + 1, (3, 1)).astype(np.float64)
+    np.testing.assert_array_equal(W, expect)
+
+
+def test_dequant_invariant_scale_q_bias():
+    """Spec invariant: the unpacked weight equals scale*q + bias per
+    64-wide group.  Checked element by element with codes from the test-side
+    packer (not the oracle's unpacker)."""
+    rng = np.random.default_rng(12)
+    codes = rng.integers(0, 16, size=(4, 192))
+    w = pack_codes_loop(codes)
+    sf = rng.uniform(0.01, 0.05, size=(4, 3)).astype(np.float32)
+    bf_ = rng.uniform(-0.4, 0.1, size=(4, 3)).astype(np.float32)
+    s, b = bf16(sf), bf16(bf_)
+    sd, bd = synth.bf16_bits_as_f32(s).astype(np.float64), synth.bf16_bits_as_f32(b).astype(np.float64)
+    W = O.dequantize(w, s, b)
+    for n in range(4):
+        for c in range(0, 192, 7):
+            assert W[n, c] == sd[n, c // 64] * codes[n, c] + bd[n, c // 64]
+
+
+def test_all_eights_with_minus_eight_scale_bias_is_zero():
+    K = 128
+    codes = np.full((6, K), 8)
+    w = pack_codes_loop(codes)
+    s = bf16(np.abs(np.random.default_rng(3).normal(0, 0.02, size=(6, 2))))
+    b = bf16(-8.0 * synth.bf16_bits_as_f32(s))
+    assert not np.any(O.dequantize(w, s, b))
+    x = bf16(np.random.default_rng(4).standard_normal((3, K)))
+    assert not np.any(O.qlinear(x, w, s, b))
+
+
+def test_qlinear_integer_exact():
+    """scale 1, bias -8, x in {-2..2}: y is an integer matmul (exact)."""
+    rng = np.random.default_rng(13)
+    M, N, K = 9, 40, 192
+    codes = rng.integers(0, 16, size=(N, K))
+    xi = rng.integers(-2, 3, size=(M, K))
+    w, s, b = integer_qtensor(codes)
+    y = O.qlinear(bf16(xi), w, s, b)
+    expect = xi.astype(np.int64) @ (codes.astype(np.int64) - 8).T
+    np.testing.assert_array_equal(y, expect.astype(np.float64))
+
+
+# ----------------------------------------------------------------------------
+# R: router
+# ----------------------------------------------------------------------------
+def test_rms_norm_constant_row_closed_form():
+    for c in (0.5, -3.0, 1e-3):
+        x = np.full((1, 128), c)
+        r = O.rms_norm_noscale(x, 1e-6)
+        np.testing.assert_allclose(r, c / math.sqrt(c * c + 1e-6), rtol=1e-14)
+
+
+def test_router_worked_example_closed_form():
+    """H = 64, E = 4, k = 2, x alternating +1/-1, norm scale 1, integer router
+    weights.  mean(x^2) = 1, so u = x / sqrt(1 + eps) / 8 and the logits are
+    l_e = sum_h x_h (q_eh - 8) / (8 sqrt(1 + eps)):
+    e0: q = 9 on +1, 7 on -1 -> 64/8;  e1: q = 8 -> 0;
+    e2: q = 7 on +1, 9 on -1 -> -64/8;  e3: q = 9 at h = 0 only -> 1/8."""
+    H, eps = 64, 1e-6
+    x = np.array([1.0 if h % 2 == 0 else -1.0 for h in range(H)])
+    q = np.full((4, H), 8)
+    q[0] = np.where(x > 0, 9, 7)
+    q[2] = np.where(x > 0, 7, 9)
+    q[3, 0] = 9
+    w, s, b = integer_qtensor(q)
+    pes = bf16([1.0, 1.0, 1.0, 0.5])
+    idx, wts, logits = O.route(bf16(x[None]), bf16(np.ones(H)), eps, w, s, b, pes, 2)
+    d = math.sqrt(1 + eps)
+    np.testing.assert_allclose(logits[0], np.float32([8 / d, 0.0, -8 / d, 0.125 / d]), rtol=1e-7)
+    assert idx.tolist() == [[0, 3]]
+    p0 = 1.0 / (1.0 + math.exp(-(8 - 0.125) / d))
+    np.testing.assert_allclose(wts[0], [p0, 0.5 * (1 - p0)], rtol=1e-6)
+
+
+def topk_selection_loop(row, k):
+    vals = list(map(float, row))
+    taken, out = set(), []
+    for _ in range(k):
+        best = None
+        for e, v in enumerate(vals):
+            if e in taken:
+                continue
+            if best is None or v > vals[best]:
+                best = e
+        taken.add(best)
+        out.append(best)
+    return out
+
+
+def test_topk_matches_selection_loop_with_ties():
+    rng = np.random.default_rng(14)
+    logits = rng.integers(-3, 4, size=(40, 12)).astype(np.float32) * 0.25  # many ties
+    for k in (1, 3, 8, 12):
+        got = O.top_k(logits, k)
+        for t in range(logits.shape[0]):
+            assert got[t].tolist() == topk_selection_loop(logits[t], k)
+
+
+def test_topk_special_cases():
+    rng = np.random.default_rng(15)
+    logits = rng.standard_normal((20, 16)).astype(np.float32)
+    np.testing.assert_array_equal(O.top_k(logits, 1)[:, 0], np.argmax(logits, axis=1))
+    full = O.top_k(logits, 16)
+    for t in range(20):
+        assert sorted(full[t].tolist()) == list(range(16))
+        assert np.all(np.diff(logits[t, full[t]]) <= 0)
+
+
+def test_softmax_invariants():
+    rng = np.random.default_rng(16)
+    v = rng.standard_normal((50, 8)) * 3
+    p = O.precise_softmax(v)
+    np.testing.assert_allclose(p.sum(-1), 1.0, atol=1e-14)
+    np.testing.assert_allclose(O.precise_softmax(v + 7.25), p, atol=1e-15)
+    np.testing.assert_allclose(O.precise_softmax(np.zeros((3, 8))), 1.0 / 8)
+    assert np.all(p > 0)
+
+
+def test_route_weights_sum_to_one_before_per_expert_scale():
+    cfg = synth.TINY
+    inp = synth.make_moe_inputs(cfg)
+    r = inp.weights.router
+    ones = bf16(np.ones(cfg.E))
+    _, w1, _ = O.route(inp.x, inp.weights.norm_scale, cfg.eps, r.w, r.scales, r.biases, ones, cfg.k)
+    np.testing.assert_allclose(w1.astype(np.float64).sum(-1), 1.0, atol=1e-6)
+    idx, w, _ = O.route(inp.x, inp.weights.norm_scale, cfg.eps, r.w, r.scales, r.biases,
+                        inp.weights.per_expert_scale, cfg.k)
+    pes = synth.bf16_bits_as_f32(inp.weights.per_expert_scale)
+    np.testing.assert_allclose(w, w1 * pes[idx], rtol=1e-6)
+    assert np.all(w >= 0) and np.all(w <= pes.max())
+
+
+# ----------------------------------------------------------------------------
+# S: sort
+# ----------------------------------------------------------------------------
+def read_kv(path):
+    out = {}
+    with open(path) as f:
+        for l in f:
+            if l.strip() and not l.startswith("#"):
+                key, *vals = l.split()
+                out[key] = [int(v) for v in vals]
+    return out
+
+
+def test_sort_golden():
+    g = read_kv(os.path.join(GOLDEN, "sort_small.txt"))
+    idx = np.array(g["indices"], dtype=np.int32).reshape(-1, g["k"][0])
+    off, sa = O.sort_assignments(idx, g["E"][0])
+    assert off.tolist() == g["offsets"]
+    assert sa.tolist() == g["sorted_assign"]
+
+
+def counting_sort_loop(flat, E):
+    buckets = [[] for _ in range(E)]
+    for a, e in enumerate(flat):
+        buckets[e].append(a)
+    offs = [0]
+    for b in buckets:
+        offs.append(offs[-1] + len(b))
+    return offs, [a for b in buckets for a in b]
+
+
+def test_sort_matches_counting_sort_loop():
+    rng = np.random.default_rng(17)
+    for T, k, E in [(16, 2, 8), (33, 4, 10), (64, 8, 128), (1, 1, 1)]:
+        idx = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+        off, sa = O.sort_assignments(idx, E)
+        offs, order = counting_sort_loop(idx.reshape(-1).tolist(), E)
+        assert off.tolist() == offs
+        assert sa.tolist() == order
+        inv = np.empty_like(sa)
+        inv[sa] = np.arange(sa.size)
+        np.testing.assert_array_equal(sa[inv], np.arange(sa.size))
+
+
+# ----------------------------------------------------------------------------
+# X: GELU and the expert path
+# ----------------------------------------------------------------------------
+def test_gelu_tanh_pins():
+    from scipy.special import erf
+    assert O.gelu_tanh(0.0) == 0.0
+    z = np.linspace(-8, 8, 4001)
+    g = O.gelu_tanh(z)
+    np.testing.assert_allclose(g - O.gelu_tanh(-z), z, atol=1e-12)  # odd-part identity
+    exact = 0.5 * z * (1 + erf(z / math.sqrt(2)))
+    assert np.abs(g - exact).max() < 5e-4  # the tanh form's known error (about 4.7e-4)
+    np.testing.assert_allclose(O.gelu_tanh(np.array([30.0, -30.0])), [30.0, 0.0], atol=1e-12)
+
+
+def test_grouped_equals_bruteforce_on_tiny():
+    cfg = synth.TINY
+    inp = synth.make_moe_inputs(cfg)
+    wt = inp.weights
+    y, idx, w, _ = O.moe_layer(inp.x, wt, cfg.k, cfg.I, cfg.eps, grouped=True)
+    yb = O.experts_bruteforce(inp.x, idx, w, wt.gate_up, wt.down, cfg.I)
+    assert O.rowwise_rel_err(y, yb) < 1e-5
+    assert y.shape == (cfg.T, cfg.H)
+
+
+def test_single_expert_reduces_to_dense_geglu_mlp():
+    """E = 1, k = 1: y = per_expert_scale[0] * down(gelu(gate(x)) * up(x)),
+    computed here with integer weights and plain numpy."""
+    rng = np.random.default_rng(18)
+    T, H, I = 5, 128, 64
+    cg = rng.integers(0, 16, size=(2 * I, H))
+    cd = rng.integers(0, 16, size=(H, I))
+    gu = synth.QTensor(*[a[None] for a in integer_qtensor(cg)])
+    dn = synth.QTensor(*[a[None] for a in integer_qtensor(cd)])
+    xf = rng.integers(-2, 3, size=(T, H)).astype(np.float64) * 0.125
+    x = bf16(xf)
+    idx = np.zeros((T, 1), dtype=np.int32)
+    pes = 1.25
+    w = np.full((T, 1), pes, dtype=np.float32)
+    y = O.experts_bruteforce(x, idx, w, gu, dn, I)
+    Wg = cg.astype(np.float64) - 8
+    Wd = cd.astype(np.float64) - 8
+    g = xf @ Wg.T
+    a = g[:, :I]
+    mid = 0.5 * a * (1 + np.tanh(math.sqrt(2 / math.pi) * (a + 0.044715 * a ** 3))) * g[:, I:]
+    np.testing.assert_allclose(y, pes * (mid @ Wd.T), rtol=1e-12, atol=1e-9)
+
+
+def test_layer_token_equivariance_and_duplicates():
+    cfg = synth.TINY
+    inp = synth.make_moe_inputs(cfg)
+    wt = inp.weights
+    y, *_ = O.moe_layer(inp.x, wt, cfg.k, cfg.I, cfg.eps, grouped=False)
+    perm = np.random.default_rng(19).permutation(cfg.T)
+    yp, *_ = O.moe_layer(inp.x[perm], wt, cfg.k, cfg.I, cfg.eps, grouped=False)
+    np.testing.assert_allclose(yp, y[perm], rtol=1e-12, atol=1e-12)
+    xd = np.concatenate([inp.x[:3], inp.x[:3]])
+    yd, *_ = O.moe_layer(xd, wt, cfg.k, cfg.I, cfg.eps, grouped=False)
+    np.testing.assert_array_equal(yd[:3], yd[3:])
+
+
+def test_layer_linear_in_down_projection():
+    cfg = synth.TINY
+    inp = synth.make_moe_inputs(cfg)
+    wt = inp.weights
+    y, idx, w, _ = O.moe_layer(inp.x, wt, cfg.k, cfg.I, cfg.eps, grouped=False)
+    d = wt.down
+    d2 = synth.QTensor(d.w, bf16(2.0 * synth.bf16_bits_as_f32(d.scales)),
+                       bf16(2.0 * synth.bf16_bits_as_f32(d.biases)))
+    y2 = O.experts_bruteforce(inp.x, idx, w, wt.gate_up, d2, cfg.I)
+    np.testing.assert_array_equal(y2, 2.0 * y)
+
+
+def test_mid_and_down_pieces_compose_to_layer():
+    cfg = synth.TINY
+    inp = synth.make_moe_inputs(cfg)
+    wt = inp.weights
+    y, idx, w, _ = O.moe_layer(inp.x, wt, cfg.k, cfg.I, cfg.eps, grouped=False)
+    A = cfg.T * cfg.k
+    mid = O.expert_mid_bruteforce(inp.x, idx, wt.gate_up, cfg.I, list(range(A)))
+    y2 = O.down_combine_from_mid(mid, idx, w, wt.down, list(range(cfg.T)))
+    np.testing.assert_allclose(y2, y, rtol=1e-12, atol=1e-12)
+
+
+def test_rowwise_rel_err_metric():
+    ref = np.array([[1.0, -2.0], [0.5, 0.25]])
+    y = ref + np.array([[0.02, 0.0], [0.0, 0.01]])
+    assert abs(O.rowwise_rel_err(y, ref) - 0.02) < 1e-15
+
+
+def test_bf16_roundtrip_and_rounding():
+    v = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -2.5, 3.140625], dtype=np.float64)
+    bits = O.f64_to_bf16_bits(v)
+    # 1 + 2^-8 is a tie between 1 and 1 + 2^-7 -> even (1.0); 1 + 3*2^-8 -> 1 + 2^-6
+    np.testing.assert_array_equal(O.bf16_to_f64(bits), [1.0, 1.0, 1.0 + 2 ** -6, -2.5, 3.140625])

@@ -1,0 +1,214 @@
+"""Benchmark of the 4-bit MoE layer on one MI355X.
+
+One step = the whole layer on one batch: moe_route -> moe_sort ->
+qswitch_gate_up_geglu -> qswitch_down_combine, on the 256-token decoder
+canvas (H = 2816, 128 experts, top-8, moe_intermediate 704, int4 group 64).
+Inputs are resident in HBM before timing starts.  Three independent weight
+sets (1.28 GB) are rotated between steps so the 256 MB Infinity Cache cannot
+serve a layer's weights from the previous step.
+
+Prints ONE JSON line (rank 0):
+  value      tokens/s of the whole layer (wall clock over K steps, bracketed
+             by device synchronisation)
+  roofline   the dominant kernel (qswitch_gate_up_geglu): algorithmic bytes
+             per launch / its mean launch time from HIP events on the launch
+             stream, against 8 TB/s HBM
+  cpu_baseline  the CPU oracle timed on this host on a bounded sample
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+METRIC = "MoE-layer tokens/s + % HBM roofline, H=2816 128-expert top-8 int4, 256 tok"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--workload", default="moe_canvas_256tok_h2816_e128_top8",
+                    help="diagnostic override; the reported line is defined on the canvas workload")
+    ap.add_argument("--weight-sets", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def expert_bytes(cfg):
+    """Algorithmic bytes of one touched expert: packed codes + bf16 scales + biases."""
+    gu = 2 * cfg.I * (cfg.H // 2 + 2 * 2 * (cfg.H // 64))
+    dn = cfg.H * (cfg.I // 2 + 2 * 2 * (cfg.I // 64))
+    return gu, dn
+
+
+def router_bytes(cfg):
+    return cfg.E * (cfg.H // 2 + 4 * (cfg.H // 64)) + 2 * cfg.H + 2 * cfg.E
+
+
+def cpu_baseline(cfg, inp, seconds):
+    import oracle as O
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads") or 0) for i in threadpool_info()) or None
+    except Exception:
+        pass
+    if threads is None:
+        threads = len(os.sched_getaffinity(0))
+    wt = inp.weights
+    times = []
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        O.moe_layer(inp.x, wt, cfg.k, cfg.I, cfg.eps, grouped=True)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start >= seconds or len(times) >= 5:
+            break
+    t = float(np.median(times))
+    return {"value": cfg.T / t, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"full {cfg.T}-token layer (route + grouped fp32 experts), {len(times)} run(s), "
+                      f"median {t:.2f} s; host has {os.cpu_count()} logical CPUs"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build measures one GPU only (the layer's multi-GPU split is a design "
+              "note, not built); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import bit_quantized_moe_diffrouter_amd as q
+    import synth
+
+    cfg = synth.CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    # ---- inputs resident in HBM: x and three independent weight sets
+    seeds = [cfg.seed_w + 10 * i for i in range(args.weight_sets)]
+    sets, host_first = [], None
+    for s in seeds:
+        w = synth.make_moe_weights(cfg, seed=s)
+        if host_first is None:
+            host_first = w
+        sets.append(q.MoEParams(
+            t(w.norm_scale), q.QuantWeight(t(w.router.w), t(w.router.scales), t(w.router.biases)),
+            t(w.per_expert_scale), q.QuantWeight(t(w.gate_up.w), t(w.gate_up.scales), t(w.gate_up.biases)),
+            q.QuantWeight(t(w.down.w), t(w.down.scales), t(w.down.biases)),
+            None if w.logit_bias is None else t(w.logit_bias)))
+    x_host = synth.make_activations(cfg.T, cfg.H, cfg.seed_x)
+    x = t(x_host)
+    T, k, E, H, I = cfg.T, cfg.k, cfg.E, cfg.H, cfg.I
+    A = T * k
+    # preallocated outputs and workspaces (the library allocates nothing)
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    wts = torch.empty((T, k), dtype=torch.float32, device=dev)
+    off = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    sa = torch.empty(A, dtype=torch.int32, device=dev)
+    mid = torch.empty((A, I), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    ws_r = torch.empty(max(1, q.moe_route_workspace(T, H, E)), dtype=torch.uint8, device=dev)
+    ws_d = torch.empty(max(1, q.qswitch_down_combine_workspace(T, k, H, 1)), dtype=torch.uint8, device=dev)
+
+    def step(p, ev=None):
+        if ev is not None:
+            ev[0].record()
+        q.moe_route(x, p.norm_scale, cfg.eps, p.router, p.per_expert_scale, k, p.logit_bias,
+                    indices=idx, weights=wts, workspace=ws_r)
+        if ev is not None:
+            ev[1].record()
+        q.moe_sort(idx, E, off, sa)
+        if ev is not None:
+            ev[2].record()
+        q.qswitch_gate_up_geglu(x, p.gate_up, I, k, off, sa, mid=mid)
+        if ev is not None:
+            ev[3].record()
+        q.qswitch_down_combine(mid, T, k, p.down, wts, off, sa, y=y, workspace=ws_d, deterministic=1)
+        if ev is not None:
+            ev[4].record()
+
+    # touched experts per weight set (routing is a function of x and the router)
+    touched = []
+    for p in sets:
+        step(p)
+        torch.cuda.synchronize()
+        touched.append(int((torch.diff(off.cpu()) > 0).sum()))
+
+    for i in range(args.warmup):
+        step(sets[i % len(sets)])
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(sets[i % len(sets)], evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    names = ["moe_route", "moe_sort", "qswitch_gate_up_geglu", "qswitch_down_combine"]
+    per = {n: [] for n in names}
+    for ev in evs:
+        for j, n in enumerate(names):
+            per[n].append(ev[j].elapsed_time(ev[j + 1]) * 1e3)  # us
+    mean_us = {n: float(np.mean(v)) for n, v in per.items()}
+
+    gu_b, dn_b = expert_bytes(cfg)
+    n_touch = float(np.mean(touched))
+    x_bytes, y_bytes = T * H * 2, T * H * 2
+    gate_up_alg = n_touch * gu_b + x_bytes + A * I * 2
+    layer_alg = n_touch * (gu_b + dn_b) + router_bytes(cfg) + x_bytes + y_bytes
+    flops = 2.0 * A * (2 * I * H + H * I) + 2.0 * T * E * H
+    ms = wall / K * 1e3
+    gbs_gu = gate_up_alg / (mean_us["qswitch_gate_up_geglu"] * 1e-6) / 1e9
+    layer_gbs = layer_alg / (ms * 1e-3) / 1e9
+
+    out = {
+        "metric": METRIC,
+        "value": T * K / wall,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "tokens": T, "hidden": H, "experts": E, "top_k": k,
+                   "moe_intermediate": I, "group": 64, "bits": 4, "weight_sets": len(sets),
+                   "experts_touched": n_touch, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": "qswitch_gate_up_geglu", "achieved": gbs_gu,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs_gu / HBM_PEAK_GBS,
+                     "traffic": None, "alg_bytes_per_launch": gate_up_alg,
+                     "mean_launch_us": mean_us["qswitch_gate_up_geglu"]},
+        "layer": {"alg_bytes": layer_alg, "achieved_GBs": layer_gbs, "hbm_frac": layer_gbs / HBM_PEAK_GBS,
+                  "flops": flops, "mfma_frac": flops / (ms * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12),
+                  "call_mean_us": mean_us,
+                  "call_sum_us": float(sum(mean_us.values()))},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        inp = synth.MoEInputs(cfg, x_host, host_first)
+        out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

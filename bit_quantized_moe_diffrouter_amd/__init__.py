@@ -1,0 +1,281 @@
+"""4-bit group-quantized mixture-of-experts layer for AMD MI355X (gfx950).
+
+Thin Python binding of ``libqmoe.so`` (C ABI in ``include/qmoe.h``): argument
+marshalling only.  Every step of the layer runs in the library's HIP kernels;
+PyTorch supplies device memory and the current stream.  If the library has not
+been built, every call raises -- there is no fallback path.
+
+The layer (diffusion-gemma model.ts page of the "@mlx-bun/inference" diff:
+DiffRouter, DiffExperts, DiffDecoderLayer.forwardWith):
+
+    indices, weights = moe_route(x_router, ...)           # DiffRouter
+    offsets, sorted  = moe_sort(indices, E)               # token-by-expert sort
+    mid = qswitch_gate_up_geglu(x_expert, gate_up, ...)   # gate_up, split, GeGLU
+    y   = qswitch_down_combine(mid, down, weights, ...)   # down, weighted sum over k
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = [
+    "QMoEError", "QuantWeight", "MoEParams", "lib", "library_path",
+    "moe_route", "moe_route_workspace", "moe_sort", "qswitch_gate_up_geglu",
+    "qswitch_down_combine", "qswitch_down_combine_workspace", "qlinear", "moe_layer",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqmoe.so")
+
+QMOE_OK, QMOE_ERR_INVALID, QMOE_ERR_UNSUPPORTED, QMOE_ERR_WORKSPACE, QMOE_ERR_HIP = 0, -1, -2, -3, -4
+
+
+class QMoEError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"[{code}] {msg}")
+        self.code = code
+
+
+class QWeightDesc(ctypes.Structure):
+    _fields_ = [
+        ("w", ctypes.c_void_p),
+        ("scales", ctypes.c_void_p),
+        ("biases", ctypes.c_void_p),
+        ("experts", ctypes.c_int32),
+        ("rows", ctypes.c_int32),
+        ("in_", ctypes.c_int32),
+        ("bits", ctypes.c_int32),
+        ("group", ctypes.c_int32),
+    ]
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_SZ = ctypes.c_size_t
+_QP = ctypes.POINTER(QWeightDesc)
+
+_SIGNATURES = {
+    "qmoe_last_error": (ctypes.c_char_p, []),
+    "moe_route_workspace": (_SZ, [_I, _I, _I]),
+    "moe_route": (ctypes.c_int, [_P, _I, _I, _P, ctypes.c_float, _QP, _P, _P, _I, _P, _P, _P, _P, _SZ, _P]),
+    "moe_sort_workspace": (_SZ, [_I, _I, _I]),
+    "moe_sort": (ctypes.c_int, [_P, _I, _I, _I, _P, _P, _P, _SZ, _P]),
+    "qswitch_gate_up_geglu": (ctypes.c_int, [_P, _I, _I, _QP, _I, _I, _P, _P, _P, _P]),
+    "qswitch_down_combine_workspace": (_SZ, [_I, _I, _I, _I]),
+    "qswitch_down_combine": (ctypes.c_int, [_P, _I, _I, _I, _QP, _I, _P, _P, _P, _P, _P, _SZ, _I, _P]),
+    "qlinear": (ctypes.c_int, [_P, _I, _QP, _P, _P]),
+}
+
+_lib = None
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def lib():
+    """The loaded libqmoe.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                               "or python -m bit_quantized_moe_diffrouter_amd.build")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(rc: int):
+    if rc != QMOE_OK:
+        raise QMoEError(rc, lib().qmoe_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, elem: int, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if t.element_size() != elem:
+        raise ValueError(f"{name}: element size {t.element_size()}, expected {elem}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+@dataclass
+class QuantWeight:
+    """Device-resident 4-bit weight: codes uint32 ``[E?, rows, in/8]``, bf16
+    scales and biases ``[E?, rows, in/64]`` (as torch.uint16 or torch.bfloat16)."""
+
+    w: torch.Tensor
+    scales: torch.Tensor
+    biases: torch.Tensor
+
+    @property
+    def experts(self) -> int:
+        return 1 if self.w.dim() == 2 else int(self.w.shape[0])
+
+    @property
+    def rows(self) -> int:
+        return int(self.w.shape[-2])
+
+    @property
+    def in_features(self) -> int:
+        return int(self.w.shape[-1]) * 8
+
+    def desc(self) -> QWeightDesc:
+        _need(self.w, "weight codes", 4)
+        _need(self.scales, "weight scales", 2)
+        _need(self.biases, "weight biases", 2)
+        g = self.in_features // 64
+        lead = tuple(self.w.shape[:-1])
+        if tuple(self.scales.shape) != lead + (g,) or tuple(self.biases.shape) != lead + (g,):
+            raise ValueError("scales/biases shape does not match the codes")
+        return QWeightDesc(self.w.data_ptr(), self.scales.data_ptr(), self.biases.data_ptr(),
+                           self.experts, self.rows, self.in_features, 4, 64)
+
+    @classmethod
+    def from_numpy(cls, w, scales, biases, device="cuda") -> "QuantWeight":
+        return cls(torch.from_numpy(w).to(device), torch.from_numpy(scales).to(device),
+                   torch.from_numpy(biases).to(device))
+
+
+def moe_route_workspace(T: int, H: int, E: int) -> int:
+    return int(lib().moe_route_workspace(T, H, E))
+
+
+def moe_route(x_router: torch.Tensor, norm_scale: torch.Tensor, eps: float, proj: QuantWeight,
+              per_expert_scale: torch.Tensor, k: int, logit_bias: Optional[torch.Tensor] = None,
+              logits_out: Optional[torch.Tensor] = None, indices: Optional[torch.Tensor] = None,
+              weights: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None
+              ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """DiffRouter: returns (indices int32 [T, k], weights fp32 [T, k])."""
+    T, H = x_router.shape
+    E = proj.rows
+    dev = x_router.device
+    _need(x_router, "x_router", 2)
+    if indices is None:
+        indices = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if weights is None:
+        weights = torch.empty((T, k), dtype=torch.float32, device=dev)
+    need = moe_route_workspace(T, H, E)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    d = proj.desc()
+    _check(lib().moe_route(_ptr(x_router), T, H, _ptr(norm_scale), float(eps), ctypes.byref(d),
+                           _ptr(per_expert_scale), _ptr(logit_bias), k, _ptr(indices), _ptr(weights),
+                           _ptr(logits_out), _ptr(workspace), ws_bytes, _stream()))
+    return indices, weights
+
+
+def moe_sort(indices: torch.Tensor, E: int, expert_offsets: Optional[torch.Tensor] = None,
+             sorted_assign: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Token-by-expert sort: returns (expert_offsets int32 [E+1], sorted_assign int32 [T*k])."""
+    T, k = indices.shape
+    _need(indices, "indices", 4)
+    dev = indices.device
+    if expert_offsets is None:
+        expert_offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    if sorted_assign is None:
+        sorted_assign = torch.empty(T * k, dtype=torch.int32, device=dev)
+    _check(lib().moe_sort(_ptr(indices), T, k, E, _ptr(expert_offsets), _ptr(sorted_assign), None, 0,
+                          _stream()))
+    return expert_offsets, sorted_assign
+
+
+def qswitch_gate_up_geglu(x_expert: torch.Tensor, gate_up: QuantWeight, I: int, k: int,
+                          expert_offsets: torch.Tensor, sorted_assign: torch.Tensor,
+                          mid: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """gate_up switch linear + split + GeGLU: returns mid bf16 [T*k, I] (sorted-row order)."""
+    T, H = x_expert.shape
+    _need(x_expert, "x_expert", 2)
+    if mid is None:
+        mid = torch.empty((T * k, I), dtype=torch.bfloat16, device=x_expert.device)
+    d = gate_up.desc()
+    _check(lib().qswitch_gate_up_geglu(_ptr(x_expert), T, H, ctypes.byref(d), I, k, _ptr(expert_offsets),
+                                       _ptr(sorted_assign), _ptr(mid), _stream()))
+    return mid
+
+
+def qswitch_down_combine_workspace(T: int, k: int, H: int, deterministic: int = 1) -> int:
+    return int(lib().qswitch_down_combine_workspace(T, k, H, deterministic))
+
+
+def qswitch_down_combine(mid: torch.Tensor, T: int, k: int, down: QuantWeight, weights: torch.Tensor,
+                         expert_offsets: torch.Tensor, sorted_assign: torch.Tensor,
+                         y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                         deterministic: int = 1) -> torch.Tensor:
+    """down switch linear + weighted sum over k: returns y bf16 [T, H]."""
+    I = int(mid.shape[1])
+    H = down.rows
+    dev = mid.device
+    if y is None:
+        y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    need = qswitch_down_combine_workspace(T, k, H, deterministic)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    d = down.desc()
+    _check(lib().qswitch_down_combine(_ptr(mid), T, k, I, ctypes.byref(d), H, _ptr(expert_offsets),
+                                      _ptr(sorted_assign), _ptr(weights), _ptr(y), _ptr(workspace), ws_bytes,
+                                      int(deterministic), _stream()))
+    return y
+
+
+def qlinear(x: torch.Tensor, W: QuantWeight, y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Dense 4-bit linear y = x . dequant(W)^T: returns bf16 [M, N]."""
+    M = int(x.shape[0])
+    _need(x, "x", 2)
+    if y is None:
+        y = torch.empty((M, W.rows), dtype=torch.bfloat16, device=x.device)
+    d = W.desc()
+    _check(lib().qlinear(_ptr(x), M, ctypes.byref(d), _ptr(y), _stream()))
+    return y
+
+
+@dataclass
+class MoEParams:
+    """Device-resident weights of one MoE layer."""
+
+    norm_scale: torch.Tensor           # bf16 [H]
+    router: QuantWeight                # [E, H/8]
+    per_expert_scale: torch.Tensor     # bf16 [E]
+    gate_up: QuantWeight               # [E, 2I, H/8]
+    down: QuantWeight                  # [E, H, I/8]
+    logit_bias: Optional[torch.Tensor] = None  # fp32 [E]
+
+    @property
+    def E(self) -> int:
+        return self.router.rows
+
+    @property
+    def I(self) -> int:
+        return self.gate_up.rows // 2
+
+
+def moe_layer(x_router: torch.Tensor, x_expert: torch.Tensor, p: MoEParams, k: int, eps: float,
+              deterministic: int = 1):
+    """The four calls in order.  Returns (y, indices, weights, offsets, sorted_assign, mid)."""
+    idx, w = moe_route(x_router, p.norm_scale, eps, p.router, p.per_expert_scale, k, p.logit_bias)
+    off, sa = moe_sort(idx, p.E)
+    mid = qswitch_gate_up_geglu(x_expert, p.gate_up, p.I, k, off, sa)
+    y = qswitch_down_combine(mid, x_expert.shape[0], k, p.down, w, off, sa, deterministic=deterministic)
+    return y, idx, w, off, sa, mid

@@ -1,0 +1,280 @@
+// C ABI of the 4-bit MoE layer: host-side validation, workspace sizing and
+// kernel launches.  Every argument is checked before anything is enqueued,
+// so a call that returns an error has done nothing on the device.
+#include <hip/hip_runtime_api.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/qmoe.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return QMOE_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+#define REQUIRE(cond, code, ...) \
+  do {                           \
+    if (!(cond)) return fail(code, __VA_ARGS__); \
+  } while (0)
+
+#define REQUIRE_PTR(p, align, name)                                                  \
+  do {                                                                                \
+    if ((p) == nullptr) return fail(QMOE_ERR_INVALID, "%s: null pointer", name);     \
+    if (!aligned((p), (align)))                                                       \
+      return fail(QMOE_ERR_INVALID, "%s: not %d-byte aligned", name, (int)(align));   \
+  } while (0)
+
+// Checks a quantized weight descriptor against the expected shape.
+int check_qweight(const qmoe_qweight* q, const char* what, int experts, int rows, int in) {
+  REQUIRE(q != nullptr, QMOE_ERR_INVALID, "%s: null weight descriptor", what);
+  REQUIRE(q->bits == 4, QMOE_ERR_UNSUPPORTED, "%s: bits=%d, only 4-bit weights are supported", what, q->bits);
+  REQUIRE(q->group == 64, QMOE_ERR_UNSUPPORTED, "%s: group=%d, only group size 64 is supported", what, q->group);
+  REQUIRE(q->experts == experts, QMOE_ERR_INVALID, "%s: experts=%d, expected %d", what, q->experts, experts);
+  REQUIRE(q->rows == rows, QMOE_ERR_INVALID, "%s: rows=%d, expected %d", what, q->rows, rows);
+  REQUIRE(q->in == in, QMOE_ERR_INVALID, "%s: in=%d, expected %d", what, q->in, in);
+  REQUIRE_PTR(q->w, 16, "weight codes");
+  REQUIRE_PTR(q->scales, 2, "weight scales");
+  REQUIRE_PTR(q->biases, 2, "weight biases");
+  return QMOE_OK;
+}
+
+// Number of compute units of the current device, cached per device.
+int num_cu_current(int* out) {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(QMOE_ERR_HIP, "hipGetDevice failed");
+  if (dev >= 0 && dev < 64) {
+    int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) {
+      *out = v;
+      return QMOE_OK;
+    }
+  }
+  int n = 0;
+  hipError_t err = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+  if (err != hipSuccess || n <= 0) return fail(QMOE_ERR_HIP, "querying the CU count failed: %s", hipGetErrorString(err));
+  if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  *out = n;
+  return QMOE_OK;
+}
+
+int launched(hipError_t err, const char* what) {
+  if (err != hipSuccess) return fail(QMOE_ERR_HIP, "%s: kernel launch failed: %s", what, hipGetErrorString(err));
+  return ok();
+}
+
+constexpr long long kMaxAssign = 1LL << 24;
+
+}  // namespace
+
+extern "C" {
+
+const char* qmoe_last_error(void) { return g_last_error.c_str(); }
+
+size_t moe_route_workspace(int32_t T, int32_t H, int32_t E) {
+  if (T <= 0 || H <= 0 || E <= 0 || H % 64 != 0) return 0;
+  return (size_t)qmoe::route_ksplit(T, H) * (size_t)T * (size_t)E * sizeof(float);
+}
+
+int moe_route(const uint16_t* x_router, int32_t T, int32_t H, const uint16_t* norm_scale, float eps,
+              const qmoe_qweight* proj, const uint16_t* per_expert_scale, const float* logit_bias, int32_t k,
+              int32_t* indices, float* weights, float* logits_out, void* workspace, size_t ws_bytes,
+              hipStream_t stream) {
+  REQUIRE(T >= 0, QMOE_ERR_INVALID, "moe_route: T=%d < 0", T);
+  REQUIRE(H > 0 && H % 64 == 0, QMOE_ERR_INVALID, "moe_route: H=%d must be a positive multiple of 64", H);
+  REQUIRE(proj != nullptr, QMOE_ERR_INVALID, "moe_route: null router weight descriptor");
+  const int E = proj->rows;
+  REQUIRE(E >= 1 && E <= 256, QMOE_ERR_UNSUPPORTED, "moe_route: E=%d outside [1, 256]", E);
+  REQUIRE(k >= 1 && k <= E && k <= 16, QMOE_ERR_UNSUPPORTED, "moe_route: k=%d outside [1, min(E, 16)]", k);
+  REQUIRE((long long)T * k <= kMaxAssign, QMOE_ERR_UNSUPPORTED, "moe_route: T*k above 2^24");
+  REQUIRE(std::isfinite(eps) && eps >= 0.f, QMOE_ERR_INVALID, "moe_route: eps must be finite and >= 0");
+  if (T == 0) return ok();
+  if (int rc = check_qweight(proj, "moe_route proj", 1, E, H)) return rc;
+  REQUIRE_PTR(x_router, 16, "moe_route x_router");
+  REQUIRE_PTR(norm_scale, 16, "moe_route norm_scale");
+  REQUIRE_PTR(per_expert_scale, 2, "moe_route per_expert_scale");
+  if (logit_bias) REQUIRE_PTR(logit_bias, 4, "moe_route logit_bias");
+  REQUIRE_PTR(indices, 4, "moe_route indices");
+  REQUIRE_PTR(weights, 4, "moe_route weights");
+  if (logits_out) REQUIRE_PTR(logits_out, 4, "moe_route logits_out");
+  const size_t need = moe_route_workspace(T, H, E);
+  REQUIRE(workspace != nullptr && ws_bytes >= need, QMOE_ERR_WORKSPACE,
+          "moe_route: workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : (size_t)0);
+  REQUIRE(aligned(workspace, 4), QMOE_ERR_INVALID, "moe_route: workspace not 4-byte aligned");
+
+  qmoe::RouteArgs a{};
+  a.x = x_router;
+  a.norm_scale = norm_scale;
+  a.w = proj->w;
+  a.s = proj->scales;
+  a.b = proj->biases;
+  a.pes = per_expert_scale;
+  a.logit_bias = logit_bias;
+  a.part = static_cast<float*>(workspace);
+  a.indices = indices;
+  a.weights = weights;
+  a.logits_out = logits_out;
+  a.eps = eps;
+  a.root = (float)std::pow((double)H, -0.5);
+  a.T = T;
+  a.H = H;
+  a.E = E;
+  a.k = k;
+  a.ksplit = qmoe::route_ksplit(T, H);
+  return launched(qmoe::launch_route(a, stream), "moe_route");
+}
+
+size_t moe_sort_workspace(int32_t, int32_t, int32_t) { return 0; }
+
+int moe_sort(const int32_t* indices, int32_t T, int32_t k, int32_t E, int32_t* expert_offsets,
+             int32_t* sorted_assign, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  (void)workspace;
+  (void)ws_bytes;
+  REQUIRE(T >= 0, QMOE_ERR_INVALID, "moe_sort: T=%d < 0", T);
+  REQUIRE(k >= 1, QMOE_ERR_INVALID, "moe_sort: k=%d < 1", k);
+  REQUIRE(E >= 1 && E <= 256, QMOE_ERR_UNSUPPORTED, "moe_sort: E=%d outside [1, 256]", E);
+  REQUIRE((long long)T * k <= kMaxAssign, QMOE_ERR_UNSUPPORTED, "moe_sort: T*k above 2^24");
+  if (T == 0) return ok();
+  REQUIRE_PTR(indices, 4, "moe_sort indices");
+  REQUIRE_PTR(expert_offsets, 4, "moe_sort expert_offsets");
+  REQUIRE_PTR(sorted_assign, 4, "moe_sort sorted_assign");
+  return launched(qmoe::launch_sort(indices, T * k, E, expert_offsets, sorted_assign, stream), "moe_sort");
+}
+
+int qswitch_gate_up_geglu(const uint16_t* x_expert, int32_t T, int32_t H, const qmoe_qweight* gate_up, int32_t I,
+                          int32_t k, const int32_t* expert_offsets, const int32_t* sorted_assign, uint16_t* mid,
+                          hipStream_t stream) {
+  REQUIRE(T >= 0, QMOE_ERR_INVALID, "qswitch_gate_up_geglu: T=%d < 0", T);
+  REQUIRE(H > 0 && H % 64 == 0, QMOE_ERR_INVALID, "qswitch_gate_up_geglu: H=%d must be a positive multiple of 64", H);
+  REQUIRE(I > 0 && I % 64 == 0, QMOE_ERR_INVALID, "qswitch_gate_up_geglu: I=%d must be a positive multiple of 64", I);
+  REQUIRE(k >= 1 && k <= 16, QMOE_ERR_UNSUPPORTED, "qswitch_gate_up_geglu: k=%d outside [1, 16]", k);
+  REQUIRE((long long)T * k <= kMaxAssign, QMOE_ERR_UNSUPPORTED, "qswitch_gate_up_geglu: T*k above 2^24");
+  REQUIRE(gate_up != nullptr, QMOE_ERR_INVALID, "qswitch_gate_up_geglu: null weight descriptor");
+  const int E = gate_up->experts;
+  REQUIRE(E >= 1 && E <= 256, QMOE_ERR_UNSUPPORTED, "qswitch_gate_up_geglu: E=%d outside [1, 256]", E);
+  if (T == 0) return ok();
+  if (int rc = check_qweight(gate_up, "qswitch_gate_up_geglu gate_up", E, 2 * I, H)) return rc;
+  REQUIRE_PTR(x_expert, 16, "qswitch_gate_up_geglu x_expert");
+  REQUIRE_PTR(expert_offsets, 4, "qswitch_gate_up_geglu expert_offsets");
+  REQUIRE_PTR(sorted_assign, 4, "qswitch_gate_up_geglu sorted_assign");
+  REQUIRE_PTR(mid, 16, "qswitch_gate_up_geglu mid");
+  int ncu = 0;
+  if (int rc = num_cu_current(&ncu)) return rc;
+  qmoe::SwitchArgs a{};
+  a.a = x_expert;
+  a.w = gate_up->w;
+  a.s = gate_up->scales;
+  a.b = gate_up->biases;
+  a.offsets = expert_offsets;
+  a.assign = sorted_assign;
+  a.out = mid;
+  a.K = H;
+  a.Nw = 2 * I;
+  a.Nout = I;
+  a.E = E;
+  a.ktop = k;
+  a.rows_total = T * k;
+  return launched(qmoe::launch_gate_up_geglu(a, ncu, stream), "qswitch_gate_up_geglu");
+}
+
+size_t qswitch_down_combine_workspace(int32_t T, int32_t k, int32_t H, int32_t deterministic) {
+  (void)deterministic;
+  if (T <= 0 || k <= 0 || H <= 0) return 0;
+  return (size_t)T * (size_t)k * (size_t)H * sizeof(float);
+}
+
+int qswitch_down_combine(const uint16_t* mid, int32_t T, int32_t k, int32_t I, const qmoe_qweight* down, int32_t H,
+                         const int32_t* expert_offsets, const int32_t* sorted_assign, const float* weights,
+                         uint16_t* y, void* workspace, size_t ws_bytes, int32_t deterministic, hipStream_t stream) {
+  REQUIRE(T >= 0, QMOE_ERR_INVALID, "qswitch_down_combine: T=%d < 0", T);
+  REQUIRE(H > 0 && H % 64 == 0, QMOE_ERR_INVALID, "qswitch_down_combine: H=%d must be a positive multiple of 64", H);
+  REQUIRE(I > 0 && I % 64 == 0, QMOE_ERR_INVALID, "qswitch_down_combine: I=%d must be a positive multiple of 64", I);
+  REQUIRE(k >= 1 && k <= 16, QMOE_ERR_UNSUPPORTED, "qswitch_down_combine: k=%d outside [1, 16]", k);
+  REQUIRE((long long)T * k <= kMaxAssign, QMOE_ERR_UNSUPPORTED, "qswitch_down_combine: T*k above 2^24");
+  REQUIRE(down != nullptr, QMOE_ERR_INVALID, "qswitch_down_combine: null weight descriptor");
+  const int E = down->experts;
+  REQUIRE(E >= 1 && E <= 256, QMOE_ERR_UNSUPPORTED, "qswitch_down_combine: E=%d outside [1, 256]", E);
+  if (T == 0) return ok();
+  if (int rc = check_qweight(down, "qswitch_down_combine down", E, H, I)) return rc;
+  REQUIRE_PTR(mid, 16, "qswitch_down_combine mid");
+  REQUIRE_PTR(expert_offsets, 4, "qswitch_down_combine expert_offsets");
+  REQUIRE_PTR(sorted_assign, 4, "qswitch_down_combine sorted_assign");
+  REQUIRE_PTR(weights, 4, "qswitch_down_combine weights");
+  REQUIRE_PTR(y, 16, "qswitch_down_combine y");
+  const size_t need = qswitch_down_combine_workspace(T, k, H, deterministic);
+  REQUIRE(workspace != nullptr && ws_bytes >= need, QMOE_ERR_WORKSPACE,
+          "qswitch_down_combine: workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : (size_t)0);
+  REQUIRE(aligned(workspace, 16), QMOE_ERR_INVALID, "qswitch_down_combine: workspace not 16-byte aligned");
+  int ncu = 0;
+  if (int rc = num_cu_current(&ncu)) return rc;
+  qmoe::SwitchArgs a{};
+  a.a = mid;
+  a.w = down->w;
+  a.s = down->scales;
+  a.b = down->biases;
+  a.offsets = expert_offsets;
+  a.assign = sorted_assign;
+  a.route_w = weights;
+  a.out = workspace;
+  a.K = I;
+  a.Nw = H;
+  a.Nout = H;
+  a.E = E;
+  a.ktop = k;
+  a.rows_total = T * k;
+  hipError_t err = qmoe::launch_down(a, ncu, stream);
+  if (err != hipSuccess) return launched(err, "qswitch_down_combine (down)");
+  return launched(qmoe::launch_combine(static_cast<const float*>(workspace), T, k, H, y, stream),
+                  "qswitch_down_combine (combine)");
+}
+
+int qlinear(const uint16_t* x, int32_t M, const qmoe_qweight* W, uint16_t* y, hipStream_t stream) {
+  REQUIRE(M >= 0, QMOE_ERR_INVALID, "qlinear: M=%d < 0", M);
+  REQUIRE(W != nullptr, QMOE_ERR_INVALID, "qlinear: null weight descriptor");
+  const int N = W->rows, K = W->in;
+  REQUIRE(K > 0 && K % 64 == 0, QMOE_ERR_INVALID, "qlinear: K=%d must be a positive multiple of 64", K);
+  REQUIRE(N > 0 && N % 16 == 0, QMOE_ERR_INVALID, "qlinear: N=%d must be a positive multiple of 16", N);
+  if (M == 0) return ok();
+  if (int rc = check_qweight(W, "qlinear W", 1, N, K)) return rc;
+  REQUIRE_PTR(x, 16, "qlinear x");
+  REQUIRE_PTR(y, 16, "qlinear y");
+  int ncu = 0;
+  if (int rc = num_cu_current(&ncu)) return rc;
+  qmoe::SwitchArgs a{};
+  a.a = x;
+  a.w = W->w;
+  a.s = W->scales;
+  a.b = W->biases;
+  a.out = y;
+  a.K = K;
+  a.Nw = N;
+  a.Nout = N;
+  a.E = 1;
+  a.ktop = 1;
+  a.rows_total = M;
+  return launched(qmoe::launch_dense(a, ncu, stream), "qlinear");
+}
+
+}  // extern "C"

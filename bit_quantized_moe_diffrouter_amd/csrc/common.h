@@ -1,0 +1,119 @@
+// Device helpers shared by the gfx950 kernels of the 4-bit MoE layer.
+//
+// Packed-code convention (the reading used across the library): code c of a
+// weight row lives in uint32 word c/8, bits 4*(c%8)..4*(c%8)+3.  A group is 64
+// codes (8 words) sharing one bf16 scale and one bf16 bias; the weight value
+// is scale*q + bias.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qmoe {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kGroup = 64;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
+__device__ __forceinline__ float bf16_lo_f32(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi_f32(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+
+// Two fp32 -> one dword of two bf16 (round to nearest even; v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2_t r = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, r);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float v) {
+  return __builtin_bit_cast(uint16_t, (__bf16)v);
+}
+
+// One packed word (codes n0..n7) -> four dwords of bf16 pairs holding 128+q
+// exactly: 0x4300 | q is the bf16 pattern of 128 + q for q < 128.  The pairs
+// come out as (n0,n4) (n1,n5) (n2,n6) (n3,n7): the activation operand is
+// stored in the same order (see permute_pairs), so the contraction is over
+// the same set of k.
+__device__ __forceinline__ u32x4_t unpack_offset_codes(uint32_t w) {
+  const uint32_t M = 0x000F000Fu, C = 0x43004300u;
+  u32x4_t r;
+  r.x = (w & M) | C;
+  r.y = ((w >> 4) & M) | C;
+  r.z = ((w >> 8) & M) | C;
+  r.w = ((w >> 12) & M) | C;
+  return r;
+}
+
+// Same as unpack_offset_codes but with the smallest offset a bf16 bit trick
+// allows for unit steps: 0x4180 | (q << 3) is the bf16 pattern of 16 + q.
+// The smaller offset keeps the MFMA partial sums small, so the fp32 rounding
+// left after the affine correction is about 8x smaller (one more op per word).
+__device__ __forceinline__ u32x4_t unpack_offset16_codes(uint32_t w) {
+  const uint32_t M = 0x00780078u, C = 0x41804180u;
+  u32x4_t r;
+  r.x = ((w << 3) & M) | C;
+  r.y = ((w >> 1) & M) | C;
+  r.z = ((w >> 5) & M) | C;
+  r.w = ((w >> 9) & M) | C;
+  return r;
+}
+
+// Eight consecutive bf16 (x0..x7 as pairs (x0,x1)(x2,x3)(x4,x5)(x6,x7)) ->
+// the order (x0,x4)(x1,x5)(x2,x6)(x3,x7) that matches unpack_offset_codes.
+__device__ __forceinline__ u32x4_t permute_pairs(u32x4_t v) {
+  u32x4_t o;
+  o.x = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);
+  o.y = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u);
+  o.z = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);
+  o.w = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);
+  return o;
+}
+
+// D = A(16x32 bf16) * B(32x16 bf16) + C, fp32 accumulate.  Lane l holds row
+// (l%16) of A and column (l%16) of B over the k-slice of lane group l/16; the
+// result holds column l%16, rows 4*(l/16)+0..3.
+__device__ __forceinline__ f32x4_t mfma16x16x32(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4_t zero4() { return f32x4_t{0.f, 0.f, 0.f, 0.f}; }
+
+// tanh-form GELU, written as z * sigmoid(2a), a = sqrt(2/pi) (z + 0.044715 z^3)
+// (0.5 (1 + tanh a) == 1 / (1 + exp(-2a))).
+__device__ __forceinline__ float gelu_tanh(float z) {
+  const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
+  const float a = k0 * (z + 0.044715f * z * z * z);
+  return z / (1.0f + __expf(-2.0f * a));
+}
+
+__device__ __forceinline__ int wave_lane() { return threadIdx.x & 63; }
+
+// Inclusive scan of one int per thread over a workgroup of NT threads
+// (NT a multiple of 64, at most 1024).  `scratch` holds NT/64 ints.  Ends with
+// a barrier; every thread gets its inclusive prefix and the total.
+template <int NT>
+__device__ __forceinline__ int block_inclusive_scan(int v, int* scratch, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    int o = __shfl_up(v, d, 64);
+    if (lane >= d) v += o;
+  }
+  if (lane == 63) scratch[wave] = v;
+  __syncthreads();
+  int before = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    int s = scratch[w];
+    before += (w < wave) ? s : 0;
+    tot += s;
+  }
+  __syncthreads();
+  *total = tot;
+  return v + before;
+}
+
+}  // namespace qmoe

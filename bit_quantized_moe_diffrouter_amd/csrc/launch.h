@@ -1,0 +1,57 @@
+// Internal kernel-launch interface between the C ABI (abi.cpp) and the
+// kernel translation units.  Not installed; not part of the public ABI.
+#pragma once
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qmoe {
+
+// ---------------------------------------------------------------- router
+struct RouteArgs {
+  const uint16_t* x;          // bf16 [T, H]
+  const uint16_t* norm_scale; // bf16 [H]
+  const uint32_t* w;          // router codes [E, H/8]
+  const uint16_t* s;          // router scales [E, H/64]
+  const uint16_t* b;          // router biases [E, H/64]
+  const uint16_t* pes;        // bf16 [E]
+  const float* logit_bias;    // fp32 [E] or null
+  float* part;                // fp32 [ksplit, T, E] partial logits (workspace)
+  int32_t* indices;           // [T, k]
+  float* weights;             // [T, k]
+  float* logits_out;          // [T, E] or null
+  float eps;
+  float root;                 // H^-0.5 rounded to fp32
+  int T, H, E, k, ksplit;
+};
+int route_ksplit(int T, int H);
+hipError_t launch_route(const RouteArgs& a, hipStream_t stream);
+
+// ---------------------------------------------------------------- sort
+hipError_t launch_sort(const int32_t* indices, int A, int E, int32_t* offsets, int32_t* sorted_assign,
+                       hipStream_t stream);
+
+// ---------------------------------------------------------------- switch / dense linears
+struct SwitchArgs {
+  const uint16_t* a;       // bf16 activation rows, row length K
+  const uint32_t* w;       // codes [E, Nw, K/8]
+  const uint16_t* s;       // bf16 scales [E, Nw, K/64]
+  const uint16_t* b;       // bf16 biases [E, Nw, K/64]
+  const int32_t* offsets;  // [E+1] sorted-row segments (switch modes)
+  const int32_t* assign;   // [A] assignment id of each sorted row (switch modes)
+  const float* route_w;    // [A] routing weight of each assignment (down mode)
+  void* out;
+  int K;           // contraction length (multiple of 64)
+  int Nw;          // weight rows per expert
+  int Nout;        // output columns
+  int E;           // experts (1 for dense)
+  int ktop;        // assignments per token
+  int rows_total;  // dense: M; switch: A = T*k
+  int ntiles;      // column tiles per row chunk (set by the launcher)
+};
+hipError_t launch_gate_up_geglu(SwitchArgs a, int num_cu, hipStream_t stream);
+hipError_t launch_down(SwitchArgs a, int num_cu, hipStream_t stream);
+hipError_t launch_dense(SwitchArgs a, int num_cu, hipStream_t stream);
+hipError_t launch_combine(const float* D, int T, int k, int H, uint16_t* y, hipStream_t stream);
+
+}  // namespace qmoe

@@ -1,0 +1,295 @@
+// DiffRouter for gfx950 (diffusion-gemma model.ts page, DiffRouter.forward;
+// the no-scale norm is vision.ts page, manualRms with a null weight):
+//   r = x / sqrt(mean(x^2) + eps);  u = r * scale * H^-0.5
+//   logits = u . dequant(W_r)^T (+ offset);  top-k (descending, ties to the
+//   lower expert);  precise softmax over the k;  times per_expert_scale.
+//
+// The top-k decision is taken on fp32 logits.  Kernel 1 computes them with
+// MFMA: u is split into three bf16 terms (u = hi + mid + lo to 24 bits), the
+// router codes are unpacked to the exact bf16 values 16 + q, and the group
+// affine is applied in fp32 (s P + (b - 16 s) U, U = sum of u over the
+// group).  A (token tile, k-range) grid fills the chip at 256 tokens; the
+// partial logits go to a workspace and kernel 2 sums them in a fixed order,
+// so the result is run-to-run reproducible.  Kernel 2 runs one wave per
+// token: k rounds of a wave-wide arg-max, then the softmax in fp32.
+#include <math.h>
+
+#include "common.h"
+#include "launch.h"
+
+namespace qmoe {
+
+namespace {
+constexpr int kRWaves = 8, kRThreads = kRWaves * 64;
+constexpr int kTT = 16;              // tokens per workgroup
+constexpr int kRKS = 4;              // groups per LDS stage
+constexpr int kRRowB = kRKS * 128 + 16;
+}  // namespace
+
+int route_ksplit(int T, int H) {
+  const int G = H / kGroup;
+  const int tiles = (T + kTT - 1) / kTT;
+  int ks = 256 / (tiles > 0 ? tiles : 1);
+  if (ks < 1) ks = 1;
+  if (ks > G) ks = G;
+  return ks;
+}
+
+template <int NPW>
+__global__ __launch_bounds__(kRThreads) void route_logits_kernel(const RouteArgs p) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds_u[3][kTT * kRRowB];
+  __shared__ float s_U[kRKS][kTT];
+  __shared__ float s_rs[kTT];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ln = lane & 15, lq = lane >> 4;
+  const int T = p.T, H = p.H, E = p.E, G = H / kGroup, KW = H / 8;
+  const int t0 = blockIdx.x * kTT;
+  const int ks = blockIdx.y;
+  const int g_begin = (int)((long long)ks * G / p.ksplit);
+  const int g_end = (int)((long long)(ks + 1) * G / p.ksplit);
+
+  // 1) reciprocal RMS per token (needs the full row)
+  for (int tt = wave; tt < kTT; tt += kRWaves) {
+    const int t = t0 + tt;
+    float ss = 0.f;
+    if (t < T) {
+      const uint16_t* xr = p.x + (size_t)t * H;
+      for (int c = lane; c < H / 8; c += 64) {
+        const u32x4_t v = *(const u32x4_t*)(xr + c * 8);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float a = bf16_lo_f32(v[q]), b = bf16_hi_f32(v[q]);
+          ss = __builtin_fmaf(a, a, ss);
+          ss = __builtin_fmaf(b, b, ss);
+        }
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
+    if (lane == 0) s_rs[tt] = (t < T) ? 1.0f / sqrtf(ss / (float)H + p.eps) : 0.0f;
+  }
+  __syncthreads();
+
+  const int nte = (E + 15) / 16;
+  int e0[NPW];
+  bool act[NPW];
+  const uint32_t* wp[NPW];
+  const uint16_t* sp[NPW];
+  const uint16_t* bp[NPW];
+#pragma unroll
+  for (int j = 0; j < NPW; ++j) {
+    const int nt = wave + kRWaves * j;
+    e0[j] = 16 * nt;
+    const int e = e0[j] + ln;
+    act[j] = nt < nte;
+    const bool rv = act[j] && e < E;
+    const size_t row = rv ? (size_t)e : 0;
+    wp[j] = p.w + row * KW + 2 * lq;
+    sp[j] = p.s + row * G;
+    bp[j] = p.b + row * G;
+  }
+
+  f32x4_t acc[NPW];
+#pragma unroll
+  for (int j = 0; j < NPW; ++j) acc[j] = zero4();
+
+  // staging piece of this thread: token tt, group-in-stage gl, block blk
+  const int s_tt = tid >> 5, s_gl = (tid >> 3) & 3, s_blk = tid & 7;
+  const float rs = s_rs[s_tt];
+
+  for (int gs = g_begin; gs < g_end; gs += kRKS) {
+    // weights of this stage (issued first so their latency hides under the staging)
+    u32x2_t wr[kRKS][NPW];
+    uint32_t sr[kRKS][NPW], br[kRKS][NPW];
+#pragma unroll
+    for (int gl = 0; gl < kRKS; ++gl)
+#pragma unroll
+      for (int j = 0; j < NPW; ++j) {
+        const int g = gs + gl;
+        const bool ok = act[j] && (e0[j] + ln < E) && g < g_end;
+        wr[gl][j] = ok ? *(const u32x2_t*)(wp[j] + g * 8) : u32x2_t{0u, 0u};
+        sr[gl][j] = ok ? (uint32_t)sp[j][g] : 0u;
+        br[gl][j] = ok ? (uint32_t)bp[j][g] : 0u;
+      }
+
+    // u for 16 tokens x 4 groups, split into three bf16 terms
+    {
+      const int t = t0 + s_tt, g = gs + s_gl;
+      float u[8];
+      if (t < T && g < g_end) {
+        const int h = g * kGroup + s_blk * 8;
+        const u32x4_t xv = *(const u32x4_t*)(p.x + (size_t)t * H + h);
+        const u32x4_t nv = *(const u32x4_t*)(p.norm_scale + h);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          u[2 * q] = ((bf16_lo_f32(xv[q]) * rs) * bf16_lo_f32(nv[q])) * p.root;
+          u[2 * q + 1] = ((bf16_hi_f32(xv[q]) * rs) * bf16_hi_f32(nv[q])) * p.root;
+        }
+      } else {
+#pragma unroll
+        for (int v = 0; v < 8; ++v) u[v] = 0.f;
+      }
+      u32x4_t hi, md, lo;
+      float usum = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float a = u[2 * q], b = u[2 * q + 1];
+        usum += a;
+        usum += b;
+        hi[q] = pack_bf16x2(a, b);
+        const float ra = a - bf16_lo_f32(hi[q]), rb = b - bf16_hi_f32(hi[q]);
+        md[q] = pack_bf16x2(ra, rb);
+        lo[q] = pack_bf16x2(ra - bf16_lo_f32(md[q]), rb - bf16_hi_f32(md[q]));
+      }
+      const int off = s_tt * kRRowB + s_gl * 128 + s_blk * 16;
+      *(u32x4_t*)(&lds_u[0][off]) = permute_pairs(hi);
+      *(u32x4_t*)(&lds_u[1][off]) = permute_pairs(md);
+      *(u32x4_t*)(&lds_u[2][off]) = permute_pairs(lo);
+      usum += __shfl_xor(usum, 1, 64);
+      usum += __shfl_xor(usum, 2, 64);
+      usum += __shfl_xor(usum, 4, 64);
+      if (s_blk == 0) s_U[s_gl][s_tt] = usum;
+    }
+    __syncthreads();
+
+#pragma unroll
+    for (int gl = 0; gl < kRKS; ++gl) {
+      if (gs + gl >= g_end) break;
+      u32x4_t a0[3], a1[3];
+#pragma unroll
+      for (int sp3 = 0; sp3 < 3; ++sp3) {
+        const uint8_t* base = &lds_u[sp3][ln * kRRowB + gl * 128 + lq * 32];
+        a0[sp3] = *(const u32x4_t*)base;
+        a1[sp3] = *(const u32x4_t*)(base + 16);
+      }
+      float U[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) U[i] = s_U[gl][4 * lq + i];
+#pragma unroll
+      for (int j = 0; j < NPW; ++j) {
+        if (!act[j]) continue;
+        const u32x4_t b0 = unpack_offset16_codes(wr[gl][j].x);
+        const u32x4_t b1 = unpack_offset16_codes(wr[gl][j].y);
+        const float sc = bf16_bits_to_f32(sr[gl][j]);
+        const float cc = bf16_bits_to_f32(br[gl][j]) - 16.0f * sc;
+        f32x4_t P = zero4();
+#pragma unroll
+        for (int sp3 = 0; sp3 < 3; ++sp3) {
+          P = mfma16x16x32(a0[sp3], b0, P);
+          P = mfma16x16x32(a1[sp3], b1, P);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[j][i] = __builtin_fmaf(cc, U[i], __builtin_fmaf(sc, P[i], acc[j][i]));
+      }
+    }
+    __syncthreads();
+  }
+
+  // partial logits: lane holds expert e0 + ln, tokens t0 + 4 lq + i
+#pragma unroll
+  for (int j = 0; j < NPW; ++j) {
+    const int e = e0[j] + ln;
+    if (!act[j] || e >= E) continue;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = t0 + 4 * lq + i;
+      if (t < T) p.part[((size_t)ks * T + t) * E + e] = acc[j][i];
+    }
+  }
+}
+
+__device__ __forceinline__ bool better(float v, int e, float bv, int be) {
+  return v > bv || (v == bv && e < be);
+}
+
+__global__ __launch_bounds__(256) void route_topk_kernel(const RouteArgs p) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= p.T) return;  // whole wave leaves; no barriers below
+  const int E = p.E, T = p.T;
+
+  float v[4];
+  bool taken[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = lane + 64 * i;
+    v[i] = -INFINITY;
+    taken[i] = true;
+    if (e < E) {
+      float s = 0.f;
+      for (int q = 0; q < p.ksplit; ++q) s += p.part[((size_t)q * T + t) * E + e];
+      if (p.logit_bias) s += p.logit_bias[e];
+      if (p.logits_out) p.logits_out[(size_t)t * E + e] = s;
+      v[i] = (s != s) ? -INFINITY : s;  // NaN never wins
+      taken[i] = false;
+    }
+  }
+
+  float sel_v[16];
+  int sel_e[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    sel_v[j] = 0.f;
+    sel_e[j] = 0;
+    if (j >= p.k) continue;
+    float bv = -INFINITY;
+    int be = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = lane + 64 * i;
+      if (!taken[i] && better(v[i], e, bv, be)) {
+        bv = v[i];
+        be = e;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, 64);
+      const int oe = __shfl_xor(be, o, 64);
+      if (better(ov, oe, bv, be)) {
+        bv = ov;
+        be = oe;
+      }
+    }
+    sel_v[j] = bv;
+    sel_e[j] = be;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (lane + 64 * i == be) taken[i] = true;
+  }
+
+  const float m = sel_v[0];
+  float sum = 0.f, mine_v = 0.f;
+  int mine_e = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    if (j >= p.k) continue;
+    sum += expf(sel_v[j] - m);
+    if (lane == j) {
+      mine_v = sel_v[j];
+      mine_e = sel_e[j];
+    }
+  }
+  if (lane < p.k) {
+    const float pj = expf(mine_v - m) / sum;
+    const float pes = bf16_bits_to_f32(p.pes[mine_e]);
+    p.indices[(size_t)t * p.k + lane] = mine_e;
+    p.weights[(size_t)t * p.k + lane] = pj * pes;
+  }
+}
+
+hipError_t launch_route(const RouteArgs& a, hipStream_t stream) {
+  const int tiles = (a.T + kTT - 1) / kTT;
+  const dim3 grid1(tiles, a.ksplit);
+  if (a.E <= 128)
+    hipLaunchKernelGGL(route_logits_kernel<1>, grid1, dim3(kRThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(route_logits_kernel<2>, grid1, dim3(kRThreads), 0, stream, a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(route_topk_kernel, dim3((a.T + 3) / 4), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace qmoe

@@ -1,0 +1,201 @@
+/*
+ * qmoe.h -- C ABI of the 4-bit group-quantized mixture-of-experts layer for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer is the one of the DiffusionGemma decoder as the
+ * "@mlx-bun/inference 0.0.0-stage -> 1.0.0" diff pages show it
+ * (diffusion-gemma model.ts page: DiffRouter, DiffExperts and
+ * DiffDecoderLayer.forwardWith; vision.ts page: VisionLinear, manualRms,
+ * DiffVisionMLP).  One call per step of the layer:
+ *
+ *   moe_route             router: norm, scale, 4-bit projection, top-k,
+ *                         precise softmax, per_expert_scale
+ *   moe_sort              token-by-expert sort of the routing assignments
+ *   qswitch_gate_up_geglu fused gate_up switch linear, split, GeGLU
+ *   qswitch_down_combine  down switch linear + weighted sum over k per token
+ *   qlinear               dense 4-bit linear
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - All array pointers are DEVICE pointers (memory of the current HIP device),
+ *   except the qmoe_qweight struct itself, which lives in host memory and is
+ *   read during the call only.  Sizes are host integers.
+ * - bf16 values are passed as their uint16_t bit patterns.  All arrays are
+ *   dense and row-major.
+ * - Quantized weights: 4-bit affine codes, group size 64, eight codes per
+ *   uint32 word with code c of a row in bits 4*(c%8)..4*(c%8)+3 of word c/8
+ *   (first code in the lowest bits); scales and biases are bf16, one per
+ *   group; the weight value is scale*q + bias (model.ts page,
+ *   dequantEmbedWeight).
+ * - Alignment: activation, weight-code, mid and output arrays must be 16-byte
+ *   aligned; scales, biases and bf16 vectors 2-byte aligned; int32/fp32
+ *   arrays 4-byte aligned.
+ * - Ownership: the caller allocates and owns every buffer, including
+ *   workspaces; the library allocates no device memory and keeps no pointer
+ *   after a call returns.
+ * - Ordering: every call enqueues its kernels on `stream` and returns
+ *   without waiting.  Arguments are validated on the host before anything is
+ *   enqueued: a call that returns an error has enqueued nothing.  Faults that
+ *   happen inside a kernel surface at the caller's next synchronisation.
+ * - T == 0 (or M == 0) is a no-op that returns QMOE_OK without reading any
+ *   pointer.
+ * - The calls are reentrant; the last error message is per thread.
+ */
+#ifndef QMOE_H
+#define QMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define QMOE_OK 0
+#define QMOE_ERR_INVALID (-1)     /* null pointer, bad size, misalignment        */
+#define QMOE_ERR_UNSUPPORTED (-2) /* bits != 4, group != 64, E > 256, k > 16 ... */
+#define QMOE_ERR_WORKSPACE (-3)   /* workspace missing or too small              */
+#define QMOE_ERR_HIP (-4)         /* a HIP launch or query failed                */
+
+/* A 4-bit group-quantized weight (one dense matrix, or `experts` stacked
+ * matrices for a switch linear).  Layout per matrix: `rows` output rows of
+ * `in` inputs:
+ *   w       uint32 [experts, rows, in/8]
+ *   scales  bf16   [experts, rows, in/64]
+ *   biases  bf16   [experts, rows, in/64]
+ * The struct is host memory; the three arrays are device memory. */
+typedef struct qmoe_qweight {
+  const uint32_t* w;
+  const uint16_t* scales;
+  const uint16_t* biases;
+  int32_t experts; /* 1 for a dense linear */
+  int32_t rows;
+  int32_t in;
+  int32_t bits;  /* must be 4  */
+  int32_t group; /* must be 64 */
+} qmoe_qweight;
+
+/* Text of the last error raised on the calling thread ("" if none).  The
+ * string is owned by the library and valid until the next call on this
+ * thread. */
+const char* qmoe_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * moe_route -- the DiffRouter (model.ts page, DiffRouter.forward; the norm
+ * is the no-scale RMS norm of vision.ts page, manualRms with a null weight):
+ *
+ *   r   = x / sqrt(mean_h(x^2) + eps)          per token
+ *   u   = r * norm_scale[h] * H^-0.5
+ *   l_e = u . dequant(proj)[e] (+ logit_bias[e])          fp32 logits
+ *   indices[t, 0..k)  = the k largest l_e, descending, ties to lower e
+ *   weights[t, j]     = softmax_j(l[indices]) * per_expert_scale[indices[t, j]]
+ *
+ * The router is evaluated in fp32 throughout (no intermediate bf16 rounding).
+ *
+ *   x_router          bf16 [T, H]   the residual stream rows the router sees
+ *   norm_scale        bf16 [H]      per-dimension scale applied after the norm
+ *   eps               norm epsilon (the build uses 1e-6)
+ *   proj              experts = 1, rows = E, in = H
+ *   per_expert_scale  bf16 [E]
+ *   logit_bias        fp32 [E] added to the logits before top-k, or NULL
+ *   k                 1 <= k <= min(E, 16);  E <= 256;  H % 64 == 0
+ *   indices (out)     int32 [T, k]
+ *   weights (out)     fp32  [T, k]
+ *   logits_out (out)  fp32  [T, E] logits incl. logit_bias, or NULL
+ *   workspace         device scratch of at least moe_route_workspace(T, H, E)
+ *                     bytes (NULL allowed when that size is 0)
+ * ---------------------------------------------------------------------- */
+size_t moe_route_workspace(int32_t T, int32_t H, int32_t E);
+int moe_route(const uint16_t* x_router, int32_t T, int32_t H, const uint16_t* norm_scale,
+              float eps, const qmoe_qweight* proj, const uint16_t* per_expert_scale,
+              const float* logit_bias, int32_t k, int32_t* indices, float* weights,
+              float* logits_out, void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * moe_sort -- token-by-expert sort (model.ts page, DiffExperts.forward:
+ * argsort of the flat routing indices).  Assignment a = t*k + j goes to
+ * expert indices[a].
+ *
+ *   indices            int32 [T*k], values in [0, E)
+ *   expert_offsets(out) int32 [E+1]: offsets[e] = number of assignments with
+ *                      an expert below e (offsets[E] = T*k)
+ *   sorted_assign (out) int32 [T*k]: assignment ids grouped by expert,
+ *                      ascending within an expert (stable)
+ *
+ * An index outside [0, E) is dropped: it is counted nowhere and offsets[E]
+ * is then below T*k (the later calls process only offsets[E] rows).
+ * E <= 256; T*k <= 2^24.  No workspace is needed (moe_sort_workspace returns
+ * 0); the arguments are kept so the size can grow without an ABI change.
+ * ---------------------------------------------------------------------- */
+size_t moe_sort_workspace(int32_t T, int32_t k, int32_t E);
+int moe_sort(const int32_t* indices, int32_t T, int32_t k, int32_t E, int32_t* expert_offsets,
+             int32_t* sorted_assign, void* workspace, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * qswitch_gate_up_geglu -- fused gate_up QuantizedSwitchLinear over the
+ * sorted rows, split at moe_intermediate, GeGLU (model.ts page,
+ * DiffExperts.forward: gateUp.forward, split, geglu; the GeGLU is
+ * gelu_approx(gate) * up as in vision.ts page, DiffVisionMLP):
+ *
+ *   for sorted row r in [0, offsets[E]):  a = sorted_assign[r], t = a / k,
+ *   e = the expert whose segment holds r,
+ *   g = x[t] . dequant(gate_up)[e]^T            (2I values, fp32 accumulate)
+ *   mid[r, n] = gelu_tanh(g[n]) * g[I + n]      n < I, stored bf16
+ *
+ *   x_expert        bf16 [T, H]  the (normalised) rows the experts see
+ *   gate_up         experts = E, rows = 2*I, in = H
+ *   I               moe_intermediate, I % 64 == 0
+ *   expert_offsets, sorted_assign   as produced by moe_sort
+ *   mid (out)       bf16 [T*k, I] in sorted-row order (rows beyond
+ *                   offsets[E] are left untouched)
+ * ---------------------------------------------------------------------- */
+int qswitch_gate_up_geglu(const uint16_t* x_expert, int32_t T, int32_t H,
+                          const qmoe_qweight* gate_up, int32_t I, int32_t k,
+                          const int32_t* expert_offsets, const int32_t* sorted_assign,
+                          uint16_t* mid, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * qswitch_down_combine -- down QuantizedSwitchLinear plus the weighted sum
+ * back per token (model.ts page, DiffExperts.forward: down.forward, unsort,
+ * (y * weights[..., None]).sum over k):
+ *
+ *   d_r  = mid[r] . dequant(down)[e]^T                     (fp32)
+ *   y[t] = sum_j weights[t, j] * d_{row of assignment t*k+j}   (fp32, j order)
+ *   y is stored bf16 (round to nearest even).
+ *
+ *   mid             bf16 [T*k, I] sorted-row order (qswitch_gate_up_geglu)
+ *   down            experts = E, rows = H, in = I
+ *   weights         fp32 [T, k] routing weights (moe_route)
+ *   y (out)         bf16 [T, H]; a token none of whose assignments is
+ *                   present (dropped indices) gets the sum of the rest
+ *   workspace       at least qswitch_down_combine_workspace(T, k, H, det)
+ *                   bytes of device scratch
+ *   deterministic   1: per-assignment rows then a fixed-order sum (bitwise
+ *                   reproducible);  0: same path today (reserved for an
+ *                   atomic scatter-sum)
+ * ---------------------------------------------------------------------- */
+size_t qswitch_down_combine_workspace(int32_t T, int32_t k, int32_t H, int32_t deterministic);
+int qswitch_down_combine(const uint16_t* mid, int32_t T, int32_t k, int32_t I,
+                         const qmoe_qweight* down, int32_t H, const int32_t* expert_offsets,
+                         const int32_t* sorted_assign, const float* weights, uint16_t* y,
+                         void* workspace, size_t ws_bytes, int32_t deterministic,
+                         hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * qlinear -- dense 4-bit QuantizedLinear (vision.ts page, VisionLinear.forward,
+ * quantized arm; model.ts page, DiffRouter.proj):  y = x . dequant(W)^T,
+ * fp32 accumulate, bf16 out.
+ *
+ *   x        bf16 [M, K]
+ *   W        experts = 1, rows = N, in = K;  K % 64 == 0, N % 16 == 0
+ *   y (out)  bf16 [M, N]
+ * ---------------------------------------------------------------------- */
+int qlinear(const uint16_t* x, int32_t M, const qmoe_qweight* W, uint16_t* y,
+            hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QMOE_H */

@@ -1,0 +1,134 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every entry point the header declares, sizes its workspaces, and rejects bad
+arguments with the documented codes before anything reaches the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from _util import ensure_built
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qmoe.h")
+
+INVALID, UNSUPPORTED, WORKSPACE = -1, -2, -3
+A16 = 0x100000  # a 16-byte aligned fake device address: validation never dereferences it
+
+
+@pytest.fixture(scope="module")
+def L():
+    return ensure_built()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return re.findall(r"^(?:int|size_t|const char\*)\s+(\w+)\s*\(", text, flags=re.M)
+
+
+def test_exports_every_declared_function(L):
+    names = header_functions()
+    assert set(names) >= {"moe_route", "moe_sort", "qswitch_gate_up_geglu", "qswitch_down_combine",
+                          "qlinear", "qmoe_last_error"}
+    for n in names:
+        assert hasattr(L, n), f"{n} is declared in qmoe.h but not exported"
+
+
+def qw(experts, rows, inp, bits=4, group=64, w=A16, s=A16, b=A16):
+    import bit_quantized_moe_diffrouter_amd as q
+    return q.QWeightDesc(w, s, b, experts, rows, inp, bits, group)
+
+
+def err(L):
+    return L.qmoe_last_error().decode()
+
+
+def route(L, T=16, H=256, E=8, k=2, x=A16, ws=A16, ws_bytes=1 << 30, **kw):
+    d = qw(1, E, H, **kw)
+    return L.moe_route(x, T, H, A16, 1e-6, ctypes.byref(d), A16, None, k, A16, A16, None, ws, ws_bytes, None)
+
+
+def test_route_validation(L):
+    assert route(L, T=0, x=None, ws=None, ws_bytes=0) == 0  # T = 0 is a no-op
+    assert route(L, H=100) == INVALID and "H=100" in err(L)
+    assert route(L, T=-1) == INVALID
+    assert route(L, E=300) == UNSUPPORTED
+    assert route(L, k=0) == UNSUPPORTED
+    assert route(L, k=9, E=8) == UNSUPPORTED
+    assert route(L, k=17, E=64) == UNSUPPORTED
+    assert route(L, bits=8) == UNSUPPORTED and "bits" in err(L)
+    assert route(L, group=32) == UNSUPPORTED
+    assert route(L, x=None) == INVALID and "null" in err(L)
+    assert route(L, x=A16 + 2) == INVALID and "aligned" in err(L)
+    assert route(L, ws_bytes=16) == WORKSPACE
+    assert route(L, ws=None) == WORKSPACE
+    d = qw(1, 8, 128)  # in != H
+    assert L.moe_route(A16, 16, 256, A16, 1e-6, ctypes.byref(d), A16, None, 2, A16, A16, None, A16, 1 << 30,
+                       None) == INVALID
+
+
+def test_sort_validation(L):
+    assert L.moe_sort(None, 0, 2, 8, None, None, None, 0, None) == 0
+    assert L.moe_sort(A16, -1, 2, 8, A16, A16, None, 0, None) == INVALID
+    assert L.moe_sort(A16, 4, 0, 8, A16, A16, None, 0, None) == INVALID
+    assert L.moe_sort(A16, 4, 2, 0, A16, A16, None, 0, None) == UNSUPPORTED
+    assert L.moe_sort(A16, 4, 2, 257, A16, A16, None, 0, None) == UNSUPPORTED
+    assert L.moe_sort(A16, 1 << 22, 8, 8, A16, A16, None, 0, None) == UNSUPPORTED
+    assert L.moe_sort(None, 4, 2, 8, A16, A16, None, 0, None) == INVALID
+    assert L.moe_sort(A16, 4, 2, 8, A16 + 2, A16, None, 0, None) == INVALID
+    assert L.moe_sort_workspace(256, 8, 128) == 0
+
+
+def gate_up(L, T=16, H=256, I=128, k=2, E=8, rows=None, inp=None, mid=A16, **kw):
+    d = qw(E, 2 * I if rows is None else rows, H if inp is None else inp, **kw)
+    return L.qswitch_gate_up_geglu(A16, T, H, ctypes.byref(d), I, k, A16, A16, mid, None)
+
+
+def test_gate_up_validation(L):
+    assert gate_up(L, T=0) == 0
+    assert gate_up(L, I=100) == INVALID
+    assert gate_up(L, H=96) == INVALID
+    assert gate_up(L, k=0) == UNSUPPORTED
+    assert gate_up(L, rows=100) == INVALID
+    assert gate_up(L, inp=512) == INVALID
+    assert gate_up(L, E=0) == UNSUPPORTED
+    assert gate_up(L, group=128) == UNSUPPORTED
+    assert gate_up(L, mid=None) == INVALID
+    assert gate_up(L, mid=A16 + 8) == INVALID
+
+
+def down(L, T=16, H=256, I=128, k=2, E=8, ws=A16, ws_bytes=1 << 30, y=A16, **kw):
+    d = qw(E, H, I, **kw)
+    return L.qswitch_down_combine(A16, T, k, I, ctypes.byref(d), H, A16, A16, A16, y, ws, ws_bytes, 1, None)
+
+
+def test_down_validation(L):
+    assert down(L, T=0, ws=None, ws_bytes=0) == 0
+    assert down(L, H=200) == INVALID
+    assert down(L, I=32) == INVALID
+    assert down(L, ws_bytes=100) == WORKSPACE and "workspace" in err(L)
+    assert down(L, ws=None) == WORKSPACE
+    assert down(L, y=None) == INVALID
+    assert down(L, bits=3) == UNSUPPORTED
+    assert L.qswitch_down_combine_workspace(256, 8, 2816, 1) == 256 * 8 * 2816 * 4
+
+
+def test_qlinear_validation(L):
+    d = qw(1, 1152, 1152)
+    assert L.qlinear(None, 0, ctypes.byref(d), None, None) == 0
+    assert L.qlinear(A16, -5, ctypes.byref(d), A16, None) == INVALID
+    bad = qw(1, 1150, 1152)
+    assert L.qlinear(A16, 8, ctypes.byref(bad), A16, None) == INVALID
+    bad = qw(1, 1152, 1000)
+    assert L.qlinear(A16, 8, ctypes.byref(bad), A16, None) == INVALID
+    bad = qw(2, 1152, 1152)
+    assert L.qlinear(A16, 8, ctypes.byref(bad), A16, None) == INVALID
+    assert L.qlinear(A16, 8, None, A16, None) == INVALID
+
+
+def test_route_workspace_size(L):
+    # 16-token tiles; the k-range split keeps about 256 workgroups busy
+    assert L.moe_route_workspace(256, 2816, 128) == 16 * 256 * 128 * 4
+    assert L.moe_route_workspace(4096, 2816, 128) == 1 * 4096 * 128 * 4
+    assert L.moe_route_workspace(16, 256, 8) == 4 * 16 * 8 * 4
+    assert L.moe_route_workspace(0, 256, 8) == 0

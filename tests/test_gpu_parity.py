@@ -1,0 +1,369 @@
+"""GPU parity: every call of the C ABI against the CPU oracle on the same
+seeded inputs, stage by stage (route, sort, mid, y) and end to end.
+
+Bars: routing indices bit-exact except tokens whose 8th/9th oracle-logit gap
+is below 1e-5 (compared as per-token sets, since equal-valued slots may come
+out in either order); weights within 1e-5; sort bit-exact; float outputs
+within a per-row relative error of 2e-2 (the layer's bound), with tighter
+stage bars where the only difference is the bf16 store."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from _util import bf16_host, dev_params, dev_qweight, dev_tensor, ensure_built, say
+
+pytestmark = pytest.mark.gpu
+
+GAP_EXEMPT = 1e-5
+Y_TOL = 2e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ensure_built()
+    torch.cuda.init()
+
+
+_cache = {}
+
+
+def canvas_weights():
+    if "w" not in _cache:
+        _cache["w"] = synth.make_moe_weights(synth.CANVAS)
+    return _cache["w"]
+
+
+def inputs(cfg):
+    if cfg.name in _cache:
+        return _cache[cfg.name]
+    if cfg.H == 2816:
+        w = canvas_weights()
+        if cfg.zipf_tau is not None:
+            w = synth.MoEWeights(w.norm_scale, w.router, w.per_expert_scale, w.gate_up, w.down,
+                                 synth.zipf_logit_bias(cfg.E, cfg.zipf_tau, cfg.zipf_perm_seed))
+        inp = synth.make_moe_inputs(cfg, w)
+    else:
+        inp = synth.make_moe_inputs(cfg)
+    _cache[cfg.name] = inp
+    return inp
+
+
+def params(cfg):
+    key = ("dev", cfg.name)
+    if key not in _cache:
+        _cache[key] = dev_params(inputs(cfg).weights)
+    return _cache[key]
+
+
+def oracle_route(inp):
+    cfg, wt = inp.cfg, inp.weights
+    r = wt.router
+    return O.route(inp.x, wt.norm_scale, cfg.eps, r.w, r.scales, r.biases, wt.per_expert_scale, cfg.k,
+                   wt.logit_bias)
+
+
+def gpu_route(inp, p, logits=True):
+    import bit_quantized_moe_diffrouter_amd as q
+    cfg = inp.cfg
+    x = dev_tensor(inp.x)
+    lo = torch.empty((cfg.T, cfg.E), dtype=torch.float32, device="cuda") if logits else None
+    idx, w = q.moe_route(x, p.norm_scale, cfg.eps, p.router, p.per_expert_scale, cfg.k, p.logit_bias,
+                         logits_out=lo)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), w.cpu().numpy(), (lo.cpu().numpy() if logits else None)
+
+
+def assert_route_parity(inp, idx_g, w_g, lg_g):
+    cfg = inp.cfg
+    idx_r, w_r, lg_r = oracle_route(inp)
+    np.testing.assert_allclose(lg_g, lg_r, rtol=0, atol=2e-6)
+    gap = O.gap_kth(lg_r, cfg.k)
+    exempt = gap < GAP_EXEMPT
+    for t in np.nonzero(~exempt)[0]:
+        assert set(idx_g[t].tolist()) == set(idx_r[t].tolist()), f"token {t}: {idx_g[t]} vs {idx_r[t]}"
+        wg = dict(zip(idx_g[t].tolist(), w_g[t].tolist()))
+        for e, wr in zip(idx_r[t].tolist(), w_r[t].tolist()):
+            assert abs(wg[e] - wr) <= 1e-5, f"token {t} expert {e}: {wg[e]} vs {wr}"
+    # every row is a valid top-k set of distinct experts, in descending logit order
+    for t in range(cfg.T):
+        assert len(set(idx_g[t].tolist())) == cfg.k
+        assert np.all(np.diff(lg_g[t, idx_g[t]]) <= 0)
+    return int(exempt.sum())
+
+
+MOE_CFGS = [synth.TINY, synth.CANVAS, synth.PREFILL, synth.SKEW]
+
+
+@pytest.mark.parametrize("cfg", MOE_CFGS, ids=lambda c: c.name)
+def test_route_parity(cfg):
+    say(f"[route] {cfg.name}")
+    inp = inputs(cfg)
+    idx_g, w_g, lg_g = gpu_route(inp, params(cfg))
+    n_ex = assert_route_parity(inp, idx_g, w_g, lg_g)
+    say(f"  exempt tokens: {n_ex}")
+
+
+def test_route_weights_sum_to_one_before_per_expert_scale():
+    cfg = synth.CANVAS
+    say(f"[route pes=1] {cfg.name}")
+    inp = inputs(cfg)
+    p = params(cfg)
+    import bit_quantized_moe_diffrouter_amd as q
+    ones = dev_tensor(synth.to_bf16_bits(np.ones(cfg.E, dtype=np.float32)))
+    _, w = q.moe_route(dev_tensor(inp.x), p.norm_scale, cfg.eps, p.router, ones, cfg.k)
+    s = w.double().sum(-1).cpu().numpy()
+    assert np.abs(s - 1.0).max() <= 1e-6
+
+
+@pytest.mark.parametrize("T,H,E,k", [(37, 320, 40, 5), (5, 128, 16, 16), (33, 256, 200, 1), (3, 64, 1, 1)])
+def test_route_ragged_and_degenerate(T, H, E, k):
+    say(f"[route ragged] T={T} H={H} E={E} k={k}")
+    cfg = synth.MoEConfig("ragged", T=T, H=H, E=E, k=k, I=64, seed_w=7, seed_x=8)
+    inp = synth.make_moe_inputs(cfg)
+    idx_g, w_g, lg_g = gpu_route(inp, dev_params(inp.weights))
+    assert_route_parity(inp, idx_g, w_g, lg_g)
+    if k == 1:
+        np.testing.assert_array_equal(idx_g[:, 0], np.argmax(lg_g, axis=1))
+
+
+# ------------------------------------------------------------------------- sort
+def gpu_sort(idx, E):
+    import bit_quantized_moe_diffrouter_amd as q
+    off, sa = q.moe_sort(dev_tensor(idx.astype(np.int32)), E)
+    torch.cuda.synchronize()
+    return off.cpu().numpy(), sa.cpu().numpy()
+
+
+@pytest.mark.parametrize("cfg", MOE_CFGS, ids=lambda c: c.name)
+def test_sort_parity(cfg):
+    say(f"[sort] {cfg.name}")
+    idx_r, _, _ = oracle_route(inputs(cfg))
+    off_g, sa_g = gpu_sort(idx_r, cfg.E)
+    off_r, sa_r = O.sort_assignments(idx_r, cfg.E)
+    np.testing.assert_array_equal(off_g, off_r)
+    np.testing.assert_array_equal(sa_g, sa_r)
+
+
+def test_sort_large_random_and_dropped():
+    say("[sort] random 3000x8 over 256 experts, with out-of-range indices")
+    rng = np.random.default_rng(21)
+    T, k, E = 3000, 8, 256
+    idx = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    off_g, sa_g = gpu_sort(idx, E)
+    off_r, sa_r = O.sort_assignments(idx, E)
+    np.testing.assert_array_equal(off_g, off_r)
+    np.testing.assert_array_equal(sa_g, sa_r)
+    bad = idx.copy()
+    bad[5, 3] = -1
+    bad[17, 0] = E
+    bad[2999, 7] = 1 << 20
+    off_g, sa_g = gpu_sort(bad, E)
+    flat = bad.reshape(-1)
+    valid = (flat >= 0) & (flat < E)
+    ids = np.nonzero(valid)[0]
+    nv = ids.size
+    expect_order = ids[np.argsort(flat[ids], kind="stable")]
+    expect_off = np.concatenate([[0], np.cumsum(np.bincount(flat[ids], minlength=E))])
+    np.testing.assert_array_equal(off_g, expect_off)
+    np.testing.assert_array_equal(sa_g[:nv], expect_order)
+    np.testing.assert_array_equal(sa_g[nv:], np.nonzero(~valid)[0])
+
+
+# ------------------------------------------------------------------ experts
+def sample_tokens(T, n, seed=5):
+    if T <= n:
+        return list(range(T))
+    rng = np.random.default_rng(seed)
+    return sorted(rng.choice(T, size=n, replace=False).tolist())
+
+
+def run_experts(inp, idx, w, deterministic=1):
+    import bit_quantized_moe_diffrouter_amd as q
+    cfg = inp.cfg
+    p = params(cfg)
+    x = dev_tensor(inp.x)
+    idx_d = dev_tensor(idx.astype(np.int32))
+    w_d = dev_tensor(w.astype(np.float32))
+    off, sa = q.moe_sort(idx_d, cfg.E)
+    mid = q.qswitch_gate_up_geglu(x, p.gate_up, cfg.I, cfg.k, off, sa)
+    y = q.qswitch_down_combine(mid, cfg.T, cfg.k, p.down, w_d, off, sa, deterministic=deterministic)
+    torch.cuda.synchronize()
+    return bf16_host(y), bf16_host(mid), sa.cpu().numpy()
+
+
+@pytest.mark.parametrize("cfg", MOE_CFGS, ids=lambda c: c.name)
+def test_gate_up_mid_parity(cfg):
+    say(f"[gate_up mid] {cfg.name}")
+    inp = inputs(cfg)
+    idx_r, w_r, _ = oracle_route(inp)
+    _, mid_g, sa = run_experts(inp, idx_r, w_r)
+    A = cfg.T * cfg.k
+    rows = list(range(A)) if A <= 64 else sample_tokens(A, 48, seed=9)
+    ref = O.expert_mid_bruteforce(inp.x, idx_r, inp.weights.gate_up, cfg.I, [int(sa[r]) for r in rows])
+    err = O.rowwise_rel_err(mid_g[rows], ref)
+    say(f"  mid rel err {err:.3e}")
+    assert err <= 1e-2
+
+
+@pytest.mark.parametrize("cfg", MOE_CFGS, ids=lambda c: c.name)
+def test_down_combine_parity_from_gpu_mid(cfg):
+    """Down + combine checked on its own: the oracle starts from the GPU's
+    bf16 mid, so only the down projection and the sum over k are compared."""
+    say(f"[down+combine] {cfg.name}")
+    inp = inputs(cfg)
+    idx_r, w_r, _ = oracle_route(inp)
+    y_g, mid_g, sa = run_experts(inp, idx_r, w_r)
+    mid_by_assign = np.zeros_like(mid_g)
+    mid_by_assign[sa] = mid_g
+    toks = sample_tokens(cfg.T, 24)
+    ref = O.down_combine_from_mid(mid_by_assign, idx_r, w_r, inp.weights.down, toks)
+    err = O.rowwise_rel_err(y_g[toks], ref)
+    say(f"  y rel err {err:.3e}")
+    assert err <= 1e-2
+
+
+@pytest.mark.parametrize("cfg", MOE_CFGS, ids=lambda c: c.name)
+def test_layer_parity(cfg):
+    """Whole layer through the four calls against the oracle (exempt tokens use
+    the GPU's own routing in the oracle's expert stage)."""
+    import bit_quantized_moe_diffrouter_amd as q
+    say(f"[layer] {cfg.name}")
+    inp = inputs(cfg)
+    p = params(cfg)
+    x = dev_tensor(inp.x)
+    y, idx, w, off, sa, mid = q.moe_layer(x, x, p, cfg.k, cfg.eps)
+    torch.cuda.synchronize()
+    idx_g, w_g = idx.cpu().numpy(), w.cpu().numpy()
+    toks = sample_tokens(cfg.T, 32)
+    ref = O.experts_bruteforce(inp.x, idx_g, w_g, inp.weights.gate_up, inp.weights.down, cfg.I, tokens=toks)
+    err = O.rowwise_rel_err(bf16_host(y)[toks], ref)
+    say(f"  layer rel err {err:.3e} over {len(toks)} tokens")
+    assert err <= Y_TOL
+    # routing of the same run matches the oracle
+    idx_r, _, lg_r = oracle_route(inp)
+    ok = O.gap_kth(lg_r, cfg.k) >= GAP_EXEMPT
+    assert all(set(idx_g[t]) == set(idx_r[t]) for t in np.nonzero(ok)[0])
+
+
+def test_layer_full_canvas_against_grouped_oracle():
+    """All 256 canvas tokens against the fp32 grouped oracle."""
+    import bit_quantized_moe_diffrouter_amd as q
+    cfg = synth.CANVAS
+    say(f"[layer all tokens] {cfg.name}")
+    inp = inputs(cfg)
+    p = params(cfg)
+    x = dev_tensor(inp.x)
+    y, idx, w, *_ = q.moe_layer(x, x, p, cfg.k, cfg.eps)
+    torch.cuda.synchronize()
+    ref = O.experts_grouped(inp.x, idx.cpu().numpy(), w.cpu().numpy(), inp.weights.gate_up,
+                            inp.weights.down, cfg.I)
+    err = O.rowwise_rel_err(bf16_host(y), ref)
+    say(f"  rel err {err:.3e}")
+    assert err <= Y_TOL
+
+
+def test_layer_deterministic_bitwise():
+    import bit_quantized_moe_diffrouter_amd as q
+    cfg = synth.CANVAS
+    say(f"[determinism] {cfg.name}")
+    inp = inputs(cfg)
+    p = params(cfg)
+    x = dev_tensor(inp.x)
+    y1 = q.moe_layer(x, x, p, cfg.k, cfg.eps)[0].clone()
+    y2 = q.moe_layer(x, x, p, cfg.k, cfg.eps)[0].clone()
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.uint16), y2.view(torch.uint16))
+
+
+@pytest.mark.parametrize("T,H,E,k,I", [(1, 64, 1, 1, 64), (37, 192, 12, 3, 192), (9, 256, 8, 8, 64)])
+def test_layer_ragged_and_degenerate(T, H, E, k, I):
+    import bit_quantized_moe_diffrouter_amd as q
+    say(f"[layer ragged] T={T} H={H} E={E} k={k} I={I}")
+    cfg = synth.MoEConfig("ragged", T=T, H=H, E=E, k=k, I=I, seed_w=31, seed_x=32)
+    inp = synth.make_moe_inputs(cfg)
+    p = dev_params(inp.weights)
+    x = dev_tensor(inp.x)
+    y, idx, w, *_ = q.moe_layer(x, x, p, k, cfg.eps)
+    torch.cuda.synchronize()
+    ref = O.experts_bruteforce(inp.x, idx.cpu().numpy(), w.cpu().numpy(), inp.weights.gate_up,
+                               inp.weights.down, I)
+    err = O.rowwise_rel_err(bf16_host(y), ref)
+    say(f"  rel err {err:.3e}")
+    assert err <= Y_TOL
+
+
+def test_layer_dropped_indices_sum_the_rest():
+    """Out-of-range routing indices are dropped: the token gets the weighted
+    sum of its remaining assignments."""
+    import bit_quantized_moe_diffrouter_amd as q
+    cfg = synth.TINY
+    say("[layer dropped indices]")
+    inp = inputs(cfg)
+    idx_r, w_r, _ = oracle_route(inp)
+    bad = idx_r.copy()
+    bad[3, 1] = -7
+    bad[10, 0] = cfg.E
+    y_g, _, _ = run_experts(inp, bad, w_r)
+    w0 = w_r.copy()
+    w0[3, 1] = 0.0
+    w0[10, 0] = 0.0
+    safe = np.where((bad >= 0) & (bad < cfg.E), bad, 0)
+    ref = O.experts_bruteforce(inp.x, safe, w0, inp.weights.gate_up, inp.weights.down, cfg.I)
+    assert O.rowwise_rel_err(y_g, ref) <= Y_TOL
+
+
+def test_zero_tokens_is_a_noop():
+    import bit_quantized_moe_diffrouter_amd as q
+    say("[T=0]")
+    p = params(synth.TINY)
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
+    idx, w = q.moe_route(x, p.norm_scale, 1e-6, p.router, p.per_expert_scale, 2)
+    assert idx.shape == (0, 2)
+
+
+# --------------------------------------------------------------------- qlinear
+def test_qlinear_vision_geometry():
+    import bit_quantized_moe_diffrouter_amd as q
+    cfg = synth.QLINEAR_VISION
+    say(f"[qlinear] {cfg.name}")
+    inp = synth.make_qlinear_inputs(cfg)
+    y = q.qlinear(dev_tensor(inp.x), dev_qweight(inp.W))
+    torch.cuda.synchronize()
+    ref = O.qlinear(inp.x, inp.W.w, inp.W.scales, inp.W.biases)
+    err = O.rowwise_rel_err(bf16_host(y), ref)
+    say(f"  rel err {err:.3e}")
+    assert err <= 1e-2
+
+
+def test_qlinear_integer_exact_bitwise():
+    """scale 1, bias -8, x in {-2..2}: the exact integer result rounded once to
+    bf16 must come out bit for bit."""
+    import bit_quantized_moe_diffrouter_amd as q
+    say("[qlinear integer-exact] 2520x1152 -> 1152")
+    rng = np.random.default_rng(41)
+    M, N, K = 2520, 1152, 1152
+    w = rng.integers(0, 2**32, size=(N, K // 8), dtype=np.uint32)
+    s = synth.to_bf16_bits(np.ones((N, K // 64), dtype=np.float32))
+    b = synth.to_bf16_bits(np.full((N, K // 64), -8.0, dtype=np.float32))
+    x = synth.to_bf16_bits(rng.integers(-2, 3, size=(M, K)).astype(np.float32))
+    y = q.qlinear(dev_tensor(x), q.QuantWeight(dev_tensor(w), dev_tensor(s), dev_tensor(b)))
+    torch.cuda.synchronize()
+    ref = O.f64_to_bf16_bits(O.qlinear(x, w, s, b))
+    np.testing.assert_array_equal(y.view(torch.uint16).cpu().numpy(), ref)
+
+
+@pytest.mark.parametrize("M,N,K", [(37, 48, 192), (1, 16, 64), (100, 400, 320)])
+def test_qlinear_ragged(M, N, K):
+    import bit_quantized_moe_diffrouter_amd as q
+    say(f"[qlinear ragged] M={M} N={N} K={K}")
+    rng = np.random.default_rng(M + N + K)
+    W = synth.random_qtensor(rng, (N,), K)
+    x = synth.make_activations(M, K, seed=3)
+    y = q.qlinear(dev_tensor(x), dev_qweight(W))
+    torch.cuda.synchronize()
+    ref = O.qlinear(x, W.w, W.scales, W.biases)
+    assert O.rowwise_rel_err(bf16_host(y), ref) <= 1e-2

@@ -23,7 +23,9 @@ HIP_SOURCES = ["qswitch.hip", "route.hip", "sort.hip"]
 HOST_SOURCES = ["abi.cpp"]
 
 # Packed-fp32 instructions are kept out of the device code.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                # matrix-core results in VGPRs (no accumulation-register round trips)
+                "-mllvm", "-amdgpu-mfma-vgpr-form"]
 COMMON_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-variable",
                 "-I", os.path.join(ROOT, "include")]
 

@@ -35,14 +35,32 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float v) {
 // exactly: 0x4300 | q is the bf16 pattern of 128 + q for q < 128.  The pairs
 // come out as (n0,n4) (n1,n5) (n2,n6) (n3,n7): the activation operand is
 // stored in the same order (see permute_pairs), so the contraction is over
-// the same set of k.
-__device__ __forceinline__ u32x4_t unpack_offset_codes(uint32_t w) {
-  const uint32_t M = 0x000F000Fu, C = 0x43004300u;
+// the same set of k.  gfx9 VOP3 encodings take no literal, so the mask rides
+// in a scalar register and the exponent pattern in a vector register, making
+// each pair one v_and_or_b32 (seven ops per word).
+struct OffsetCodeConsts {
+  uint32_t mask;  // 0x000F000F, uniform (SGPR)
+  uint32_t expo;  // 0x43004300, in a VGPR
+};
+__device__ __forceinline__ OffsetCodeConsts offset_code_consts() {
+  OffsetCodeConsts k;
+  k.mask = __builtin_amdgcn_readfirstlane(0x000F000Fu);
+  uint32_t e = 0x43004300u;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(e) : "i"(0x43004300u));
+  k.expo = e;
+  return k;
+}
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t smask, uint32_t vor) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(smask), "v"(vor));
+  return r;
+}
+__device__ __forceinline__ u32x4_t unpack_offset_codes(uint32_t w, const OffsetCodeConsts& k) {
   u32x4_t r;
-  r.x = (w & M) | C;
-  r.y = ((w >> 4) & M) | C;
-  r.z = ((w >> 8) & M) | C;
-  r.w = ((w >> 12) & M) | C;
+  r.x = and_or(w, k.mask, k.expo);
+  r.y = and_or(w >> 4, k.mask, k.expo);
+  r.z = and_or(w >> 8, k.mask, k.expo);
+  r.w = and_or(w >> 12, k.mask, k.expo);
   return r;
 }
 

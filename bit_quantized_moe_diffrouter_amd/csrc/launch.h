@@ -48,6 +48,7 @@ struct SwitchArgs {
   int ktop;        // assignments per token
   int rows_total;  // dense: M; switch: A = T*k
   int ntiles;      // column tiles per row chunk (set by the launcher)
+  int sb_vec;      // scales/biases readable 4 groups at a time (set by the launcher)
 };
 hipError_t launch_gate_up_geglu(SwitchArgs a, int num_cu, hipStream_t stream);
 hipError_t launch_down(SwitchArgs a, int num_cu, hipStream_t stream);

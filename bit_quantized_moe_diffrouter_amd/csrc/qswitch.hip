@@ -11,18 +11,28 @@
 // sorted rows, tile of output columns).  The persistent grid walks the items
 // derived on the device from expert_offsets, so no host synchronisation is
 // needed for routing-dependent sizes.  Per 64-wide quantization group:
-//  * each wave streams its own weight rows straight from HBM into registers
-//    (8 bytes per lane, prefetched KS groups ahead) and turns every code into
-//    the exact bf16 value 128 + q with two integer ops per pair;
-//  * the activation chunk is staged once per workgroup in LDS, in the k order
-//    the code unpacking produces;
+//  * each wave streams its own weight rows from HBM straight into a private
+//    LDS ring with global_load_lds_dwordx4 (no VGPRs held while in flight;
+//    the ring keeps D groups outstanding) and reads them one group ahead;
+//  * every code becomes the exact bf16 value 128 + q with one v_and_or_b32
+//    per pair (see unpack_offset_codes);
+//  * the activation chunk and the group scales/biases are staged once per
+//    workgroup in LDS, the activations in the k order the unpacking produces;
 //  * v_mfma_f32_16x16x32_bf16 forms P = sum_k x_k (128 + q_k) and, against a
 //    ones operand, X = sum_k x_k; the group's affine is applied in fp32:
 //        sum_k x_k (s q_k + b) = s P + (b - 128 s) X.
 // All products are exact and the dequantized weight is never rounded, so the
 // only roundings are fp32 accumulation (and the bf16 output).
+//
+// The compiler does not order LDS reads after the LDS DMA that fills them,
+// so the ring waits are explicit: every wave issues the same vector-memory
+// operations in the same order, and the wait before reading group g+1 counts
+// exactly the operations issued after that group's DMA (RING_WAIT below).
 #include "common.h"
 #include "launch.h"
+
+#define QMOE_AS_GLOBAL __attribute__((address_space(1)))
+#define QMOE_AS_LDS __attribute__((address_space(3)))
 
 namespace qmoe {
 
@@ -31,17 +41,88 @@ enum : int { MODE_GATE_UP = 0, MODE_DOWN = 1, MODE_DENSE = 2 };
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 
-template <int MODE, int MT, int NS, int KS>
-__global__ __launch_bounds__(kThreads) void qswitch_kernel(const SwitchArgs p) {
+#ifndef QMOE_SWITCH_WAVES_PER_SIMD
+#define QMOE_SWITCH_WAVES_PER_SIMD 2
+#endif
+
+// The switch kernels move every operand with LDS DMA (global_load_lds_*),
+// issued from inline asm so the compiler neither reorders them nor adds its
+// own (conservative) waits; the waits below are placed by hand from the fixed
+// per-wave issue order (see the pipeline description in the kernel).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(size_t)((QMOE_AS_LDS const void*)p);
+}
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// 64 lanes x 16 bytes from per-lane global addresses to lds + 16 * lane.
+__device__ __forceinline__ void dma_b128(const void* g, uint32_t lds) {
+  lds = __builtin_amdgcn_readfirstlane(lds);  // wave-uniform LDS base for M0
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(lds), "v"(g) : "memory", "m0");
+}
+// 64 lanes x 4 bytes to lds + 4 * lane.
+__device__ __forceinline__ void dma_b32(const void* g, uint32_t lds) {
+  lds = __builtin_amdgcn_readfirstlane(lds);  // wave-uniform LDS base for M0
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+               :: "s"(lds), "v"(g) : "memory", "m0");
+}
+// 64 lanes x 2 bytes, each zero-extended into the 4-byte slot lds + 4 * lane.
+__device__ __forceinline__ void dma_u16(const void* g, uint32_t lds) {
+  lds = __builtin_amdgcn_readfirstlane(lds);  // wave-uniform LDS base for M0
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_ushort %1, off"
+               :: "s"(lds), "v"(g) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
+template <int MODE, int MT, int NS, int KS, bool SBVEC>
+__global__ __launch_bounds__(kThreads, QMOE_SWITCH_WAVES_PER_SIMD) void qswitch_kernel(const SwitchArgs p) {
   constexpr int BM = 16 * MT;                 // rows per work item
-  constexpr int ROWB = KS * 128 + 16;         // LDS bytes per staged row (padded)
-  constexpr int CHUNKS = BM * KS * 8;         // 16-byte pieces per stage
-  constexpr int CPT = CHUNKS / kThreads;      // pieces per thread
+  constexpr int CHUNKS = BM * KS * 8;         // 16-byte activation pieces per stage
   static_assert(CHUNKS % kThreads == 0, "stage must split evenly over the workgroup");
+  static_assert(BM % 8 == 0, "row-xor swizzle spans 8 rows");
   constexpr int NSH = (MODE == MODE_GATE_UP) ? NS / 2 : NS;  // output subtiles per wave
   static_assert(MODE != MODE_GATE_UP || NS % 2 == 0, "gate_up pairs gate and up subtiles");
+  static_assert(NS == 2, "one 1 KB ring slot per group holds two 16-row subtiles");
+#ifndef QMOE_SWITCH_RING
+#define QMOE_SWITCH_RING 8
+#endif
+  constexpr int D = QMOE_SWITCH_RING;          // weight ring depth (groups in flight per wave)
+  static_assert(D % KS == 0 && D >= 2 * KS && D / KS <= 4, "ring holds 2..4 whole stages");
+  constexpr int SB_ROWS = kWaves * NS * 16;   // weight rows of the workgroup
+  static_assert(2 * SB_ROWS == kThreads, "one thread per (row, scale|bias)");
+  static_assert(!SBVEC || KS % 2 == 0, "vector scale loads read group pairs");
+  // Pipeline (per wave, all DMA): stage st of KS groups needs the activation
+  // pieces and scales of the stage (shared by the workgroup, double-buffered)
+  // and, per group, the wave's two 16-row weight subtiles (private ring of D
+  // groups).  Issue order per item:
+  //   prologue: act/scales(0); weights(0 .. D-1)
+  //   stage st: [wait act/scales(st)] barrier; act/scales(st+1);
+  //             per group g: [wait weights(g+1)] read them; compute g; weights(g+D)
+  // Every wave issues the same ops in the same order, so "ops issued after X"
+  // is a fixed number at each wait (checked against a simulation of the order):
+  //   first ring read:        D - 1
+  //   act/scales of stage st: D (st = 0) or KS
+  //   weights(g+1):           D - 2 + LA * c, c = min(st + 1, D/KS) - [gl == KS-1 and st + 1 >= D/KS]
+  constexpr int APW = CHUNKS / kThreads;               // activation DMAs per wave per stage
+  constexpr int SPW = SBVEC ? KS / 2 : KS;             // scale DMAs per wave per stage
+  constexpr int LA = APW + SPW;
+  constexpr int RS = D / KS;                   // stages held by the ring
+  static_assert(D - 2 + RS * LA < 64, "wait count must fit vmcnt");
+  constexpr int A_BYTES = CHUNKS * 16;                 // activation bytes per stage
+  constexpr int S_WORDS = SPW * kThreads;              // 4-byte scale slots per stage
 
-  __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][BM * ROWB];
+  // activations of a stage: piece p = (gl * BM + row) * 8 + (blk ^ (row & 7)) at 16 p
+  __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][A_BYTES];
+  // scales: slot [q][t], t = 2 * row + (0: scale, 1: bias); q = group pair (vector
+  // path, two bf16 per slot) or group (scalar path, one zero-extended bf16)
+  __shared__ __attribute__((aligned(16))) uint32_t lds_s[2][S_WORDS];
+  // per-wave weight ring: slot = group % D, 2 subtiles x 16 rows x 32 bytes
+  __shared__ __attribute__((aligned(16))) uint8_t lds_w[kWaves][D][1024];
   __shared__ int s_cum[kThreads + 2];
   __shared__ int s_scan[kWaves];
   __shared__ int s_src[BM];
@@ -68,7 +149,7 @@ __global__ __launch_bounds__(kThreads) void qswitch_kernel(const SwitchArgs p) {
     int tot;
     const int incl = block_inclusive_scan<kThreads>(c0 + c1, s_scan, &tot);
     if (tid < nb) s_cum[tid + 1] = incl - c1;
-    if (c1 > 0 || (tid == kThreads - 1 && nb > kThreads)) s_cum[kThreads + 1] = incl;
+    if (tid == kThreads - 1 && nb > kThreads) s_cum[kThreads + 1] = incl;
     if (tid == 0) s_cum[0] = 0;
     total_chunks = tot;
     __syncthreads();
@@ -76,6 +157,7 @@ __global__ __launch_bounds__(kThreads) void qswitch_kernel(const SwitchArgs p) {
   const int total_items = total_chunks * p.ntiles;
 
   const u32x4_t ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  const OffsetCodeConsts kc = offset_code_consts();
 
   for (int item = blockIdx.x; item < total_items; item += gridDim.x) {
     const int chunk = item / p.ntiles;
@@ -91,7 +173,7 @@ __global__ __launch_bounds__(kThreads) void qswitch_kernel(const SwitchArgs p) {
         const int mid = (lo + hi) >> 1;
         if (s_cum[mid] <= chunk) lo = mid; else hi = mid;
       }
-      e = lo;
+      e = __builtin_amdgcn_readfirstlane(lo);
       const int A = p.rows_total;
       const int seg_lo = min(max(p.offsets[e], 0), A);
       const int seg_hi = (e < p.E) ? min(max(p.offsets[e + 1], seg_lo), A) : A;
@@ -100,7 +182,7 @@ __global__ __launch_bounds__(kThreads) void qswitch_kernel(const SwitchArgs p) {
       zero_only = (MODE == MODE_DOWN) && (e == p.E);
     }
 
-    __syncthreads();  // the previous item is done with s_src / s_dst / lds_a
+    __syncthreads();  // the previous item is done with s_src / s_dst / lds_a / lds_sb
     if (tid < BM) {
       const int r = r0 + tid;
       int src = -1, dst = -1;
@@ -125,19 +207,28 @@ __global__ __launch_bounds__(kThreads) void qswitch_kernel(const SwitchArgs p) {
     }
     __syncthreads();
 
-    // ---- this wave's output subtiles and weight rows
-    int wrow[NS], ocol[NSH];
-    bool act[NS];
+    // weight row (within the expert) of the workgroup's row slot t: wave t/(16 NS),
+    // subtile t/16 % NS, row t % 16; rows of column tiles past the end map to a
+    // valid row (computed on, never stored)
+    auto wg_row = [&](int t) {
+      const int tw = t / (16 * NS), tj = (t / 16) % NS, tn = t % 16;
+      int c, row;
+      if constexpr (MODE == MODE_GATE_UP) {
+        c = ntile * (kWaves * 16 * NSH) + tw * (16 * NSH) + 16 * (tj % NSH);
+        row = (tj < NSH) ? c : p.Nout + c;
+      } else {
+        c = ntile * (kWaves * 16 * NS) + tw * (16 * NS) + 16 * tj;
+        row = c;
+      }
+      return (c < p.Nout ? row : 0) + tn;
+    };
+    // this wave's output subtiles
+    int ocol[NSH];
+    bool act[NSH];
 #pragma unroll
     for (int j = 0; j < NSH; ++j) {
-      const int c = ntile * (kWaves * 16 * NSH) + wave * (16 * NSH) + 16 * j;
-      ocol[j] = c;
-      act[j] = c < p.Nout;
-      wrow[j] = c;
-      if constexpr (MODE == MODE_GATE_UP) {
-        act[NSH + j] = act[j];
-        wrow[NSH + j] = p.Nout + c;
-      }
+      ocol[j] = ntile * (kWaves * 16 * NSH) + wave * (16 * NSH) + 16 * j;
+      act[j] = ocol[j] < p.Nout;
     }
 
     f32x4_t acc[MT][NS];
@@ -147,114 +238,127 @@ __global__ __launch_bounds__(kThreads) void qswitch_kernel(const SwitchArgs p) {
       for (int j = 0; j < NS; ++j) acc[m][j] = zero4();
 
     if (!zero_only) {
-      const uint32_t* wp[NS];
-      const uint16_t* sp[NS];
-      const uint16_t* bp[NS];
+      // weight DMA: lane -> (subtile l/32, row l/2 % 16, half l % 2) of the 32-byte
+      // group segment; past the last group it reloads the last one (not used)
+      const uint32_t* wsrc =
+          p.w + ((size_t)e * p.Nw + wg_row(wave * 32 + (lane >> 1))) * KW + (lane & 1) * 4;
+      const uint8_t* ring = &lds_w[wave][0][0];
+      const uint32_t ring_lds = lds_addr(ring);
+      auto dma_weights = [&](int g) { dma_b128(wsrc + min(g, G - 1) * 8, ring_lds + (g % D) * 1024); };
+
+      // scale DMA: thread t = 2 * row + which copies scale (which 0) or bias of row
+      const uint16_t* ssrc = ((tid & 1) ? p.b : p.s) + ((size_t)e * p.Nw + wg_row(tid >> 1)) * G;
+      // activation DMA: instruction i of this wave fills pieces (i * kWaves + wave) * 64 + lane
+      const uint16_t* asrc[APW];
 #pragma unroll
-      for (int j = 0; j < NS; ++j) {
-        const size_t row = (size_t)e * p.Nw + (size_t)(act[j] ? wrow[j] + ln : 0);
-        wp[j] = p.w + row * KW + 2 * lq;
-        sp[j] = p.s + row * G;
-        bp[j] = p.b + row * G;
+      for (int i = 0; i < APW; ++i) {
+        const int pc = (i * kWaves + wave) * 64 + lane;
+        const int row = (pc >> 3) % BM, gl = (pc >> 3) / BM, blk = (pc & 7) ^ (row & 7);
+        const int src = s_src[row];
+        asrc[i] = p.a + (size_t)(src >= 0 ? src : 0) * K + gl * kGroup + blk * 8;
       }
-
-      // weight prefetch ring: slot = group % KS
-      u32x2_t wr[KS][NS];
-      uint32_t sr[KS][NS], br[KS][NS];
-#pragma unroll
-      for (int sl = 0; sl < KS; ++sl)
-#pragma unroll
-        for (int j = 0; j < NS; ++j) {
-          if (act[j] && sl < G) {
-            wr[sl][j] = *(const u32x2_t*)(wp[j] + sl * 8);
-            sr[sl][j] = sp[j][sl];
-            br[sl][j] = bp[j][sl];
-          } else {
-            wr[sl][j] = u32x2_t{0u, 0u};
-            sr[sl][j] = 0u;
-            br[sl][j] = 0u;
-          }
-        }
-
-      // activation staging: piece c -> row c/(KS*8), group c/8 % KS, block c%8
-      u32x4_t areg[CPT];
-      auto load_stage = [&](int st) {
-#pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-          const int c = tid + kThreads * i;
-          const int row = c / (KS * 8), rem = c % (KS * 8);
-          const int g = st * KS + (rem >> 3), blk = rem & 7;
-          const int src = s_src[row];
-          if (src >= 0 && g < G)
-            areg[i] = *(const u32x4_t*)(p.a + (size_t)src * K + g * kGroup + blk * 8);
-          else
-            areg[i] = u32x4_t{0u, 0u, 0u, 0u};
-        }
-      };
-      auto store_stage = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-          const int c = tid + kThreads * i;
-          const int row = c / (KS * 8), rem = c % (KS * 8);
-          *(u32x4_t*)(&lds_a[buf][row * ROWB + (rem >> 3) * 128 + (rem & 7) * 16]) =
-              permute_pairs(areg[i]);
-        }
-      };
-
-      load_stage(0);
-      store_stage(0);
-      __syncthreads();
-
       const int NST = (G + KS - 1) / KS;
+      auto dma_stage = [&](int st) {  // exactly LA DMAs
+        const int stc = min(st, NST - 1);  // past the end: the last stage again (not used)
+        const int buf = st & 1;
+#pragma unroll
+        for (int i = 0; i < APW; ++i) {
+          // groups past G (last partial stage) reload group G-1; they are skipped in compute
+          const int gl = ((i * kWaves + wave) * 64 + lane) / (8 * BM);
+          const int g = min(stc * KS + gl, G - 1);
+          dma_b128(asrc[i] + (g - gl) * kGroup, lds_addr(&lds_a[buf][(i * kWaves + wave) * 1024]));
+        }
+        const int g0 = stc * KS;
+#pragma unroll
+        for (int q = 0; q < SPW; ++q) {
+          const uint32_t dst = lds_addr(&lds_s[buf][q * kThreads + wave * 64]);
+          if constexpr (SBVEC)
+            dma_b32(ssrc + g0 + 2 * q, dst);
+          else
+            dma_u16(ssrc + min(g0 + q, G - 1), dst);
+        }
+      };
+
+      // ---- prologue
+      dma_stage(0);
+#pragma unroll
+      for (int d = 0; d < D; ++d) dma_weights(d);
+      wait_vmcnt<D - 1>();
+      u32x2_t wcur[NS];
+#pragma unroll
+      for (int j = 0; j < NS; ++j) wcur[j] = *(const u32x2_t*)(ring + j * 512 + ln * 32 + lq * 8);
+
       for (int st = 0; st < NST; ++st) {
         const int buf = st & 1;
-        if (st + 1 < NST) load_stage(st + 1);
+        if (st == 0) wait_vmcnt<D>(); else wait_vmcnt<KS>();
+        __syncthreads();  // stage st landed for every wave; stage st-1's buffers are free
+        dma_stage(st + 1);
 #pragma unroll
         for (int gl = 0; gl < KS; ++gl) {
           const int g = st * KS + gl;
+          {
+            const int c = min(st + 1, RS) - ((gl == KS - 1 && st + 1 >= RS) ? 1 : 0);
+            if (c <= 1) wait_vmcnt<D - 2 + LA>();
+            else if (c == 2) wait_vmcnt<D - 2 + 2 * LA>();
+            else if (c == 3) wait_vmcnt<D - 2 + (RS >= 3 ? 3 : 2) * LA>();
+            else wait_vmcnt<D - 2 + (RS >= 4 ? 4 : 2) * LA>();
+          }
+          u32x2_t wnext[NS];
+#pragma unroll
+          for (int j = 0; j < NS; ++j)
+            wnext[j] = *(const u32x2_t*)(ring + ((g + 1) % D) * 1024 + j * 512 + ln * 32 + lq * 8);
+
           if (g < G) {
             u32x4_t b0[NS], b1[NS];
             float sc[NS], cc[NS];
 #pragma unroll
             for (int j = 0; j < NS; ++j) {
-              b0[j] = unpack_offset_codes(wr[gl][j].x);
-              b1[j] = unpack_offset_codes(wr[gl][j].y);
-              sc[j] = bf16_bits_to_f32(sr[gl][j]);
-              cc[j] = bf16_bits_to_f32(br[gl][j]) - 128.0f * sc[j];
+              b0[j] = unpack_offset_codes(wcur[j].x, kc);
+              b1[j] = unpack_offset_codes(wcur[j].y, kc);
+              const int t2 = 2 * (wave * (16 * NS) + 16 * j + ln);
+              const u32x2_t sb = *(const u32x2_t*)&lds_s[buf][(SBVEC ? gl / 2 : gl) * kThreads + t2];
+              const int sh = (SBVEC && (gl & 1)) ? 0 : 16;
+              sc[j] = __uint_as_float(sh ? (sb.x << 16) : (sb.x & 0xffff0000u));
+              const float bias = __uint_as_float(sh ? (sb.y << 16) : (sb.y & 0xffff0000u));
+              cc[j] = bias - 128.0f * sc[j];
             }
-            // refill this slot with group g + KS
-            const int gn = g + KS;
+            // all MFMAs of the group first, then the fp32 affine
+            u32x4_t a0[MT], a1[MT];
 #pragma unroll
-            for (int j = 0; j < NS; ++j) {
-              if (act[j] && gn < G) {
-                wr[gl][j] = *(const u32x2_t*)(wp[j] + gn * 8);
-                sr[gl][j] = sp[j][gn];
-                br[gl][j] = bp[j][gn];
-              }
+            for (int m = 0; m < MT; ++m) {
+              const int row = 16 * m + ln;
+              const uint8_t* base = &lds_a[buf][(gl * BM + row) * 128];
+              a0[m] = permute_pairs(*(const u32x4_t*)(base + (((2 * lq) ^ (row & 7)) * 16)));
+              a1[m] = permute_pairs(*(const u32x4_t*)(base + (((2 * lq + 1) ^ (row & 7)) * 16)));
+            }
+            f32x4_t X[MT], P[MT][NS];
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+              X[m] = mfma16x16x32(a0[m], ones, zero4());
+#pragma unroll
+              for (int j = 0; j < NS; ++j) P[m][j] = mfma16x16x32(a0[m], b0[j], zero4());
             }
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
-              const uint8_t* base = &lds_a[buf][(16 * m + ln) * ROWB + gl * 128 + lq * 32];
-              const u32x4_t a0 = *(const u32x4_t*)base;
-              const u32x4_t a1 = *(const u32x4_t*)(base + 16);
-              f32x4_t X = mfma16x16x32(a0, ones, zero4());
-              X = mfma16x16x32(a1, ones, X);
+              X[m] = mfma16x16x32(a1[m], ones, X[m]);
 #pragma unroll
-              for (int j = 0; j < NS; ++j) {
-                if (act[j]) {
-                  f32x4_t P = mfma16x16x32(a0, b0[j], zero4());
-                  P = mfma16x16x32(a1, b1[j], P);
-#pragma unroll
-                  for (int i = 0; i < 4; ++i)
-                    acc[m][j][i] = __builtin_fmaf(cc[j], X[i], __builtin_fmaf(sc[j], P[i], acc[m][j][i]));
-                }
-              }
+              for (int j = 0; j < NS; ++j) P[m][j] = mfma16x16x32(a1[m], b1[j], P[m][j]);
             }
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+              for (int j = 0; j < NS; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                  acc[m][j][i] = __builtin_fmaf(cc[j], X[m][i], __builtin_fmaf(sc[j], P[m][j][i], acc[m][j][i]));
           }
+          // refill the slot of group g (read into wcur one group ago) with group g + D
+          dma_weights(g + D);
+#pragma unroll
+          for (int j = 0; j < NS; ++j) wcur[j] = wnext[j];
         }
-        if (st + 1 < NST) store_stage(buf ^ 1);
-        __syncthreads();
       }
+      wait_vmcnt<0>();  // drain the tail (reloads) before the buffers are reused
     }
 
     // ---- epilogue: lane holds column ocol[j] + ln, rows 16m + 4lq + i
@@ -317,15 +421,27 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 // ------------------------------------------------------------------ launchers
 namespace {
-constexpr int kMT = 2, kKS = 4;
+// Tile shape of the switch kernels (overridable at build time for tuning sweeps).
+#ifndef QMOE_SWITCH_MT
+#define QMOE_SWITCH_MT 2
+#endif
+#ifndef QMOE_SWITCH_KS
+#define QMOE_SWITCH_KS 4
+#endif
+#ifndef QMOE_SWITCH_WG_PER_CU
+#define QMOE_SWITCH_WG_PER_CU 4
+#endif
+constexpr int kMT = QMOE_SWITCH_MT, kKS = QMOE_SWITCH_KS;
 constexpr int kBM = 16 * kMT;
-constexpr int kWgPerCu = 4;
+constexpr int kWgPerCu = QMOE_SWITCH_WG_PER_CU;  // resident workgroups per CU (LDS-bound)
 
 template <int MODE, int NS>
 hipError_t launch_switch(SwitchArgs a, int extra_buckets, int num_cu, hipStream_t stream) {
   constexpr int NSH = (MODE == MODE_GATE_UP) ? NS / 2 : NS;
   const int cols = kWaves * 16 * NSH;
   a.ntiles = (a.Nout + cols - 1) / cols;
+  const int G = a.K / 64;
+  a.sb_vec = (kKS % 2 == 0) && (G % kKS == 0) && ((uintptr_t)a.s % 4 == 0) && ((uintptr_t)a.b % 4 == 0);
   long long chunks;
   if (MODE == MODE_DENSE)
     chunks = (a.rows_total + kBM - 1) / kBM;
@@ -334,7 +450,10 @@ hipError_t launch_switch(SwitchArgs a, int extra_buckets, int num_cu, hipStream_
   long long items = chunks * a.ntiles;
   long long grid = min(items, (long long)num_cu * kWgPerCu);
   if (grid < 1) grid = 1;
-  hipLaunchKernelGGL((qswitch_kernel<MODE, kMT, NS, kKS>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+  if (a.sb_vec)
+    hipLaunchKernelGGL((qswitch_kernel<MODE, kMT, NS, kKS, kKS % 2 == 0>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL((qswitch_kernel<MODE, kMT, NS, kKS, false>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 }  // namespace

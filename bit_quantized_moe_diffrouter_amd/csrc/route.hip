@@ -8,10 +8,12 @@
 // MFMA: u is split into three bf16 terms (u = hi + mid + lo to 24 bits), the
 // router codes are unpacked to the exact bf16 values 16 + q, and the group
 // affine is applied in fp32 (s P + (b - 16 s) U, U = sum of u over the
-// group).  A (token tile, k-range) grid fills the chip at 256 tokens; the
-// partial logits go to a workspace and kernel 2 sums them in a fixed order,
-// so the result is run-to-run reproducible.  Kernel 2 runs one wave per
-// token: k rounds of a wave-wide arg-max, then the softmax in fp32.
+// group).  The norm is one positive factor per token, so kernel 1 works on
+// x * scale * H^-0.5 and kernel 2 multiplies the summed logits by
+// 1 / sqrt(mean(x^2) + eps).  A (token tile, k-range) grid fills the chip at
+// 256 tokens; the partial logits go to a workspace and kernel 2 sums them in
+// a fixed order, so the result is run-to-run reproducible.  Kernel 2 runs one
+// wave per token: k rounds of a wave-wide arg-max, then the softmax in fp32.
 #include <math.h>
 
 #include "common.h"
@@ -39,7 +41,6 @@ template <int NPW>
 __global__ __launch_bounds__(kRThreads) void route_logits_kernel(const RouteArgs p) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_u[3][kTT * kRRowB];
   __shared__ float s_U[kRKS][kTT];
-  __shared__ float s_rs[kTT];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ln = lane & 15, lq = lane >> 4;
@@ -48,28 +49,6 @@ __global__ __launch_bounds__(kRThreads) void route_logits_kernel(const RouteArgs
   const int ks = blockIdx.y;
   const int g_begin = (int)((long long)ks * G / p.ksplit);
   const int g_end = (int)((long long)(ks + 1) * G / p.ksplit);
-
-  // 1) reciprocal RMS per token (needs the full row)
-  for (int tt = wave; tt < kTT; tt += kRWaves) {
-    const int t = t0 + tt;
-    float ss = 0.f;
-    if (t < T) {
-      const uint16_t* xr = p.x + (size_t)t * H;
-      for (int c = lane; c < H / 8; c += 64) {
-        const u32x4_t v = *(const u32x4_t*)(xr + c * 8);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float a = bf16_lo_f32(v[q]), b = bf16_hi_f32(v[q]);
-          ss = __builtin_fmaf(a, a, ss);
-          ss = __builtin_fmaf(b, b, ss);
-        }
-      }
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
-    if (lane == 0) s_rs[tt] = (t < T) ? 1.0f / sqrtf(ss / (float)H + p.eps) : 0.0f;
-  }
-  __syncthreads();
 
   const int nte = (E + 15) / 16;
   int e0[NPW];
@@ -96,7 +75,6 @@ __global__ __launch_bounds__(kRThreads) void route_logits_kernel(const RouteArgs
 
   // staging piece of this thread: token tt, group-in-stage gl, block blk
   const int s_tt = tid >> 5, s_gl = (tid >> 3) & 3, s_blk = tid & 7;
-  const float rs = s_rs[s_tt];
 
   for (int gs = g_begin; gs < g_end; gs += kRKS) {
     // weights of this stage (issued first so their latency hides under the staging)
@@ -123,8 +101,8 @@ __global__ __launch_bounds__(kRThreads) void route_logits_kernel(const RouteArgs
         const u32x4_t nv = *(const u32x4_t*)(p.norm_scale + h);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          u[2 * q] = ((bf16_lo_f32(xv[q]) * rs) * bf16_lo_f32(nv[q])) * p.root;
-          u[2 * q + 1] = ((bf16_hi_f32(xv[q]) * rs) * bf16_hi_f32(nv[q])) * p.root;
+          u[2 * q] = (bf16_lo_f32(xv[q]) * bf16_lo_f32(nv[q])) * p.root;
+          u[2 * q + 1] = (bf16_hi_f32(xv[q]) * bf16_hi_f32(nv[q])) * p.root;
         }
       } else {
 #pragma unroll
@@ -209,16 +187,41 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const RouteArgs p) {
   if (t >= p.T) return;  // whole wave leaves; no barriers below
   const int E = p.E, T = p.T;
 
+  // reciprocal RMS of the token row (the logit kernel works on the un-normalised
+  // row: the norm is one positive factor per token, applied here)
+  float ss = 0.f;
+  const uint16_t* xr = p.x + (size_t)t * p.H;
+  for (int c = lane; c < p.H / 8; c += 64) {
+    const u32x4_t xv = *(const u32x4_t*)(xr + c * 8);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float a = bf16_lo_f32(xv[q]), b = bf16_hi_f32(xv[q]);
+      ss = __builtin_fmaf(a, a, ss);
+      ss = __builtin_fmaf(b, b, ss);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
+  const float rs = 1.0f / sqrtf(ss / (float)p.H + p.eps);
+
   float v[4];
   bool taken[4];
+  float part[4] = {0.f, 0.f, 0.f, 0.f};
+  const float* pb = p.part + (size_t)t * E + lane;
+  const size_t pstride = (size_t)T * E;
+#pragma unroll 4
+  for (int q = 0; q < p.ksplit; ++q) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (lane + 64 * i < E) part[i] += pb[q * pstride + 64 * i];
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = lane + 64 * i;
     v[i] = -INFINITY;
     taken[i] = true;
     if (e < E) {
-      float s = 0.f;
-      for (int q = 0; q < p.ksplit; ++q) s += p.part[((size_t)q * T + t) * E + e];
+      float s = part[i] * rs;
       if (p.logit_bias) s += p.logit_bias[e];
       if (p.logits_out) p.logits_out[(size_t)t * E + e] = s;
       v[i] = (s != s) ? -INFINITY : s;  // NaN never wins

@@ -88,39 +88,47 @@ __global__ __launch_bounds__(kThreads, QMOE_SWITCH_WAVES_PER_SIMD) void qswitch_
   constexpr int NSH = (MODE == MODE_GATE_UP) ? NS / 2 : NS;  // output subtiles per wave
   static_assert(MODE != MODE_GATE_UP || NS % 2 == 0, "gate_up pairs gate and up subtiles");
   static_assert(NS == 2, "one 1 KB ring slot per group holds two 16-row subtiles");
-#ifndef QMOE_SWITCH_RING
-#define QMOE_SWITCH_RING 8
-#endif
-  constexpr int D = QMOE_SWITCH_RING;          // weight ring depth (groups in flight per wave)
-  static_assert(D % KS == 0 && D >= 2 * KS && D / KS <= 4, "ring holds 2..4 whole stages");
   constexpr int SB_ROWS = kWaves * NS * 16;   // weight rows of the workgroup
+#ifndef QMOE_SWITCH_STAGES_AHEAD
+#define QMOE_SWITCH_STAGES_AHEAD 4
+#endif
+  // stages issued ahead of the one computed (the scalar scale path stages twice
+  // the scale bytes, so it keeps one stage less to stay within 80 KB of LDS)
+  constexpr int R = SBVEC ? QMOE_SWITCH_STAGES_AHEAD : QMOE_SWITCH_STAGES_AHEAD - 1;
+  constexpr int D = R * KS;                    // weight ring depth (groups in flight per wave)
+  static_assert(R >= 2, "at least two stages ahead");
   static_assert(2 * SB_ROWS == kThreads, "one thread per (row, scale|bias)");
   static_assert(!SBVEC || KS % 2 == 0, "vector scale loads read group pairs");
-  // Pipeline (per wave, all DMA): stage st of KS groups needs the activation
-  // pieces and scales of the stage (shared by the workgroup, double-buffered)
-  // and, per group, the wave's two 16-row weight subtiles (private ring of D
-  // groups).  Issue order per item:
-  //   prologue: act/scales(0); weights(0 .. D-1)
-  //   stage st: [wait act/scales(st)] barrier; act/scales(st+1);
-  //             per group g: [wait weights(g+1)] read them; compute g; weights(g+D)
-  // Every wave issues the same ops in the same order, so "ops issued after X"
-  // is a fixed number at each wait (checked against a simulation of the order):
-  //   first ring read:        D - 1
-  //   act/scales of stage st: D (st = 0) or KS
-  //   weights(g+1):           D - 2 + LA * c, c = min(st + 1, D/KS) - [gl == KS-1 and st + 1 >= D/KS]
+  // Pipeline (per wave, all DMA).  Stage s = KS groups; its activation pieces and
+  // scales (shared by the workgroup) live in slot s % (R+1) of a ring, and each
+  // wave's two 16-row weight subtiles of group g live in slot g % D of the
+  // wave's private ring.  Issue order, which every wave follows exactly:
+  //   prologue:   for s < R: act/scales(s), weights(s*KS .. s*KS+KS-1)
+  //   stage st:   [wait act/scales(st)] barrier; act/scales(st+R);
+  //               per group g: [wait weights(g+1)] read them; compute g; weights(g+D)
+  // so the activations of a stage always precede its weights in the in-order
+  // vmcnt counter and no wait drains the ring.  Ops issued after the one each
+  // wait needs (checked against a simulation of this order):
+  //   first ring read:       D - 1 + (R-1) LA
+  //   act/scales(st):        KS + (R-1)(LA+KS)
+  //   weights(g+1):          KS - 2 + (R-1)(LA+KS) + LA   (gl < KS-1)
+  //                          2(KS-1) + (R-2)(LA+KS) + LA  (gl = KS-1)
   constexpr int APW = CHUNKS / kThreads;               // activation DMAs per wave per stage
   constexpr int SPW = SBVEC ? KS / 2 : KS;             // scale DMAs per wave per stage
   constexpr int LA = APW + SPW;
-  constexpr int RS = D / KS;                   // stages held by the ring
-  static_assert(D - 2 + RS * LA < 64, "wait count must fit vmcnt");
+  constexpr int N_W0 = D - 1 + (R - 1) * LA;
+  constexpr int N_ACT = KS + (R - 1) * (LA + KS);
+  constexpr int N_RING = KS - 2 + (R - 1) * (LA + KS) + LA;
+  constexpr int N_RING_LAST = 2 * (KS - 1) + (R - 2) * (LA + KS) + LA;
+  static_assert(N_RING < 64 && N_W0 < 64 && N_ACT < 64, "wait counts must fit vmcnt");
   constexpr int A_BYTES = CHUNKS * 16;                 // activation bytes per stage
   constexpr int S_WORDS = SPW * kThreads;              // 4-byte scale slots per stage
 
   // activations of a stage: piece p = (gl * BM + row) * 8 + (blk ^ (row & 7)) at 16 p
-  __shared__ __attribute__((aligned(16))) uint8_t lds_a[2][A_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_a[R + 1][A_BYTES];
   // scales: slot [q][t], t = 2 * row + (0: scale, 1: bias); q = group pair (vector
   // path, two bf16 per slot) or group (scalar path, one zero-extended bf16)
-  __shared__ __attribute__((aligned(16))) uint32_t lds_s[2][S_WORDS];
+  __shared__ __attribute__((aligned(16))) uint32_t lds_s[R + 1][S_WORDS];
   // per-wave weight ring: slot = group % D, 2 subtiles x 16 rows x 32 bytes
   __shared__ __attribute__((aligned(16))) uint8_t lds_w[kWaves][D][1024];
   __shared__ int s_cum[kThreads + 2];
@@ -258,9 +266,8 @@ __global__ __launch_bounds__(kThreads, QMOE_SWITCH_WAVES_PER_SIMD) void qswitch_
         asrc[i] = p.a + (size_t)(src >= 0 ? src : 0) * K + gl * kGroup + blk * 8;
       }
       const int NST = (G + KS - 1) / KS;
-      auto dma_stage = [&](int st) {  // exactly LA DMAs
+      auto dma_stage = [&](int st, int buf) {  // exactly LA DMAs into activation/scale slot buf
         const int stc = min(st, NST - 1);  // past the end: the last stage again (not used)
-        const int buf = st & 1;
 #pragma unroll
         for (int i = 0; i < APW; ++i) {
           // groups past G (last partial stage) reload group G-1; they are skipped in compute
@@ -279,30 +286,27 @@ __global__ __launch_bounds__(kThreads, QMOE_SWITCH_WAVES_PER_SIMD) void qswitch_
         }
       };
 
-      // ---- prologue
-      dma_stage(0);
+      // ---- prologue: R stages, each activations/scales then its weights
 #pragma unroll
-      for (int d = 0; d < D; ++d) dma_weights(d);
-      wait_vmcnt<D - 1>();
+      for (int s0 = 0; s0 < R; ++s0) {
+        dma_stage(s0, s0);
+#pragma unroll
+        for (int gl = 0; gl < KS; ++gl) dma_weights(s0 * KS + gl);
+      }
+      wait_vmcnt<N_W0>();
       u32x2_t wcur[NS];
 #pragma unroll
       for (int j = 0; j < NS; ++j) wcur[j] = *(const u32x2_t*)(ring + j * 512 + ln * 32 + lq * 8);
 
+      int buf = 0, issue_buf = R;  // activation slots of the stage computed / being issued
       for (int st = 0; st < NST; ++st) {
-        const int buf = st & 1;
-        if (st == 0) wait_vmcnt<D>(); else wait_vmcnt<KS>();
-        __syncthreads();  // stage st landed for every wave; stage st-1's buffers are free
-        dma_stage(st + 1);
+        wait_vmcnt<N_ACT>();
+        __syncthreads();  // stage st landed for every wave; stage st-1's slot is free
+        dma_stage(st + R, issue_buf);
 #pragma unroll
         for (int gl = 0; gl < KS; ++gl) {
           const int g = st * KS + gl;
-          {
-            const int c = min(st + 1, RS) - ((gl == KS - 1 && st + 1 >= RS) ? 1 : 0);
-            if (c <= 1) wait_vmcnt<D - 2 + LA>();
-            else if (c == 2) wait_vmcnt<D - 2 + 2 * LA>();
-            else if (c == 3) wait_vmcnt<D - 2 + (RS >= 3 ? 3 : 2) * LA>();
-            else wait_vmcnt<D - 2 + (RS >= 4 ? 4 : 2) * LA>();
-          }
+          if (gl < KS - 1) wait_vmcnt<N_RING>(); else wait_vmcnt<N_RING_LAST>();
           u32x2_t wnext[NS];
 #pragma unroll
           for (int j = 0; j < NS; ++j)
@@ -357,6 +361,8 @@ __global__ __launch_bounds__(kThreads, QMOE_SWITCH_WAVES_PER_SIMD) void qswitch_
 #pragma unroll
           for (int j = 0; j < NS; ++j) wcur[j] = wnext[j];
         }
+        buf = (buf == R) ? 0 : buf + 1;
+        issue_buf = (issue_buf == R) ? 0 : issue_buf + 1;
       }
       wait_vmcnt<0>();  // drain the tail (reloads) before the buffers are reused
     }
@@ -426,10 +432,10 @@ namespace {
 #define QMOE_SWITCH_MT 2
 #endif
 #ifndef QMOE_SWITCH_KS
-#define QMOE_SWITCH_KS 4
+#define QMOE_SWITCH_KS 2
 #endif
 #ifndef QMOE_SWITCH_WG_PER_CU
-#define QMOE_SWITCH_WG_PER_CU 4
+#define QMOE_SWITCH_WG_PER_CU 2
 #endif
 constexpr int kMT = QMOE_SWITCH_MT, kKS = QMOE_SWITCH_KS;
 constexpr int kBM = 16 * kMT;

@@ -105,7 +105,7 @@ def main():
         w = synth.make_moe_weights(cfg, seed=s)
         if host_first is None:
             host_first = w
-        sets.append(q.MoEParams(
+        sets.append(q.MoEParams.from_rows(
             t(w.norm_scale), q.QuantWeight(t(w.router.w), t(w.router.scales), t(w.router.biases)),
             t(w.per_expert_scale), q.QuantWeight(t(w.gate_up.w), t(w.gate_up.scales), t(w.gate_up.biases)),
             q.QuantWeight(t(w.down.w), t(w.down.scales), t(w.down.biases)),

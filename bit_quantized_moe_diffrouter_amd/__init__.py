@@ -23,7 +23,7 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = [
-    "QMoEError", "QuantWeight", "MoEParams", "lib", "library_path",
+    "QMoEError", "QuantWeight", "TiledWeight", "MoEParams", "lib", "library_path",
     "moe_route", "moe_route_workspace", "moe_sort", "qswitch_gate_up_geglu",
     "qswitch_down_combine", "qswitch_down_combine_workspace", "qlinear", "moe_layer",
 ]
@@ -50,7 +50,11 @@ class QWeightDesc(ctypes.Structure):
         ("in_", ctypes.c_int32),
         ("bits", ctypes.c_int32),
         ("group", ctypes.c_int32),
+        ("layout", ctypes.c_int32),
+        ("split", ctypes.c_int32),
     ]
+
+LAYOUT_ROWS, LAYOUT_TILED = 0, 1
 
 
 _P = ctypes.c_void_p
@@ -68,6 +72,8 @@ _SIGNATURES = {
     "qswitch_down_combine_workspace": (_SZ, [_I, _I, _I, _I]),
     "qswitch_down_combine": (ctypes.c_int, [_P, _I, _I, _I, _QP, _I, _P, _P, _P, _P, _P, _SZ, _I, _P]),
     "qlinear": (ctypes.c_int, [_P, _I, _QP, _P, _P]),
+    "qmoe_tiled_weight_bytes": (_SZ, [_I, _I, _I, _I]),
+    "qmoe_tile_weight": (ctypes.c_int, [_QP, _I, _P, _SZ, _P]),
 }
 
 _lib = None
@@ -149,12 +155,39 @@ class QuantWeight:
         if tuple(self.scales.shape) != lead + (g,) or tuple(self.biases.shape) != lead + (g,):
             raise ValueError("scales/biases shape does not match the codes")
         return QWeightDesc(self.w.data_ptr(), self.scales.data_ptr(), self.biases.data_ptr(),
-                           self.experts, self.rows, self.in_features, 4, 64)
+                           self.experts, self.rows, self.in_features, 4, 64, LAYOUT_ROWS, 0)
 
     @classmethod
     def from_numpy(cls, w, scales, biases, device="cuda") -> "QuantWeight":
         return cls(torch.from_numpy(w).to(device), torch.from_numpy(scales).to(device),
                    torch.from_numpy(biases).to(device))
+
+    def tiled(self, split: int = 0) -> "TiledWeight":
+        """The tiled copy the switch linears and qlinear read (qmoe_tile_weight)."""
+        n = int(lib().qmoe_tiled_weight_bytes(self.experts, self.rows, self.in_features, split))
+        if n == 0:
+            raise ValueError(f"cannot tile a [{self.experts}, {self.rows}, {self.in_features}] weight "
+                             f"with split={split}")
+        buf = torch.empty(n, dtype=torch.uint8, device=self.w.device)
+        d = self.desc()
+        _check(lib().qmoe_tile_weight(ctypes.byref(d), int(split), _ptr(buf), n, _stream()))
+        return TiledWeight(buf, self.experts, self.rows, self.in_features, int(split))
+
+
+@dataclass
+class TiledWeight:
+    """A weight in the tiled layout (one device byte buffer; see qmoe_tile_weight)."""
+
+    buf: torch.Tensor
+    experts: int
+    rows: int
+    in_features: int
+    split: int = 0
+
+    def desc(self) -> QWeightDesc:
+        _need(self.buf, "tiled weight", 1)
+        return QWeightDesc(self.buf.data_ptr(), None, None, self.experts, self.rows, self.in_features, 4, 64,
+                           LAYOUT_TILED, self.split)
 
 
 def moe_route_workspace(T: int, H: int, E: int) -> int:
@@ -201,7 +234,7 @@ def moe_sort(indices: torch.Tensor, E: int, expert_offsets: Optional[torch.Tenso
     return expert_offsets, sorted_assign
 
 
-def qswitch_gate_up_geglu(x_expert: torch.Tensor, gate_up: QuantWeight, I: int, k: int,
+def qswitch_gate_up_geglu(x_expert: torch.Tensor, gate_up: "TiledWeight", I: int, k: int,
                           expert_offsets: torch.Tensor, sorted_assign: torch.Tensor,
                           mid: Optional[torch.Tensor] = None) -> torch.Tensor:
     """gate_up switch linear + split + GeGLU: returns mid bf16 [T*k, I] (sorted-row order)."""
@@ -219,7 +252,7 @@ def qswitch_down_combine_workspace(T: int, k: int, H: int, deterministic: int = 
     return int(lib().qswitch_down_combine_workspace(T, k, H, deterministic))
 
 
-def qswitch_down_combine(mid: torch.Tensor, T: int, k: int, down: QuantWeight, weights: torch.Tensor,
+def qswitch_down_combine(mid: torch.Tensor, T: int, k: int, down: "TiledWeight", weights: torch.Tensor,
                          expert_offsets: torch.Tensor, sorted_assign: torch.Tensor,
                          y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                          deterministic: int = 1) -> torch.Tensor:
@@ -240,7 +273,7 @@ def qswitch_down_combine(mid: torch.Tensor, T: int, k: int, down: QuantWeight, w
     return y
 
 
-def qlinear(x: torch.Tensor, W: QuantWeight, y: Optional[torch.Tensor] = None) -> torch.Tensor:
+def qlinear(x: torch.Tensor, W: "TiledWeight", y: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Dense 4-bit linear y = x . dequant(W)^T: returns bf16 [M, N]."""
     M = int(x.shape[0])
     _need(x, "x", 2)
@@ -256,11 +289,17 @@ class MoEParams:
     """Device-resident weights of one MoE layer."""
 
     norm_scale: torch.Tensor           # bf16 [H]
-    router: QuantWeight                # [E, H/8]
+    router: QuantWeight                # [E, H/8], row-major
     per_expert_scale: torch.Tensor     # bf16 [E]
-    gate_up: QuantWeight               # [E, 2I, H/8]
-    down: QuantWeight                  # [E, H, I/8]
+    gate_up: TiledWeight               # [E, 2I, H], tiled with split = I
+    down: TiledWeight                  # [E, H, I], tiled with split = 0
     logit_bias: Optional[torch.Tensor] = None  # fp32 [E]
+
+    @classmethod
+    def from_rows(cls, norm_scale, router: QuantWeight, per_expert_scale, gate_up: QuantWeight, down: QuantWeight,
+                  logit_bias=None) -> "MoEParams":
+        """Tiles the two switch weights (once, when the layer is loaded)."""
+        return cls(norm_scale, router, per_expert_scale, gate_up.tiled(gate_up.rows // 2), down.tiled(0), logit_bias)
 
     @property
     def E(self) -> int:

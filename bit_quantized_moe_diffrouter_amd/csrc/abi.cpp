@@ -46,14 +46,23 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
       return fail(QMOE_ERR_INVALID, "%s: not %d-byte aligned", name, (int)(align));   \
   } while (0)
 
-// Checks a quantized weight descriptor against the expected shape.
-int check_qweight(const qmoe_qweight* q, const char* what, int experts, int rows, int in) {
+// Checks a quantized weight descriptor against the expected shape and layout
+// (for the tiled layout also the fused-pair split it was tiled with).
+int check_qweight(const qmoe_qweight* q, const char* what, int experts, int rows, int in, int layout = QMOE_LAYOUT_ROWS,
+                  int split = 0) {
   REQUIRE(q != nullptr, QMOE_ERR_INVALID, "%s: null weight descriptor", what);
   REQUIRE(q->bits == 4, QMOE_ERR_UNSUPPORTED, "%s: bits=%d, only 4-bit weights are supported", what, q->bits);
   REQUIRE(q->group == 64, QMOE_ERR_UNSUPPORTED, "%s: group=%d, only group size 64 is supported", what, q->group);
   REQUIRE(q->experts == experts, QMOE_ERR_INVALID, "%s: experts=%d, expected %d", what, q->experts, experts);
   REQUIRE(q->rows == rows, QMOE_ERR_INVALID, "%s: rows=%d, expected %d", what, q->rows, rows);
   REQUIRE(q->in == in, QMOE_ERR_INVALID, "%s: in=%d, expected %d", what, q->in, in);
+  REQUIRE(q->layout == layout, QMOE_ERR_INVALID, "%s: layout=%d, expected %d (%s)", what, q->layout, layout,
+          layout == QMOE_LAYOUT_TILED ? "tile it with qmoe_tile_weight" : "row-major codes");
+  if (layout == QMOE_LAYOUT_TILED) {
+    REQUIRE(q->split == split, QMOE_ERR_INVALID, "%s: tiled with split=%d, expected %d", what, q->split, split);
+    REQUIRE_PTR(q->w, 16, "tiled weight");
+    return QMOE_OK;
+  }
   REQUIRE_PTR(q->w, 16, "weight codes");
   REQUIRE_PTR(q->scales, 2, "weight scales");
   REQUIRE_PTR(q->biases, 2, "weight biases");
@@ -95,7 +104,8 @@ const char* qmoe_last_error(void) { return g_last_error.c_str(); }
 
 size_t moe_route_workspace(int32_t T, int32_t H, int32_t E) {
   if (T <= 0 || H <= 0 || E <= 0 || H % 64 != 0) return 0;
-  return (size_t)qmoe::route_ksplit(T, H) * (size_t)T * (size_t)E * sizeof(float);
+  // per k-range: partial logits [T, E] and partial sums of squares [T]
+  return (size_t)qmoe::route_ksplit(T, H) * (size_t)T * (size_t)(E + 1) * sizeof(float);
 }
 
 int moe_route(const uint16_t* x_router, int32_t T, int32_t H, const uint16_t* norm_scale, float eps,
@@ -175,23 +185,23 @@ int qswitch_gate_up_geglu(const uint16_t* x_expert, int32_t T, int32_t H, const 
   const int E = gate_up->experts;
   REQUIRE(E >= 1 && E <= 256, QMOE_ERR_UNSUPPORTED, "qswitch_gate_up_geglu: E=%d outside [1, 256]", E);
   if (T == 0) return ok();
-  if (int rc = check_qweight(gate_up, "qswitch_gate_up_geglu gate_up", E, 2 * I, H)) return rc;
+  if (int rc = check_qweight(gate_up, "qswitch_gate_up_geglu gate_up", E, 2 * I, H, QMOE_LAYOUT_TILED, I)) return rc;
   REQUIRE_PTR(x_expert, 16, "qswitch_gate_up_geglu x_expert");
   REQUIRE_PTR(expert_offsets, 4, "qswitch_gate_up_geglu expert_offsets");
   REQUIRE_PTR(sorted_assign, 4, "qswitch_gate_up_geglu sorted_assign");
   REQUIRE_PTR(mid, 16, "qswitch_gate_up_geglu mid");
+  REQUIRE((long long)T * H * 2 < (1LL << 32), QMOE_ERR_UNSUPPORTED,
+          "qswitch_gate_up_geglu: activation bytes reach 2^32");
   int ncu = 0;
   if (int rc = num_cu_current(&ncu)) return rc;
   qmoe::SwitchArgs a{};
   a.a = x_expert;
   a.w = gate_up->w;
-  a.s = gate_up->scales;
-  a.b = gate_up->biases;
+  a.nblk = qmoe::tiled_blocks(2 * I, I);
   a.offsets = expert_offsets;
   a.assign = sorted_assign;
   a.out = mid;
   a.K = H;
-  a.Nw = 2 * I;
   a.Nout = I;
   a.E = E;
   a.ktop = k;
@@ -217,12 +227,13 @@ int qswitch_down_combine(const uint16_t* mid, int32_t T, int32_t k, int32_t I, c
   const int E = down->experts;
   REQUIRE(E >= 1 && E <= 256, QMOE_ERR_UNSUPPORTED, "qswitch_down_combine: E=%d outside [1, 256]", E);
   if (T == 0) return ok();
-  if (int rc = check_qweight(down, "qswitch_down_combine down", E, H, I)) return rc;
+  if (int rc = check_qweight(down, "qswitch_down_combine down", E, H, I, QMOE_LAYOUT_TILED, 0)) return rc;
   REQUIRE_PTR(mid, 16, "qswitch_down_combine mid");
   REQUIRE_PTR(expert_offsets, 4, "qswitch_down_combine expert_offsets");
   REQUIRE_PTR(sorted_assign, 4, "qswitch_down_combine sorted_assign");
   REQUIRE_PTR(weights, 4, "qswitch_down_combine weights");
   REQUIRE_PTR(y, 16, "qswitch_down_combine y");
+  REQUIRE((long long)T * k * I * 2 < (1LL << 32), QMOE_ERR_UNSUPPORTED, "qswitch_down_combine: mid bytes reach 2^32");
   const size_t need = qswitch_down_combine_workspace(T, k, H, deterministic);
   REQUIRE(workspace != nullptr && ws_bytes >= need, QMOE_ERR_WORKSPACE,
           "qswitch_down_combine: workspace of %zu bytes needed, %zu given", need, workspace ? ws_bytes : (size_t)0);
@@ -232,22 +243,45 @@ int qswitch_down_combine(const uint16_t* mid, int32_t T, int32_t k, int32_t I, c
   qmoe::SwitchArgs a{};
   a.a = mid;
   a.w = down->w;
-  a.s = down->scales;
-  a.b = down->biases;
+  a.nblk = qmoe::tiled_blocks(H, 0);
   a.offsets = expert_offsets;
   a.assign = sorted_assign;
-  a.route_w = weights;
   a.out = workspace;
   a.K = I;
-  a.Nw = H;
   a.Nout = H;
   a.E = E;
   a.ktop = k;
   a.rows_total = T * k;
   hipError_t err = qmoe::launch_down(a, ncu, stream);
   if (err != hipSuccess) return launched(err, "qswitch_down_combine (down)");
-  return launched(qmoe::launch_combine(static_cast<const float*>(workspace), T, k, H, y, stream),
+  return launched(qmoe::launch_combine(static_cast<const float*>(workspace), weights, T, k, H, y, stream),
                   "qswitch_down_combine (combine)");
+}
+
+size_t qmoe_tiled_weight_bytes(int32_t experts, int32_t rows, int32_t in, int32_t split) {
+  if (experts <= 0 || rows <= 0 || in <= 0 || in % 64 != 0 || split < 0) return 0;
+  if (split > 0 && (split % 64 != 0 || rows != 2 * split)) return 0;
+  return (size_t)experts * (size_t)qmoe::tiled_blocks(rows, split) * (size_t)(in / 64) * (size_t)qmoe::kTiledUnit;
+}
+
+int qmoe_tile_weight(const qmoe_qweight* src, int32_t split, void* dst, size_t dst_bytes, hipStream_t stream) {
+  REQUIRE(src != nullptr, QMOE_ERR_INVALID, "qmoe_tile_weight: null weight descriptor");
+  REQUIRE(src->experts >= 1 && src->rows >= 1, QMOE_ERR_INVALID, "qmoe_tile_weight: experts=%d rows=%d",
+          src->experts, src->rows);
+  REQUIRE(src->in > 0 && src->in % 64 == 0, QMOE_ERR_INVALID, "qmoe_tile_weight: in=%d must be a positive multiple of 64",
+          src->in);
+  REQUIRE(split >= 0, QMOE_ERR_INVALID, "qmoe_tile_weight: split=%d < 0", split);
+  REQUIRE(split == 0 || (split % 64 == 0 && src->rows == 2 * split), QMOE_ERR_INVALID,
+          "qmoe_tile_weight: split=%d needs rows == 2*split and split %% 64 == 0 (rows=%d)", split, src->rows);
+  if (int rc = check_qweight(src, "qmoe_tile_weight src", src->experts, src->rows, src->in)) return rc;
+  REQUIRE((long long)src->experts * src->rows * (src->in / 8) < (1LL << 31), QMOE_ERR_UNSUPPORTED,
+          "qmoe_tile_weight: more than 2^31 code words");
+  const size_t need = qmoe_tiled_weight_bytes(src->experts, src->rows, src->in, split);
+  REQUIRE_PTR(dst, 16, "qmoe_tile_weight dst");
+  REQUIRE(dst_bytes >= need, QMOE_ERR_INVALID, "qmoe_tile_weight: %zu bytes needed, %zu given", need, dst_bytes);
+  return launched(qmoe::launch_tile_weight(src->w, src->scales, src->biases, src->experts, src->rows, src->in, split,
+                                           static_cast<uint8_t*>(dst), stream),
+                  "qmoe_tile_weight");
 }
 
 int qlinear(const uint16_t* x, int32_t M, const qmoe_qweight* W, uint16_t* y, hipStream_t stream) {
@@ -257,19 +291,18 @@ int qlinear(const uint16_t* x, int32_t M, const qmoe_qweight* W, uint16_t* y, hi
   REQUIRE(K > 0 && K % 64 == 0, QMOE_ERR_INVALID, "qlinear: K=%d must be a positive multiple of 64", K);
   REQUIRE(N > 0 && N % 16 == 0, QMOE_ERR_INVALID, "qlinear: N=%d must be a positive multiple of 16", N);
   if (M == 0) return ok();
-  if (int rc = check_qweight(W, "qlinear W", 1, N, K)) return rc;
+  if (int rc = check_qweight(W, "qlinear W", 1, N, K, QMOE_LAYOUT_TILED, 0)) return rc;
   REQUIRE_PTR(x, 16, "qlinear x");
   REQUIRE_PTR(y, 16, "qlinear y");
+  REQUIRE((long long)M * K * 2 < (1LL << 32), QMOE_ERR_UNSUPPORTED, "qlinear: activation bytes reach 2^32");
   int ncu = 0;
   if (int rc = num_cu_current(&ncu)) return rc;
   qmoe::SwitchArgs a{};
   a.a = x;
   a.w = W->w;
-  a.s = W->scales;
-  a.b = W->biases;
+  a.nblk = qmoe::tiled_blocks(N, 0);
   a.out = y;
   a.K = K;
-  a.Nw = N;
   a.Nout = N;
   a.E = 1;
   a.ktop = 1;

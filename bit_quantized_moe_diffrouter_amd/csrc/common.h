@@ -8,6 +8,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+#include <type_traits>
+#include <utility>
+
 namespace qmoe {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));

@@ -32,27 +32,30 @@ hipError_t launch_sort(const int32_t* indices, int A, int E, int32_t* offsets, i
                        hipStream_t stream);
 
 // ---------------------------------------------------------------- switch / dense linears
+// Bytes of one tiled unit: (expert, block of 128 weight rows, 64-wide group) ->
+// 4096 bytes of codes in operand order + 128 (scale, bias) pairs.
+constexpr int kTiledUnit = 4608;
+int tiled_blocks(int rows, int split);
+hipError_t launch_tile_weight(const uint32_t* w, const uint16_t* s, const uint16_t* b, int E, int rows, int K,
+                              int split, uint8_t* dst, hipStream_t stream);
+
 struct SwitchArgs {
   const uint16_t* a;       // bf16 activation rows, row length K
-  const uint32_t* w;       // codes [E, Nw, K/8]
-  const uint16_t* s;       // bf16 scales [E, Nw, K/64]
-  const uint16_t* b;       // bf16 biases [E, Nw, K/64]
+  const void* w;           // tiled weight [E, nblk, K/64] units of kTiledUnit bytes
+  int nblk;                // tiled blocks per expert
   const int32_t* offsets;  // [E+1] sorted-row segments (switch modes)
   const int32_t* assign;   // [A] assignment id of each sorted row (switch modes)
-  const float* route_w;    // [A] routing weight of each assignment (down mode)
   void* out;
   int K;           // contraction length (multiple of 64)
-  int Nw;          // weight rows per expert
   int Nout;        // output columns
   int E;           // experts (1 for dense)
   int ktop;        // assignments per token
   int rows_total;  // dense: M; switch: A = T*k
   int ntiles;      // column tiles per row chunk (set by the launcher)
-  int sb_vec;      // scales/biases readable 4 groups at a time (set by the launcher)
 };
 hipError_t launch_gate_up_geglu(SwitchArgs a, int num_cu, hipStream_t stream);
 hipError_t launch_down(SwitchArgs a, int num_cu, hipStream_t stream);
 hipError_t launch_dense(SwitchArgs a, int num_cu, hipStream_t stream);
-hipError_t launch_combine(const float* D, int T, int k, int H, uint16_t* y, hipStream_t stream);
+hipError_t launch_combine(const float* D, const float* w, int T, int k, int H, uint16_t* y, hipStream_t stream);
 
 }  // namespace qmoe

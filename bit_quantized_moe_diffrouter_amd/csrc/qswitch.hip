@@ -1,159 +1,131 @@
-// 4-bit switch linears (gate_up + GeGLU, down + weighted combine) and the
-// dense 4-bit linear for gfx950.
+// 4-bit switch linears (gate_up + GeGLU, down) and the dense 4-bit linear
+// for gfx950, the weight tiling they read, and the weighted combine of the
+// down rows.
 //
 // What is computed (diffusion-gemma model.ts page, DiffExperts.forward):
 // every sorted row r of expert e multiplies its activation row by the
 // dequantized weight of e; gate_up splits the 2I outputs at I and applies
-// GeGLU (gelu_approx(gate) * up, vision.ts page, DiffVisionMLP); down scales
-// each row by its routing weight for the per-token sum over k.
+// GeGLU (gelu_approx(gate) * up, vision.ts page, DiffVisionMLP); the down rows
+// are summed per token with the routing weights.
 //
-// How.  A workgroup (4 waves) owns a work item = (expert, chunk of up to BM
-// sorted rows, tile of output columns).  The persistent grid walks the items
-// derived on the device from expert_offsets, so no host synchronisation is
-// needed for routing-dependent sizes.  Per 64-wide quantization group:
-//  * each wave streams its own weight rows from HBM straight into a private
-//    LDS ring with global_load_lds_dwordx4 (no VGPRs held while in flight;
-//    the ring keeps D groups outstanding) and reads them one group ahead;
-//  * every code becomes the exact bf16 value 128 + q with one v_and_or_b32
-//    per pair (see unpack_offset_codes);
-//  * the activation chunk and the group scales/biases are staged once per
-//    workgroup in LDS, the activations in the k order the unpacking produces;
-//  * v_mfma_f32_16x16x32_bf16 forms P = sum_k x_k (128 + q_k) and, against a
-//    ones operand, X = sum_k x_k; the group's affine is applied in fp32:
-//        sum_k x_k (s q_k + b) = s P + (b - 128 s) X.
-// All products are exact and the dequantized weight is never rounded, so the
-// only roundings are fp32 accumulation (and the bf16 output).
+// Weight tiling.  v_mfma_f32_16x16x32_bf16 wants lane l to hold operand row
+// l % 16; read straight from row-major codes every lane of a load touches a
+// different row and the vector L1 handles each lane as its own access.  The
+// weights are therefore re-laid once (qmoe_tile_weight) into 4608-byte units,
+// one per (expert, block of 128 weight rows, 64-wide group): 4096 bytes of
+// codes in the exact per-lane operand order, then the 128 rows' (scale, bias)
+// pairs in the order the lanes read them.  A wave streams one block: per group
+// four 1 KB and two 256-byte fully coalesced loads.  Within a code word the
+// nibbles are placed so that one v_and_or_b32 per pair yields two bf16 of
+// 128 + q in natural k order (no activation shuffling).
 //
-// The compiler does not order LDS reads after the LDS DMA that fills them,
-// so the ring waits are explicit: every wave issues the same vector-memory
-// operations in the same order, and the wait before reading group g+1 counts
-// exactly the operations issued after that group's DMA (RING_WAIT below).
+// Work items.  An item is (expert e, chunk of up to 32 sorted rows of e, tile
+// of NW weight blocks).  A persistent grid walks the items, derived on the
+// device from expert_offsets (no host synchronisation).  A chunk of at most 16
+// rows computes one 16-row MFMA tile, a larger one two.  The 4 waves of a
+// workgroup split the contraction KW ways and the blocks NW ways (KW*NW = 4);
+// each wave streams its operands straight into registers through a ring of D
+// slots that runs on across items.  The K-split partial sums meet once per
+// item in LDS, in a fixed order.
+//
+// Arithmetic per group: P = sum_k x_k (128 + q_k) and, against a ones operand,
+// X = sum_k x_k come from the MFMA; the group's affine is applied in fp32:
+//     sum_k x_k (s q_k + b) = s P + (b - 128 s) X.
+// The products are exact and the dequantized weight is never rounded; the
+// only roundings are the fp32 accumulation and the output conversion.
 #include "common.h"
 #include "launch.h"
-
-#define QMOE_AS_GLOBAL __attribute__((address_space(1)))
-#define QMOE_AS_LDS __attribute__((address_space(3)))
 
 namespace qmoe {
 
 enum : int { MODE_GATE_UP = 0, MODE_DOWN = 1, MODE_DENSE = 2 };
 
+namespace {
+
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
+constexpr int kBM = 32;            // sorted rows per chunk (at most two 16-row tiles)
+constexpr int kMaxBuckets = 257;   // experts (<= 256) + the dropped bucket of the down pass
+constexpr int kNS = 8;             // 16-row subtiles per tiled block
 
-#ifndef QMOE_SWITCH_WAVES_PER_SIMD
-#define QMOE_SWITCH_WAVES_PER_SIMD 2
-#endif
+struct Item {
+  int e;     // expert whose weights are used (0 for the dropped bucket)
+  int r0;    // first sorted row
+  int rows;  // rows of the chunk, 1..32
+  int tile;  // block tile
+  int zero;  // down pass, dropped bucket: the rows are written as zeros
+};
 
-// The switch kernels move every operand with LDS DMA (global_load_lds_*),
-// issued from inline asm so the compiler neither reorders them nor adds its
-// own (conservative) waits; the waits below are placed by hand from the fixed
-// per-wave issue order (see the pipeline description in the kernel).
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(size_t)((QMOE_AS_LDS const void*)p);
-}
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-// 64 lanes x 16 bytes from per-lane global addresses to lds + 16 * lane.
-__device__ __forceinline__ void dma_b128(const void* g, uint32_t lds) {
-  lds = __builtin_amdgcn_readfirstlane(lds);  // wave-uniform LDS base for M0
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-               :: "s"(lds), "v"(g) : "memory", "m0");
-}
-// 64 lanes x 4 bytes to lds + 4 * lane.
-__device__ __forceinline__ void dma_b32(const void* g, uint32_t lds) {
-  lds = __builtin_amdgcn_readfirstlane(lds);  // wave-uniform LDS base for M0
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
-               :: "s"(lds), "v"(g) : "memory", "m0");
-}
-// 64 lanes x 2 bytes, each zero-extended into the 4-byte slot lds + 4 * lane.
-__device__ __forceinline__ void dma_u16(const void* g, uint32_t lds) {
-  lds = __builtin_amdgcn_readfirstlane(lds);  // wave-uniform LDS base for M0
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_ushort %1, off"
-               :: "s"(lds), "v"(g) : "memory", "m0");
-}
-#pragma clang diagnostic pop
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit counter");
-  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+// What one wave does for one item.  The 4 waves split (K part, row tile,
+// block): a chunk of up to 16 rows has one row tile, so the waves split K
+// 4 / NBI ways; a larger chunk has two, each taken by its own waves, which
+// then split K 2 / NBI ways.  Each wave thus always computes one 16-row tile
+// against a whole 128-row block (8 subtiles).
+struct Role {
+  int nk;   // K parts of the item
+  int kp;   // this wave's K part
+  int m;    // row tile (0: rows 0-15, 1: rows 16-31)
+  int blk;  // weight block (within the expert)
+  int gk0, gk1;  // groups [gk0, gk1) of the contraction
+};
+
+// One ring slot: operands of one quantization group for one wave.
+struct Slot {
+  u32x4_t w[4];  // codes: 16 bytes = the operand words of subtiles 2i, 2i+1
+  u32x4_t s[2];  // (scale, bias) bf16 pairs of subtiles 4h .. 4h+3
+  u32x4_t a[2];  // activations of the lane's row: k = 16lq .. 16lq+7, 16lq+8 .. 16lq+15
+};
+
+// Pins the ring order: the slot's registers pass through an empty asm, so the
+// wait for its loads lands here and its consumers cannot be hoisted above the
+// loads issued by earlier steps.
+__device__ __forceinline__ void fence_slot(Slot& sl) {
+  asm volatile("" : "+v"(sl.w[0]), "+v"(sl.w[1]), "+v"(sl.w[2]), "+v"(sl.w[3])::"memory");
+  asm volatile("" : "+v"(sl.s[0]), "+v"(sl.s[1]), "+v"(sl.a[0]), "+v"(sl.a[1])::"memory");
 }
 
-template <int MODE, int MT, int NS, int KS, bool SBVEC>
-__global__ __launch_bounds__(kThreads, QMOE_SWITCH_WAVES_PER_SIMD) void qswitch_kernel(const SwitchArgs p) {
-  constexpr int BM = 16 * MT;                 // rows per work item
-  constexpr int CHUNKS = BM * KS * 8;         // 16-byte activation pieces per stage
-  static_assert(CHUNKS % kThreads == 0, "stage must split evenly over the workgroup");
-  static_assert(BM % 8 == 0, "row-xor swizzle spans 8 rows");
-  constexpr int NSH = (MODE == MODE_GATE_UP) ? NS / 2 : NS;  // output subtiles per wave
-  static_assert(MODE != MODE_GATE_UP || NS % 2 == 0, "gate_up pairs gate and up subtiles");
-  static_assert(NS == 2, "one 1 KB ring slot per group holds two 16-row subtiles");
-  constexpr int SB_ROWS = kWaves * NS * 16;   // weight rows of the workgroup
-#ifndef QMOE_SWITCH_STAGES_AHEAD
-#define QMOE_SWITCH_STAGES_AHEAD 4
-#endif
-  // stages issued ahead of the one computed (the scalar scale path stages twice
-  // the scale bytes, so it keeps one stage less to stay within 80 KB of LDS)
-  constexpr int R = SBVEC ? QMOE_SWITCH_STAGES_AHEAD : QMOE_SWITCH_STAGES_AHEAD - 1;
-  constexpr int D = R * KS;                    // weight ring depth (groups in flight per wave)
-  static_assert(R >= 2, "at least two stages ahead");
-  static_assert(2 * SB_ROWS == kThreads, "one thread per (row, scale|bias)");
-  static_assert(!SBVEC || KS % 2 == 0, "vector scale loads read group pairs");
-  // Pipeline (per wave, all DMA).  Stage s = KS groups; its activation pieces and
-  // scales (shared by the workgroup) live in slot s % (R+1) of a ring, and each
-  // wave's two 16-row weight subtiles of group g live in slot g % D of the
-  // wave's private ring.  Issue order, which every wave follows exactly:
-  //   prologue:   for s < R: act/scales(s), weights(s*KS .. s*KS+KS-1)
-  //   stage st:   [wait act/scales(st)] barrier; act/scales(st+R);
-  //               per group g: [wait weights(g+1)] read them; compute g; weights(g+D)
-  // so the activations of a stage always precede its weights in the in-order
-  // vmcnt counter and no wait drains the ring.  Ops issued after the one each
-  // wait needs (checked against a simulation of this order):
-  //   first ring read:       D - 1 + (R-1) LA
-  //   act/scales(st):        KS + (R-1)(LA+KS)
-  //   weights(g+1):          KS - 2 + (R-1)(LA+KS) + LA   (gl < KS-1)
-  //                          2(KS-1) + (R-2)(LA+KS) + LA  (gl = KS-1)
-  constexpr int APW = CHUNKS / kThreads;               // activation DMAs per wave per stage
-  constexpr int SPW = SBVEC ? KS / 2 : KS;             // scale DMAs per wave per stage
-  constexpr int LA = APW + SPW;
-  constexpr int N_W0 = D - 1 + (R - 1) * LA;
-  constexpr int N_ACT = KS + (R - 1) * (LA + KS);
-  constexpr int N_RING = KS - 2 + (R - 1) * (LA + KS) + LA;
-  constexpr int N_RING_LAST = 2 * (KS - 1) + (R - 2) * (LA + KS) + LA;
-  static_assert(N_RING < 64 && N_W0 < 64 && N_ACT < 64, "wait counts must fit vmcnt");
-  constexpr int A_BYTES = CHUNKS * 16;                 // activation bytes per stage
-  constexpr int S_WORDS = SPW * kThreads;              // 4-byte scale slots per stage
+// Calls f(0), f(1), ... with compile-time indices.
+template <class F, int... I>
+__device__ __forceinline__ void run_steps(F& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
 
-  // activations of a stage: piece p = (gl * BM + row) * 8 + (blk ^ (row & 7)) at 16 p
-  __shared__ __attribute__((aligned(16))) uint8_t lds_a[R + 1][A_BYTES];
-  // scales: slot [q][t], t = 2 * row + (0: scale, 1: bias); q = group pair (vector
-  // path, two bf16 per slot) or group (scalar path, one zero-extended bf16)
-  __shared__ __attribute__((aligned(16))) uint32_t lds_s[R + 1][S_WORDS];
-  // per-wave weight ring: slot = group % D, 2 subtiles x 16 rows x 32 bytes
-  __shared__ __attribute__((aligned(16))) uint8_t lds_w[kWaves][D][1024];
-  __shared__ int s_cum[kThreads + 2];
+}  // namespace
+
+template <int MODE, int NBI, int D>
+__global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
+  constexpr int BCOLS = (MODE == MODE_GATE_UP) ? 64 : 128;  // output columns per block
+
+  extern __shared__ __attribute__((aligned(16))) uint8_t qmm_lds[];  // partial sums [wave][kNS][64] f32x4
+  __shared__ int s_cum[kMaxBuckets + 1];  // chunk prefix per bucket
+  __shared__ int s_lo[kMaxBuckets];       // clamped segment [lo, hi) of each bucket
+  __shared__ int s_hi[kMaxBuckets];
   __shared__ int s_scan[kWaves];
-  __shared__ int s_src[BM];
-  __shared__ int s_dst[BM];
+  __shared__ int s_dst[2][kBM];           // down pass: assignment id of each chunk row
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar branches below)
   const int ln = lane & 15, lq = lane >> 4;
-  const int K = p.K, G = K / kGroup, KW = K / 8;
+  const int K = p.K, G = K / kGroup;
+  const int A = p.rows_total;
 
-  // ---- work decomposition: chunks of BM rows per expert bucket
-  const int nb = (MODE == MODE_DOWN) ? p.E + 1 : p.E;  // down also zero-fills dropped rows
+  // ---- chunks per bucket (switch modes) and the item count
+  const int nb = (MODE == MODE_DOWN) ? p.E + 1 : p.E;
   int total_chunks;
   if constexpr (MODE == MODE_DENSE) {
-    total_chunks = (p.rows_total + BM - 1) / BM;
+    total_chunks = (A + kBM - 1) / kBM;
   } else {
-    auto bucket_chunks = [&](int e) {
-      const int A = p.rows_total;
-      int lo = min(max(p.offsets[e], 0), A);
-      int hi = (e < p.E) ? min(max(p.offsets[e + 1], lo), A) : A;
-      return (hi - lo + BM - 1) / BM;
+    // bucket b < E is expert b's segment; bucket E (down only) holds the dropped rows
+    auto chunks_of = [&](int b) __attribute__((always_inline)) {
+      const int lo = min(max(p.offsets[b], 0), A);
+      const int hi = (b < p.E) ? min(max(p.offsets[b + 1], lo), A) : A;
+      s_lo[b] = lo;
+      s_hi[b] = hi;
+      return (hi - lo + kBM - 1) / kBM;
     };
-    const int c0 = (tid < nb) ? bucket_chunks(tid) : 0;
-    const int c1 = (tid == kThreads - 1 && nb > kThreads) ? bucket_chunks(kThreads) : 0;
+    // thread t counts bucket t; the last thread also bucket kThreads (E = 256, down)
+    const int c0 = (tid < nb) ? chunks_of(tid) : 0;
+    const int c1 = (tid == kThreads - 1 && nb > kThreads) ? chunks_of(kThreads) : 0;
     int tot;
     const int incl = block_inclusive_scan<kThreads>(c0 + c1, s_scan, &tot);
     if (tid < nb) s_cum[tid + 1] = incl - c1;
@@ -162,253 +134,334 @@ __global__ __launch_bounds__(kThreads, QMOE_SWITCH_WAVES_PER_SIMD) void qswitch_
     total_chunks = tot;
     __syncthreads();
   }
-  const int total_items = total_chunks * p.ntiles;
+  const int total_items = __builtin_amdgcn_readfirstlane(total_chunks * p.ntiles);
+  if ((int)blockIdx.x >= total_items) return;  // uniform: no barrier follows for this workgroup
 
-  const u32x4_t ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
-  const OffsetCodeConsts kc = offset_code_consts();
-
-  for (int item = blockIdx.x; item < total_items; item += gridDim.x) {
+  // item -> (expert, rows, tile); wave-uniform
+  auto decode = [&](int item) __attribute__((always_inline)) {
+    Item it;
     const int chunk = item / p.ntiles;
-    const int ntile = item - chunk * p.ntiles;
-    int e = 0, r0, rows;
-    bool zero_only = false;
+    it.tile = item - chunk * p.ntiles;
     if constexpr (MODE == MODE_DENSE) {
-      r0 = chunk * BM;
-      rows = min(BM, p.rows_total - r0);
+      it.e = 0;
+      it.zero = 0;
+      it.r0 = chunk * kBM;
+      it.rows = min(kBM, A - it.r0);
     } else {
       int lo = 0, hi = nb;  // s_cum[lo] <= chunk < s_cum[hi]
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
         if (s_cum[mid] <= chunk) lo = mid; else hi = mid;
       }
-      e = __builtin_amdgcn_readfirstlane(lo);
-      const int A = p.rows_total;
-      const int seg_lo = min(max(p.offsets[e], 0), A);
-      const int seg_hi = (e < p.E) ? min(max(p.offsets[e + 1], seg_lo), A) : A;
-      r0 = seg_lo + (chunk - s_cum[e]) * BM;
-      rows = min(BM, seg_hi - r0);
-      zero_only = (MODE == MODE_DOWN) && (e == p.E);
+      const int e = lo;
+      it.r0 = s_lo[e] + (chunk - s_cum[e]) * kBM;
+      it.rows = min(kBM, s_hi[e] - it.r0);
+      it.zero = (MODE == MODE_DOWN) && (e >= p.E);
+      it.e = it.zero ? 0 : e;
     }
+    it.e = __builtin_amdgcn_readfirstlane(it.e);
+    it.r0 = __builtin_amdgcn_readfirstlane(it.r0);
+    it.rows = __builtin_amdgcn_readfirstlane(it.rows);
+    it.tile = __builtin_amdgcn_readfirstlane(it.tile);
+    it.zero = __builtin_amdgcn_readfirstlane(it.zero);
+    return it;
+  };
+  auto role_of = [&](const Item& it) __attribute__((always_inline)) {
+    Role r;
+    const int nm = (it.rows > 16) ? 2 : 1;
+    r.nk = min(kWaves / (nm * NBI), G);  // no K part without a group
+    if (wave < r.nk * nm * NBI) {
+      r.kp = wave % r.nk;
+      r.m = (wave / r.nk) % nm;
+      r.blk = it.tile * NBI + wave / (r.nk * nm);
+      r.gk0 = r.kp * G / r.nk;
+      r.gk1 = (r.kp + 1) * G / r.nk;
+    } else {  // spare wave (contraction shorter than the K split): streams, never stores
+      r.kp = 0;
+      r.m = 0;
+      r.blk = 0x7fffffff;
+      r.gk0 = 0;
+      r.gk1 = G;
+    }
+    return r;
+  };
+  // owner (K part) of subtile j among the waves of one (row tile, block):
+  // gate_up keeps gate j and up j + 4 together
+  auto owner_of = [&](int j, int nk) __attribute__((always_inline)) {
+    return ((MODE == MODE_GATE_UP) ? (j & 3) : j) % nk;
+  };
 
-    __syncthreads();  // the previous item is done with s_src / s_dst / lds_a / lds_sb
-    if (tid < BM) {
-      const int r = r0 + tid;
-      int src = -1, dst = -1;
-      if (tid < rows) {
-        if constexpr (MODE == MODE_DENSE) {
-          src = r;
-          dst = r;
-        } else {
-          const int a = p.assign[r];
-          const bool ok = (a >= 0) && (a < p.rows_total);
-          if constexpr (MODE == MODE_GATE_UP) {
-            src = ok ? a / p.ktop : -1;
-            dst = r;
-          } else {
-            src = r;
-            dst = ok ? a : -1;
-          }
-        }
-      }
-      s_src[tid] = src;
-      s_dst[tid] = dst;
+  // ---- load cursor (per wave): the item and group whose operands are issued next
+  const uint8_t* const wbytes = (const uint8_t*)p.w;
+  const uint8_t* const abytes = (const uint8_t*)p.a;
+  const uint32_t arow = K * 2;                     // bytes per activation row
+  const uint32_t c_off = lane * 16;                // code bytes of this lane in a unit
+  const uint32_t s_off = 4096 + ln * 16;           // scale bytes of this lane in a unit
+  Item linfo = decode(blockIdx.x);
+  Role lrole = role_of(linfo);
+  int lg = lrole.gk0;
+  int n_item = blockIdx.x + gridDim.x;
+  bool n_valid = n_item < total_items;
+  Item ninfo = n_valid ? decode(n_item) : linfo;
+  const uint8_t* l_wbase;  // unit (expert, block, group 0) of this wave
+  uint32_t l_aoff;         // activation row offset (bytes) of the lane's row
+  int l_loc = 0;           // items the load cursor has entered (s_dst parity)
+  // Assignment ids of the item after the load cursor's, loaded at the end of
+  // every step (so the item switch uses a value loaded at least a step before):
+  // gate_up: of the lane's row (its token); down: of chunk row lane % 32.
+  int pf_raw = 0;
+
+  auto set_weight_base = [&](const Item& it, const Role& r) __attribute__((always_inline)) {
+    const int blk = min(r.blk, p.nblk - 1);  // past the last block: any valid one (never stored)
+    l_wbase = wbytes + ((size_t)it.e * p.nblk + blk) * (size_t)G * kTiledUnit;
+  };
+  auto raw_assign = [&](const Item& it) __attribute__((always_inline)) {
+    if constexpr (MODE == MODE_GATE_UP) {
+      const Role r = role_of(it);
+      return p.assign[it.r0 + min(16 * r.m + ln, it.rows - 1)];
+    } else if constexpr (MODE == MODE_DOWN) {
+      return p.assign[min(it.r0 + (lane & 31), A - 1)];
+    } else {
+      return 0;
+    }
+  };
+  auto put_dst = [&](int loc, const Item& it, int raw) __attribute__((always_inline)) {  // down only
+    const int lr = lane & 31;
+    s_dst[loc & 1][lr] = (lr < it.rows && raw >= 0 && raw < A) ? raw : -1;
+  };
+  auto set_act_offset = [&](const Item& it, const Role& r, int raw) __attribute__((always_inline)) {
+    int src;
+    if constexpr (MODE == MODE_GATE_UP) {
+      src = (raw >= 0 && raw < A) ? raw / p.ktop : 0;
+    } else {
+      src = it.r0 + min(16 * r.m + ln, it.rows - 1);  // down: sorted mid row; dense: input row
+    }
+    l_aoff = (uint32_t)src * arow + lq * 32;
+  };
+  {
+    const int raw0 = raw_assign(linfo);
+    pf_raw = raw_assign(ninfo);
+    set_weight_base(linfo, lrole);
+    set_act_offset(linfo, lrole, raw0);
+    if constexpr (MODE == MODE_DOWN) put_dst(0, linfo, raw0);
+  }
+
+  auto issue = [&](Slot& sl) __attribute__((always_inline)) {
+    const uint8_t* u = l_wbase + (size_t)lg * kTiledUnit;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sl.w[i] = *(const u32x4_t*)(u + c_off + i * 1024);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) sl.s[h] = *(const u32x4_t*)(u + s_off + h * 256);
+    const uint8_t* ab = abytes + (size_t)lg * 128 + l_aoff;
+    sl.a[0] = *(const u32x4_t*)(ab);
+    sl.a[1] = *(const u32x4_t*)(ab + 16);
+  };
+  auto advance_load = [&]() __attribute__((always_inline)) {
+    if (++lg < lrole.gk1) return;
+    if (!n_valid) {  // past the last item: keep re-reading the last item's groups (never used)
+      lg = lrole.gk0;
+      return;
+    }
+    linfo = ninfo;
+    lrole = role_of(linfo);
+    lg = lrole.gk0;
+    set_weight_base(linfo, lrole);
+    set_act_offset(linfo, lrole, pf_raw);
+    ++l_loc;
+    if constexpr (MODE == MODE_DOWN) put_dst(l_loc, linfo, pf_raw);
+    n_item += gridDim.x;
+    n_valid = n_item < total_items;
+    if (n_valid) ninfo = decode(n_item);
+  };
+
+  Slot ring[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    issue(ring[d]);
+    asm volatile("" ::: "memory");  // keeps the slots' loads in ring order
+    advance_load();
+    if constexpr (MODE != MODE_DENSE) pf_raw = raw_assign(ninfo);
+  }
+
+  const u32x4_t ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  const OffsetCodeConsts kc = offset_code_consts();
+
+  f32x4_t acc[kNS];
+#pragma unroll
+  for (int j = 0; j < kNS; ++j) acc[j] = zero4();
+
+  int c_item = blockIdx.x, c_loc = 0;
+  Item cinfo = decode(c_item);
+  Role crole = role_of(cinfo);
+  int cg = crole.gk0;
+
+  // one group of the current item from slot `sl`
+  auto compute = [&](Slot& sl) __attribute__((always_inline)) {
+    f32x4_t X = mfma16x16x32(sl.a[0], ones, zero4());
+    X = mfma16x16x32(sl.a[1], ones, X);
+#pragma unroll
+    for (int j = 0; j < kNS; ++j) {
+      const uint32_t sb = sl.s[j >> 2][j & 3];
+      const float sc = __uint_as_float(sb << 16);
+      const float cc = __uint_as_float(sb & 0xffff0000u) - 128.0f * sc;
+      const u32x4_t b0 = unpack_offset_codes(sl.w[j >> 1][(j & 1) * 2], kc);
+      const u32x4_t b1 = unpack_offset_codes(sl.w[j >> 1][(j & 1) * 2 + 1], kc);
+      f32x4_t P = mfma16x16x32(sl.a[0], b0, zero4());
+      P = mfma16x16x32(sl.a[1], b1, P);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[j][i] = __builtin_fmaf(cc, X[i], __builtin_fmaf(sc, P[i], acc[j][i]));
+    }
+  };
+
+  // end of the current item: every wave parks its partial sums in LDS (its
+  // accumulators are then free for the next item); the owner of each subtile
+  // adds the K parts in K order and writes the outputs
+  auto finish_item = [&]() __attribute__((always_inline)) {
+    f32x4_t* red = (f32x4_t*)qmm_lds;
+    const int nk = crole.nk;
+    const int nm = (cinfo.rows > 16) ? 2 : 1;
+#pragma unroll
+    for (int j = 0; j < kNS; ++j) {
+      red[(wave * kNS + j) * 64 + lane] = acc[j];
+      acc[j] = zero4();
     }
     __syncthreads();
-
-    // weight row (within the expert) of the workgroup's row slot t: wave t/(16 NS),
-    // subtile t/16 % NS, row t % 16; rows of column tiles past the end map to a
-    // valid row (computed on, never stored)
-    auto wg_row = [&](int t) {
-      const int tw = t / (16 * NS), tj = (t / 16) % NS, tn = t % 16;
-      int c, row;
-      if constexpr (MODE == MODE_GATE_UP) {
-        c = ntile * (kWaves * 16 * NSH) + tw * (16 * NSH) + 16 * (tj % NSH);
-        row = (tj < NSH) ? c : p.Nout + c;
-      } else {
-        c = ntile * (kWaves * 16 * NS) + tw * (16 * NS) + 16 * tj;
-        row = c;
-      }
-      return (c < p.Nout ? row : 0) + tn;
-    };
-    // this wave's output subtiles
-    int ocol[NSH];
-    bool act[NSH];
+    if (!cinfo.zero || MODE == MODE_DOWN) {
+      const int blk = crole.blk;
+      const int wbase = wave - crole.kp;  // wave of K part 0 with the same row tile and block
+      if (blk < p.nblk) {
+        constexpr int NOUT = (MODE == MODE_GATE_UP) ? 4 : kNS;  // output subtiles of a block
 #pragma unroll
-    for (int j = 0; j < NSH; ++j) {
-      ocol[j] = ntile * (kWaves * 16 * NSH) + wave * (16 * NSH) + 16 * j;
-      act[j] = ocol[j] < p.Nout;
+        for (int j = 0; j < NOUT; ++j) {
+          if (owner_of(j, nk) != crole.kp) continue;
+          const int col = blk * BCOLS + 16 * j + ln;
+          if (col >= p.Nout) continue;
+          f32x4_t v0 = red[(wbase * kNS + j) * 64 + lane], v1;
+          if constexpr (MODE == MODE_GATE_UP) v1 = red[(wbase * kNS + j + 4) * 64 + lane];
+          for (int k = 1; k < nk; ++k) {
+            const f32x4_t t0 = red[((wbase + k) * kNS + j) * 64 + lane];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v0[i] += t0[i];
+            if constexpr (MODE == MODE_GATE_UP) {
+              const f32x4_t t1 = red[((wbase + k) * kNS + j + 4) * 64 + lane];
+#pragma unroll
+              for (int i = 0; i < 4; ++i) v1[i] += t1[i];
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int lr = 16 * crole.m + 4 * lq + i;
+            if (lr >= cinfo.rows) continue;
+            if constexpr (MODE == MODE_GATE_UP) {
+              ((uint16_t*)p.out)[(size_t)(cinfo.r0 + lr) * p.Nout + col] = f32_to_bf16_bits(gelu_tanh(v0[i]) * v1[i]);
+            } else if constexpr (MODE == MODE_DOWN) {
+              const int a = s_dst[c_loc & 1][lr];
+              if (a >= 0) ((float*)p.out)[(size_t)a * p.Nout + col] = cinfo.zero ? 0.0f : v0[i];
+            } else {
+              ((uint16_t*)p.out)[(size_t)(cinfo.r0 + lr) * p.Nout + col] = f32_to_bf16_bits(v0[i]);
+            }
+          }
+        }
+      }
     }
+    (void)nm;
+    __syncthreads();  // partial-sum buffer free again
+  };
 
-    f32x4_t acc[MT][NS];
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-#pragma unroll
-      for (int j = 0; j < NS; ++j) acc[m][j] = zero4();
-
-    if (!zero_only) {
-      // weight DMA: lane -> (subtile l/32, row l/2 % 16, half l % 2) of the 32-byte
-      // group segment; past the last group it reloads the last one (not used)
-      const uint32_t* wsrc =
-          p.w + ((size_t)e * p.Nw + wg_row(wave * 32 + (lane >> 1))) * KW + (lane & 1) * 4;
-      const uint8_t* ring = &lds_w[wave][0][0];
-      const uint32_t ring_lds = lds_addr(ring);
-      auto dma_weights = [&](int g) { dma_b128(wsrc + min(g, G - 1) * 8, ring_lds + (g % D) * 1024); };
-
-      // scale DMA: thread t = 2 * row + which copies scale (which 0) or bias of row
-      const uint16_t* ssrc = ((tid & 1) ? p.b : p.s) + ((size_t)e * p.Nw + wg_row(tid >> 1)) * G;
-      // activation DMA: instruction i of this wave fills pieces (i * kWaves + wave) * 64 + lane
-      const uint16_t* asrc[APW];
-#pragma unroll
-      for (int i = 0; i < APW; ++i) {
-        const int pc = (i * kWaves + wave) * 64 + lane;
-        const int row = (pc >> 3) % BM, gl = (pc >> 3) / BM, blk = (pc & 7) ^ (row & 7);
-        const int src = s_src[row];
-        asrc[i] = p.a + (size_t)(src >= 0 ? src : 0) * K + gl * kGroup + blk * 8;
-      }
-      const int NST = (G + KS - 1) / KS;
-      auto dma_stage = [&](int st, int buf) {  // exactly LA DMAs into activation/scale slot buf
-        const int stc = min(st, NST - 1);  // past the end: the last stage again (not used)
-#pragma unroll
-        for (int i = 0; i < APW; ++i) {
-          // groups past G (last partial stage) reload group G-1; they are skipped in compute
-          const int gl = ((i * kWaves + wave) * 64 + lane) / (8 * BM);
-          const int g = min(stc * KS + gl, G - 1);
-          dma_b128(asrc[i] + (g - gl) * kGroup, lds_addr(&lds_a[buf][(i * kWaves + wave) * 1024]));
-        }
-        const int g0 = stc * KS;
-#pragma unroll
-        for (int q = 0; q < SPW; ++q) {
-          const uint32_t dst = lds_addr(&lds_s[buf][q * kThreads + wave * 64]);
-          if constexpr (SBVEC)
-            dma_b32(ssrc + g0 + 2 * q, dst);
-          else
-            dma_u16(ssrc + min(g0 + q, G - 1), dst);
-        }
-      };
-
-      // ---- prologue: R stages, each activations/scales then its weights
-#pragma unroll
-      for (int s0 = 0; s0 < R; ++s0) {
-        dma_stage(s0, s0);
-#pragma unroll
-        for (int gl = 0; gl < KS; ++gl) dma_weights(s0 * KS + gl);
-      }
-      wait_vmcnt<N_W0>();
-      u32x2_t wcur[NS];
-#pragma unroll
-      for (int j = 0; j < NS; ++j) wcur[j] = *(const u32x2_t*)(ring + j * 512 + ln * 32 + lq * 8);
-
-      int buf = 0, issue_buf = R;  // activation slots of the stage computed / being issued
-      for (int st = 0; st < NST; ++st) {
-        wait_vmcnt<N_ACT>();
-        __syncthreads();  // stage st landed for every wave; stage st-1's slot is free
-        dma_stage(st + R, issue_buf);
-#pragma unroll
-        for (int gl = 0; gl < KS; ++gl) {
-          const int g = st * KS + gl;
-          if (gl < KS - 1) wait_vmcnt<N_RING>(); else wait_vmcnt<N_RING_LAST>();
-          u32x2_t wnext[NS];
-#pragma unroll
-          for (int j = 0; j < NS; ++j)
-            wnext[j] = *(const u32x2_t*)(ring + ((g + 1) % D) * 1024 + j * 512 + ln * 32 + lq * 8);
-
-          if (g < G) {
-            u32x4_t b0[NS], b1[NS];
-            float sc[NS], cc[NS];
-#pragma unroll
-            for (int j = 0; j < NS; ++j) {
-              b0[j] = unpack_offset_codes(wcur[j].x, kc);
-              b1[j] = unpack_offset_codes(wcur[j].y, kc);
-              const int t2 = 2 * (wave * (16 * NS) + 16 * j + ln);
-              const u32x2_t sb = *(const u32x2_t*)&lds_s[buf][(SBVEC ? gl / 2 : gl) * kThreads + t2];
-              const int sh = (SBVEC && (gl & 1)) ? 0 : 16;
-              sc[j] = __uint_as_float(sh ? (sb.x << 16) : (sb.x & 0xffff0000u));
-              const float bias = __uint_as_float(sh ? (sb.y << 16) : (sb.y & 0xffff0000u));
-              cc[j] = bias - 128.0f * sc[j];
-            }
-            // all MFMAs of the group first, then the fp32 affine
-            u32x4_t a0[MT], a1[MT];
-#pragma unroll
-            for (int m = 0; m < MT; ++m) {
-              const int row = 16 * m + ln;
-              const uint8_t* base = &lds_a[buf][(gl * BM + row) * 128];
-              a0[m] = permute_pairs(*(const u32x4_t*)(base + (((2 * lq) ^ (row & 7)) * 16)));
-              a1[m] = permute_pairs(*(const u32x4_t*)(base + (((2 * lq + 1) ^ (row & 7)) * 16)));
-            }
-            f32x4_t X[MT], P[MT][NS];
-#pragma unroll
-            for (int m = 0; m < MT; ++m) {
-              X[m] = mfma16x16x32(a0[m], ones, zero4());
-#pragma unroll
-              for (int j = 0; j < NS; ++j) P[m][j] = mfma16x16x32(a0[m], b0[j], zero4());
-            }
-#pragma unroll
-            for (int m = 0; m < MT; ++m) {
-              X[m] = mfma16x16x32(a1[m], ones, X[m]);
-#pragma unroll
-              for (int j = 0; j < NS; ++j) P[m][j] = mfma16x16x32(a1[m], b1[j], P[m][j]);
-            }
-#pragma unroll
-            for (int m = 0; m < MT; ++m)
-#pragma unroll
-              for (int j = 0; j < NS; ++j)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                  acc[m][j][i] = __builtin_fmaf(cc[j], X[m][i], __builtin_fmaf(sc[j], P[m][j][i], acc[m][j][i]));
-          }
-          // refill the slot of group g (read into wcur one group ago) with group g + D
-          dma_weights(g + D);
-#pragma unroll
-          for (int j = 0; j < NS; ++j) wcur[j] = wnext[j];
-        }
-        buf = (buf == R) ? 0 : buf + 1;
-        issue_buf = (issue_buf == R) ? 0 : issue_buf + 1;
-      }
-      wait_vmcnt<0>();  // drain the tail (reloads) before the buffers are reused
+  // One ring step on slot d: compute the current group, refill the slot.  Every
+  // step issues its loads, also after the last item (compute is skipped then):
+  // the loop has a single exit at the end of a block of D steps and the wait
+  // before each slot always counts the loads of the D - 1 slots issued after it.
+  bool done = false;
+  auto step = [&](auto d_tag) __attribute__((always_inline)) {
+    constexpr int d = decltype(d_tag)::value;
+    fence_slot(ring[d]);
+    if (!done && !cinfo.zero && crole.blk < p.nblk) compute(ring[d]);
+    issue(ring[d]);
+    asm volatile("" ::: "memory");  // keeps the slots' loads in ring order
+    advance_load();
+    if constexpr (MODE != MODE_DENSE) pf_raw = raw_assign(ninfo);
+    if (done || ++cg < crole.gk1) return;
+    finish_item();
+    c_item += gridDim.x;
+    if (c_item >= total_items) {
+      done = true;
+      return;
     }
+    ++c_loc;
+    cinfo = decode(c_item);
+    crole = role_of(cinfo);
+    cg = crole.gk0;
+  };
+  do {
+    run_steps(step, std::make_integer_sequence<int, D>{});
+  } while (!done);
+  // the loads issued past the end are consumed here (they complete before the wave ends)
+#pragma unroll
+  for (int d = 0; d < D; ++d) fence_slot(ring[d]);
+}
 
-    // ---- epilogue: lane holds column ocol[j] + ln, rows 16m + 4lq + i
+// ---------------------------------------------------------------- weight tiling
+// Weight row of block b, subtile j, row n (split > 0: gate rows then up rows).
+__device__ __forceinline__ int tiled_row(int b, int j, int n, int split) {
+  if (split > 0) return (j < 4) ? 64 * b + 16 * j + n : split + 64 * b + 16 * (j - 4) + n;
+  return 128 * b + 16 * j + n;
+}
+
+// Code word of 8 codes c0..c7 (code c at bits 4c) -> the operand order: code 2p
+// at bits 4p, code 2p+1 at bits 16 + 4p (p = 0..3).
+__device__ __forceinline__ uint32_t operand_word(uint32_t w) {
+  uint32_t r = 0;
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
+  for (int pp = 0; pp < 4; ++pp) {
+    r |= ((w >> (8 * pp)) & 0xFu) << (4 * pp);
+    r |= ((w >> (8 * pp + 4)) & 0xFu) << (16 + 4 * pp);
+  }
+  return r;
+}
+
+// One thread per 16-byte piece of the tiled buffer.
+__global__ __launch_bounds__(256) void tile_weight_kernel(const uint32_t* __restrict__ w, const uint16_t* __restrict__ s,
+                                                          const uint16_t* __restrict__ bi, int E, int rows, int K,
+                                                          int split, int nblk, uint8_t* __restrict__ dst) {
+  const int G = K / 64, KW = K / 8;
+  const long long pieces = (long long)E * nblk * G * (kTiledUnit / 16);
+  const long long c = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (c >= pieces) return;
+  const long long u = c / (kTiledUnit / 16);
+  const int q = (int)(c - u * (kTiledUnit / 16));
+  const int g = (int)(u % G);
+  const int b = (int)((u / G) % nblk);
+  const int e = (int)(u / ((long long)G * nblk));
+  u32x4_t out = {0u, 0u, 0u, 0u};
+  if (q < 256) {  // codes: instruction i, lane L -> subtiles 2i, 2i+1 of lane (L % 16, L / 16)
+    const int i = q >> 6, L = q & 63, n = L & 15, kq = L >> 4;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int lr = 16 * m + 4 * lq + i;
-        if (lr >= rows) continue;
-        if constexpr (MODE == MODE_GATE_UP) {
-          uint16_t* out = (uint16_t*)p.out;
-          const size_t orow = (size_t)s_dst[lr] * p.Nout;
+    for (int t = 0; t < 2; ++t) {
+      const int row = tiled_row(b, 2 * i + t, n, split);
+      if (row < rows) {
+        const uint32_t* src = w + ((size_t)e * rows + row) * KW + g * 8 + 2 * kq;
+        out[2 * t] = operand_word(src[0]);
+        out[2 * t + 1] = operand_word(src[1]);
+      }
+    }
+  } else {  // (scale, bias) of subtiles 4h .. 4h+3 for row n of each
+    const int h = (q - 256) >> 4, n = (q - 256) & 15;
 #pragma unroll
-          for (int j = 0; j < NSH; ++j) {
-            if (!act[j]) continue;
-            const float gte = acc[m][j][i], up = acc[m][NSH + j][i];
-            out[orow + ocol[j] + ln] = f32_to_bf16_bits(gelu_tanh(gte) * up);
-          }
-        } else if constexpr (MODE == MODE_DOWN) {
-          const int a = s_dst[lr];
-          if (a < 0) continue;
-          float* out = (float*)p.out;
-          const float wgt = zero_only ? 0.0f : p.route_w[a];
-#pragma unroll
-          for (int j = 0; j < NS; ++j) {
-            if (!act[j]) continue;
-            out[(size_t)a * p.Nout + ocol[j] + ln] = zero_only ? 0.0f : wgt * acc[m][j][i];
-          }
-        } else {
-          uint16_t* out = (uint16_t*)p.out;
-#pragma unroll
-          for (int j = 0; j < NS; ++j) {
-            if (!act[j]) continue;
-            out[(size_t)(r0 + lr) * p.Nout + ocol[j] + ln] = f32_to_bf16_bits(acc[m][j][i]);
-          }
-        }
+    for (int jj = 0; jj < 4; ++jj) {
+      const int row = tiled_row(b, 4 * h + jj, n, split);
+      if (row < rows) {
+        const size_t si = ((size_t)e * rows + row) * G + g;
+        out[jj] = (uint32_t)s[si] | ((uint32_t)bi[si] << 16);
       }
     }
   }
+  *(u32x4_t*)(dst + c * 16) = out;
 }
 
-// y[t, h] = bf16( sum_{j<k} D[t*k + j, h] ), summed in j order (fp32).
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ D, int T, int k, int H,
-                                                      uint16_t* __restrict__ y) {
+// y[t, h] = bf16( sum_{j<k} w[t, j] * D[t*k + j, h] ), products and sum in fp32, j order.
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ D, const float* __restrict__ w, int T,
+                                                      int k, int H, uint16_t* __restrict__ y) {
   const int H4 = H / 4;
   const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
   if (idx >= (long long)T * H4) return;
@@ -417,7 +470,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int j = 0; j < k; ++j) {
     const float4 v = *(const float4*)(base + (size_t)j * H);
-    s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+    const float wj = w[(size_t)t * k + j];
+    s.x += wj * v.x;
+    s.y += wj * v.y;
+    s.z += wj * v.z;
+    s.w += wj * v.w;
   }
   u32x2_t o;
   o.x = pack_bf16x2(s.x, s.y);
@@ -427,56 +484,67 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 // ------------------------------------------------------------------ launchers
 namespace {
-// Tile shape of the switch kernels (overridable at build time for tuning sweeps).
-#ifndef QMOE_SWITCH_MT
-#define QMOE_SWITCH_MT 2
-#endif
-#ifndef QMOE_SWITCH_KS
-#define QMOE_SWITCH_KS 2
-#endif
-#ifndef QMOE_SWITCH_WG_PER_CU
-#define QMOE_SWITCH_WG_PER_CU 2
-#endif
-constexpr int kMT = QMOE_SWITCH_MT, kKS = QMOE_SWITCH_KS;
-constexpr int kBM = 16 * kMT;
-constexpr int kWgPerCu = QMOE_SWITCH_WG_PER_CU;  // resident workgroups per CU (LDS-bound)
 
-template <int MODE, int NS>
-hipError_t launch_switch(SwitchArgs a, int extra_buckets, int num_cu, hipStream_t stream) {
-  constexpr int NSH = (MODE == MODE_GATE_UP) ? NS / 2 : NS;
-  const int cols = kWaves * 16 * NSH;
-  a.ntiles = (a.Nout + cols - 1) / cols;
-  const int G = a.K / 64;
-  a.sb_vec = (kKS % 2 == 0) && (G % kKS == 0) && ((uintptr_t)a.s % 4 == 0) && ((uintptr_t)a.b % 4 == 0);
+template <int MODE, int NBI, int D>
+hipError_t launch_cfg(SwitchArgs a, int extra_buckets, int num_cu, hipStream_t stream) {
+  a.ntiles = (a.nblk + NBI - 1) / NBI;
+  const size_t lds = (size_t)kWaves * kNS * 64 * 16;  // partial sums of every wave
   long long chunks;
   if (MODE == MODE_DENSE)
     chunks = (a.rows_total + kBM - 1) / kBM;
   else
-    chunks = (a.rows_total + kBM - 1) / kBM + (long long)min(a.E, a.rows_total) + extra_buckets;
-  long long items = chunks * a.ntiles;
-  long long grid = min(items, (long long)num_cu * kWgPerCu);
+    chunks = (a.rows_total + kBM - 1) / kBM + (long long)std::min(a.E, a.rows_total) + extra_buckets;
+  const long long items = chunks * a.ntiles;
+  long long grid = std::min(items, (long long)num_cu * 2);
   if (grid < 1) grid = 1;
-  if (a.sb_vec)
-    hipLaunchKernelGGL((qswitch_kernel<MODE, kMT, NS, kKS, kKS % 2 == 0>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL((qswitch_kernel<MODE, kMT, NS, kKS, false>), dim3((unsigned)grid), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL((qmm_kernel<MODE, NBI, D>), dim3((unsigned)grid), dim3(kThreads), lds, stream, a);
   return hipGetLastError();
 }
+
+// Blocks per item and ring depth: one block per item when a single-tile chunk
+// still leaves each of the 4 K parts at least 3 groups, else two; the ring is
+// as deep as the fewest groups a wave owns allow (at most 4), so the load
+// cursor is never more than one item ahead of the compute cursor.
+template <int MODE>
+hipError_t launch_mode(SwitchArgs a, int extra_buckets, int num_cu, hipStream_t stream) {
+  const int G = a.K / 64;
+  const int nbi = (G >= 12) ? 1 : 2;
+  const int depth = std::min(4, std::max(1, G / (kWaves / nbi)));  // groups of the smallest K part
+  if (nbi == 1) {
+    if (depth >= 4) return launch_cfg<MODE, 1, 4>(a, extra_buckets, num_cu, stream);
+    return launch_cfg<MODE, 1, 3>(a, extra_buckets, num_cu, stream);
+  }
+  if (depth >= 4) return launch_cfg<MODE, 2, 4>(a, extra_buckets, num_cu, stream);
+  if (depth == 3) return launch_cfg<MODE, 2, 3>(a, extra_buckets, num_cu, stream);
+  if (depth == 2) return launch_cfg<MODE, 2, 2>(a, extra_buckets, num_cu, stream);
+  return launch_cfg<MODE, 2, 1>(a, extra_buckets, num_cu, stream);
+}
+
 }  // namespace
 
 hipError_t launch_gate_up_geglu(SwitchArgs a, int num_cu, hipStream_t stream) {
-  return launch_switch<MODE_GATE_UP, 2>(a, 0, num_cu, stream);
+  return launch_mode<MODE_GATE_UP>(a, 0, num_cu, stream);
 }
 hipError_t launch_down(SwitchArgs a, int num_cu, hipStream_t stream) {
-  return launch_switch<MODE_DOWN, 2>(a, 1, num_cu, stream);
+  return launch_mode<MODE_DOWN>(a, 1, num_cu, stream);
 }
 hipError_t launch_dense(SwitchArgs a, int num_cu, hipStream_t stream) {
-  return launch_switch<MODE_DENSE, 2>(a, 0, num_cu, stream);
+  return launch_mode<MODE_DENSE>(a, 0, num_cu, stream);
 }
-hipError_t launch_combine(const float* D, int T, int k, int H, uint16_t* y, hipStream_t stream) {
+hipError_t launch_combine(const float* D, const float* w, int T, int k, int H, uint16_t* y, hipStream_t stream) {
   const long long n = (long long)T * (H / 4);
   const long long blocks = (n + 255) / 256;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, D, T, k, H, y);
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, D, w, T, k, H, y);
+  return hipGetLastError();
+}
+int tiled_blocks(int rows, int split) { return split > 0 ? split / 64 : (rows + 127) / 128; }
+hipError_t launch_tile_weight(const uint32_t* w, const uint16_t* s, const uint16_t* b, int E, int rows, int K,
+                              int split, uint8_t* dst, hipStream_t stream) {
+  const int nblk = tiled_blocks(rows, split);
+  const long long pieces = (long long)E * nblk * (K / 64) * (kTiledUnit / 16);
+  const long long blocks = (pieces + 255) / 256;
+  hipLaunchKernelGGL(tile_weight_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, w, s, b, E, rows, K, split,
+                     nblk, dst);
   return hipGetLastError();
 }
 

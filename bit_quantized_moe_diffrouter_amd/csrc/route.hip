@@ -75,6 +75,7 @@ __global__ __launch_bounds__(kRThreads) void route_logits_kernel(const RouteArgs
 
   // staging piece of this thread: token tt, group-in-stage gl, block blk
   const int s_tt = tid >> 5, s_gl = (tid >> 3) & 3, s_blk = tid & 7;
+  float ssq = 0.f;  // this thread's share of sum(x^2) over the k-range (for the norm)
 
   for (int gs = g_begin; gs < g_end; gs += kRKS) {
     // weights of this stage (issued first so their latency hides under the staging)
@@ -101,8 +102,11 @@ __global__ __launch_bounds__(kRThreads) void route_logits_kernel(const RouteArgs
         const u32x4_t nv = *(const u32x4_t*)(p.norm_scale + h);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          u[2 * q] = (bf16_lo_f32(xv[q]) * bf16_lo_f32(nv[q])) * p.root;
-          u[2 * q + 1] = (bf16_hi_f32(xv[q]) * bf16_hi_f32(nv[q])) * p.root;
+          const float xa = bf16_lo_f32(xv[q]), xb = bf16_hi_f32(xv[q]);
+          ssq = __builtin_fmaf(xa, xa, ssq);
+          ssq = __builtin_fmaf(xb, xb, ssq);
+          u[2 * q] = (xa * bf16_lo_f32(nv[q])) * p.root;
+          u[2 * q + 1] = (xb * bf16_hi_f32(nv[q])) * p.root;
         }
       } else {
 #pragma unroll
@@ -164,6 +168,11 @@ __global__ __launch_bounds__(kRThreads) void route_logits_kernel(const RouteArgs
     __syncthreads();
   }
 
+  // partial sum of squares of each token row over this k-range (32 threads per token)
+#pragma unroll
+  for (int o = 16; o >= 1; o >>= 1) ssq += __shfl_xor(ssq, o, 64);
+  if ((tid & 31) == 0 && t0 + s_tt < T) p.part[(size_t)p.ksplit * T * E + (size_t)ks * T + t0 + s_tt] = ssq;
+
   // partial logits: lane holds expert e0 + ln, tokens t0 + 4 lq + i
 #pragma unroll
   for (int j = 0; j < NPW; ++j) {
@@ -187,34 +196,34 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const RouteArgs p) {
   if (t >= p.T) return;  // whole wave leaves; no barriers below
   const int E = p.E, T = p.T;
 
-  // reciprocal RMS of the token row (the logit kernel works on the un-normalised
-  // row: the norm is one positive factor per token, applied here)
-  float ss = 0.f;
-  const uint16_t* xr = p.x + (size_t)t * p.H;
-  for (int c = lane; c < p.H / 8; c += 64) {
-    const u32x4_t xv = *(const u32x4_t*)(xr + c * 8);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float a = bf16_lo_f32(xv[q]), b = bf16_hi_f32(xv[q]);
-      ss = __builtin_fmaf(a, a, ss);
-      ss = __builtin_fmaf(b, b, ss);
-    }
-  }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
-  const float rs = 1.0f / sqrtf(ss / (float)p.H + p.eps);
-
+  // The logit kernel works on the un-normalised row: the norm is one positive
+  // factor per token, 1 / sqrt(mean(x^2) + eps), applied here.  All partial
+  // loads of a batch are issued before any is summed (fixed q order).
   float v[4];
   bool taken[4];
   float part[4] = {0.f, 0.f, 0.f, 0.f};
+  float ss = 0.f;
   const float* pb = p.part + (size_t)t * E + lane;
+  const float* pss = p.part + (size_t)p.ksplit * T * E + t;
   const size_t pstride = (size_t)T * E;
-#pragma unroll 4
-  for (int q = 0; q < p.ksplit; ++q) {
+  for (int q0 = 0; q0 < p.ksplit; q0 += 8) {
+    float lv[8][4], sv[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (lane + 64 * i < E) part[i] += pb[q * pstride + 64 * i];
+    for (int q = 0; q < 8; ++q) {
+      const bool qok = q0 + q < p.ksplit;
+      sv[q] = qok ? pss[(size_t)(q0 + q) * T] : 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lv[q][i] = (qok && lane + 64 * i < E) ? pb[(q0 + q) * pstride + 64 * i] : 0.f;
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      ss += sv[q];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) part[i] += lv[q][i];
+    }
   }
+  const float rs = 1.0f / sqrtf(ss / (float)p.H + p.eps);
+
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = lane + 64 * i;

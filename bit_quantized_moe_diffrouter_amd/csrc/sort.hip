@@ -2,7 +2,8 @@
 // DiffExperts.forward: argsort of the flat routing indices, read as a stable
 // sort).  One workgroup of 1024 threads:
 //   1. LDS histogram of the T*k expert indices (bucket E collects indices
-//      outside [0, E), which are dropped);
+//      outside [0, E), which are dropped); up to 32768 bucket ids are kept in
+//      LDS for step 3, larger inputs are read again;
 //   2. exclusive prefix sum over the buckets -> expert_offsets;
 //   3. stable scatter, 1024 assignments per round: each wave finds the lanes
 //      that share its bucket with nine ballots (one per bit of the bucket id),
@@ -17,6 +18,7 @@ namespace qmoe {
 namespace {
 constexpr int kSThreads = 1024, kSWaves = kSThreads / 64;
 constexpr int kMaxBuckets = 257;  // E <= 256, plus the dropped bucket
+constexpr int kCacheMax = 32768;  // assignments whose bucket ids stay in LDS between the passes
 }  // namespace
 
 __global__ __launch_bounds__(kSThreads) void sort_kernel(const int32_t* __restrict__ idx, int A, int E,
@@ -26,6 +28,7 @@ __global__ __launch_bounds__(kSThreads) void sort_kernel(const int32_t* __restri
   __shared__ int base[kMaxBuckets];
   __shared__ int wcnt[kSWaves][kMaxBuckets];
   __shared__ int scan_tmp[kSWaves];
+  __shared__ uint16_t bcache[kCacheMax];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int NB = E + 1;
@@ -37,8 +40,23 @@ __global__ __launch_bounds__(kSThreads) void sort_kernel(const int32_t* __restri
     const int e = idx[a];
     return (e >= 0 && e < E) ? e : E;
   };
+  const bool cached = A <= kCacheMax;
 
-  for (int a = tid; a < A; a += kSThreads) atomicAdd(&cnt[bucket_of(a)], 1);
+  // histogram; four loads in flight per thread before their atomics
+  for (int a0 = tid; a0 < A; a0 += 4 * kSThreads) {
+    int bk[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int a = a0 + u * kSThreads;
+      bk[u] = a < A ? bucket_of(a) : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (bk[u] < 0) continue;
+      atomicAdd(&cnt[bk[u]], 1);
+      if (cached) bcache[a0 + u * kSThreads] = (uint16_t)bk[u];
+    }
+  }
   __syncthreads();
 
   const int v = (tid < NB) ? cnt[tid] : 0;
@@ -54,7 +72,7 @@ __global__ __launch_bounds__(kSThreads) void sort_kernel(const int32_t* __restri
   for (int c0 = 0; c0 < A; c0 += kSThreads) {
     const int a = c0 + tid;
     const bool valid = a < A;
-    const int bk = valid ? bucket_of(a) : 0;
+    const int bk = !valid ? 0 : cached ? (int)bcache[a] : bucket_of(a);
     unsigned long long peers = __ballot(valid);
 #pragma unroll
     for (int bit = 0; bit < 9; ++bit) {

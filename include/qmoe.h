@@ -26,7 +26,9 @@
  *   uint32 word with code c of a row in bits 4*(c%8)..4*(c%8)+3 of word c/8
  *   (first code in the lowest bits); scales and biases are bf16, one per
  *   group; the weight value is scale*q + bias (model.ts page,
- *   dequantEmbedWeight).
+ *   dequantEmbedWeight).  The router takes this row-major layout as it is;
+ *   the switch linears and qlinear take the tiled layout that
+ *   qmoe_tile_weight produces from it once (same values, same bytes).
  * - Alignment: activation, weight-code, mid and output arrays must be 16-byte
  *   aligned; scales, biases and bf16 vectors 2-byte aligned; int32/fp32
  *   arrays 4-byte aligned.
@@ -59,13 +61,22 @@ extern "C" {
 #define QMOE_ERR_WORKSPACE (-3)   /* workspace missing or too small              */
 #define QMOE_ERR_HIP (-4)         /* a HIP launch or query failed                */
 
+/* Weight layouts (qmoe_qweight.layout). */
+#define QMOE_LAYOUT_ROWS 0  /* row-major codes + separate scale/bias arrays   */
+#define QMOE_LAYOUT_TILED 1 /* the tiled buffer written by qmoe_tile_weight   */
+
 /* A 4-bit group-quantized weight (one dense matrix, or `experts` stacked
- * matrices for a switch linear).  Layout per matrix: `rows` output rows of
- * `in` inputs:
+ * matrices for a switch linear) of `rows` output rows and `in` inputs.
+ *
+ * layout QMOE_LAYOUT_ROWS:
  *   w       uint32 [experts, rows, in/8]
  *   scales  bf16   [experts, rows, in/64]
  *   biases  bf16   [experts, rows, in/64]
- * The struct is host memory; the three arrays are device memory. */
+ *   split   ignored
+ * layout QMOE_LAYOUT_TILED: `w` points to the qmoe_tile_weight buffer (codes,
+ *   scales and biases together); `scales` and `biases` are ignored; `split`
+ *   is the value the buffer was tiled with.
+ * The struct is host memory; the arrays are device memory. */
 typedef struct qmoe_qweight {
   const uint32_t* w;
   const uint16_t* scales;
@@ -73,14 +84,47 @@ typedef struct qmoe_qweight {
   int32_t experts; /* 1 for a dense linear */
   int32_t rows;
   int32_t in;
-  int32_t bits;  /* must be 4  */
-  int32_t group; /* must be 64 */
+  int32_t bits;   /* must be 4  */
+  int32_t group;  /* must be 64 */
+  int32_t layout; /* QMOE_LAYOUT_ROWS or QMOE_LAYOUT_TILED */
+  int32_t split;  /* tiled only: 0, or the first row of the second half of a fused pair */
 } qmoe_qweight;
 
 /* Text of the last error raised on the calling thread ("" if none).  The
  * string is owned by the library and valid until the next call on this
  * thread. */
 const char* qmoe_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * qmoe_tile_weight -- re-lays a row-major 4-bit weight into the tiled layout
+ * the switch linears and qlinear read.  A pure permutation of the codes,
+ * scales and biases (no arithmetic): the operation is the same QuantizedLinear
+ * / QuantizedSwitchLinear weight (model.ts page, DiffExperts: gateUp, down;
+ * vision.ts page, VisionLinear).  Done once when the weights are loaded.
+ *
+ * Tiled layout: units of 4608 bytes, unit index ((e * nblk + b) * (in/64) + g)
+ * for expert e, row block b (nblk blocks of 128 rows), group g.  Block b holds
+ * 8 subtiles of 16 rows; row n of subtile j is weight row
+ *   split == 0:  128 b + 16 j + n
+ *   split  > 0:  j < 4: 64 b + 16 j + n;  j >= 4: split + 64 b + 16 (j-4) + n
+ * (so a fused gate|up weight keeps gate row c and up row split + c in one
+ * block); rows past `rows` read as zero.  Bytes [0, 4096) of a unit: for
+ * i = 0..3 and lane L = 0..63 (n = L % 16, q = L / 16), 16 bytes at
+ * 1024 i + 16 L = two code words of subtile 2i then two of subtile 2i+1 of
+ * row n: word 2q and word 2q+1 of the group (codes 16q .. 16q+15), each with
+ * its code 2p moved to bits 4p and code 2p+1 to bits 16+4p (p = 0..3).
+ * Bytes [4096, 4608): for h = 0..1 and n = 0..15, 16 bytes at
+ * 4096 + 256 h + 16 n = (scale, bias) bf16 pairs of subtiles 4h .. 4h+3, row n.
+ *
+ *   src        layout QMOE_LAYOUT_ROWS, in % 64 == 0
+ *   split      0, or rows/2 for a fused pair (split % 64 == 0)
+ *   dst        device buffer of qmoe_tiled_weight_bytes(...) bytes, 16-byte
+ *              aligned, owned by the caller (the tiled weight's `w`)
+ * qmoe_tiled_weight_bytes returns 0 for sizes it does not accept.
+ * ---------------------------------------------------------------------- */
+size_t qmoe_tiled_weight_bytes(int32_t experts, int32_t rows, int32_t in, int32_t split);
+int qmoe_tile_weight(const qmoe_qweight* src, int32_t split, void* dst, size_t dst_bytes,
+                     hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * moe_route -- the DiffRouter (model.ts page, DiffRouter.forward; the norm
@@ -97,7 +141,7 @@ const char* qmoe_last_error(void);
  *   x_router          bf16 [T, H]   the residual stream rows the router sees
  *   norm_scale        bf16 [H]      per-dimension scale applied after the norm
  *   eps               norm epsilon (the build uses 1e-6)
- *   proj              experts = 1, rows = E, in = H
+ *   proj              experts = 1, rows = E, in = H, layout QMOE_LAYOUT_ROWS
  *   per_expert_scale  bf16 [E]
  *   logit_bias        fp32 [E] added to the logits before top-k, or NULL
  *   k                 1 <= k <= min(E, 16);  E <= 256;  H % 64 == 0
@@ -105,7 +149,8 @@ const char* qmoe_last_error(void);
  *   weights (out)     fp32  [T, k]
  *   logits_out (out)  fp32  [T, E] logits incl. logit_bias, or NULL
  *   workspace         device scratch of at least moe_route_workspace(T, H, E)
- *                     bytes (NULL allowed when that size is 0)
+ *                     bytes (partial logits and row sums of squares of the
+ *                     k-range split; NULL allowed when that size is 0)
  * ---------------------------------------------------------------------- */
 size_t moe_route_workspace(int32_t T, int32_t H, int32_t E);
 int moe_route(const uint16_t* x_router, int32_t T, int32_t H, const uint16_t* norm_scale,
@@ -145,7 +190,8 @@ int moe_sort(const int32_t* indices, int32_t T, int32_t k, int32_t E, int32_t* e
  *   mid[r, n] = gelu_tanh(g[n]) * g[I + n]      n < I, stored bf16
  *
  *   x_expert        bf16 [T, H]  the (normalised) rows the experts see
- *   gate_up         experts = E, rows = 2*I, in = H
+ *   gate_up         experts = E, rows = 2*I, in = H, layout QMOE_LAYOUT_TILED
+ *                   tiled with split = I
  *   I               moe_intermediate, I % 64 == 0
  *   expert_offsets, sorted_assign   as produced by moe_sort
  *   mid (out)       bf16 [T*k, I] in sorted-row order (rows beyond
@@ -166,7 +212,8 @@ int qswitch_gate_up_geglu(const uint16_t* x_expert, int32_t T, int32_t H,
  *   y is stored bf16 (round to nearest even).
  *
  *   mid             bf16 [T*k, I] sorted-row order (qswitch_gate_up_geglu)
- *   down            experts = E, rows = H, in = I
+ *   down            experts = E, rows = H, in = I, layout QMOE_LAYOUT_TILED
+ *                   tiled with split = 0
  *   weights         fp32 [T, k] routing weights (moe_route)
  *   y (out)         bf16 [T, H]; a token none of whose assignments is
  *                   present (dropped indices) gets the sum of the rest
@@ -189,7 +236,8 @@ int qswitch_down_combine(const uint16_t* mid, int32_t T, int32_t k, int32_t I,
  * fp32 accumulate, bf16 out.
  *
  *   x        bf16 [M, K]
- *   W        experts = 1, rows = N, in = K;  K % 64 == 0, N % 16 == 0
+ *   W        experts = 1, rows = N, in = K;  K % 64 == 0, N % 16 == 0;
+ *            layout QMOE_LAYOUT_TILED, split = 0
  *   y (out)  bf16 [M, N]
  * ---------------------------------------------------------------------- */
 int qlinear(const uint16_t* x, int32_t M, const qmoe_qweight* W, uint16_t* y,

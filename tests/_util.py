@@ -28,9 +28,9 @@ def dev_qweight(qt, device="cuda"):
 def dev_params(wt, device="cuda"):
     import bit_quantized_moe_diffrouter_amd as q
     bias = None if wt.logit_bias is None else dev_tensor(wt.logit_bias, device)
-    return q.MoEParams(dev_tensor(wt.norm_scale, device), dev_qweight(wt.router, device),
-                       dev_tensor(wt.per_expert_scale, device), dev_qweight(wt.gate_up, device),
-                       dev_qweight(wt.down, device), bias)
+    return q.MoEParams.from_rows(dev_tensor(wt.norm_scale, device), dev_qweight(wt.router, device),
+                                 dev_tensor(wt.per_expert_scale, device), dev_qweight(wt.gate_up, device),
+                                 dev_qweight(wt.down, device), bias)
 
 
 def bf16_host(t):

@@ -34,9 +34,9 @@ def test_exports_every_declared_function(L):
         assert hasattr(L, n), f"{n} is declared in qmoe.h but not exported"
 
 
-def qw(experts, rows, inp, bits=4, group=64, w=A16, s=A16, b=A16):
+def qw(experts, rows, inp, bits=4, group=64, w=A16, s=A16, b=A16, layout=0, split=0):
     import bit_quantized_moe_diffrouter_amd as q
-    return q.QWeightDesc(w, s, b, experts, rows, inp, bits, group)
+    return q.QWeightDesc(w, s, b, experts, rows, inp, bits, group, layout, split)
 
 
 def err(L):
@@ -79,8 +79,9 @@ def test_sort_validation(L):
     assert L.moe_sort_workspace(256, 8, 128) == 0
 
 
-def gate_up(L, T=16, H=256, I=128, k=2, E=8, rows=None, inp=None, mid=A16, **kw):
-    d = qw(E, 2 * I if rows is None else rows, H if inp is None else inp, **kw)
+def gate_up(L, T=16, H=256, I=128, k=2, E=8, rows=None, inp=None, mid=A16, layout=1, split=None, **kw):
+    d = qw(E, 2 * I if rows is None else rows, H if inp is None else inp, layout=layout,
+           split=I if split is None else split, **kw)
     return L.qswitch_gate_up_geglu(A16, T, H, ctypes.byref(d), I, k, A16, A16, mid, None)
 
 
@@ -95,10 +96,12 @@ def test_gate_up_validation(L):
     assert gate_up(L, group=128) == UNSUPPORTED
     assert gate_up(L, mid=None) == INVALID
     assert gate_up(L, mid=A16 + 8) == INVALID
+    assert gate_up(L, layout=0) == INVALID and "qmoe_tile_weight" in err(L)
+    assert gate_up(L, split=0) == INVALID and "split" in err(L)
 
 
-def down(L, T=16, H=256, I=128, k=2, E=8, ws=A16, ws_bytes=1 << 30, y=A16, **kw):
-    d = qw(E, H, I, **kw)
+def down(L, T=16, H=256, I=128, k=2, E=8, ws=A16, ws_bytes=1 << 30, y=A16, layout=1, **kw):
+    d = qw(E, H, I, layout=layout, **kw)
     return L.qswitch_down_combine(A16, T, k, I, ctypes.byref(d), H, A16, A16, A16, y, ws, ws_bytes, 1, None)
 
 
@@ -110,25 +113,53 @@ def test_down_validation(L):
     assert down(L, ws=None) == WORKSPACE
     assert down(L, y=None) == INVALID
     assert down(L, bits=3) == UNSUPPORTED
+    assert down(L, layout=0) == INVALID
+    assert down(L, split=64) == INVALID
     assert L.qswitch_down_combine_workspace(256, 8, 2816, 1) == 256 * 8 * 2816 * 4
 
 
 def test_qlinear_validation(L):
-    d = qw(1, 1152, 1152)
+    d = qw(1, 1152, 1152, layout=1)
     assert L.qlinear(None, 0, ctypes.byref(d), None, None) == 0
     assert L.qlinear(A16, -5, ctypes.byref(d), A16, None) == INVALID
-    bad = qw(1, 1150, 1152)
+    bad = qw(1, 1150, 1152, layout=1)
     assert L.qlinear(A16, 8, ctypes.byref(bad), A16, None) == INVALID
-    bad = qw(1, 1152, 1000)
+    bad = qw(1, 1152, 1000, layout=1)
     assert L.qlinear(A16, 8, ctypes.byref(bad), A16, None) == INVALID
-    bad = qw(2, 1152, 1152)
+    bad = qw(2, 1152, 1152, layout=1)
+    assert L.qlinear(A16, 8, ctypes.byref(bad), A16, None) == INVALID
+    bad = qw(1, 1152, 1152, layout=0)
     assert L.qlinear(A16, 8, ctypes.byref(bad), A16, None) == INVALID
     assert L.qlinear(A16, 8, None, A16, None) == INVALID
 
 
+def test_route_rejects_tiled_proj(L):
+    d = qw(1, 8, 256, layout=1)
+    assert L.moe_route(A16, 16, 256, A16, 1e-6, ctypes.byref(d), A16, None, 2, A16, A16, None, A16, 1 << 30,
+                       None) == INVALID
+
+
+def test_tile_weight_sizes_and_validation(L):
+    # units of 4608 bytes per (expert, 128-row block, 64-wide group)
+    assert L.qmoe_tiled_weight_bytes(128, 1408, 2816, 704) == 128 * 11 * 44 * 4608
+    assert L.qmoe_tiled_weight_bytes(128, 2816, 704, 0) == 128 * 22 * 11 * 4608
+    assert L.qmoe_tiled_weight_bytes(1, 1152, 1152, 0) == 1 * 9 * 18 * 4608
+    assert L.qmoe_tiled_weight_bytes(1, 48, 192, 0) == 1 * 1 * 3 * 4608  # rows padded to a block
+    assert L.qmoe_tiled_weight_bytes(8, 256, 100, 0) == 0
+    assert L.qmoe_tiled_weight_bytes(8, 200, 256, 100) == 0  # split must be rows / 2, a multiple of 64
+    src = qw(8, 256, 256)
+    need = L.qmoe_tiled_weight_bytes(8, 256, 256, 128)
+    assert L.qmoe_tile_weight(ctypes.byref(src), 128, A16, need - 1, None) == INVALID
+    assert L.qmoe_tile_weight(ctypes.byref(src), 100, A16, 1 << 30, None) == INVALID
+    assert L.qmoe_tile_weight(ctypes.byref(src), 128, None, 1 << 30, None) == INVALID
+    tiled_src = qw(8, 256, 256, layout=1)
+    assert L.qmoe_tile_weight(ctypes.byref(tiled_src), 0, A16, 1 << 30, None) == INVALID
+    assert L.qmoe_tile_weight(None, 0, A16, 1 << 30, None) == INVALID
+
+
 def test_route_workspace_size(L):
     # 16-token tiles; the k-range split keeps about 256 workgroups busy
-    assert L.moe_route_workspace(256, 2816, 128) == 16 * 256 * 128 * 4
-    assert L.moe_route_workspace(4096, 2816, 128) == 1 * 4096 * 128 * 4
-    assert L.moe_route_workspace(16, 256, 8) == 4 * 16 * 8 * 4
+    assert L.moe_route_workspace(256, 2816, 128) == 16 * 256 * 129 * 4
+    assert L.moe_route_workspace(4096, 2816, 128) == 1 * 4096 * 129 * 4
+    assert L.moe_route_workspace(16, 256, 8) == 4 * 16 * 9 * 4
     assert L.moe_route_workspace(0, 256, 8) == 0

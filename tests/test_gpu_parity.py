@@ -331,7 +331,7 @@ def test_qlinear_vision_geometry():
     cfg = synth.QLINEAR_VISION
     say(f"[qlinear] {cfg.name}")
     inp = synth.make_qlinear_inputs(cfg)
-    y = q.qlinear(dev_tensor(inp.x), dev_qweight(inp.W))
+    y = q.qlinear(dev_tensor(inp.x), dev_qweight(inp.W).tiled())
     torch.cuda.synchronize()
     ref = O.qlinear(inp.x, inp.W.w, inp.W.scales, inp.W.biases)
     err = O.rowwise_rel_err(bf16_host(y), ref)
@@ -350,7 +350,7 @@ def test_qlinear_integer_exact_bitwise():
     s = synth.to_bf16_bits(np.ones((N, K // 64), dtype=np.float32))
     b = synth.to_bf16_bits(np.full((N, K // 64), -8.0, dtype=np.float32))
     x = synth.to_bf16_bits(rng.integers(-2, 3, size=(M, K)).astype(np.float32))
-    y = q.qlinear(dev_tensor(x), q.QuantWeight(dev_tensor(w), dev_tensor(s), dev_tensor(b)))
+    y = q.qlinear(dev_tensor(x), q.QuantWeight(dev_tensor(w), dev_tensor(s), dev_tensor(b)).tiled())
     torch.cuda.synchronize()
     ref = O.f64_to_bf16_bits(O.qlinear(x, w, s, b))
     np.testing.assert_array_equal(y.view(torch.uint16).cpu().numpy(), ref)
@@ -363,7 +363,60 @@ def test_qlinear_ragged(M, N, K):
     rng = np.random.default_rng(M + N + K)
     W = synth.random_qtensor(rng, (N,), K)
     x = synth.make_activations(M, K, seed=3)
-    y = q.qlinear(dev_tensor(x), dev_qweight(W))
+    y = q.qlinear(dev_tensor(x), dev_qweight(W).tiled())
     torch.cuda.synchronize()
     ref = O.qlinear(x, W.w, W.scales, W.biases)
     assert O.rowwise_rel_err(bf16_host(y), ref) <= 1e-2
+
+
+def tiled_reference(w, s, b, split):
+    """The tiled layout of include/qmoe.h (qmoe_tile_weight), built on the host
+    from its definition: a pure rearrangement of codes, scales and biases."""
+    E, rows, KW = w.shape
+    G = KW // 8
+    nblk = split // 64 if split else -(-rows // 128)
+    out = np.zeros((E, nblk, G, 4608), dtype=np.uint8)
+    n = np.arange(16)
+    for blk in range(nblk):
+        for j in range(8):
+            if split:
+                r = (64 * blk + 16 * j + n) if j < 4 else (split + 64 * blk + 16 * (j - 4) + n)
+            else:
+                r = 128 * blk + 16 * j + n
+            ok = r < rows
+            rr = np.where(ok, r, 0)
+            for q in range(4):  # lane L = 16 q + n: words 2q, 2q+1 of the group
+                for t in range(2):
+                    word = w[:, rr, :].reshape(E, 16, G, 8)[:, :, :, 2 * q + t].astype(np.uint64)
+                    nib = [(word >> (4 * c)) & 0xF for c in range(8)]
+                    new = sum(nib[2 * pp] << (4 * pp) for pp in range(4)) + \
+                        sum(nib[2 * pp + 1] << (16 + 4 * pp) for pp in range(4))
+                    new = np.where(ok[None, :, None], new, 0).astype(np.uint32)  # [E, 16, G]
+                    i, half = j // 2, j % 2
+                    off = 1024 * i + 16 * (16 * q + n) + 8 * half + 4 * t  # [16]
+                    by = new.view(np.uint8).reshape(E, 16, G, 4)
+                    for bb in range(4):  # advanced index first: [16, E, G]
+                        out[:, blk, :, off + bb] = np.transpose(by[:, :, :, bb], (1, 0, 2))
+            sv = np.where(ok[None, :, None], s[:, rr, :], 0).astype(np.uint32)
+            bv = np.where(ok[None, :, None], b[:, rr, :], 0).astype(np.uint32)
+            pair = (sv | (bv << 16)).astype(np.uint32).view(np.uint8).reshape(E, 16, G, 4)
+            off = 4096 + 256 * (j // 4) + 16 * n + 4 * (j % 4)
+            for bb in range(4):
+                out[:, blk, :, off + bb] = np.transpose(pair[:, :, :, bb], (1, 0, 2))
+    return out.reshape(-1)
+
+
+@pytest.mark.parametrize("E,rows,K,split", [(3, 256, 192, 128), (2, 200, 128, 0), (1, 48, 64, 0),
+                                           (2, 1408, 2816, 704)])
+def test_tile_weight_layout_bitwise(E, rows, K, split):
+    import bit_quantized_moe_diffrouter_amd as q
+    say(f"[tile] E={E} rows={rows} K={K} split={split}")
+    rng = np.random.default_rng(E * 1000 + rows + K)
+    W = synth.random_qtensor(rng, (E, rows), K)
+    t = dev_qweight(W).tiled(split)
+    torch.cuda.synchronize()
+    got = t.buf.cpu().numpy()
+    ref = tiled_reference(W.w.reshape(E, rows, K // 8), W.scales.reshape(E, rows, K // 64),
+                          W.biases.reshape(E, rows, K // 64), split)
+    assert got.shape == ref.shape
+    np.testing.assert_array_equal(got, ref)

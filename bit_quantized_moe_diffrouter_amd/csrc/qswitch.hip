@@ -97,7 +97,8 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
   constexpr int BCOLS = (MODE == MODE_GATE_UP) ? 64 : 128;  // output columns per block
 
   extern __shared__ __attribute__((aligned(16))) uint8_t qmm_lds[];  // partial sums [wave][kNS][64] f32x4
-  __shared__ int s_cum[kMaxBuckets + 1];  // chunk prefix per bucket
+  __shared__ int s_cum2[kMaxBuckets + 1];  // prefix per bucket of its two-tile chunks
+  __shared__ int s_cum1[kMaxBuckets + 1];  // prefix per bucket of its one-tile chunk (0 or 1)
   __shared__ int s_lo[kMaxBuckets];       // clamped segment [lo, hi) of each bucket
   __shared__ int s_hi[kMaxBuckets];
   __shared__ int s_scan[kWaves];
@@ -109,35 +110,55 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
   const int K = p.K, G = K / kGroup;
   const int A = p.rows_total;
 
-  // ---- chunks per bucket (switch modes) and the item count
+  // ---- work items.  A chunk is 32 sorted rows of one bucket (the last chunk of
+  // a bucket may be shorter); chunks of more than 16 rows cost two tiles, the
+  // others one.  Items are ranked two-tile chunks first, then one-tile ones
+  // (tile-minor), and workgroup b takes ranks b, 2 grid - 1 - b, 2 grid + b, ...
+  // (a boustrophedon over the cost-sorted list), which evens out the work.
   const int nb = (MODE == MODE_DOWN) ? p.E + 1 : p.E;
-  int total_chunks;
+  int total2, total1;
   if constexpr (MODE == MODE_DENSE) {
-    total_chunks = (A + kBM - 1) / kBM;
+    const int rem = A % kBM;
+    total2 = A / kBM + (rem > 16 ? 1 : 0);
+    total1 = (rem > 0 && rem <= 16) ? 1 : 0;
   } else {
     // bucket b < E is expert b's segment; bucket E (down only) holds the dropped rows
-    auto chunks_of = [&](int b) __attribute__((always_inline)) {
+    auto counts_of = [&](int b, int& one) __attribute__((always_inline)) {
       const int lo = min(max(p.offsets[b], 0), A);
       const int hi = (b < p.E) ? min(max(p.offsets[b + 1], lo), A) : A;
       s_lo[b] = lo;
       s_hi[b] = hi;
-      return (hi - lo + kBM - 1) / kBM;
+      const int n = hi - lo, rem = n % kBM;
+      one = (rem > 0 && rem <= 16) ? 1 : 0;
+      return n / kBM + (rem > 16 ? 1 : 0);
     };
     // thread t counts bucket t; the last thread also bucket kThreads (E = 256, down)
-    const int c0 = (tid < nb) ? chunks_of(tid) : 0;
-    const int c1 = (tid == kThreads - 1 && nb > kThreads) ? chunks_of(kThreads) : 0;
+    int o0 = 0, o1 = 0;
+    const int c0 = (tid < nb) ? counts_of(tid, o0) : 0;
+    const int c1 = (tid == kThreads - 1 && nb > kThreads) ? counts_of(kThreads, o1) : 0;
     int tot;
-    const int incl = block_inclusive_scan<kThreads>(c0 + c1, s_scan, &tot);
-    if (tid < nb) s_cum[tid + 1] = incl - c1;
-    if (tid == kThreads - 1 && nb > kThreads) s_cum[kThreads + 1] = incl;
-    if (tid == 0) s_cum[0] = 0;
-    total_chunks = tot;
+    int incl = block_inclusive_scan<kThreads>(c0 + c1, s_scan, &tot);
+    if (tid < nb) s_cum2[tid + 1] = incl - c1;
+    if (tid == kThreads - 1 && nb > kThreads) s_cum2[kThreads + 1] = incl;
+    total2 = tot;
+    incl = block_inclusive_scan<kThreads>(o0 + o1, s_scan, &tot);
+    if (tid < nb) s_cum1[tid + 1] = incl - o1;
+    if (tid == kThreads - 1 && nb > kThreads) s_cum1[kThreads + 1] = incl;
+    total1 = tot;
+    if (tid == 0) {
+      s_cum2[0] = 0;
+      s_cum1[0] = 0;
+    }
     __syncthreads();
   }
-  const int total_items = __builtin_amdgcn_readfirstlane(total_chunks * p.ntiles);
-  if ((int)blockIdx.x >= total_items) return;  // uniform: no barrier follows for this workgroup
+  total2 = __builtin_amdgcn_readfirstlane(total2);
+  const int total_items = __builtin_amdgcn_readfirstlane((total2 + total1) * p.ntiles);
+  auto item_of = [&](int j) __attribute__((always_inline)) {  // rank of this workgroup's j-th item
+    return j * (int)gridDim.x + ((j & 1) ? (int)(gridDim.x - 1 - blockIdx.x) : (int)blockIdx.x);
+  };
+  if (item_of(0) >= total_items) return;  // uniform: no barrier follows for this workgroup
 
-  // item -> (expert, rows, tile); wave-uniform
+  // item rank -> (expert, rows, tile); wave-uniform
   auto decode = [&](int item) __attribute__((always_inline)) {
     Item it;
     const int chunk = item / p.ntiles;
@@ -145,16 +166,21 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
     if constexpr (MODE == MODE_DENSE) {
       it.e = 0;
       it.zero = 0;
-      it.r0 = chunk * kBM;
+      it.r0 = chunk * kBM;  // the only possible one-tile chunk is the last one
       it.rows = min(kBM, A - it.r0);
     } else {
-      int lo = 0, hi = nb;  // s_cum[lo] <= chunk < s_cum[hi]
+      const bool two = chunk < total2;
+      const int c = two ? chunk : chunk - total2;
+      const int* cum = two ? s_cum2 : s_cum1;
+      int lo = 0, hi = nb;  // cum[lo] <= c < cum[hi]
       while (hi - lo > 1) {
         const int mid = (lo + hi) >> 1;
-        if (s_cum[mid] <= chunk) lo = mid; else hi = mid;
+        if (cum[mid] <= c) lo = mid; else hi = mid;
       }
       const int e = lo;
-      it.r0 = s_lo[e] + (chunk - s_cum[e]) * kBM;
+      // two-tile chunks are a bucket's first ones; its one-tile chunk is its last
+      const int local = two ? c - s_cum2[e] : (s_cum2[e + 1] - s_cum2[e]);
+      it.r0 = s_lo[e] + local * kBM;
       it.rows = min(kBM, s_hi[e] - it.r0);
       it.zero = (MODE == MODE_DOWN) && (e >= p.E);
       it.e = it.zero ? 0 : e;
@@ -197,12 +223,12 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
   const uint32_t arow = K * 2;                     // bytes per activation row
   const uint32_t c_off = lane * 16;                // code bytes of this lane in a unit
   const uint32_t s_off = 4096 + ln * 16;           // scale bytes of this lane in a unit
-  Item linfo = decode(blockIdx.x);
+  Item linfo = decode(item_of(0));
   Role lrole = role_of(linfo);
   int lg = lrole.gk0;
-  int n_item = blockIdx.x + gridDim.x;
-  bool n_valid = n_item < total_items;
-  Item ninfo = n_valid ? decode(n_item) : linfo;
+  int n_j = 1;  // index (in this workgroup's sequence) of the item after the load cursor's
+  bool n_valid = item_of(n_j) < total_items;
+  Item ninfo = n_valid ? decode(item_of(n_j)) : linfo;
   const uint8_t* l_wbase;  // unit (expert, block, group 0) of this wave
   uint32_t l_aoff;         // activation row offset (bytes) of the lane's row
   int l_loc = 0;           // items the load cursor has entered (s_dst parity)
@@ -269,9 +295,9 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
     set_act_offset(linfo, lrole, pf_raw);
     ++l_loc;
     if constexpr (MODE == MODE_DOWN) put_dst(l_loc, linfo, pf_raw);
-    n_item += gridDim.x;
-    n_valid = n_item < total_items;
-    if (n_valid) ninfo = decode(n_item);
+    ++n_j;
+    n_valid = item_of(n_j) < total_items;
+    if (n_valid) ninfo = decode(item_of(n_j));
   };
 
   Slot ring[D];
@@ -290,8 +316,8 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
 #pragma unroll
   for (int j = 0; j < kNS; ++j) acc[j] = zero4();
 
-  int c_item = blockIdx.x, c_loc = 0;
-  Item cinfo = decode(c_item);
+  int c_loc = 0;  // index of the compute cursor's item in this workgroup's sequence
+  Item cinfo = decode(item_of(0));
   Role crole = role_of(cinfo);
   int cg = crole.gk0;
 
@@ -383,13 +409,12 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
     if constexpr (MODE != MODE_DENSE) pf_raw = raw_assign(ninfo);
     if (done || ++cg < crole.gk1) return;
     finish_item();
-    c_item += gridDim.x;
-    if (c_item >= total_items) {
+    if (item_of(c_loc + 1) >= total_items) {
       done = true;
       return;
     }
     ++c_loc;
-    cinfo = decode(c_item);
+    cinfo = decode(item_of(c_loc));
     crole = role_of(cinfo);
     cg = crole.gk0;
   };

@@ -1,7 +1,7 @@
 """Benchmark of the 4-bit MoE layer on one MI355X.
 
-One step = the whole layer on one batch: moe_route -> moe_sort ->
-qswitch_gate_up_geglu -> qswitch_down_combine, on the 256-token decoder
+One step = the whole layer on one batch: moe_route -> moe_sort -> moe_gather
+-> qswitch_gate_up_geglu -> qswitch_down_combine, on the 256-token decoder
 canvas (H = 2816, 128 experts, top-8, moe_intermediate 704, int4 group 64).
 Inputs are resident in HBM before timing starts.  Three independent weight
 sets (1.28 GB) are rotated between steps so the 256 MB Infinity Cache cannot
@@ -9,10 +9,12 @@ serve a layer's weights from the previous step.
 
 Prints ONE JSON line (rank 0):
   value      tokens/s of the whole layer (wall clock over K steps, bracketed
-             by device synchronisation)
-  roofline   the dominant kernel (qswitch_gate_up_geglu): algorithmic bytes
-             per launch / its mean launch time from HIP events on the launch
-             stream, against 8 TB/s HBM
+             by device synchronisation; no events inside)
+  roofline   the dominant kernel (qswitch_gate_up_geglu, one kernel per call):
+             algorithmic bytes per launch / its mean launch time, from HIP
+             events recorded between the calls on the launch stream in a
+             second pass of K steps (events between kernels add a few
+             microseconds of idle time per call, so they stay out of `value`)
   cpu_baseline  the CPU oracle timed on this host on a bounded sample
 """
 from __future__ import annotations
@@ -119,7 +121,8 @@ def main():
     wts = torch.empty((T, k), dtype=torch.float32, device=dev)
     off = torch.empty(E + 1, dtype=torch.int32, device=dev)
     sa = torch.empty(A, dtype=torch.int32, device=dev)
-    mid = torch.empty((A, I), dtype=torch.bfloat16, device=dev)
+    xt = torch.empty(q.qswitch_mid_bytes(T, k, H, E), dtype=torch.uint8, device=dev)
+    mid = torch.empty(q.qswitch_mid_bytes(T, k, I, E), dtype=torch.uint8, device=dev)
     y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     ws_r = torch.empty(max(1, q.moe_route_workspace(T, H, E)), dtype=torch.uint8, device=dev)
     ws_d = torch.empty(max(1, q.qswitch_down_combine_workspace(T, k, H, 1)), dtype=torch.uint8, device=dev)
@@ -134,12 +137,15 @@ def main():
         q.moe_sort(idx, E, off, sa)
         if ev is not None:
             ev[2].record()
-        q.qswitch_gate_up_geglu(x, p.gate_up, I, k, off, sa, mid=mid)
+        q.moe_gather(x, k, E, off, sa, x_tiles=xt)
         if ev is not None:
             ev[3].record()
-        q.qswitch_down_combine(mid, T, k, p.down, wts, off, sa, y=y, workspace=ws_d, deterministic=1)
+        q.qswitch_gate_up_geglu(xt, T, p.gate_up, I, k, off, sa, mid=mid)
         if ev is not None:
             ev[4].record()
+        q.qswitch_down_combine(mid, T, k, p.down, wts, off, sa, y=y, workspace=ws_d, deterministic=1)
+        if ev is not None:
+            ev[5].record()
 
     # touched experts per weight set (routing is a function of x and the router)
     touched = []
@@ -153,15 +159,21 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        step(sets[i % len(sets)], evs[i])
+        step(sets[i % len(sets)])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    names = ["moe_route", "moe_sort", "qswitch_gate_up_geglu", "qswitch_down_combine"]
+    # per-call times: the same K steps again with events between the calls
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(K)]
+    torch.cuda.synchronize()
+    for i in range(K):
+        step(sets[i % len(sets)], evs[i])
+    torch.cuda.synchronize()
+
+    names = ["moe_route", "moe_sort", "moe_gather", "qswitch_gate_up_geglu", "qswitch_down_combine"]
     per = {n: [] for n in names}
     for ev in evs:
         for j, n in enumerate(names):
@@ -171,7 +183,7 @@ def main():
     gu_b, dn_b = expert_bytes(cfg)
     n_touch = float(np.mean(touched))
     x_bytes, y_bytes = T * H * 2, T * H * 2
-    gate_up_alg = n_touch * gu_b + x_bytes + A * I * 2
+    gate_up_alg = n_touch * gu_b + A * H * 2 + A * I * 2  # weights + gathered rows in + mid out
     layer_alg = n_touch * (gu_b + dn_b) + router_bytes(cfg) + x_bytes + y_bytes
     flops = 2.0 * A * (2 * I * H + H * I) + 2.0 * T * E * H
     ms = wall / K * 1e3

@@ -10,7 +10,8 @@ DiffRouter, DiffExperts, DiffDecoderLayer.forwardWith):
 
     indices, weights = moe_route(x_router, ...)           # DiffRouter
     offsets, sorted  = moe_sort(indices, E)               # token-by-expert sort
-    mid = qswitch_gate_up_geglu(x_expert, gate_up, ...)   # gate_up, split, GeGLU
+    x_tiles = moe_gather(x_expert, k, E, offsets, sorted) # token rows in expert order
+    mid = qswitch_gate_up_geglu(x_tiles, T, gate_up, ...) # gate_up, split, GeGLU
     y   = qswitch_down_combine(mid, down, weights, ...)   # down, weighted sum over k
 """
 from __future__ import annotations
@@ -24,7 +25,8 @@ import torch
 
 __all__ = [
     "QMoEError", "QuantWeight", "TiledWeight", "MoEParams", "lib", "library_path",
-    "moe_route", "moe_route_workspace", "moe_sort", "qswitch_gate_up_geglu",
+    "moe_route", "moe_route_workspace", "moe_sort", "qswitch_mid_bytes", "moe_gather",
+    "qswitch_gate_up_geglu",
     "qswitch_down_combine", "qswitch_down_combine_workspace", "qlinear", "moe_layer",
 ]
 
@@ -68,7 +70,9 @@ _SIGNATURES = {
     "moe_route": (ctypes.c_int, [_P, _I, _I, _P, ctypes.c_float, _QP, _P, _P, _I, _P, _P, _P, _P, _SZ, _P]),
     "moe_sort_workspace": (_SZ, [_I, _I, _I]),
     "moe_sort": (ctypes.c_int, [_P, _I, _I, _I, _P, _P, _P, _SZ, _P]),
-    "qswitch_gate_up_geglu": (ctypes.c_int, [_P, _I, _I, _QP, _I, _I, _P, _P, _P, _P]),
+    "qswitch_mid_bytes": (_SZ, [_I, _I, _I, _I]),
+    "moe_gather": (ctypes.c_int, [_P, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]),
+    "qswitch_gate_up_geglu": (ctypes.c_int, [_P, _I, _I, _QP, _I, _I, _P, _P, _P, _SZ, _P]),
     "qswitch_down_combine_workspace": (_SZ, [_I, _I, _I, _I]),
     "qswitch_down_combine": (ctypes.c_int, [_P, _I, _I, _I, _QP, _I, _P, _P, _P, _P, _P, _SZ, _I, _P]),
     "qlinear": (ctypes.c_int, [_P, _I, _QP, _P, _P]),
@@ -234,17 +238,39 @@ def moe_sort(indices: torch.Tensor, E: int, expert_offsets: Optional[torch.Tenso
     return expert_offsets, sorted_assign
 
 
-def qswitch_gate_up_geglu(x_expert: torch.Tensor, gate_up: "TiledWeight", I: int, k: int,
+def qswitch_mid_bytes(T: int, k: int, C: int, E: int) -> int:
+    """Bytes of an activation-tile buffer of C columns (the layout of mid, see qmoe.h)."""
+    return int(lib().qswitch_mid_bytes(T, k, C, E))
+
+
+def _nbytes(t: Optional[torch.Tensor]) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def moe_gather(x: torch.Tensor, k: int, E: int, expert_offsets: torch.Tensor, sorted_assign: torch.Tensor,
+               x_tiles: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Token rows in expert order: returns a uint8 buffer of activation tiles (H columns)."""
+    T, H = x.shape
+    _need(x, "x", 2)
+    if x_tiles is None:
+        x_tiles = torch.empty(max(1, qswitch_mid_bytes(T, k, H, E)), dtype=torch.uint8, device=x.device)
+    _check(lib().moe_gather(_ptr(x), T, H, k, E, _ptr(expert_offsets), _ptr(sorted_assign), _ptr(x_tiles),
+                            _nbytes(x_tiles), _stream()))
+    return x_tiles
+
+
+def qswitch_gate_up_geglu(x_tiles: torch.Tensor, T: int, gate_up: "TiledWeight", I: int, k: int,
                           expert_offsets: torch.Tensor, sorted_assign: torch.Tensor,
                           mid: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """gate_up switch linear + split + GeGLU: returns mid bf16 [T*k, I] (sorted-row order)."""
-    T, H = x_expert.shape
-    _need(x_expert, "x_expert", 2)
+    """gate_up switch linear + split + GeGLU on moe_gather's tiles: returns mid, a uint8 buffer of
+    activation tiles (I columns; layout in qmoe.h)."""
+    H = gate_up.in_features
+    E = gate_up.experts
     if mid is None:
-        mid = torch.empty((T * k, I), dtype=torch.bfloat16, device=x_expert.device)
+        mid = torch.empty(max(1, qswitch_mid_bytes(T, k, I, E)), dtype=torch.uint8, device=x_tiles.device)
     d = gate_up.desc()
-    _check(lib().qswitch_gate_up_geglu(_ptr(x_expert), T, H, ctypes.byref(d), I, k, _ptr(expert_offsets),
-                                       _ptr(sorted_assign), _ptr(mid), _stream()))
+    _check(lib().qswitch_gate_up_geglu(_ptr(x_tiles), T, H, ctypes.byref(d), I, k, _ptr(expert_offsets),
+                                       _ptr(sorted_assign), _ptr(mid), _nbytes(mid), _stream()))
     return mid
 
 
@@ -256,8 +282,9 @@ def qswitch_down_combine(mid: torch.Tensor, T: int, k: int, down: "TiledWeight",
                          expert_offsets: torch.Tensor, sorted_assign: torch.Tensor,
                          y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                          deterministic: int = 1) -> torch.Tensor:
-    """down switch linear + weighted sum over k: returns y bf16 [T, H]."""
-    I = int(mid.shape[1])
+    """down switch linear + weighted sum over k: returns y bf16 [T, H].  mid is the
+    activation-tile buffer qswitch_gate_up_geglu wrote."""
+    I = down.in_features
     H = down.rows
     dev = mid.device
     if y is None:
@@ -312,9 +339,10 @@ class MoEParams:
 
 def moe_layer(x_router: torch.Tensor, x_expert: torch.Tensor, p: MoEParams, k: int, eps: float,
               deterministic: int = 1):
-    """The four calls in order.  Returns (y, indices, weights, offsets, sorted_assign, mid)."""
+    """The five calls in order.  Returns (y, indices, weights, offsets, sorted_assign, mid)."""
     idx, w = moe_route(x_router, p.norm_scale, eps, p.router, p.per_expert_scale, k, p.logit_bias)
     off, sa = moe_sort(idx, p.E)
-    mid = qswitch_gate_up_geglu(x_expert, p.gate_up, p.I, k, off, sa)
+    xt = moe_gather(x_expert, k, p.E, off, sa)
+    mid = qswitch_gate_up_geglu(xt, x_expert.shape[0], p.gate_up, p.I, k, off, sa)
     y = qswitch_down_combine(mid, x_expert.shape[0], k, p.down, w, off, sa, deterministic=deterministic)
     return y, idx, w, off, sa, mid

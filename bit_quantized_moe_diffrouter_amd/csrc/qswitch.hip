@@ -17,16 +17,20 @@
 // pairs in the order the lanes read them.  A wave streams one block: per group
 // four 1 KB and two 256-byte fully coalesced loads.  Within a code word the
 // nibbles are placed so that one v_and_or_b32 per pair yields two bf16 of
-// 128 + q in natural k order (no activation shuffling).
+// 128 + q in natural k order (no activation shuffling).  The activations come
+// as activation tiles (16 sorted rows x 64 columns in operand order, written
+// by moe_gather for gate_up and by the gate_up epilogue for down): two more
+// coalesced 1 KB loads per 16-row tile and group.
 //
 // Work items.  An item is (expert e, chunk of up to 32 sorted rows of e, tile
 // of NW weight blocks).  A persistent grid walks the items, derived on the
 // device from expert_offsets (no host synchronisation).  A chunk of at most 16
-// rows computes one 16-row MFMA tile, a larger one two.  The 4 waves of a
-// workgroup split the contraction KW ways and the blocks NW ways (KW*NW = 4);
-// each wave streams its operands straight into registers through a ring of D
-// slots that runs on across items.  The K-split partial sums meet once per
-// item in LDS, in a fixed order.
+// rows is one 16-row MFMA tile, a larger one two; a wave computes every tile
+// of its chunk from one unpacking of the weights (a one-tile chunk skips the
+// second tile's arithmetic).  The 4 waves of a workgroup split the contraction
+// KW ways and the blocks NW ways (KW*NW = 4); each wave streams its operands
+// straight into registers through a ring of slots that runs on across items.
+// The K-split partial sums meet once per item in LDS, in a fixed order.
 //
 // Arithmetic per group: P = sum_k x_k (128 + q_k) and, against a ones operand,
 // X = sum_k x_k come from the MFMA; the group's affine is applied in fp32:
@@ -47,6 +51,7 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kBM = 32;            // sorted rows per chunk (at most two 16-row tiles)
 constexpr int kMaxBuckets = 257;   // experts (<= 256) + the dropped bucket of the down pass
 constexpr int kNS = 8;             // 16-row subtiles per tiled block
+constexpr int kRingMax = 2;        // ring slots: two-tile slots fill the register file at 2 waves/SIMD
 
 struct Item {
   int e;     // expert whose weights are used (0 for the dropped bucket)
@@ -56,32 +61,33 @@ struct Item {
   int zero;  // down pass, dropped bucket: the rows are written as zeros
 };
 
-// What one wave does for one item.  The 4 waves split (K part, row tile,
-// block): a chunk of up to 16 rows has one row tile, so the waves split K
-// 4 / NBI ways; a larger chunk has two, each taken by its own waves, which
-// then split K 2 / NBI ways.  Each wave thus always computes one 16-row tile
-// against a whole 128-row block (8 subtiles).
+// What one wave does for one item: the 4 waves split (K part, block), K
+// 4 / NBI ways; each wave computes all row tiles of the chunk (one or two
+// 16-row tiles) against a whole 128-row block (8 subtiles).
 struct Role {
   int nk;   // K parts of the item
   int kp;   // this wave's K part
-  int m;    // row tile (0: rows 0-15, 1: rows 16-31)
   int blk;  // weight block (within the expert)
   int gk0, gk1;  // groups [gk0, gk1) of the contraction
 };
 
-// One ring slot: operands of one quantization group for one wave.
+// One ring slot: operands of one quantization group for one wave and MT row tiles.
+template <int MT>
 struct Slot {
-  u32x4_t w[4];  // codes: 16 bytes = the operand words of subtiles 2i, 2i+1
-  u32x4_t s[2];  // (scale, bias) bf16 pairs of subtiles 4h .. 4h+3
-  u32x4_t a[2];  // activations of the lane's row: k = 16lq .. 16lq+7, 16lq+8 .. 16lq+15
+  u32x4_t w[4];      // codes: 16 bytes = the operand words of subtiles 2i, 2i+1
+  u32x4_t s[2];      // (scale, bias) bf16 pairs of subtiles 4h .. 4h+3
+  u32x4_t a[MT][2];  // activations of row tile m: k = 16lq .. 16lq+7, 16lq+8 .. 16lq+15
 };
 
 // Pins the ring order: the slot's registers pass through an empty asm, so the
 // wait for its loads lands here and its consumers cannot be hoisted above the
 // loads issued by earlier steps.
-__device__ __forceinline__ void fence_slot(Slot& sl) {
+template <int MT>
+__device__ __forceinline__ void fence_slot(Slot<MT>& sl) {
   asm volatile("" : "+v"(sl.w[0]), "+v"(sl.w[1]), "+v"(sl.w[2]), "+v"(sl.w[3])::"memory");
-  asm volatile("" : "+v"(sl.s[0]), "+v"(sl.s[1]), "+v"(sl.a[0]), "+v"(sl.a[1])::"memory");
+  asm volatile("" : "+v"(sl.s[0]), "+v"(sl.s[1])::"memory");
+#pragma unroll
+  for (int m = 0; m < MT; ++m) asm volatile("" : "+v"(sl.a[m][0]), "+v"(sl.a[m][1])::"memory");
 }
 
 // Calls f(0), f(1), ... with compile-time indices.
@@ -96,11 +102,12 @@ template <int MODE, int NBI, int D>
 __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
   constexpr int BCOLS = (MODE == MODE_GATE_UP) ? 64 : 128;  // output columns per block
 
-  extern __shared__ __attribute__((aligned(16))) uint8_t qmm_lds[];  // partial sums [wave][kNS][64] f32x4
+  extern __shared__ __attribute__((aligned(16))) uint8_t qmm_lds[];  // partial sums [wave][m][kNS][64] f32x4
   __shared__ int s_cum2[kMaxBuckets + 1];  // prefix per bucket of its two-tile chunks
   __shared__ int s_cum1[kMaxBuckets + 1];  // prefix per bucket of its one-tile chunk (0 or 1)
   __shared__ int s_lo[kMaxBuckets];       // clamped segment [lo, hi) of each bucket
   __shared__ int s_hi[kMaxBuckets];
+  __shared__ int s_tcum[kMaxBuckets + 1];  // switch modes: first activation tile of each expert
   __shared__ int s_scan[kWaves];
   __shared__ int s_dst[2][kBM];           // down pass: assignment id of each chunk row
 
@@ -123,19 +130,20 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
     total1 = (rem > 0 && rem <= 16) ? 1 : 0;
   } else {
     // bucket b < E is expert b's segment; bucket E (down only) holds the dropped rows
-    auto counts_of = [&](int b, int& one) __attribute__((always_inline)) {
+    auto counts_of = [&](int b, int& one, int& tl) __attribute__((always_inline)) {
       const int lo = min(max(p.offsets[b], 0), A);
       const int hi = (b < p.E) ? min(max(p.offsets[b + 1], lo), A) : A;
       s_lo[b] = lo;
       s_hi[b] = hi;
       const int n = hi - lo, rem = n % kBM;
       one = (rem > 0 && rem <= 16) ? 1 : 0;
+      tl = (b < p.E) ? (n + 15) / 16 : 0;  // the dropped bucket has no activation tiles
       return n / kBM + (rem > 16 ? 1 : 0);
     };
     // thread t counts bucket t; the last thread also bucket kThreads (E = 256, down)
-    int o0 = 0, o1 = 0;
-    const int c0 = (tid < nb) ? counts_of(tid, o0) : 0;
-    const int c1 = (tid == kThreads - 1 && nb > kThreads) ? counts_of(kThreads, o1) : 0;
+    int o0 = 0, o1 = 0, t0 = 0, t1 = 0;
+    const int c0 = (tid < nb) ? counts_of(tid, o0, t0) : 0;
+    const int c1 = (tid == kThreads - 1 && nb > kThreads) ? counts_of(kThreads, o1, t1) : 0;
     int tot;
     int incl = block_inclusive_scan<kThreads>(c0 + c1, s_scan, &tot);
     if (tid < nb) s_cum2[tid + 1] = incl - c1;
@@ -145,6 +153,9 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
     if (tid < nb) s_cum1[tid + 1] = incl - o1;
     if (tid == kThreads - 1 && nb > kThreads) s_cum1[kThreads + 1] = incl;
     total1 = tot;
+    incl = block_inclusive_scan<kThreads>(t0 + t1, s_scan, &tot);
+    if (tid < nb) s_tcum[tid] = incl - t1 - t0;
+    if (tid == kThreads - 1 && nb > kThreads) s_tcum[kThreads] = incl - t1;
     if (tid == 0) {
       s_cum2[0] = 0;
       s_cum1[0] = 0;
@@ -152,11 +163,17 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
     __syncthreads();
   }
   total2 = __builtin_amdgcn_readfirstlane(total2);
+  total1 = __builtin_amdgcn_readfirstlane(total1);
+  // Items are ranked two-tile chunks first (the costlier ones), then one-tile
+  // chunks; workgroup b takes ranks b, 2 grid - 1 - b, 2 grid + b, ... (a
+  // boustrophedon over the cost-sorted list, which evens out the work).
   const int total_items = __builtin_amdgcn_readfirstlane((total2 + total1) * p.ntiles);
+  const int grid = (int)gridDim.x, gb = (int)blockIdx.x;
   auto item_of = [&](int j) __attribute__((always_inline)) {  // rank of this workgroup's j-th item
-    return j * (int)gridDim.x + ((j & 1) ? (int)(gridDim.x - 1 - blockIdx.x) : (int)blockIdx.x);
+    return j * grid + ((j & 1) ? grid - 1 - gb : gb);
   };
-  if (item_of(0) >= total_items) return;  // uniform: no barrier follows for this workgroup
+  auto has_item = [&](int j) __attribute__((always_inline)) { return item_of(j) < total_items; };
+  if (!has_item(0)) return;  // uniform: no barrier follows for this workgroup
 
   // item rank -> (expert, rows, tile); wave-uniform
   auto decode = [&](int item) __attribute__((always_inline)) {
@@ -194,22 +211,30 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
   };
   auto role_of = [&](const Item& it) __attribute__((always_inline)) {
     Role r;
-    const int nm = (it.rows > 16) ? 2 : 1;
-    r.nk = min(kWaves / (nm * NBI), G);  // no K part without a group
-    if (wave < r.nk * nm * NBI) {
+    r.nk = min(kWaves / NBI, G);  // no K part without a group
+    if (wave < r.nk * NBI) {
       r.kp = wave % r.nk;
-      r.m = (wave / r.nk) % nm;
-      r.blk = it.tile * NBI + wave / (r.nk * nm);
+      r.blk = it.tile * NBI + wave / r.nk;
       r.gk0 = r.kp * G / r.nk;
       r.gk1 = (r.kp + 1) * G / r.nk;
     } else {  // spare wave (contraction shorter than the K split): streams, never stores
       r.kp = 0;
-      r.m = 0;
       r.blk = 0x7fffffff;
       r.gk0 = 0;
       r.gk1 = G;
     }
     return r;
+  };
+  // activation tile of row tile m of an item (switch modes); a tile past the
+  // buffers (inconsistent offsets) reads tile 0 and is never stored
+  auto tile_of = [&](const Item& it, int m) __attribute__((always_inline)) {
+    if constexpr (MODE == MODE_DENSE) {
+      return 0;
+    } else {
+      if (it.zero) return 0;
+      const int tau = s_tcum[it.e] + (it.r0 - s_lo[it.e]) / 16 + m;
+      return (tau >= 0 && tau < p.max_tiles) ? tau : -1;
+    }
   };
   // owner (K part) of subtile j among the waves of one (row tile, block):
   // gate_up keeps gate j and up j + 4 together
@@ -217,213 +242,258 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
     return ((MODE == MODE_GATE_UP) ? (j & 3) : j) % nk;
   };
 
-  // ---- load cursor (per wave): the item and group whose operands are issued next
-  const uint8_t* const wbytes = (const uint8_t*)p.w;
-  const uint8_t* const abytes = (const uint8_t*)p.a;
-  const uint32_t arow = K * 2;                     // bytes per activation row
-  const uint32_t c_off = lane * 16;                // code bytes of this lane in a unit
-  const uint32_t s_off = 4096 + ln * 16;           // scale bytes of this lane in a unit
-  Item linfo = decode(item_of(0));
-  Role lrole = role_of(linfo);
-  int lg = lrole.gk0;
-  int n_j = 1;  // index (in this workgroup's sequence) of the item after the load cursor's
-  bool n_valid = item_of(n_j) < total_items;
-  Item ninfo = n_valid ? decode(item_of(n_j)) : linfo;
-  const uint8_t* l_wbase;  // unit (expert, block, group 0) of this wave
-  uint32_t l_aoff;         // activation row offset (bytes) of the lane's row
-  int l_loc = 0;           // items the load cursor has entered (s_dst parity)
-  // Assignment ids of the item after the load cursor's, loaded at the end of
-  // every step (so the item switch uses a value loaded at least a step before):
-  // gate_up: of the lane's row (its token); down: of chunk row lane % 32.
-  int pf_raw = 0;
+  // Slots and accumulators hold two row tiles; a one-tile chunk reads tile 0
+  // twice and skips the second tile's arithmetic.
+  auto body = [&](auto mt_tag) __attribute__((always_inline)) {
+    constexpr int MT = decltype(mt_tag)::value;
+    constexpr int DR = (D > kRingMax) ? kRingMax : D;  // ring depth
+    // ---- load cursor (per wave): the item and group whose operands are issued next
+    const uint8_t* const wbytes = (const uint8_t*)p.w;
+    const uint8_t* const abytes = (const uint8_t*)p.a;
+    const uint32_t arow = K * 2;                     // dense: bytes per activation row
+    const uint32_t c_off = lane * 16;                // code bytes of this lane in a unit
+    const uint32_t s_off = 4096 + ln * 16;           // scale bytes of this lane in a unit
+    Item linfo = decode(item_of(0));
+    Role lrole = role_of(linfo);
+    int lg = lrole.gk0;
+    int n_j = 1;  // index (in this workgroup's sequence) of the item after the load cursor's
+    bool n_valid = has_item(n_j);
+    Item ninfo = n_valid ? decode(item_of(n_j)) : linfo;
+    const uint8_t* l_wbase;  // unit (expert, block, group 0) of this wave
+    uint32_t l_aoff[MT];     // per row tile; dense: offset of the lane's row and k slice; switch: of the
+                             // lane's operand words in the tile's group-0 block
+    int l_loc = 0;           // items the load cursor has entered (s_dst parity)
+    // Down pass: assignment id of chunk row lane % 32 of the item after the load
+    // cursor's, loaded at the end of every step (so the item switch uses a value
+    // loaded at least a step before).
+    int pf_raw = 0;
 
-  auto set_weight_base = [&](const Item& it, const Role& r) __attribute__((always_inline)) {
-    const int blk = min(r.blk, p.nblk - 1);  // past the last block: any valid one (never stored)
-    l_wbase = wbytes + ((size_t)it.e * p.nblk + blk) * (size_t)G * kTiledUnit;
-  };
-  auto raw_assign = [&](const Item& it) __attribute__((always_inline)) {
-    if constexpr (MODE == MODE_GATE_UP) {
-      const Role r = role_of(it);
-      return p.assign[it.r0 + min(16 * r.m + ln, it.rows - 1)];
-    } else if constexpr (MODE == MODE_DOWN) {
-      return p.assign[min(it.r0 + (lane & 31), A - 1)];
-    } else {
-      return 0;
+    auto set_weight_base = [&](const Item& it, const Role& r) __attribute__((always_inline)) {
+      const int blk = min(r.blk, p.nblk - 1);  // past the last block: any valid one (never stored)
+      l_wbase = wbytes + ((size_t)it.e * p.nblk + blk) * (size_t)G * kTiledUnit;
+    };
+    auto raw_assign = [&](const Item& it) __attribute__((always_inline)) {
+      if constexpr (MODE == MODE_DOWN) {
+        return p.assign[min(it.r0 + (lane & 31), A - 1)];
+      } else {
+        return 0;
+      }
+    };
+    auto put_dst = [&](int loc, const Item& it, int raw) __attribute__((always_inline)) {  // down only
+      const int lr = lane & 31;
+      s_dst[loc & 1][lr] = (lr < it.rows && raw >= 0 && raw < A) ? raw : -1;
+    };
+    auto set_act_offset = [&](const Item& it, const Role& r) __attribute__((always_inline)) {
+      (void)r;
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        const int mm = (it.rows > 16) ? m : 0;  // a one-tile chunk reads its tile twice
+        if constexpr (MODE == MODE_DENSE) {
+          const int src = it.r0 + min(16 * mm + ln, it.rows - 1);
+          l_aoff[m] = (uint32_t)src * arow + lq * 32;
+        } else {
+          const int tau = max(tile_of(it, mm), 0);
+          l_aoff[m] = (uint32_t)tau * (uint32_t)(G * kActBlock) + lane * 16;
+        }
+      }
+    };
+    {
+      const int raw0 = raw_assign(linfo);
+      pf_raw = raw_assign(ninfo);
+      set_weight_base(linfo, lrole);
+      set_act_offset(linfo, lrole);
+      if constexpr (MODE == MODE_DOWN) put_dst(0, linfo, raw0);
     }
-  };
-  auto put_dst = [&](int loc, const Item& it, int raw) __attribute__((always_inline)) {  // down only
-    const int lr = lane & 31;
-    s_dst[loc & 1][lr] = (lr < it.rows && raw >= 0 && raw < A) ? raw : -1;
-  };
-  auto set_act_offset = [&](const Item& it, const Role& r, int raw) __attribute__((always_inline)) {
-    int src;
-    if constexpr (MODE == MODE_GATE_UP) {
-      src = (raw >= 0 && raw < A) ? raw / p.ktop : 0;
-    } else {
-      src = it.r0 + min(16 * r.m + ln, it.rows - 1);  // down: sorted mid row; dense: input row
-    }
-    l_aoff = (uint32_t)src * arow + lq * 32;
-  };
-  {
-    const int raw0 = raw_assign(linfo);
-    pf_raw = raw_assign(ninfo);
-    set_weight_base(linfo, lrole);
-    set_act_offset(linfo, lrole, raw0);
-    if constexpr (MODE == MODE_DOWN) put_dst(0, linfo, raw0);
-  }
 
-  auto issue = [&](Slot& sl) __attribute__((always_inline)) {
-    const uint8_t* u = l_wbase + (size_t)lg * kTiledUnit;
+    auto issue = [&](Slot<MT>& sl) __attribute__((always_inline)) {
+      const uint8_t* u = l_wbase + (size_t)lg * kTiledUnit;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sl.w[i] = *(const u32x4_t*)(u + c_off + i * 1024);
+      for (int i = 0; i < 4; ++i) sl.w[i] = *(const u32x4_t*)(u + c_off + i * 1024);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) sl.s[h] = *(const u32x4_t*)(u + s_off + h * 256);
-    const uint8_t* ab = abytes + (size_t)lg * 128 + l_aoff;
-    sl.a[0] = *(const u32x4_t*)(ab);
-    sl.a[1] = *(const u32x4_t*)(ab + 16);
-  };
-  auto advance_load = [&]() __attribute__((always_inline)) {
-    if (++lg < lrole.gk1) return;
-    if (!n_valid) {  // past the last item: keep re-reading the last item's groups (never used)
+      for (int h = 0; h < 2; ++h) sl.s[h] = *(const u32x4_t*)(u + s_off + h * 256);
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        if constexpr (MODE == MODE_DENSE) {
+          const uint8_t* ab = abytes + (size_t)lg * 128 + l_aoff[m];
+          sl.a[m][0] = *(const u32x4_t*)(ab);
+          sl.a[m][1] = *(const u32x4_t*)(ab + 16);
+        } else {  // one coalesced kilobyte per operand register
+          const uint8_t* ab = abytes + l_aoff[m] + (uint32_t)lg * kActBlock;
+          sl.a[m][0] = *(const u32x4_t*)(ab);
+          sl.a[m][1] = *(const u32x4_t*)(ab + kActBlock / 2);
+        }
+      }
+    };
+    auto advance_load = [&]() __attribute__((always_inline)) {
+      if (++lg < lrole.gk1) return;
+      if (!n_valid) {  // past the last item: keep re-reading the last item's groups (never used)
+        lg = lrole.gk0;
+        return;
+      }
+      linfo = ninfo;
+      lrole = role_of(linfo);
       lg = lrole.gk0;
-      return;
+      set_weight_base(linfo, lrole);
+      set_act_offset(linfo, lrole);
+      ++l_loc;
+      if constexpr (MODE == MODE_DOWN) put_dst(l_loc, linfo, pf_raw);
+      ++n_j;
+      n_valid = has_item(n_j);
+      if (n_valid) ninfo = decode(item_of(n_j));
+    };
+
+    Slot<MT> ring[DR];
+#pragma unroll
+    for (int d = 0; d < DR; ++d) {
+      issue(ring[d]);
+      asm volatile("" ::: "memory");  // keeps the slots' loads in ring order
+      advance_load();
+      if constexpr (MODE == MODE_DOWN) pf_raw = raw_assign(ninfo);
     }
-    linfo = ninfo;
-    lrole = role_of(linfo);
-    lg = lrole.gk0;
-    set_weight_base(linfo, lrole);
-    set_act_offset(linfo, lrole, pf_raw);
-    ++l_loc;
-    if constexpr (MODE == MODE_DOWN) put_dst(l_loc, linfo, pf_raw);
-    ++n_j;
-    n_valid = item_of(n_j) < total_items;
-    if (n_valid) ninfo = decode(item_of(n_j));
-  };
 
-  Slot ring[D];
+    const u32x4_t ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+    const OffsetCodeConsts kc = offset_code_consts();
+
+    f32x4_t acc[MT][kNS];
 #pragma unroll
-  for (int d = 0; d < D; ++d) {
-    issue(ring[d]);
-    asm volatile("" ::: "memory");  // keeps the slots' loads in ring order
-    advance_load();
-    if constexpr (MODE != MODE_DENSE) pf_raw = raw_assign(ninfo);
-  }
-
-  const u32x4_t ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
-  const OffsetCodeConsts kc = offset_code_consts();
-
-  f32x4_t acc[kNS];
+    for (int m = 0; m < MT; ++m)
 #pragma unroll
-  for (int j = 0; j < kNS; ++j) acc[j] = zero4();
+      for (int j = 0; j < kNS; ++j) acc[m][j] = zero4();
 
-  int c_loc = 0;  // index of the compute cursor's item in this workgroup's sequence
-  Item cinfo = decode(item_of(0));
-  Role crole = role_of(cinfo);
-  int cg = crole.gk0;
+    int c_loc = 0;  // index of the compute cursor's item in this workgroup's sequence
+    Item cinfo = decode(item_of(0));
+    Role crole = role_of(cinfo);
+    int cg = crole.gk0;
 
-  // one group of the current item from slot `sl`
-  auto compute = [&](Slot& sl) __attribute__((always_inline)) {
-    f32x4_t X = mfma16x16x32(sl.a[0], ones, zero4());
-    X = mfma16x16x32(sl.a[1], ones, X);
+    // one group of the current item from slot `sl`, for the MT row tiles; the
+    // weights are unpacked once for all of them
+    auto compute = [&](Slot<MT>& sl) __attribute__((always_inline)) {
+      const bool t2 = cinfo.rows > 16;  // uniform: a second row tile to compute
+      f32x4_t X[MT];
 #pragma unroll
-    for (int j = 0; j < kNS; ++j) {
-      const uint32_t sb = sl.s[j >> 2][j & 3];
-      const float sc = __uint_as_float(sb << 16);
-      const float cc = __uint_as_float(sb & 0xffff0000u) - 128.0f * sc;
-      const u32x4_t b0 = unpack_offset_codes(sl.w[j >> 1][(j & 1) * 2], kc);
-      const u32x4_t b1 = unpack_offset_codes(sl.w[j >> 1][(j & 1) * 2 + 1], kc);
-      f32x4_t P = mfma16x16x32(sl.a[0], b0, zero4());
-      P = mfma16x16x32(sl.a[1], b1, P);
+      for (int m = 0; m < MT; ++m) {
+        if (m > 0 && !t2) continue;
+        X[m] = mfma16x16x32(sl.a[m][0], ones, zero4());
+        X[m] = mfma16x16x32(sl.a[m][1], ones, X[m]);
+      }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[j][i] = __builtin_fmaf(cc, X[i], __builtin_fmaf(sc, P[i], acc[j][i]));
-    }
-  };
+      for (int j = 0; j < kNS; ++j) {
+        const uint32_t sb = sl.s[j >> 2][j & 3];
+        const float sc = __uint_as_float(sb << 16);
+        const float cc = __uint_as_float(sb & 0xffff0000u) - 128.0f * sc;
+        const u32x4_t b0 = unpack_offset_codes(sl.w[j >> 1][(j & 1) * 2], kc);
+        const u32x4_t b1 = unpack_offset_codes(sl.w[j >> 1][(j & 1) * 2 + 1], kc);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          if (m > 0 && !t2) continue;
+          f32x4_t P = mfma16x16x32(sl.a[m][0], b0, zero4());
+          P = mfma16x16x32(sl.a[m][1], b1, P);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            acc[m][j][i] = __builtin_fmaf(cc, X[m][i], __builtin_fmaf(sc, P[i], acc[m][j][i]));
+        }
+      }
+    };
 
-  // end of the current item: every wave parks its partial sums in LDS (its
-  // accumulators are then free for the next item); the owner of each subtile
-  // adds the K parts in K order and writes the outputs
-  auto finish_item = [&]() __attribute__((always_inline)) {
-    f32x4_t* red = (f32x4_t*)qmm_lds;
-    const int nk = crole.nk;
-    const int nm = (cinfo.rows > 16) ? 2 : 1;
+    // end of the current item: every wave parks its partial sums in LDS (its
+    // accumulators are then free for the next item); the owner of each subtile
+    // adds the K parts in K order and writes the outputs of every row tile
+    auto finish_item = [&]() __attribute__((always_inline)) {
+      f32x4_t* red = (f32x4_t*)qmm_lds;
+      const int nk = crole.nk;
+      auto slot_of = [&](int w, int m, int j) __attribute__((always_inline)) {
+        return ((w * 2 + m) * kNS + j) * 64 + lane;
+      };
 #pragma unroll
-    for (int j = 0; j < kNS; ++j) {
-      red[(wave * kNS + j) * 64 + lane] = acc[j];
-      acc[j] = zero4();
-    }
-    __syncthreads();
-    if (!cinfo.zero || MODE == MODE_DOWN) {
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int j = 0; j < kNS; ++j) {
+          if (m == 0 || cinfo.rows > 16) red[slot_of(wave, m, j)] = acc[m][j];
+          acc[m][j] = zero4();
+        }
+      __syncthreads();
       const int blk = crole.blk;
-      const int wbase = wave - crole.kp;  // wave of K part 0 with the same row tile and block
-      if (blk < p.nblk) {
+      const int wbase = wave - crole.kp;  // wave of K part 0 with the same block
+      if (blk < p.nblk && (!cinfo.zero || MODE == MODE_DOWN)) {
         constexpr int NOUT = (MODE == MODE_GATE_UP) ? 4 : kNS;  // output subtiles of a block
 #pragma unroll
-        for (int j = 0; j < NOUT; ++j) {
-          if (owner_of(j, nk) != crole.kp) continue;
-          const int col = blk * BCOLS + 16 * j + ln;
-          if (col >= p.Nout) continue;
-          f32x4_t v0 = red[(wbase * kNS + j) * 64 + lane], v1;
-          if constexpr (MODE == MODE_GATE_UP) v1 = red[(wbase * kNS + j + 4) * 64 + lane];
-          for (int k = 1; k < nk; ++k) {
-            const f32x4_t t0 = red[((wbase + k) * kNS + j) * 64 + lane];
+        for (int m = 0; m < MT; ++m) {
+          if (m > 0 && cinfo.rows <= 16) continue;
+          // gate_up: mid goes out as the down pass's activation tiles; this
+          // block's 64 columns are that pass's group blk
+          const int tau = (MODE == MODE_GATE_UP) ? tile_of(cinfo, m) : 0;
+          if (tau < 0) continue;
+          uint8_t* const mblk = (uint8_t*)p.out + ((size_t)tau * (p.Nout / 64) + blk) * kActBlock;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) v0[i] += t0[i];
-            if constexpr (MODE == MODE_GATE_UP) {
-              const f32x4_t t1 = red[((wbase + k) * kNS + j + 4) * 64 + lane];
+          for (int j = 0; j < NOUT; ++j) {
+            if (owner_of(j, nk) != crole.kp) continue;
+            const int col = blk * BCOLS + 16 * j + ln;
+            if (col >= p.Nout) continue;
+            f32x4_t v0 = red[slot_of(wbase, m, j)], v1;
+            if constexpr (MODE == MODE_GATE_UP) v1 = red[slot_of(wbase, m, j + 4)];
+            for (int k = 1; k < nk; ++k) {
+              const f32x4_t t0 = red[slot_of(wbase + k, m, j)];
 #pragma unroll
-              for (int i = 0; i < 4; ++i) v1[i] += t1[i];
+              for (int i = 0; i < 4; ++i) v0[i] += t0[i];
+              if constexpr (MODE == MODE_GATE_UP) {
+                const f32x4_t t1 = red[slot_of(wbase + k, m, j + 4)];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) v1[i] += t1[i];
+              }
             }
-          }
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int lr = 16 * crole.m + 4 * lq + i;
-            if (lr >= cinfo.rows) continue;
-            if constexpr (MODE == MODE_GATE_UP) {
-              ((uint16_t*)p.out)[(size_t)(cinfo.r0 + lr) * p.Nout + col] = f32_to_bf16_bits(gelu_tanh(v0[i]) * v1[i]);
-            } else if constexpr (MODE == MODE_DOWN) {
-              const int a = s_dst[c_loc & 1][lr];
-              if (a >= 0) ((float*)p.out)[(size_t)a * p.Nout + col] = cinfo.zero ? 0.0f : v0[i];
-            } else {
-              ((uint16_t*)p.out)[(size_t)(cinfo.r0 + lr) * p.Nout + col] = f32_to_bf16_bits(v0[i]);
+            for (int i = 0; i < 4; ++i) {
+              const int lr = 16 * m + 4 * lq + i;
+              if (lr >= cinfo.rows) continue;
+              if constexpr (MODE == MODE_GATE_UP) {
+                // column 16 j + ln of tile row 4 lq + i -> operand lane 4 lq + i + 16 j, register ln / 8
+                *(uint16_t*)(mblk + (ln >> 3) * (kActBlock / 2) + (4 * lq + i + 16 * j) * 16 + (ln & 7) * 2) =
+                    f32_to_bf16_bits(gelu_tanh(v0[i]) * v1[i]);
+              } else if constexpr (MODE == MODE_DOWN) {
+                const int a = s_dst[c_loc & 1][lr];
+                if (a >= 0) ((float*)p.out)[(size_t)a * p.Nout + col] = cinfo.zero ? 0.0f : v0[i];
+              } else {
+                ((uint16_t*)p.out)[(size_t)(cinfo.r0 + lr) * p.Nout + col] = f32_to_bf16_bits(v0[i]);
+              }
             }
           }
         }
       }
-    }
-    (void)nm;
-    __syncthreads();  // partial-sum buffer free again
-  };
+      __syncthreads();  // partial-sum buffer free again
+    };
 
-  // One ring step on slot d: compute the current group, refill the slot.  Every
-  // step issues its loads, also after the last item (compute is skipped then):
-  // the loop has a single exit at the end of a block of D steps and the wait
-  // before each slot always counts the loads of the D - 1 slots issued after it.
-  bool done = false;
-  auto step = [&](auto d_tag) __attribute__((always_inline)) {
-    constexpr int d = decltype(d_tag)::value;
-    fence_slot(ring[d]);
-    if (!done && !cinfo.zero && crole.blk < p.nblk) compute(ring[d]);
-    issue(ring[d]);
-    asm volatile("" ::: "memory");  // keeps the slots' loads in ring order
-    advance_load();
-    if constexpr (MODE != MODE_DENSE) pf_raw = raw_assign(ninfo);
-    if (done || ++cg < crole.gk1) return;
-    finish_item();
-    if (item_of(c_loc + 1) >= total_items) {
-      done = true;
-      return;
-    }
-    ++c_loc;
-    cinfo = decode(item_of(c_loc));
-    crole = role_of(cinfo);
-    cg = crole.gk0;
-  };
-  do {
-    run_steps(step, std::make_integer_sequence<int, D>{});
-  } while (!done);
-  // the loads issued past the end are consumed here (they complete before the wave ends)
+    // One ring step on slot d: compute the current group, refill the slot.  Every
+    // step issues its loads, also after the last item (compute is skipped then):
+    // the loop has a single exit at the end of a block of D steps and the wait
+    // before each slot always counts the loads of the D - 1 slots issued after it.
+    bool done = false;
+    auto step = [&](auto d_tag) __attribute__((always_inline)) {
+      constexpr int d = decltype(d_tag)::value;
+      fence_slot(ring[d]);
+      if (!done && !cinfo.zero && crole.blk < p.nblk) compute(ring[d]);
+      issue(ring[d]);
+      asm volatile("" ::: "memory");  // keeps the slots' loads in ring order
+      advance_load();
+      if constexpr (MODE == MODE_DOWN) pf_raw = raw_assign(ninfo);
+      if (done || ++cg < crole.gk1) return;
+      finish_item();
+      if (!has_item(c_loc + 1)) {
+        done = true;
+        return;
+      }
+      ++c_loc;
+      cinfo = decode(item_of(c_loc));
+      crole = role_of(cinfo);
+      cg = crole.gk0;
+    };
+    do {
+      run_steps(step, std::make_integer_sequence<int, DR>{});
+    } while (!done);
+    // the loads issued past the end are consumed here (they complete before the wave ends)
 #pragma unroll
-  for (int d = 0; d < D; ++d) fence_slot(ring[d]);
+    for (int d = 0; d < DR; ++d) fence_slot(ring[d]);
+  };
+  body(std::integral_constant<int, 2>{});
 }
 
 // ---------------------------------------------------------------- weight tiling
@@ -484,6 +554,69 @@ __global__ __launch_bounds__(256) void tile_weight_kernel(const uint32_t* __rest
   *(u32x4_t*)(dst + c * 16) = out;
 }
 
+// ------------------------------------------------------------ activation tiles
+long long act_tiles_max(long long A, int E) { return (A + 15) / 16 + std::min<long long>(E, A); }
+
+// Gathers the token rows of the sorted assignments into activation tiles.
+// Workgroup (tau, c) writes groups 4c .. 4c+3 of tile tau, one thread per two
+// 16-byte operand pieces; piece (g, h, L) of a tile holds columns
+// 64 g + 16 (L / 16) + 8 h .. + 7 of tile row L % 16.  Rows past a segment's
+// end are not written.
+constexpr int kGatherGroups = 4;
+__global__ __launch_bounds__(256) void act_gather_kernel(const uint16_t* __restrict__ x, int H, int k,
+                                                         const int32_t* __restrict__ offsets,
+                                                         const int32_t* __restrict__ sorted_assign, int E, int A,
+                                                         uint8_t* __restrict__ dst) {
+  __shared__ int s_tc[kMaxBuckets + 1];
+  __shared__ int s_lo[kMaxBuckets];
+  __shared__ int s_hi[kMaxBuckets];
+  __shared__ int s_scan[kWaves];
+  __shared__ int s_tok[16];
+  __shared__ int s_e;
+  const int tid = threadIdx.x;
+  int nt = 0;
+  if (tid < E) {
+    const int lo = min(max(offsets[tid], 0), A);
+    const int hi = min(max(offsets[tid + 1], lo), A);
+    s_lo[tid] = lo;
+    s_hi[tid] = hi;
+    nt = (hi - lo + 15) / 16;
+  }
+  int total;
+  const int incl = block_inclusive_scan<kThreads>(nt, s_scan, &total);
+  if (tid < E) s_tc[tid] = incl - nt;
+  if (tid == 0) s_tc[E] = total;
+  __syncthreads();
+  const int tau = blockIdx.x;
+  if (tau >= total) return;  // uniform
+  if (tid < E && s_tc[tid] <= tau && tau < s_tc[tid + 1]) s_e = tid;
+  __syncthreads();
+  const int e = s_e;
+  const int r0 = s_lo[e] + 16 * (tau - s_tc[e]);
+  if (tid < 16) {
+    const int r = r0 + tid;
+    const int a = (r < s_hi[e]) ? sorted_assign[r] : -1;
+    s_tok[tid] = (a >= 0 && a < A) ? a / k : -1;
+  }
+  __syncthreads();
+  const int G = H / 64;
+  const int g0 = blockIdx.y * kGatherGroups;
+  const int pieces = min(kGatherGroups, G - g0) * (kActBlock / 16);
+  uint8_t* const out = dst + ((size_t)tau * G + g0) * kActBlock;
+  u32x4_t v[2];
+  int tok[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int pc = tid + u * kThreads;
+    const int g = g0 + (pc >> 7), h = (pc >> 6) & 1, L = pc & 63;
+    tok[u] = (pc < pieces) ? s_tok[L & 15] : -1;
+    if (tok[u] >= 0) v[u] = *(const u32x4_t*)(x + (size_t)tok[u] * H + 64 * g + 16 * (L >> 4) + 8 * h);
+  }
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+    if (tok[u] >= 0) *(u32x4_t*)(out + (size_t)(tid + u * kThreads) * 16) = v[u];
+}
+
 // y[t, h] = bf16( sum_{j<k} w[t, j] * D[t*k + j, h] ), products and sum in fp32, j order.
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ D, const float* __restrict__ w, int T,
                                                       int k, int H, uint16_t* __restrict__ y) {
@@ -513,7 +646,7 @@ namespace {
 template <int MODE, int NBI, int D>
 hipError_t launch_cfg(SwitchArgs a, int extra_buckets, int num_cu, hipStream_t stream) {
   a.ntiles = (a.nblk + NBI - 1) / NBI;
-  const size_t lds = (size_t)kWaves * kNS * 64 * 16;  // partial sums of every wave
+  const size_t lds = (size_t)kWaves * 2 * kNS * 64 * 16;  // partial sums of every wave and row tile
   long long chunks;
   if (MODE == MODE_DENSE)
     chunks = (a.rows_total + kBM - 1) / kBM;
@@ -522,6 +655,9 @@ hipError_t launch_cfg(SwitchArgs a, int extra_buckets, int num_cu, hipStream_t s
   const long long items = chunks * a.ntiles;
   long long grid = std::min(items, (long long)num_cu * 2);
   if (grid < 1) grid = 1;
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&qmm_kernel<MODE, NBI, D>),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL((qmm_kernel<MODE, NBI, D>), dim3((unsigned)grid), dim3(kThreads), lds, stream, a);
   return hipGetLastError();
 }
@@ -560,6 +696,16 @@ hipError_t launch_combine(const float* D, const float* w, int T, int k, int H, u
   const long long n = (long long)T * (H / 4);
   const long long blocks = (n + 255) / 256;
   hipLaunchKernelGGL(combine_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, D, w, T, k, H, y);
+  return hipGetLastError();
+}
+hipError_t launch_act_gather(const uint16_t* x, int T, int H, int k, const int32_t* offsets,
+                             const int32_t* sorted_assign, int E, int A, uint8_t* dst, hipStream_t stream) {
+  (void)T;
+  const long long tiles = act_tiles_max(A, E);
+  if (tiles <= 0) return hipSuccess;
+  const int cg = (H / 64 + kGatherGroups - 1) / kGatherGroups;
+  hipLaunchKernelGGL(act_gather_kernel, dim3((unsigned)tiles, (unsigned)cg), dim3(kThreads), 0, stream, x, H, k,
+                     offsets, sorted_assign, E, A, dst);
   return hipGetLastError();
 }
 int tiled_blocks(int rows, int split) { return split > 0 ? split / 64 : (rows + 127) / 128; }

@@ -186,107 +186,114 @@ __global__ __launch_bounds__(kRThreads) void route_logits_kernel(const RouteArgs
   }
 }
 
-__device__ __forceinline__ bool better(float v, int e, float bv, int be) {
-  return v > bv || (v == bv && e < be);
+// Orders the wave's logits for selection: a larger key is a better expert.
+// The high word is the logit mapped to an unsigned integer that sorts like
+// the float (-0 folded into +0, so the two compare equal as floats do); the
+// low word is 0xffff - e, so among equal logits the lower index wins.  Every
+// real key is non-zero, which leaves 0 free to pad the table.
+__device__ __forceinline__ unsigned long long select_key(float v, int e) {
+  uint32_t u = v == 0.f ? 0u : __float_as_uint(v);
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((unsigned long long)u << 32) | (uint32_t)(0xffff - e);
 }
 
+// Lanes of one wave exchange data through LDS: this orders the stores before
+// the loads that follow (a wave's LDS operations complete in issue order).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// One wave per token; NI = ceil(E / 64) logits per lane (expert lane + 64 i).
+// Top-k by rank: every lane counts, for each of its logits, how many of the
+// token's E keys beat it, reading the key table from LDS by broadcast; the
+// logits of rank < k land in slot rank, which is the descending order the
+// softmax and the outputs take.
+template <int NI>
 __global__ __launch_bounds__(256) void route_topk_kernel(const RouteArgs p) {
+  __shared__ __align__(16) unsigned long long s_key[4][64 * NI];
+  __shared__ float s_sv[4][16];
+  __shared__ int s_se[4][16];
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= p.T) return;  // whole wave leaves; no barriers below
+  const int wv = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wv;
+  if (t >= p.T) return;  // whole wave leaves; only wave-level syncs below
   const int E = p.E, T = p.T;
 
   // The logit kernel works on the un-normalised row: the norm is one positive
   // factor per token, 1 / sqrt(mean(x^2) + eps), applied here.  All partial
   // loads of a batch are issued before any is summed (fixed q order).
-  float v[4];
-  bool taken[4];
-  float part[4] = {0.f, 0.f, 0.f, 0.f};
+  float part[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) part[i] = 0.f;
   float ss = 0.f;
   const float* pb = p.part + (size_t)t * E + lane;
   const float* pss = p.part + (size_t)p.ksplit * T * E + t;
   const size_t pstride = (size_t)T * E;
   for (int q0 = 0; q0 < p.ksplit; q0 += 8) {
-    float lv[8][4], sv[8];
+    float lv[8][NI], sv[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const bool qok = q0 + q < p.ksplit;
       sv[q] = qok ? pss[(size_t)(q0 + q) * T] : 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) lv[q][i] = (qok && lane + 64 * i < E) ? pb[(q0 + q) * pstride + 64 * i] : 0.f;
+      for (int i = 0; i < NI; ++i) lv[q][i] = (qok && lane + 64 * i < E) ? pb[(q0 + q) * pstride + 64 * i] : 0.f;
     }
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       ss += sv[q];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) part[i] += lv[q][i];
+      for (int i = 0; i < NI; ++i) part[i] += lv[q][i];
     }
   }
   const float rs = 1.0f / sqrtf(ss / (float)p.H + p.eps);
 
+  float v[NI];
+  unsigned long long key[NI];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < NI; ++i) {
     const int e = lane + 64 * i;
     v[i] = -INFINITY;
-    taken[i] = true;
+    key[i] = 0;
     if (e < E) {
       float s = part[i] * rs;
       if (p.logit_bias) s += p.logit_bias[e];
       if (p.logits_out) p.logits_out[(size_t)t * E + e] = s;
       v[i] = (s != s) ? -INFINITY : s;  // NaN never wins
-      taken[i] = false;
+      key[i] = select_key(v[i], e);
     }
+    s_key[wv][e] = key[i];
   }
+  wave_lds_sync();
 
-  float sel_v[16];
-  int sel_e[16];
+  int rank[NI];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    sel_v[j] = 0.f;
-    sel_e[j] = 0;
-    if (j >= p.k) continue;
-    float bv = -INFINITY;
-    int be = 0x7fffffff;
+  for (int i = 0; i < NI; ++i) rank[i] = 0;
+  const int E4 = (E + 3) & ~3;  // keys past E are 0 and beat nothing
+  const ulonglong2* tab = reinterpret_cast<const ulonglong2*>(s_key[wv]);
+  for (int c = 0; c < E4 / 2; c += 2) {
+    const ulonglong2 k01 = tab[c], k23 = tab[c + 1];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = lane + 64 * i;
-      if (!taken[i] && better(v[i], e, bv, be)) {
-        bv = v[i];
-        be = e;
-      }
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, 64);
-      const int oe = __shfl_xor(be, o, 64);
-      if (better(ov, oe, bv, be)) {
-        bv = ov;
-        be = oe;
-      }
-    }
-    sel_v[j] = bv;
-    sel_e[j] = be;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (lane + 64 * i == be) taken[i] = true;
+    for (int i = 0; i < NI; ++i)
+      rank[i] += (int)(k01.x > key[i]) + (int)(k01.y > key[i]) + (int)(k23.x > key[i]) + (int)(k23.y > key[i]);
   }
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+    if (key[i] != 0 && rank[i] < p.k) {
+      s_sv[wv][rank[i]] = v[i];
+      s_se[wv][rank[i]] = lane + 64 * i;
+    }
+  wave_lds_sync();
 
-  const float m = sel_v[0];
-  float sum = 0.f, mine_v = 0.f;
-  int mine_e = 0;
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    if (j >= p.k) continue;
-    sum += expf(sel_v[j] - m);
-    if (lane == j) {
-      mine_v = sel_v[j];
-      mine_e = sel_e[j];
-    }
-  }
   if (lane < p.k) {
-    const float pj = expf(mine_v - m) / sum;
-    const float pes = bf16_bits_to_f32(p.pes[mine_e]);
-    p.indices[(size_t)t * p.k + lane] = mine_e;
+    const float m = s_sv[wv][0];
+    float sum = 0.f;
+    for (int j = 0; j < p.k; ++j) sum += expf(s_sv[wv][j] - m);
+    const int e = s_se[wv][lane];
+    const float pj = expf(s_sv[wv][lane] - m) / sum;
+    const float pes = bf16_bits_to_f32(p.pes[e]);
+    p.indices[(size_t)t * p.k + lane] = e;
     p.weights[(size_t)t * p.k + lane] = pj * pes;
   }
 }
@@ -300,7 +307,13 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(route_logits_kernel<2>, grid1, dim3(kRThreads), 0, stream, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(route_topk_kernel, dim3((a.T + 3) / 4), dim3(256), 0, stream, a);
+  const dim3 grid2((a.T + 3) / 4);
+  if (a.E <= 64)
+    hipLaunchKernelGGL(route_topk_kernel<1>, grid2, dim3(256), 0, stream, a);
+  else if (a.E <= 128)
+    hipLaunchKernelGGL(route_topk_kernel<2>, grid2, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(route_topk_kernel<4>, grid2, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -11,6 +11,7 @@
  *   moe_route             router: norm, scale, 4-bit projection, top-k,
  *                         precise softmax, per_expert_scale
  *   moe_sort              token-by-expert sort of the routing assignments
+ *   moe_gather            the token rows in expert order, as activation tiles
  *   qswitch_gate_up_geglu fused gate_up switch linear, split, GeGLU
  *   qswitch_down_combine  down switch linear + weighted sum over k per token
  *   qlinear               dense 4-bit linear
@@ -179,6 +180,39 @@ int moe_sort(const int32_t* indices, int32_t T, int32_t k, int32_t E, int32_t* e
              int32_t* sorted_assign, void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Activation tiles (the layout of moe_gather's x_tiles and of mid)
+ *
+ * The sorted rows of expert e's segment [offsets[e], offsets[e+1]) are cut
+ * into tiles of 16 rows (the last one of a segment may be partial); tiles are
+ * numbered expert by expert, so tile tau of expert e's local tile j is
+ *   tau = sum_{e' < e} ceil(n_e' / 16) + j,   n_e = offsets[e+1] - offsets[e].
+ * Each (tile tau, 64-wide column group g) owns one 2048-byte block at
+ *   (tau * (C / 64) + g) * 2048            (C = columns of the matrix)
+ * holding the tile's 16 x 64 bf16 values in the operand order of
+ * v_mfma_f32_16x16x32_bf16: the bf16 at byte h*1024 + L*16 + 2*i
+ * (h in {0,1}, L in [0,64), i in [0,8)) is column 64 g + 16 (L/16) + 8 h + i
+ * of tile row L % 16.  Rows past the end of a segment hold unspecified
+ * values.  A buffer of C columns for T*k assignments and E experts takes
+ *   qswitch_mid_bytes(T, k, C, E) = (ceil(T*k / 16) + min(E, T*k)) * (C/64) * 2048
+ * bytes, which covers every possible split of the rows among the experts.
+ * ---------------------------------------------------------------------- */
+size_t qswitch_mid_bytes(int32_t T, int32_t k, int32_t C, int32_t E);
+
+/* ------------------------------------------------------------------------
+ * moe_gather -- the rows the experts see, in expert order (model.ts page,
+ * DiffExperts.forward: x gathered by order // k): the token row of every
+ * sorted assignment, written as activation tiles of H columns.
+ *
+ *   x               bf16 [T, H]  the (normalised) rows the experts see
+ *   expert_offsets, sorted_assign   as produced by moe_sort for the same T, k, E
+ *   x_tiles (out)   at least qswitch_mid_bytes(T, k, H, E) bytes (tiles_bytes)
+ * Rows of sorted_assign outside [0, T*k) leave their tile row unwritten.
+ * ---------------------------------------------------------------------- */
+int moe_gather(const uint16_t* x, int32_t T, int32_t H, int32_t k, int32_t E,
+               const int32_t* expert_offsets, const int32_t* sorted_assign,
+               void* x_tiles, size_t tiles_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * qswitch_gate_up_geglu -- fused gate_up QuantizedSwitchLinear over the
  * sorted rows, split at moe_intermediate, GeGLU (model.ts page,
  * DiffExperts.forward: gateUp.forward, split, geglu; the GeGLU is
@@ -189,18 +223,18 @@ int moe_sort(const int32_t* indices, int32_t T, int32_t k, int32_t E, int32_t* e
  *   g = x[t] . dequant(gate_up)[e]^T            (2I values, fp32 accumulate)
  *   mid[r, n] = gelu_tanh(g[n]) * g[I + n]      n < I, stored bf16
  *
- *   x_expert        bf16 [T, H]  the (normalised) rows the experts see
+ *   x_tiles         the rows x[t] as moe_gather wrote them (H columns)
  *   gate_up         experts = E, rows = 2*I, in = H, layout QMOE_LAYOUT_TILED
  *                   tiled with split = I
  *   I               moe_intermediate, I % 64 == 0
  *   expert_offsets, sorted_assign   as produced by moe_sort
- *   mid (out)       bf16 [T*k, I] in sorted-row order (rows beyond
- *                   offsets[E] are left untouched)
+ *   mid (out)       activation tiles of I columns (layout above), at least
+ *                   qswitch_mid_bytes(T, k, I, E) bytes (mid_bytes)
  * ---------------------------------------------------------------------- */
-int qswitch_gate_up_geglu(const uint16_t* x_expert, int32_t T, int32_t H,
+int qswitch_gate_up_geglu(const void* x_tiles, int32_t T, int32_t H,
                           const qmoe_qweight* gate_up, int32_t I, int32_t k,
                           const int32_t* expert_offsets, const int32_t* sorted_assign,
-                          uint16_t* mid, hipStream_t stream);
+                          void* mid, size_t mid_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * qswitch_down_combine -- down QuantizedSwitchLinear plus the weighted sum
@@ -211,7 +245,8 @@ int qswitch_gate_up_geglu(const uint16_t* x_expert, int32_t T, int32_t H,
  *   y[t] = sum_j weights[t, j] * d_{row of assignment t*k+j}   (fp32, j order)
  *   y is stored bf16 (round to nearest even).
  *
- *   mid             bf16 [T*k, I] sorted-row order (qswitch_gate_up_geglu)
+ *   mid             activation tiles of I columns as qswitch_gate_up_geglu
+ *                   writes them, for the same expert_offsets
  *   down            experts = E, rows = H, in = I, layout QMOE_LAYOUT_TILED
  *                   tiled with split = 0
  *   weights         fp32 [T, k] routing weights (moe_route)
@@ -224,7 +259,7 @@ int qswitch_gate_up_geglu(const uint16_t* x_expert, int32_t T, int32_t H,
  *                   atomic scatter-sum)
  * ---------------------------------------------------------------------- */
 size_t qswitch_down_combine_workspace(int32_t T, int32_t k, int32_t H, int32_t deterministic);
-int qswitch_down_combine(const uint16_t* mid, int32_t T, int32_t k, int32_t I,
+int qswitch_down_combine(const void* mid, int32_t T, int32_t k, int32_t I,
                          const qmoe_qweight* down, int32_t H, const int32_t* expert_offsets,
                          const int32_t* sorted_assign, const float* weights, uint16_t* y,
                          void* workspace, size_t ws_bytes, int32_t deterministic,

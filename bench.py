@@ -1,7 +1,7 @@
 """Benchmark of the 4-bit MoE layer on one MI355X.
 
-One step = the whole layer on one batch: moe_route -> moe_sort -> moe_gather
--> qswitch_gate_up_geglu -> qswitch_down_combine, on the 256-token decoder
+One step = the whole layer on one batch: moe_route -> moe_sort ->
+qswitch_gate_up_geglu -> qswitch_down_combine, on the 256-token decoder
 canvas (H = 2816, 128 experts, top-8, moe_intermediate 704, int4 group 64).
 Inputs are resident in HBM before timing starts.  Three independent weight
 sets (1.28 GB) are rotated between steps so the 256 MB Infinity Cache cannot
@@ -16,6 +16,14 @@ Prints ONE JSON line (rank 0):
              second pass of K steps (events between kernels add a few
              microseconds of idle time per call, so they stay out of `value`)
   cpu_baseline  the CPU oracle timed on this host on a bounded sample
+
+Two helper modes serve the committed profiles (see profiles/):
+  --copy-probe        one plain 256 MiB device copy, five times (the known-size
+                      kernel that calibrates rocprofv3's FETCH_SIZE/WRITE_SIZE)
+  --summarize DIR     turns the rocprofv3 output under DIR (kt/, fetch/, write/,
+                      copy_fetch/, copy_write/) into the summaries under profiles/
+roofline.traffic is read from profiles/qswitch_gate_up_canvas_traffic.txt and
+is null when the kernel sources no longer match the hash recorded there.
 """
 from __future__ import annotations
 
@@ -31,6 +39,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+KERNEL_SOURCES = ["bit_quantized_moe_diffrouter_amd/csrc/qswitch.hip", "bit_quantized_moe_diffrouter_amd/csrc/common.h",
+                  "bit_quantized_moe_diffrouter_amd/csrc/launch.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "qswitch_gate_up_canvas_traffic.txt")
+GATE_UP_KERNEL = "qmm_kernel<0,"   # rocprofv3 name of the gate_up switch kernel
+COPY_BYTES = 256 << 20
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 METRIC = "MoE-layer tokens/s + % HBM roofline, H=2816 128-expert top-8 int4, 256 tok"
 
@@ -45,7 +58,100 @@ def parse():
     ap.add_argument("--weight-sets", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--summarize", metavar="DIR")
     return ap.parse_args()
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def read_traffic():
+    """HBM bytes per gate_up launch from the committed counter summary, or None
+    when the kernel sources changed since the counters were taken."""
+    try:
+        kv = dict(line.strip().split("=", 1) for line in open(TRAFFIC_FILE)
+                  if "=" in line and not line.startswith("#"))
+    except OSError:
+        return None
+    if kv.get("source_sha256") != kernel_source_hash():
+        return None
+    return float(kv["traffic_bytes_per_launch"])
+
+
+def copy_probe():
+    import torch
+    src = torch.full((COPY_BYTES // 4,), 7, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": COPY_BYTES, "launches": 5}), flush=True)
+
+
+def _pmc_per_dispatch(d, counter, match):
+    """Mean over matching dispatches of one counter (rocprofv3 csv), and the count."""
+    import csv
+    import glob
+    vals = {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] == counter and match(r["Kernel_Name"]):
+                vals[r["Dispatch_Id"]] = vals.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    v = list(vals.values())
+    return (sum(v) / len(v) if v else float("nan")), len(v)
+
+
+def summarize(d):
+    import csv
+    import glob
+    cmd_kt = ("rocprofv3 --kernel-trace --stats -d DIR/kt -o kt --output-format csv -- "
+              "python3 bench.py --steps 60 --warmup 10 --no-cpu-baseline")
+    stats = glob.glob(os.path.join(d, "kt", "**", "*kernel_stats.csv"), recursive=True)
+    lines = ["# Kernel durations, canvas workload (256 tokens, H 2816, 128 experts, top-8, I 704)", "",
+             "Command (from the repository root, TMPDIR=/tmp):", "", "    " + cmd_kt, "",
+             "rocprofv3 kernel-trace statistics; every dispatch of the run (warm-up, the timed",
+             "pass and the event pass).  qmm_kernel<0,...> is qswitch_gate_up_geglu,",
+             "qmm_kernel<1,...> the down switch linear of qswitch_down_combine.", "",
+             "| kernel | calls | average us | min us | max us | share |", "|---|---|---|---|---|---|"]
+    for r in sorted(csv.DictReader(open(stats[0])), key=lambda r: -float(r["TotalDurationNs"])):
+        lines.append(f"| `{r['Name'][:70]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |")
+    out_kt = os.path.join(ROOT, "profiles", "switch_kernels_canvas_kernel_trace.md")
+    open(out_kt, "w").write("\n".join(lines) + "\n")
+
+    fetch, nf = _pmc_per_dispatch(os.path.join(d, "fetch"), "FETCH_SIZE", lambda n: "qmm_kernel<0" in n)
+    write, nw = _pmc_per_dispatch(os.path.join(d, "write"), "WRITE_SIZE", lambda n: "qmm_kernel<0" in n)
+    # the copy: the dispatches of the largest kernel in the probe run
+    cf, ncf = _pmc_per_dispatch(os.path.join(d, "copy_fetch"), "FETCH_SIZE", lambda n: "opy" in n)
+    cw, ncw = _pmc_per_dispatch(os.path.join(d, "copy_write"), "WRITE_SIZE", lambda n: "opy" in n)
+    kf = COPY_BYTES / (cf * 1024.0)   # true bytes per reported byte, reads
+    kw = COPY_BYTES / (cw * 1024.0)   # and writes
+    traffic = fetch * 1024.0 * kf + write * 1024.0 * kw
+    cmd = ("rocprofv3 --pmc {c} -d DIR/{d} -o p --output-format csv -- python3 bench.py {a}")
+    txt = ["# HBM traffic of qswitch_gate_up_geglu (qmm_kernel<0,...>), canvas workload",
+           "# Commands (from the repository root, TMPDIR=/tmp), one counter per run:",
+           "#   " + cmd.format(c="FETCH_SIZE", d="fetch", a="--steps 20 --warmup 5 --no-cpu-baseline"),
+           "#   " + cmd.format(c="WRITE_SIZE", d="write", a="--steps 20 --warmup 5 --no-cpu-baseline"),
+           "#   " + cmd.format(c="FETCH_SIZE", d="copy_fetch", a="--copy-probe"),
+           "#   " + cmd.format(c="WRITE_SIZE", d="copy_write", a="--copy-probe"),
+           "# FETCH_SIZE / WRITE_SIZE are KiB per dispatch; each is scaled by what the same",
+           "# counter reads for a plain device copy of copy_bytes (read and written once).",
+           f"source_sha256={kernel_source_hash()}",
+           f"fetch_kib_per_dispatch={fetch:.1f}", f"fetch_dispatches={nf}",
+           f"write_kib_per_dispatch={write:.1f}", f"write_dispatches={nw}",
+           f"copy_bytes={COPY_BYTES}", f"copy_fetch_kib={cf:.1f}", f"copy_write_kib={cw:.1f}",
+           f"fetch_scale={kf:.4f}", f"write_scale={kw:.4f}",
+           f"traffic_bytes_per_launch={traffic:.0f}"]
+    open(TRAFFIC_FILE, "w").write("\n".join(txt) + "\n")
+    print("\n".join(lines[-12:]))
+    print("\n".join(txt[-11:]))
 
 
 def expert_bytes(cfg):
@@ -86,10 +192,17 @@ def cpu_baseline(cfg, inp, seconds):
 
 def main():
     args = parse()
+    if args.summarize:
+        summarize(args.summarize)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU only (the layer's multi-GPU split is a design "
               "note, not built); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+
+    if args.copy_probe:
+        copy_probe()
+        return
 
     import torch
 
@@ -121,7 +234,6 @@ def main():
     wts = torch.empty((T, k), dtype=torch.float32, device=dev)
     off = torch.empty(E + 1, dtype=torch.int32, device=dev)
     sa = torch.empty(A, dtype=torch.int32, device=dev)
-    xt = torch.empty(q.qswitch_mid_bytes(T, k, H, E), dtype=torch.uint8, device=dev)
     mid = torch.empty(q.qswitch_mid_bytes(T, k, I, E), dtype=torch.uint8, device=dev)
     y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     ws_r = torch.empty(max(1, q.moe_route_workspace(T, H, E)), dtype=torch.uint8, device=dev)
@@ -137,15 +249,12 @@ def main():
         q.moe_sort(idx, E, off, sa)
         if ev is not None:
             ev[2].record()
-        q.moe_gather(x, k, E, off, sa, x_tiles=xt)
+        q.qswitch_gate_up_geglu(x, p.gate_up, I, k, off, sa, mid=mid)
         if ev is not None:
             ev[3].record()
-        q.qswitch_gate_up_geglu(xt, T, p.gate_up, I, k, off, sa, mid=mid)
-        if ev is not None:
-            ev[4].record()
         q.qswitch_down_combine(mid, T, k, p.down, wts, off, sa, y=y, workspace=ws_d, deterministic=1)
         if ev is not None:
-            ev[5].record()
+            ev[4].record()
 
     # touched experts per weight set (routing is a function of x and the router)
     touched = []
@@ -167,13 +276,13 @@ def main():
     wall = time.perf_counter() - t0
 
     # per-call times: the same K steps again with events between the calls
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(K)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
     torch.cuda.synchronize()
     for i in range(K):
         step(sets[i % len(sets)], evs[i])
     torch.cuda.synchronize()
 
-    names = ["moe_route", "moe_sort", "moe_gather", "qswitch_gate_up_geglu", "qswitch_down_combine"]
+    names = ["moe_route", "moe_sort", "qswitch_gate_up_geglu", "qswitch_down_combine"]
     per = {n: [] for n in names}
     for ev in evs:
         for j, n in enumerate(names):
@@ -183,7 +292,7 @@ def main():
     gu_b, dn_b = expert_bytes(cfg)
     n_touch = float(np.mean(touched))
     x_bytes, y_bytes = T * H * 2, T * H * 2
-    gate_up_alg = n_touch * gu_b + A * H * 2 + A * I * 2  # weights + gathered rows in + mid out
+    gate_up_alg = n_touch * gu_b + x_bytes + A * I * 2  # weights + rows in + mid out
     layer_alg = n_touch * (gu_b + dn_b) + router_bytes(cfg) + x_bytes + y_bytes
     flops = 2.0 * A * (2 * I * H + H * I) + 2.0 * T * E * H
     ms = wall / K * 1e3
@@ -208,7 +317,7 @@ def main():
                    "experts_touched": n_touch, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": "qswitch_gate_up_geglu", "achieved": gbs_gu,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs_gu / HBM_PEAK_GBS,
-                     "traffic": None, "alg_bytes_per_launch": gate_up_alg,
+                     "traffic": read_traffic(), "alg_bytes_per_launch": gate_up_alg,
                      "mean_launch_us": mean_us["qswitch_gate_up_geglu"]},
         "layer": {"alg_bytes": layer_alg, "achieved_GBs": layer_gbs, "hbm_frac": layer_gbs / HBM_PEAK_GBS,
                   "flops": flops, "mfma_frac": flops / (ms * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12),

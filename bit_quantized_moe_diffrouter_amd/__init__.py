@@ -10,8 +10,7 @@ DiffRouter, DiffExperts, DiffDecoderLayer.forwardWith):
 
     indices, weights = moe_route(x_router, ...)           # DiffRouter
     offsets, sorted  = moe_sort(indices, E)               # token-by-expert sort
-    x_tiles = moe_gather(x_expert, k, E, offsets, sorted) # token rows in expert order
-    mid = qswitch_gate_up_geglu(x_tiles, T, gate_up, ...) # gate_up, split, GeGLU
+    mid = qswitch_gate_up_geglu(x_expert, gate_up, ...)   # gate_up, split, GeGLU
     y   = qswitch_down_combine(mid, down, weights, ...)   # down, weighted sum over k
 """
 from __future__ import annotations
@@ -25,7 +24,7 @@ import torch
 
 __all__ = [
     "QMoEError", "QuantWeight", "TiledWeight", "MoEParams", "lib", "library_path",
-    "moe_route", "moe_route_workspace", "moe_sort", "qswitch_mid_bytes", "moe_gather",
+    "moe_route", "moe_route_workspace", "moe_sort", "qswitch_mid_bytes",
     "qswitch_gate_up_geglu",
     "qswitch_down_combine", "qswitch_down_combine_workspace", "qlinear", "moe_layer",
 ]
@@ -71,7 +70,6 @@ _SIGNATURES = {
     "moe_sort_workspace": (_SZ, [_I, _I, _I]),
     "moe_sort": (ctypes.c_int, [_P, _I, _I, _I, _P, _P, _P, _SZ, _P]),
     "qswitch_mid_bytes": (_SZ, [_I, _I, _I, _I]),
-    "moe_gather": (ctypes.c_int, [_P, _I, _I, _I, _I, _P, _P, _P, _SZ, _P]),
     "qswitch_gate_up_geglu": (ctypes.c_int, [_P, _I, _I, _QP, _I, _I, _P, _P, _P, _SZ, _P]),
     "qswitch_down_combine_workspace": (_SZ, [_I, _I, _I, _I]),
     "qswitch_down_combine": (ctypes.c_int, [_P, _I, _I, _I, _QP, _I, _P, _P, _P, _P, _P, _SZ, _I, _P]),
@@ -247,29 +245,18 @@ def _nbytes(t: Optional[torch.Tensor]) -> int:
     return 0 if t is None else t.numel() * t.element_size()
 
 
-def moe_gather(x: torch.Tensor, k: int, E: int, expert_offsets: torch.Tensor, sorted_assign: torch.Tensor,
-               x_tiles: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Token rows in expert order: returns a uint8 buffer of activation tiles (H columns)."""
-    T, H = x.shape
-    _need(x, "x", 2)
-    if x_tiles is None:
-        x_tiles = torch.empty(max(1, qswitch_mid_bytes(T, k, H, E)), dtype=torch.uint8, device=x.device)
-    _check(lib().moe_gather(_ptr(x), T, H, k, E, _ptr(expert_offsets), _ptr(sorted_assign), _ptr(x_tiles),
-                            _nbytes(x_tiles), _stream()))
-    return x_tiles
-
-
-def qswitch_gate_up_geglu(x_tiles: torch.Tensor, T: int, gate_up: "TiledWeight", I: int, k: int,
+def qswitch_gate_up_geglu(x_expert: torch.Tensor, gate_up: "TiledWeight", I: int, k: int,
                           expert_offsets: torch.Tensor, sorted_assign: torch.Tensor,
                           mid: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """gate_up switch linear + split + GeGLU on moe_gather's tiles: returns mid, a uint8 buffer of
-    activation tiles (I columns; layout in qmoe.h)."""
-    H = gate_up.in_features
+    """gate_up switch linear + split + GeGLU: returns mid, a uint8 buffer of activation tiles
+    (I columns, the sorted rows of each expert in 16-row tiles; layout in qmoe.h)."""
+    T, H = x_expert.shape
+    _need(x_expert, "x_expert", 2)
     E = gate_up.experts
     if mid is None:
-        mid = torch.empty(max(1, qswitch_mid_bytes(T, k, I, E)), dtype=torch.uint8, device=x_tiles.device)
+        mid = torch.empty(max(1, qswitch_mid_bytes(T, k, I, E)), dtype=torch.uint8, device=x_expert.device)
     d = gate_up.desc()
-    _check(lib().qswitch_gate_up_geglu(_ptr(x_tiles), T, H, ctypes.byref(d), I, k, _ptr(expert_offsets),
+    _check(lib().qswitch_gate_up_geglu(_ptr(x_expert), T, H, ctypes.byref(d), I, k, _ptr(expert_offsets),
                                        _ptr(sorted_assign), _ptr(mid), _nbytes(mid), _stream()))
     return mid
 
@@ -339,10 +326,9 @@ class MoEParams:
 
 def moe_layer(x_router: torch.Tensor, x_expert: torch.Tensor, p: MoEParams, k: int, eps: float,
               deterministic: int = 1):
-    """The five calls in order.  Returns (y, indices, weights, offsets, sorted_assign, mid)."""
+    """The four calls in order.  Returns (y, indices, weights, offsets, sorted_assign, mid)."""
     idx, w = moe_route(x_router, p.norm_scale, eps, p.router, p.per_expert_scale, k, p.logit_bias)
     off, sa = moe_sort(idx, p.E)
-    xt = moe_gather(x_expert, k, p.E, off, sa)
-    mid = qswitch_gate_up_geglu(xt, x_expert.shape[0], p.gate_up, p.I, k, off, sa)
+    mid = qswitch_gate_up_geglu(x_expert, p.gate_up, p.I, k, off, sa)
     y = qswitch_down_combine(mid, x_expert.shape[0], k, p.down, w, off, sa, deterministic=deterministic)
     return y, idx, w, off, sa, mid

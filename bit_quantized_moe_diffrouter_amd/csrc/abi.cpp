@@ -178,27 +178,7 @@ size_t qswitch_mid_bytes(int32_t T, int32_t k, int32_t I, int32_t E) {
   return (size_t)qmoe::act_tiles_max((long long)T * k, E) * (size_t)(I / 64) * qmoe::kActBlock;
 }
 
-int moe_gather(const uint16_t* x, int32_t T, int32_t H, int32_t k, int32_t E, const int32_t* expert_offsets,
-               const int32_t* sorted_assign, void* x_tiles, size_t tiles_bytes, hipStream_t stream) {
-  REQUIRE(T >= 0, QMOE_ERR_INVALID, "moe_gather: T=%d < 0", T);
-  REQUIRE(H > 0 && H % 64 == 0, QMOE_ERR_INVALID, "moe_gather: H=%d must be a positive multiple of 64", H);
-  REQUIRE(k >= 1 && k <= 16, QMOE_ERR_UNSUPPORTED, "moe_gather: k=%d outside [1, 16]", k);
-  REQUIRE(E >= 1 && E <= 256, QMOE_ERR_UNSUPPORTED, "moe_gather: E=%d outside [1, 256]", E);
-  REQUIRE((long long)T * k <= kMaxAssign, QMOE_ERR_UNSUPPORTED, "moe_gather: T*k above 2^24");
-  if (T == 0) return ok();
-  REQUIRE_PTR(x, 16, "moe_gather x");
-  REQUIRE_PTR(expert_offsets, 4, "moe_gather expert_offsets");
-  REQUIRE_PTR(sorted_assign, 4, "moe_gather sorted_assign");
-  REQUIRE_PTR(x_tiles, 16, "moe_gather x_tiles");
-  const size_t need = qswitch_mid_bytes(T, k, H, E);
-  REQUIRE(tiles_bytes >= need, QMOE_ERR_INVALID, "moe_gather: x_tiles of %zu bytes needed, %zu given", need,
-          tiles_bytes);
-  return launched(qmoe::launch_act_gather(x, T, H, k, expert_offsets, sorted_assign, E, T * k,
-                                          static_cast<uint8_t*>(x_tiles), stream),
-                  "moe_gather");
-}
-
-int qswitch_gate_up_geglu(const void* x_tiles, int32_t T, int32_t H, const qmoe_qweight* gate_up, int32_t I,
+int qswitch_gate_up_geglu(const uint16_t* x_expert, int32_t T, int32_t H, const qmoe_qweight* gate_up, int32_t I,
                           int32_t k, const int32_t* expert_offsets, const int32_t* sorted_assign, void* mid,
                           size_t mid_bytes, hipStream_t stream) {
   REQUIRE(T >= 0, QMOE_ERR_INVALID, "qswitch_gate_up_geglu: T=%d < 0", T);
@@ -211,19 +191,20 @@ int qswitch_gate_up_geglu(const void* x_tiles, int32_t T, int32_t H, const qmoe_
   REQUIRE(E >= 1 && E <= 256, QMOE_ERR_UNSUPPORTED, "qswitch_gate_up_geglu: E=%d outside [1, 256]", E);
   if (T == 0) return ok();
   if (int rc = check_qweight(gate_up, "qswitch_gate_up_geglu gate_up", E, 2 * I, H, QMOE_LAYOUT_TILED, I)) return rc;
-  REQUIRE_PTR(x_tiles, 16, "qswitch_gate_up_geglu x_tiles");
+  REQUIRE_PTR(x_expert, 16, "qswitch_gate_up_geglu x_expert");
   REQUIRE_PTR(expert_offsets, 4, "qswitch_gate_up_geglu expert_offsets");
   REQUIRE_PTR(sorted_assign, 4, "qswitch_gate_up_geglu sorted_assign");
   REQUIRE_PTR(mid, 16, "qswitch_gate_up_geglu mid");
-  const size_t need_x = qswitch_mid_bytes(T, k, H, E), need_mid = qswitch_mid_bytes(T, k, I, E);
-  REQUIRE(need_x < (1ULL << 32), QMOE_ERR_UNSUPPORTED, "qswitch_gate_up_geglu: x tiles reach 2^32 bytes");
+  const size_t need_mid = qswitch_mid_bytes(T, k, I, E);
+  REQUIRE((long long)T * H * 2 < (1LL << 32), QMOE_ERR_UNSUPPORTED,
+          "qswitch_gate_up_geglu: activation bytes reach 2^32");
   REQUIRE(need_mid < (1ULL << 32), QMOE_ERR_UNSUPPORTED, "qswitch_gate_up_geglu: mid tiles reach 2^32 bytes");
   REQUIRE(mid_bytes >= need_mid, QMOE_ERR_INVALID, "qswitch_gate_up_geglu: mid of %zu bytes needed, %zu given",
           need_mid, mid_bytes);
   int ncu = 0;
   if (int rc = num_cu_current(&ncu)) return rc;
   qmoe::SwitchArgs a{};
-  a.a = static_cast<const uint16_t*>(x_tiles);
+  a.a = x_expert;
   a.max_tiles = (int)qmoe::act_tiles_max((long long)T * k, E);
   a.w = gate_up->w;
   a.nblk = qmoe::tiled_blocks(2 * I, I);

@@ -39,16 +39,15 @@ int tiled_blocks(int rows, int split);
 hipError_t launch_tile_weight(const uint32_t* w, const uint16_t* s, const uint16_t* b, int E, int rows, int K,
                               int split, uint8_t* dst, hipStream_t stream);
 
-// Activation tiles (switch modes): the rows of expert e's segment are cut into
-// 16-row tiles, numbered expert by expert; per (tile, 64-wide group) one block
-// of kActBlock bytes in MFMA operand order (layout in qmoe.h).
+// Activation tiles (mid, between the two switch linears): the rows of expert
+// e's segment are cut into 16-row tiles, numbered expert by expert; per (tile,
+// 64-wide group) one block of kActBlock bytes in MFMA operand order (layout in
+// qmoe.h).
 constexpr int kActBlock = 2048;
 long long act_tiles_max(long long A, int E);
-hipError_t launch_act_gather(const uint16_t* x, int T, int H, int k, const int32_t* offsets,
-                             const int32_t* sorted_assign, int E, int A, uint8_t* dst, hipStream_t stream);
 
 struct SwitchArgs {
-  const uint16_t* a;       // dense: bf16 rows of length K; switch: activation tiles
+  const uint16_t* a;       // gate_up, dense: bf16 rows of length K; down: activation tiles
   const void* w;           // tiled weight [E, nblk, K/64] units of kTiledUnit bytes
   int nblk;                // tiled blocks per expert
   const int32_t* offsets;  // [E+1] sorted-row segments (switch modes)

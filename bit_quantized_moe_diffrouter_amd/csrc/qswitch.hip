@@ -17,10 +17,12 @@
 // pairs in the order the lanes read them.  A wave streams one block: per group
 // four 1 KB and two 256-byte fully coalesced loads.  Within a code word the
 // nibbles are placed so that one v_and_or_b32 per pair yields two bf16 of
-// 128 + q in natural k order (no activation shuffling).  The activations come
-// as activation tiles (16 sorted rows x 64 columns in operand order, written
-// by moe_gather for gate_up and by the gate_up epilogue for down): two more
-// coalesced 1 KB loads per 16-row tile and group.
+// 128 + q in natural k order (no activation shuffling).  Activations: gate_up
+// and the dense linear read bf16 rows, 128 contiguous bytes per row and
+// group (two loads of 8 rows per 16-row tile), and put them in operand order
+// through LDS; the down pass reads mid as activation tiles (16 sorted rows x
+// 64 columns already in operand order, written by the gate_up epilogue): two
+// coalesced 1 KB loads per tile and group.
 //
 // Work items.  An item is (expert e, chunk of up to 32 sorted rows of e, tile
 // of NW weight blocks).  A persistent grid walks the items, derived on the
@@ -51,7 +53,9 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kBM = 32;            // sorted rows per chunk (at most two 16-row tiles)
 constexpr int kMaxBuckets = 257;   // experts (<= 256) + the dropped bucket of the down pass
 constexpr int kNS = 8;             // 16-row subtiles per tiled block
-constexpr int kRingMax = 2;        // ring slots: two-tile slots fill the register file at 2 waves/SIMD
+constexpr int kXcds = 8;           // accelerator dies; workgroup b runs on die b % 8
+constexpr int kRingMax = 2;
+constexpr int kMaxWgItems = 64;    // gate_up: items of one workgroup (token table in LDS)        // ring slots: two-tile slots fill the register file at 2 waves/SIMD
 
 struct Item {
   int e;     // expert whose weights are used (0 for the dropped bucket)
@@ -110,6 +114,7 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
   __shared__ int s_tcum[kMaxBuckets + 1];  // switch modes: first activation tile of each expert
   __shared__ int s_scan[kWaves];
   __shared__ int s_dst[2][kBM];           // down pass: assignment id of each chunk row
+  __shared__ int s_tok[(MODE == MODE_GATE_UP) ? kMaxWgItems : 1][kBM];  // gate_up: token of each chunk row
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar branches below)
@@ -165,10 +170,14 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
   total2 = __builtin_amdgcn_readfirstlane(total2);
   total1 = __builtin_amdgcn_readfirstlane(total1);
   // Items are ranked two-tile chunks first (the costlier ones), then one-tile
-  // chunks; workgroup b takes ranks b, 2 grid - 1 - b, 2 grid + b, ... (a
-  // boustrophedon over the cost-sorted list, which evens out the work).
+  // chunks; the workgroup at position q takes ranks q, 2 grid - 1 - q,
+  // 2 grid + q, ... (a boustrophedon over the cost-sorted list, which evens out
+  // the work).  Workgroups are dealt to the 8 XCDs round-robin; positions are
+  // numbered XCD by XCD, so consecutive ranks -- the column tiles of one chunk,
+  // which read the same activation tiles -- run on one XCD and share its L2.
   const int total_items = __builtin_amdgcn_readfirstlane((total2 + total1) * p.ntiles);
-  const int grid = (int)gridDim.x, gb = (int)blockIdx.x;
+  const int grid = (int)gridDim.x, b = (int)blockIdx.x;
+  const int gb = (grid % kXcds == 0) ? (b % kXcds) * (grid / kXcds) + b / kXcds : b;
   auto item_of = [&](int j) __attribute__((always_inline)) {  // rank of this workgroup's j-th item
     return j * grid + ((j & 1) ? grid - 1 - gb : gb);
   };
@@ -176,7 +185,7 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
   if (!has_item(0)) return;  // uniform: no barrier follows for this workgroup
 
   // item rank -> (expert, rows, tile); wave-uniform
-  auto decode = [&](int item) __attribute__((always_inline)) {
+  auto decode_raw = [&](int item) __attribute__((always_inline)) {
     Item it;
     const int chunk = item / p.ntiles;
     it.tile = item - chunk * p.ntiles;
@@ -202,6 +211,10 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
       it.zero = (MODE == MODE_DOWN) && (e >= p.E);
       it.e = it.zero ? 0 : e;
     }
+    return it;
+  };
+  auto decode = [&](int item) __attribute__((always_inline)) {
+    Item it = decode_raw(item);
     it.e = __builtin_amdgcn_readfirstlane(it.e);
     it.r0 = __builtin_amdgcn_readfirstlane(it.r0);
     it.rows = __builtin_amdgcn_readfirstlane(it.rows);
@@ -225,6 +238,19 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
     }
     return r;
   };
+  // gate_up: the token of every row of this workgroup's items, once (the
+  // launcher keeps a workgroup's items within kMaxWgItems)
+  if constexpr (MODE == MODE_GATE_UP) {
+    int nj = 0;
+    while (nj < kMaxWgItems && has_item(nj)) ++nj;
+    for (int t = tid; t < nj * kBM; t += kThreads) {
+      const Item it = decode_raw(item_of(t / kBM));
+      const int a = p.assign[it.r0 + min(t % kBM, it.rows - 1)];
+      s_tok[t / kBM][t % kBM] = (a >= 0 && a < A) ? a / p.ktop : 0;
+    }
+    __syncthreads();
+  }
+
   // activation tile of row tile m of an item (switch modes); a tile past the
   // buffers (inconsistent offsets) reads tile 0 and is never stored
   auto tile_of = [&](const Item& it, int m) __attribute__((always_inline)) {
@@ -250,7 +276,7 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
     // ---- load cursor (per wave): the item and group whose operands are issued next
     const uint8_t* const wbytes = (const uint8_t*)p.w;
     const uint8_t* const abytes = (const uint8_t*)p.a;
-    const uint32_t arow = K * 2;                     // dense: bytes per activation row
+    const uint32_t arow = K * 2;                     // gate_up, dense: bytes per activation row
     const uint32_t c_off = lane * 16;                // code bytes of this lane in a unit
     const uint32_t s_off = 4096 + ln * 16;           // scale bytes of this lane in a unit
     Item linfo = decode(item_of(0));
@@ -260,8 +286,11 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
     bool n_valid = has_item(n_j);
     Item ninfo = n_valid ? decode(item_of(n_j)) : linfo;
     const uint8_t* l_wbase;  // unit (expert, block, group 0) of this wave
-    uint32_t l_aoff[MT];     // per row tile; dense: offset of the lane's row and k slice; switch: of the
-                             // lane's operand words in the tile's group-0 block
+    // per row tile m and half h: gate_up, dense: offset of the lane's 16 bytes
+    // (row 8 h + lane / 8 of the tile, columns 8 (lane % 8) .. + 7 of a group)
+    // in the activation rows; down: of the lane's operand words in the tile's
+    // group-0 block (h = 1 unused)
+    uint32_t l_aoff[MT][2];
     int l_loc = 0;           // items the load cursor has entered (s_dst parity)
     // Down pass: assignment id of chunk row lane % 32 of the item after the load
     // cursor's, loaded at the end of every step (so the item switch uses a value
@@ -283,17 +312,23 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
       const int lr = lane & 31;
       s_dst[loc & 1][lr] = (lr < it.rows && raw >= 0 && raw < A) ? raw : -1;
     };
-    auto set_act_offset = [&](const Item& it, const Role& r) __attribute__((always_inline)) {
-      (void)r;
+    auto set_act_offset = [&](const Item& it, int j) __attribute__((always_inline)) {
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
         const int mm = (it.rows > 16) ? m : 0;  // a one-tile chunk reads its tile twice
-        if constexpr (MODE == MODE_DENSE) {
-          const int src = it.r0 + min(16 * mm + ln, it.rows - 1);
-          l_aoff[m] = (uint32_t)src * arow + lq * 32;
-        } else {
+        if constexpr (MODE == MODE_DOWN) {
           const int tau = max(tile_of(it, mm), 0);
-          l_aoff[m] = (uint32_t)tau * (uint32_t)(G * kActBlock) + lane * 16;
+          l_aoff[m][0] = (uint32_t)tau * (uint32_t)(G * kActBlock) + lane * 16;
+          l_aoff[m][1] = 0;
+        } else {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int rr = min(16 * mm + 8 * h + (lane >> 3), it.rows - 1);  // row of the chunk
+            int src;
+            if constexpr (MODE == MODE_GATE_UP) src = s_tok[min(j, kMaxWgItems - 1)][rr];
+            else src = it.r0 + rr;
+            l_aoff[m][h] = (uint32_t)src * arow + (lane & 7) * 16;
+          }
         }
       }
     };
@@ -301,7 +336,7 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
       const int raw0 = raw_assign(linfo);
       pf_raw = raw_assign(ninfo);
       set_weight_base(linfo, lrole);
-      set_act_offset(linfo, lrole);
+      set_act_offset(linfo, 0);
       if constexpr (MODE == MODE_DOWN) put_dst(0, linfo, raw0);
     }
 
@@ -313,14 +348,13 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
       for (int h = 0; h < 2; ++h) sl.s[h] = *(const u32x4_t*)(u + s_off + h * 256);
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
-        if constexpr (MODE == MODE_DENSE) {
-          const uint8_t* ab = abytes + (size_t)lg * 128 + l_aoff[m];
-          sl.a[m][0] = *(const u32x4_t*)(ab);
-          sl.a[m][1] = *(const u32x4_t*)(ab + 16);
-        } else {  // one coalesced kilobyte per operand register
-          const uint8_t* ab = abytes + l_aoff[m] + (uint32_t)lg * kActBlock;
+        if constexpr (MODE == MODE_DOWN) {  // one coalesced kilobyte per operand register
+          const uint8_t* ab = abytes + l_aoff[m][0] + (uint32_t)lg * kActBlock;
           sl.a[m][0] = *(const u32x4_t*)(ab);
           sl.a[m][1] = *(const u32x4_t*)(ab + kActBlock / 2);
+        } else {  // 8 rows x 128 bytes per load; compute puts them in operand order
+#pragma unroll
+          for (int h = 0; h < 2; ++h) sl.a[m][h] = *(const u32x4_t*)(abytes + l_aoff[m][h] + (uint32_t)lg * 128);
         }
       }
     };
@@ -334,7 +368,7 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
       lrole = role_of(linfo);
       lg = lrole.gk0;
       set_weight_base(linfo, lrole);
-      set_act_offset(linfo, lrole);
+      set_act_offset(linfo, n_j);
       ++l_loc;
       if constexpr (MODE == MODE_DOWN) put_dst(l_loc, linfo, pf_raw);
       ++n_j;
@@ -369,12 +403,45 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
     // weights are unpacked once for all of them
     auto compute = [&](Slot<MT>& sl) __attribute__((always_inline)) {
       const bool t2 = cinfo.rows > 16;  // uniform: a second row tile to compute
+      u32x4_t a[MT][2];  // operands: lane (ln, lq) holds row ln, columns 16 lq .. 16 lq + 15
+      if constexpr (MODE == MODE_DOWN) {
+#pragma unroll
+        for (int m = 0; m < MT; ++m) a[m][0] = sl.a[m][0], a[m][1] = sl.a[m][1];
+      } else {
+        // through this wave's own slice of the partial-sum buffer (free while
+        // steps run): row r's 16-byte chunk c sits at slot c ^ swz(r), so both
+        // the 8-lanes-per-row writes and the operand reads are conflict free
+        uint8_t* const scr = qmm_lds + wave * (2 * kNS * 64 * 16);
+        auto swz = [](int r) __attribute__((always_inline)) { return ((r & 1) << 2) | ((r >> 1) & 3); };
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          if (m > 0 && !t2) continue;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int r = 8 * h + (lane >> 3);
+            *(u32x4_t*)(scr + m * 2048 + r * 128 + ((lane & 7) ^ swz(r)) * 16) = sl.a[m][h];
+          }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          if (m > 0 && !t2) continue;
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            a[m][h] = *(const u32x4_t*)(scr + m * 2048 + ln * 128 + ((2 * lq + h) ^ swz(ln)) * 16);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      }
       f32x4_t X[MT];
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
         if (m > 0 && !t2) continue;
-        X[m] = mfma16x16x32(sl.a[m][0], ones, zero4());
-        X[m] = mfma16x16x32(sl.a[m][1], ones, X[m]);
+        X[m] = mfma16x16x32(a[m][0], ones, zero4());
+        X[m] = mfma16x16x32(a[m][1], ones, X[m]);
       }
 #pragma unroll
       for (int j = 0; j < kNS; ++j) {
@@ -386,8 +453,8 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
           if (m > 0 && !t2) continue;
-          f32x4_t P = mfma16x16x32(sl.a[m][0], b0, zero4());
-          P = mfma16x16x32(sl.a[m][1], b1, P);
+          f32x4_t P = mfma16x16x32(a[m][0], b0, zero4());
+          P = mfma16x16x32(a[m][1], b1, P);
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             acc[m][j][i] = __builtin_fmaf(cc, X[m][i], __builtin_fmaf(sc, P[i], acc[m][j][i]));
@@ -557,66 +624,6 @@ __global__ __launch_bounds__(256) void tile_weight_kernel(const uint32_t* __rest
 // ------------------------------------------------------------ activation tiles
 long long act_tiles_max(long long A, int E) { return (A + 15) / 16 + std::min<long long>(E, A); }
 
-// Gathers the token rows of the sorted assignments into activation tiles.
-// Workgroup (tau, c) writes groups 4c .. 4c+3 of tile tau, one thread per two
-// 16-byte operand pieces; piece (g, h, L) of a tile holds columns
-// 64 g + 16 (L / 16) + 8 h .. + 7 of tile row L % 16.  Rows past a segment's
-// end are not written.
-constexpr int kGatherGroups = 4;
-__global__ __launch_bounds__(256) void act_gather_kernel(const uint16_t* __restrict__ x, int H, int k,
-                                                         const int32_t* __restrict__ offsets,
-                                                         const int32_t* __restrict__ sorted_assign, int E, int A,
-                                                         uint8_t* __restrict__ dst) {
-  __shared__ int s_tc[kMaxBuckets + 1];
-  __shared__ int s_lo[kMaxBuckets];
-  __shared__ int s_hi[kMaxBuckets];
-  __shared__ int s_scan[kWaves];
-  __shared__ int s_tok[16];
-  __shared__ int s_e;
-  const int tid = threadIdx.x;
-  int nt = 0;
-  if (tid < E) {
-    const int lo = min(max(offsets[tid], 0), A);
-    const int hi = min(max(offsets[tid + 1], lo), A);
-    s_lo[tid] = lo;
-    s_hi[tid] = hi;
-    nt = (hi - lo + 15) / 16;
-  }
-  int total;
-  const int incl = block_inclusive_scan<kThreads>(nt, s_scan, &total);
-  if (tid < E) s_tc[tid] = incl - nt;
-  if (tid == 0) s_tc[E] = total;
-  __syncthreads();
-  const int tau = blockIdx.x;
-  if (tau >= total) return;  // uniform
-  if (tid < E && s_tc[tid] <= tau && tau < s_tc[tid + 1]) s_e = tid;
-  __syncthreads();
-  const int e = s_e;
-  const int r0 = s_lo[e] + 16 * (tau - s_tc[e]);
-  if (tid < 16) {
-    const int r = r0 + tid;
-    const int a = (r < s_hi[e]) ? sorted_assign[r] : -1;
-    s_tok[tid] = (a >= 0 && a < A) ? a / k : -1;
-  }
-  __syncthreads();
-  const int G = H / 64;
-  const int g0 = blockIdx.y * kGatherGroups;
-  const int pieces = min(kGatherGroups, G - g0) * (kActBlock / 16);
-  uint8_t* const out = dst + ((size_t)tau * G + g0) * kActBlock;
-  u32x4_t v[2];
-  int tok[2];
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int pc = tid + u * kThreads;
-    const int g = g0 + (pc >> 7), h = (pc >> 6) & 1, L = pc & 63;
-    tok[u] = (pc < pieces) ? s_tok[L & 15] : -1;
-    if (tok[u] >= 0) v[u] = *(const u32x4_t*)(x + (size_t)tok[u] * H + 64 * g + 16 * (L >> 4) + 8 * h);
-  }
-#pragma unroll
-  for (int u = 0; u < 2; ++u)
-    if (tok[u] >= 0) *(u32x4_t*)(out + (size_t)(tid + u * kThreads) * 16) = v[u];
-}
-
 // y[t, h] = bf16( sum_{j<k} w[t, j] * D[t*k + j, h] ), products and sum in fp32, j order.
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ D, const float* __restrict__ w, int T,
                                                       int k, int H, uint16_t* __restrict__ y) {
@@ -654,6 +661,7 @@ hipError_t launch_cfg(SwitchArgs a, int extra_buckets, int num_cu, hipStream_t s
     chunks = (a.rows_total + kBM - 1) / kBM + (long long)std::min(a.E, a.rows_total) + extra_buckets;
   const long long items = chunks * a.ntiles;
   long long grid = std::min(items, (long long)num_cu * 2);
+  if (MODE == MODE_GATE_UP) grid = std::max(grid, (items + kMaxWgItems - 1) / kMaxWgItems);
   if (grid < 1) grid = 1;
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&qmm_kernel<MODE, NBI, D>),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -696,16 +704,6 @@ hipError_t launch_combine(const float* D, const float* w, int T, int k, int H, u
   const long long n = (long long)T * (H / 4);
   const long long blocks = (n + 255) / 256;
   hipLaunchKernelGGL(combine_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, D, w, T, k, H, y);
-  return hipGetLastError();
-}
-hipError_t launch_act_gather(const uint16_t* x, int T, int H, int k, const int32_t* offsets,
-                             const int32_t* sorted_assign, int E, int A, uint8_t* dst, hipStream_t stream) {
-  (void)T;
-  const long long tiles = act_tiles_max(A, E);
-  if (tiles <= 0) return hipSuccess;
-  const int cg = (H / 64 + kGatherGroups - 1) / kGatherGroups;
-  hipLaunchKernelGGL(act_gather_kernel, dim3((unsigned)tiles, (unsigned)cg), dim3(kThreads), 0, stream, x, H, k,
-                     offsets, sorted_assign, E, A, dst);
   return hipGetLastError();
 }
 int tiled_blocks(int rows, int split) { return split > 0 ? split / 64 : (rows + 127) / 128; }

@@ -11,7 +11,6 @@
  *   moe_route             router: norm, scale, 4-bit projection, top-k,
  *                         precise softmax, per_expert_scale
  *   moe_sort              token-by-expert sort of the routing assignments
- *   moe_gather            the token rows in expert order, as activation tiles
  *   qswitch_gate_up_geglu fused gate_up switch linear, split, GeGLU
  *   qswitch_down_combine  down switch linear + weighted sum over k per token
  *   qlinear               dense 4-bit linear
@@ -180,7 +179,7 @@ int moe_sort(const int32_t* indices, int32_t T, int32_t k, int32_t E, int32_t* e
              int32_t* sorted_assign, void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
- * Activation tiles (the layout of moe_gather's x_tiles and of mid)
+ * Activation tiles (the layout of mid)
  *
  * The sorted rows of expert e's segment [offsets[e], offsets[e+1]) are cut
  * into tiles of 16 rows (the last one of a segment may be partial); tiles are
@@ -199,20 +198,6 @@ int moe_sort(const int32_t* indices, int32_t T, int32_t k, int32_t E, int32_t* e
 size_t qswitch_mid_bytes(int32_t T, int32_t k, int32_t C, int32_t E);
 
 /* ------------------------------------------------------------------------
- * moe_gather -- the rows the experts see, in expert order (model.ts page,
- * DiffExperts.forward: x gathered by order // k): the token row of every
- * sorted assignment, written as activation tiles of H columns.
- *
- *   x               bf16 [T, H]  the (normalised) rows the experts see
- *   expert_offsets, sorted_assign   as produced by moe_sort for the same T, k, E
- *   x_tiles (out)   at least qswitch_mid_bytes(T, k, H, E) bytes (tiles_bytes)
- * Rows of sorted_assign outside [0, T*k) leave their tile row unwritten.
- * ---------------------------------------------------------------------- */
-int moe_gather(const uint16_t* x, int32_t T, int32_t H, int32_t k, int32_t E,
-               const int32_t* expert_offsets, const int32_t* sorted_assign,
-               void* x_tiles, size_t tiles_bytes, hipStream_t stream);
-
-/* ------------------------------------------------------------------------
  * qswitch_gate_up_geglu -- fused gate_up QuantizedSwitchLinear over the
  * sorted rows, split at moe_intermediate, GeGLU (model.ts page,
  * DiffExperts.forward: gateUp.forward, split, geglu; the GeGLU is
@@ -223,7 +208,7 @@ int moe_gather(const uint16_t* x, int32_t T, int32_t H, int32_t k, int32_t E,
  *   g = x[t] . dequant(gate_up)[e]^T            (2I values, fp32 accumulate)
  *   mid[r, n] = gelu_tanh(g[n]) * g[I + n]      n < I, stored bf16
  *
- *   x_tiles         the rows x[t] as moe_gather wrote them (H columns)
+ *   x_expert        bf16 [T, H]  the (normalised) rows the experts see
  *   gate_up         experts = E, rows = 2*I, in = H, layout QMOE_LAYOUT_TILED
  *                   tiled with split = I
  *   I               moe_intermediate, I % 64 == 0
@@ -231,7 +216,7 @@ int moe_gather(const uint16_t* x, int32_t T, int32_t H, int32_t k, int32_t E,
  *   mid (out)       activation tiles of I columns (layout above), at least
  *                   qswitch_mid_bytes(T, k, I, E) bytes (mid_bytes)
  * ---------------------------------------------------------------------- */
-int qswitch_gate_up_geglu(const void* x_tiles, int32_t T, int32_t H,
+int qswitch_gate_up_geglu(const uint16_t* x_expert, int32_t T, int32_t H,
                           const qmoe_qweight* gate_up, int32_t I, int32_t k,
                           const int32_t* expert_offsets, const int32_t* sorted_assign,
                           void* mid, size_t mid_bytes, hipStream_t stream);

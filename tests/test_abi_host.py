@@ -79,11 +79,11 @@ def test_sort_validation(L):
     assert L.moe_sort_workspace(256, 8, 128) == 0
 
 
-def gate_up(L, T=16, H=256, I=128, k=2, E=8, rows=None, inp=None, xt=A16, mid=A16, mid_bytes=1 << 30, layout=1,
+def gate_up(L, T=16, H=256, I=128, k=2, E=8, rows=None, inp=None, x=A16, mid=A16, mid_bytes=1 << 30, layout=1,
             split=None, **kw):
     d = qw(E, 2 * I if rows is None else rows, H if inp is None else inp, layout=layout,
            split=I if split is None else split, **kw)
-    return L.qswitch_gate_up_geglu(xt, T, H, ctypes.byref(d), I, k, A16, A16, mid, mid_bytes, None)
+    return L.qswitch_gate_up_geglu(x, T, H, ctypes.byref(d), I, k, A16, A16, mid, mid_bytes, None)
 
 
 def test_gate_up_validation(L):
@@ -97,25 +97,12 @@ def test_gate_up_validation(L):
     assert gate_up(L, group=128) == UNSUPPORTED
     assert gate_up(L, mid=None) == INVALID
     assert gate_up(L, mid=A16 + 8) == INVALID
-    assert gate_up(L, xt=None) == INVALID
+    assert gate_up(L, x=None) == INVALID
+    assert gate_up(L, x=A16 + 2) == INVALID
     assert gate_up(L, layout=0) == INVALID and "qmoe_tile_weight" in err(L)
     assert gate_up(L, split=0) == INVALID and "split" in err(L)
     need_mid = L.qswitch_mid_bytes(16, 2, 128, 8)
     assert gate_up(L, mid_bytes=need_mid - 1) == INVALID and "mid" in err(L)
-
-
-def gather(L, T=16, H=256, k=2, E=8, x=A16, tiles=A16, nbytes=1 << 30):
-    return L.moe_gather(x, T, H, k, E, A16, A16, tiles, nbytes, None)
-
-
-def test_gather_validation(L):
-    assert gather(L, T=0, x=None, tiles=None, nbytes=0) == 0
-    assert gather(L, H=100) == INVALID
-    assert gather(L, k=0) == UNSUPPORTED
-    assert gather(L, E=300) == UNSUPPORTED
-    assert gather(L, x=None) == INVALID
-    assert gather(L, tiles=A16 + 4) == INVALID
-    assert gather(L, nbytes=L.qswitch_mid_bytes(16, 2, 256, 8) - 1) == INVALID and "x_tiles" in err(L)
 
 
 def test_activation_tile_sizes(L):

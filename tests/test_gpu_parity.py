@@ -189,8 +189,7 @@ def run_experts(inp, idx, w, deterministic=1):
     idx_d = dev_tensor(idx.astype(np.int32))
     w_d = dev_tensor(w.astype(np.float32))
     off, sa = q.moe_sort(idx_d, cfg.E)
-    xt = q.moe_gather(x, cfg.k, cfg.E, off, sa)
-    mid = q.qswitch_gate_up_geglu(xt, cfg.T, p.gate_up, cfg.I, cfg.k, off, sa)
+    mid = q.qswitch_gate_up_geglu(x, p.gate_up, cfg.I, cfg.k, off, sa)
     y = q.qswitch_down_combine(mid, cfg.T, cfg.k, p.down, w_d, off, sa, deterministic=deterministic)
     torch.cuda.synchronize()
     return bf16_host(y), untile_activations(mid, off, cfg.T * cfg.k, cfg.I), sa.cpu().numpy()

@@ -262,10 +262,11 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
       return (tau >= 0 && tau < p.max_tiles) ? tau : -1;
     }
   };
-  // owner (K part) of subtile j among the waves of one (row tile, block):
-  // gate_up keeps gate j and up j + 4 together
+  // owner (K part) of subtile j among the waves of one block: gate_up keeps
+  // gate j and up j + 4 together; the other modes give each K part a run of
+  // kNS / nk contiguous subtiles
   auto owner_of = [&](int j, int nk) __attribute__((always_inline)) {
-    return ((MODE == MODE_GATE_UP) ? (j & 3) : j) % nk;
+    return (MODE == MODE_GATE_UP) ? (j & 3) % nk : j / (kNS / nk);
   };
 
   // Slots and accumulators hold two row tiles; a one-tile chunk reads tile 0
@@ -462,70 +463,123 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
       }
     };
 
-    // end of the current item: every wave parks its partial sums in LDS (its
-    // accumulators are then free for the next item); the owner of each subtile
-    // adds the K parts in K order and writes the outputs of every row tile
+    // End of the current item.  Each wave parks in LDS the partial sums of the
+    // subtiles that other waves own; after a barrier every owner adds the K
+    // parts of its subtiles in K order (its own part straight from registers),
+    // stages the results in the part of its own LDS slice that nobody parked
+    // into, and writes them with 16-byte stores.
     auto finish_item = [&]() __attribute__((always_inline)) {
       f32x4_t* red = (f32x4_t*)qmm_lds;
-      const int nk = crole.nk;
+      const int nk = crole.nk, kp = crole.kp, blk = crole.blk;
+      const bool t2 = cinfo.rows > 16;
+      const bool member = wave < nk * NBI;  // not a spare wave
       auto slot_of = [&](int w, int m, int j) __attribute__((always_inline)) {
         return ((w * 2 + m) * kNS + j) * 64 + lane;
       };
+      if (member) {
 #pragma unroll
-      for (int m = 0; m < MT; ++m)
+        for (int m = 0; m < MT; ++m)
 #pragma unroll
-        for (int j = 0; j < kNS; ++j) {
-          if (m == 0 || cinfo.rows > 16) red[slot_of(wave, m, j)] = acc[m][j];
-          acc[m][j] = zero4();
-        }
+          for (int j = 0; j < kNS; ++j)
+            if ((m == 0 || t2) && owner_of(j, nk) != kp) red[slot_of(wave, m, j)] = acc[m][j];
+      }
       __syncthreads();
-      const int blk = crole.blk;
-      const int wbase = wave - crole.kp;  // wave of K part 0 with the same block
-      if (blk < p.nblk && (!cinfo.zero || MODE == MODE_DOWN)) {
-        constexpr int NOUT = (MODE == MODE_GATE_UP) ? 4 : kNS;  // output subtiles of a block
+      const int wbase = wave - kp;  // wave of K part 0 with the same block
+      // K parts of subtile j in K order; `mine` is this wave's part
+      auto ksum = [&](int m, int j, f32x4_t mine) __attribute__((always_inline)) {
+        f32x4_t v = (kp == 0) ? mine : red[slot_of(wbase, m, j)];
+        for (int q = 1; q < nk; ++q) {
+          const f32x4_t t = (q == kp) ? mine : red[slot_of(wbase + q, m, j)];
 #pragma unroll
-        for (int m = 0; m < MT; ++m) {
-          if (m > 0 && cinfo.rows <= 16) continue;
-          // gate_up: mid goes out as the down pass's activation tiles; this
-          // block's 64 columns are that pass's group blk
-          const int tau = (MODE == MODE_GATE_UP) ? tile_of(cinfo, m) : 0;
-          if (tau < 0) continue;
-          uint8_t* const mblk = (uint8_t*)p.out + ((size_t)tau * (p.Nout / 64) + blk) * kActBlock;
+          for (int i = 0; i < 4; ++i) v[i] += t[i];
+        }
+        return v;
+      };
+      uint8_t* const own = qmm_lds + (size_t)wave * (2 * kNS * 1024);  // this wave's slice
+      if (member && blk < p.nblk) {
+        if constexpr (MODE == MODE_GATE_UP) {
+          // gate j and up j + 4 -> 16 columns of mid, which the down pass reads as
+          // group blk of activation tile tau: column 16 j + c of tile row r sits at
+          // byte (c / 8) * 1024 + (r + 16 j) * 16 + (c % 8) * 2 of the block
 #pragma unroll
-          for (int j = 0; j < NOUT; ++j) {
-            if (owner_of(j, nk) != crole.kp) continue;
-            const int col = blk * BCOLS + 16 * j + ln;
-            if (col >= p.Nout) continue;
-            f32x4_t v0 = red[slot_of(wbase, m, j)], v1;
-            if constexpr (MODE == MODE_GATE_UP) v1 = red[slot_of(wbase, m, j + 4)];
-            for (int k = 1; k < nk; ++k) {
-              const f32x4_t t0 = red[slot_of(wbase + k, m, j)];
+          for (int j = 0; j < 4; ++j) {
+            if (owner_of(j, nk) != kp || cinfo.zero) continue;
+            uint8_t* const stg = own + j * 1024;  // slot (0, j): owned, so never parked
 #pragma unroll
-              for (int i = 0; i < 4; ++i) v0[i] += t0[i];
-              if constexpr (MODE == MODE_GATE_UP) {
-                const f32x4_t t1 = red[slot_of(wbase + k, m, j + 4)];
+            for (int m = 0; m < MT; ++m) {
+              if (m > 0 && !t2) continue;
+              const f32x4_t g = ksum(m, j, acc[m][j]), u = ksum(m, j + 4, acc[m][j + 4]);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) v1[i] += t1[i];
-              }
+              for (int i = 0; i < 4; ++i)
+                *(uint16_t*)(stg + m * 512 + (4 * lq + i) * 32 + ln * 2) = f32_to_bf16_bits(gelu_tanh(g[i]) * u[i]);
             }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            const int m = lane >> 5, r = lane & 15, h = (lane >> 4) & 1;
+            const int tau = (m == 0 || t2) ? tile_of(cinfo, m) : -1;
+            if (tau >= 0) {
+              const u32x4_t v = *(const u32x4_t*)(stg + m * 512 + r * 32 + h * 16);
+              *(u32x4_t*)((uint8_t*)p.out + ((size_t)tau * (p.Nout / 64) + blk) * kActBlock + h * (kActBlock / 2) +
+                          (r + 16 * j) * 16) = v;
+            }
+          }
+        } else if constexpr (MODE == MODE_DOWN) {
+          // subtiles [j0, j0 + 8/nk) are this wave's: W = 128 / nk contiguous
+          // columns, staged per row tile as fp32 [16 rows][W] in slots (m, j0 ..)
+          const int per = kNS / nk, j0 = kp * per, W = 16 * per;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int lr = 16 * m + 4 * lq + i;
-              if (lr >= cinfo.rows) continue;
-              if constexpr (MODE == MODE_GATE_UP) {
-                // column 16 j + ln of tile row 4 lq + i -> operand lane 4 lq + i + 16 j, register ln / 8
-                *(uint16_t*)(mblk + (ln >> 3) * (kActBlock / 2) + (4 * lq + i + 16 * j) * 16 + (ln & 7) * 2) =
-                    f32_to_bf16_bits(gelu_tanh(v0[i]) * v1[i]);
-              } else if constexpr (MODE == MODE_DOWN) {
-                const int a = s_dst[c_loc & 1][lr];
-                if (a >= 0) ((float*)p.out)[(size_t)a * p.Nout + col] = cinfo.zero ? 0.0f : v0[i];
-              } else {
-                ((uint16_t*)p.out)[(size_t)(cinfo.r0 + lr) * p.Nout + col] = f32_to_bf16_bits(v0[i]);
+          for (int m = 0; m < MT; ++m) {
+            if (m > 0 && !t2) continue;
+            float* const stg = (float*)(own + (m * kNS + j0) * 1024);
+#pragma unroll
+            for (int j = 0; j < kNS; ++j) {
+              if (owner_of(j, nk) != kp) continue;
+              const f32x4_t v = ksum(m, j, acc[m][j]);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) stg[(4 * lq + i) * W + 16 * (j - j0) + ln] = cinfo.zero ? 0.0f : v[i];
+            }
+          }
+          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+          __builtin_amdgcn_wave_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+          const int cpr = W / 4, rpi = 64 / cpr;  // 16-byte chunks per row, rows per store
+#pragma unroll
+          for (int m = 0; m < MT; ++m) {
+            if (m > 0 && !t2) continue;
+            const float* const stg = (const float*)(own + (m * kNS + j0) * 1024);
+            for (int r0 = 0; r0 < 16; r0 += rpi) {
+              const int r = r0 + lane / cpr, c = lane % cpr;
+              const int a = s_dst[c_loc & 1][16 * m + r];
+              // a block past the last output row (H % 128 == 64) has no columns there
+              if (a >= 0 && blk * BCOLS + 16 * j0 + 4 * c < p.Nout)
+                *(u32x4_t*)((float*)p.out + (size_t)a * p.Nout + blk * BCOLS + 16 * j0 + 4 * c) =
+                    *(const u32x4_t*)(stg + r * W + 4 * c);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int m = 0; m < MT; ++m) {
+            if (m > 0 && !t2) continue;
+#pragma unroll
+            for (int j = 0; j < kNS; ++j) {
+              if (owner_of(j, nk) != kp) continue;
+              const int col = blk * BCOLS + 16 * j + ln;
+              const f32x4_t v = ksum(m, j, acc[m][j]);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int lr = 16 * m + 4 * lq + i;
+                if (lr < cinfo.rows && col < p.Nout)
+                  ((uint16_t*)p.out)[(size_t)(cinfo.r0 + lr) * p.Nout + col] = f32_to_bf16_bits(v[i]);
               }
             }
           }
         }
       }
+#pragma unroll
+      for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int j = 0; j < kNS; ++j) acc[m][j] = zero4();
       __syncthreads();  // partial-sum buffer free again
     };
 

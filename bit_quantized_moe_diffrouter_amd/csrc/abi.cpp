@@ -222,7 +222,7 @@ int qswitch_gate_up_geglu(const uint16_t* x_expert, int32_t T, int32_t H, const 
 size_t qswitch_down_combine_workspace(int32_t T, int32_t k, int32_t H, int32_t deterministic) {
   (void)deterministic;
   if (T <= 0 || k <= 0 || H <= 0) return 0;
-  return (size_t)T * (size_t)k * (size_t)H * sizeof(float);
+  return (size_t)T * (size_t)k * (size_t)H * sizeof(uint16_t);  // the down rows, bf16
 }
 
 int qswitch_down_combine(const void* mid, int32_t T, int32_t k, int32_t I, const qmoe_qweight* down, int32_t H,
@@ -266,7 +266,7 @@ int qswitch_down_combine(const void* mid, int32_t T, int32_t k, int32_t I, const
   a.rows_total = T * k;
   hipError_t err = qmoe::launch_down(a, ncu, stream);
   if (err != hipSuccess) return launched(err, "qswitch_down_combine (down)");
-  return launched(qmoe::launch_combine(static_cast<const float*>(workspace), weights, T, k, H, y, stream),
+  return launched(qmoe::launch_combine(static_cast<const uint16_t*>(workspace), weights, T, k, H, y, stream),
                   "qswitch_down_combine (combine)");
 }
 

@@ -64,6 +64,6 @@ struct SwitchArgs {
 hipError_t launch_gate_up_geglu(SwitchArgs a, int num_cu, hipStream_t stream);
 hipError_t launch_down(SwitchArgs a, int num_cu, hipStream_t stream);
 hipError_t launch_dense(SwitchArgs a, int num_cu, hipStream_t stream);
-hipError_t launch_combine(const float* D, const float* w, int T, int k, int H, uint16_t* y, hipStream_t stream);
+hipError_t launch_combine(const uint16_t* D, const float* w, int T, int k, int H, uint16_t* y, hipStream_t stream);
 
 }  // namespace qmoe

@@ -526,35 +526,36 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
           }
         } else if constexpr (MODE == MODE_DOWN) {
           // subtiles [j0, j0 + 8/nk) are this wave's: W = 128 / nk contiguous
-          // columns, staged per row tile as fp32 [16 rows][W] in slots (m, j0 ..)
+          // columns, staged per row tile as bf16 [16 rows][W] in slots (m, j0 ..)
           const int per = kNS / nk, j0 = kp * per, W = 16 * per;
 #pragma unroll
           for (int m = 0; m < MT; ++m) {
             if (m > 0 && !t2) continue;
-            float* const stg = (float*)(own + (m * kNS + j0) * 1024);
+            uint16_t* const stg = (uint16_t*)(own + (m * kNS + j0) * 1024);
 #pragma unroll
             for (int j = 0; j < kNS; ++j) {
               if (owner_of(j, nk) != kp) continue;
               const f32x4_t v = ksum(m, j, acc[m][j]);
 #pragma unroll
-              for (int i = 0; i < 4; ++i) stg[(4 * lq + i) * W + 16 * (j - j0) + ln] = cinfo.zero ? 0.0f : v[i];
+              for (int i = 0; i < 4; ++i)
+                stg[(4 * lq + i) * W + 16 * (j - j0) + ln] = cinfo.zero ? (uint16_t)0 : f32_to_bf16_bits(v[i]);
             }
           }
           __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
           __builtin_amdgcn_wave_barrier();
           __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-          const int cpr = W / 4, rpi = 64 / cpr;  // 16-byte chunks per row, rows per store
+          const int cpr = W / 8, rpi = 64 / cpr;  // 16-byte chunks per row, rows per store
 #pragma unroll
           for (int m = 0; m < MT; ++m) {
             if (m > 0 && !t2) continue;
-            const float* const stg = (const float*)(own + (m * kNS + j0) * 1024);
+            const uint16_t* const stg = (const uint16_t*)(own + (m * kNS + j0) * 1024);
             for (int r0 = 0; r0 < 16; r0 += rpi) {
               const int r = r0 + lane / cpr, c = lane % cpr;
               const int a = s_dst[c_loc & 1][16 * m + r];
               // a block past the last output row (H % 128 == 64) has no columns there
-              if (a >= 0 && blk * BCOLS + 16 * j0 + 4 * c < p.Nout)
-                *(u32x4_t*)((float*)p.out + (size_t)a * p.Nout + blk * BCOLS + 16 * j0 + 4 * c) =
-                    *(const u32x4_t*)(stg + r * W + 4 * c);
+              if (a >= 0 && blk * BCOLS + 16 * j0 + 8 * c < p.Nout)
+                *(u32x4_t*)((uint16_t*)p.out + (size_t)a * p.Nout + blk * BCOLS + 16 * j0 + 8 * c) =
+                    *(const u32x4_t*)(stg + r * W + 8 * c);
             }
           }
         } else {
@@ -678,27 +679,29 @@ __global__ __launch_bounds__(256) void tile_weight_kernel(const uint32_t* __rest
 // ------------------------------------------------------------ activation tiles
 long long act_tiles_max(long long A, int E) { return (A + 15) / 16 + std::min<long long>(E, A); }
 
-// y[t, h] = bf16( sum_{j<k} w[t, j] * D[t*k + j, h] ), products and sum in fp32, j order.
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ D, const float* __restrict__ w, int T,
-                                                      int k, int H, uint16_t* __restrict__ y) {
-  const int H4 = H / 4;
+// y[t, h] = bf16( sum_{j<k} w[t, j] * D[t*k + j, h] ), D in bf16 (the down
+// rows as the switch linear returns them), products and sum in fp32, j order.
+__global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ D, const float* __restrict__ w,
+                                                      int T, int k, int H, uint16_t* __restrict__ y) {
+  const int H8 = H / 8;
   const long long idx = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (long long)T * H4) return;
-  const int t = (int)(idx / H4), h = (int)(idx - (long long)t * H4) * 4;
-  const float* base = D + (size_t)t * k * H + h;
-  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (idx >= (long long)T * H8) return;
+  const int t = (int)(idx / H8), h = (int)(idx - (long long)t * H8) * 8;
+  const uint16_t* base = D + (size_t)t * k * H + h;
+  float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int j = 0; j < k; ++j) {
-    const float4 v = *(const float4*)(base + (size_t)j * H);
+    const u32x4_t v = *(const u32x4_t*)(base + (size_t)j * H);
     const float wj = w[(size_t)t * k + j];
-    s.x += wj * v.x;
-    s.y += wj * v.y;
-    s.z += wj * v.z;
-    s.w += wj * v.w;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      s[2 * q] += wj * bf16_lo_f32(v[q]);
+      s[2 * q + 1] += wj * bf16_hi_f32(v[q]);
+    }
   }
-  u32x2_t o;
-  o.x = pack_bf16x2(s.x, s.y);
-  o.y = pack_bf16x2(s.z, s.w);
-  *(u32x2_t*)(y + (size_t)t * H + h) = o;
+  u32x4_t o;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(s[2 * q], s[2 * q + 1]);
+  *(u32x4_t*)(y + (size_t)t * H + h) = o;
 }
 
 // ------------------------------------------------------------------ launchers
@@ -754,8 +757,8 @@ hipError_t launch_down(SwitchArgs a, int num_cu, hipStream_t stream) {
 hipError_t launch_dense(SwitchArgs a, int num_cu, hipStream_t stream) {
   return launch_mode<MODE_DENSE>(a, 0, num_cu, stream);
 }
-hipError_t launch_combine(const float* D, const float* w, int T, int k, int H, uint16_t* y, hipStream_t stream) {
-  const long long n = (long long)T * (H / 4);
+hipError_t launch_combine(const uint16_t* D, const float* w, int T, int k, int H, uint16_t* y, hipStream_t stream) {
+  const long long n = (long long)T * (H / 8);
   const long long blocks = (n + 255) / 256;
   hipLaunchKernelGGL(combine_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, D, w, T, k, H, y);
   return hipGetLastError();

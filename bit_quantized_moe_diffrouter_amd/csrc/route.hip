@@ -231,17 +231,18 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const RouteArgs p) {
   const float* pb = p.part + (size_t)t * E + lane;
   const float* pss = p.part + (size_t)p.ksplit * T * E + t;
   const size_t pstride = (size_t)T * E;
-  for (int q0 = 0; q0 < p.ksplit; q0 += 8) {
-    float lv[8][NI], sv[8];
+  constexpr int kBatch = 16;  // partial loads in flight (the k-range split is at most 16 at 256 tokens)
+  for (int q0 = 0; q0 < p.ksplit; q0 += kBatch) {
+    float lv[kBatch][NI], sv[kBatch];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < kBatch; ++q) {
       const bool qok = q0 + q < p.ksplit;
       sv[q] = qok ? pss[(size_t)(q0 + q) * T] : 0.f;
 #pragma unroll
       for (int i = 0; i < NI; ++i) lv[q][i] = (qok && lane + 64 * i < E) ? pb[(q0 + q) * pstride + 64 * i] : 0.f;
     }
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < kBatch; ++q) {
       ss += sv[q];
 #pragma unroll
       for (int i = 0; i < NI; ++i) part[i] += lv[q][i];

@@ -226,7 +226,8 @@ int qswitch_gate_up_geglu(const uint16_t* x_expert, int32_t T, int32_t H,
  * back per token (model.ts page, DiffExperts.forward: down.forward, unsort,
  * (y * weights[..., None]).sum over k):
  *
- *   d_r  = mid[r] . dequant(down)[e]^T                     (fp32)
+ *   d_r  = mid[r] . dequant(down)[e]^T   (fp32 accumulate, rounded to bf16 as
+ *          the pages' quantized matmul returns it)
  *   y[t] = sum_j weights[t, j] * d_{row of assignment t*k+j}   (fp32, j order)
  *   y is stored bf16 (round to nearest even).
  *
@@ -239,7 +240,8 @@ int qswitch_gate_up_geglu(const uint16_t* x_expert, int32_t T, int32_t H,
  *                   present (dropped indices) gets the sum of the rest
  *   workspace       at least qswitch_down_combine_workspace(T, k, H, det)
  *                   bytes of device scratch
- *   deterministic   1: per-assignment rows then a fixed-order sum (bitwise
+ *   deterministic   1: per-assignment bf16 rows d_r in the workspace, then a
+ *                   fixed-order sum (bitwise
  *                   reproducible);  0: same path today (reserved for an
  *                   atomic scatter-sum)
  * ---------------------------------------------------------------------- */

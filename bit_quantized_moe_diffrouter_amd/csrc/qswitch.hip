@@ -222,9 +222,12 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
     it.zero = __builtin_amdgcn_readfirstlane(it.zero);
     return it;
   };
+  // K parts per item: kWaves / NBI, fewer only for a contraction of fewer
+  // groups.  The launcher takes NBI = 1 only when G >= 12, so nk is 1, 2 or 4
+  // and the divisions by it below are shifts.
   auto role_of = [&](const Item& it) __attribute__((always_inline)) {
     Role r;
-    r.nk = min(kWaves / NBI, G);  // no K part without a group
+    r.nk = min(kWaves / NBI, G);
     if (wave < r.nk * NBI) {
       r.kp = wave % r.nk;
       r.blk = it.tile * NBI + wave / r.nk;
@@ -266,7 +269,7 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
   // gate j and up j + 4 together; the other modes give each K part a run of
   // kNS / nk contiguous subtiles
   auto owner_of = [&](int j, int nk) __attribute__((always_inline)) {
-    return (MODE == MODE_GATE_UP) ? (j & 3) % nk : j / (kNS / nk);
+    return (MODE == MODE_GATE_UP) ? (j & 3) & (nk - 1) : (j * nk) >> 3;  // nk in {1, 2, 4}
   };
 
   // Slots and accumulators hold two row tiles; a one-tile chunk reads tile 0
@@ -527,7 +530,8 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
         } else if constexpr (MODE == MODE_DOWN) {
           // subtiles [j0, j0 + 8/nk) are this wave's: W = 128 / nk contiguous
           // columns, staged per row tile as bf16 [16 rows][W] in slots (m, j0 ..)
-          const int per = kNS / nk, j0 = kp * per, W = 16 * per;
+          const int lgnk = nk >> 1;  // log2 nk for nk in {1, 2}
+          const int per = kNS >> lgnk, j0 = kp * per, W = 16 * per;
 #pragma unroll
           for (int m = 0; m < MT; ++m) {
             if (m > 0 && !t2) continue;
@@ -544,13 +548,13 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
           __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
           __builtin_amdgcn_wave_barrier();
           __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-          const int cpr = W / 8, rpi = 64 / cpr;  // 16-byte chunks per row, rows per store
+          const int lgcpr = 4 - lgnk, rpi = 64 >> lgcpr;  // 16-byte chunks per row (W / 8), rows per store
 #pragma unroll
           for (int m = 0; m < MT; ++m) {
             if (m > 0 && !t2) continue;
             const uint16_t* const stg = (const uint16_t*)(own + (m * kNS + j0) * 1024);
             for (int r0 = 0; r0 < 16; r0 += rpi) {
-              const int r = r0 + lane / cpr, c = lane % cpr;
+              const int r = r0 + (lane >> lgcpr), c = lane & ((1 << lgcpr) - 1);
               const int a = s_dst[c_loc & 1][16 * m + r];
               // a block past the last output row (H % 128 == 64) has no columns there
               if (a >= 0 && blk * BCOLS + 16 * j0 + 8 * c < p.Nout)

@@ -35,13 +35,16 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float v) {
   return __builtin_bit_cast(uint16_t, (__bf16)v);
 }
 
-// One packed word (codes n0..n7) -> four dwords of bf16 pairs holding 128+q
-// exactly: 0x4300 | q is the bf16 pattern of 128 + q for q < 128.  The pairs
-// come out as (n0,n4) (n1,n5) (n2,n6) (n3,n7): the activation operand is
-// stored in the same order (see permute_pairs), so the contraction is over
-// the same set of k.  gfx9 VOP3 encodings take no literal, so the mask rides
-// in a scalar register and the exponent pattern in a vector register, making
-// each pair one v_and_or_b32 (seven ops per word).
+// Two packed words (codes n0..n7 each) -> four dwords of bf16 pairs per word
+// holding 128+q exactly: 0x4300 | q is the bf16 pattern of 128 + q for
+// q < 128.  The pairs come out as (n0,n4) (n1,n5) (n2,n6) (n3,n7): the
+// activation operand is stored in the same order (see permute_pairs), or the
+// codes are pre-placed so that this order is the natural one.  gfx9 VOP3
+// encodings take no literal, so the mask rides in a scalar register and the
+// exponent pattern in a vector register, making each pair one v_and_or_b32;
+// one 64-bit shift moves the nibbles of both words at once (the bits of the
+// second word that enter the first word's top nibble fall outside the mask),
+// so two words take 3 shifts + 8 v_and_or_b32.
 struct OffsetCodeConsts {
   uint32_t mask;  // 0x000F000F, uniform (SGPR)
   uint32_t expo;  // 0x43004300, in a VGPR
@@ -59,17 +62,23 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t smask, uint32_t 
   asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(smask), "v"(vor));
   return r;
 }
-__device__ __forceinline__ u32x4_t unpack_offset_codes(uint32_t w, const OffsetCodeConsts& k) {
-  u32x4_t r;
-  r.x = and_or(w, k.mask, k.expo);
-  r.y = and_or(w >> 4, k.mask, k.expo);
-  r.z = and_or(w >> 8, k.mask, k.expo);
-  r.w = and_or(w >> 12, k.mask, k.expo);
-  return r;
+__device__ __forceinline__ void unpack_offset_code_pair(uint32_t w0, uint32_t w1, const OffsetCodeConsts& k,
+                                                        u32x4_t& b0, u32x4_t& b1) {
+  const u32x2_t pr = {w0, w1};
+  b0[0] = and_or(w0, k.mask, k.expo);
+  b1[0] = and_or(w1, k.mask, k.expo);
+#pragma unroll
+  for (int p = 1; p < 4; ++p) {
+    u32x2_t sh;
+    asm("v_lshrrev_b64 %0, %1, %2" : "=v"(sh) : "i"(4 * p), "v"(pr));
+    b0[p] = and_or(sh.x, k.mask, k.expo);
+    b1[p] = and_or(sh.y, k.mask, k.expo);
+  }
 }
 
-// Same as unpack_offset_codes but with the smallest offset a bf16 bit trick
-// allows for unit steps: 0x4180 | (q << 3) is the bf16 pattern of 16 + q.
+// One word as unpack_offset_code_pair unpacks it, but with the smallest offset
+// a bf16 bit trick allows for unit steps: 0x4180 | (q << 3) is the bf16
+// pattern of 16 + q.
 // The smaller offset keeps the MFMA partial sums small, so the fp32 rounding
 // left after the affine correction is about 8x smaller (one more op per word).
 __device__ __forceinline__ u32x4_t unpack_offset16_codes(uint32_t w) {
@@ -83,7 +92,7 @@ __device__ __forceinline__ u32x4_t unpack_offset16_codes(uint32_t w) {
 }
 
 // Eight consecutive bf16 (x0..x7 as pairs (x0,x1)(x2,x3)(x4,x5)(x6,x7)) ->
-// the order (x0,x4)(x1,x5)(x2,x6)(x3,x7) that matches unpack_offset_codes.
+// the order (x0,x4)(x1,x5)(x2,x6)(x3,x7) that matches unpack_offset_code_pair.
 __device__ __forceinline__ u32x4_t permute_pairs(u32x4_t v) {
   u32x4_t o;
   o.x = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);

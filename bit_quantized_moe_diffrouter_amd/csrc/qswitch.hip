@@ -36,9 +36,11 @@
 //
 // Arithmetic per group: P = sum_k x_k (128 + q_k) and, against a ones operand,
 // X = sum_k x_k come from the MFMA; the group's affine is applied in fp32:
-//     sum_k x_k (s q_k + b) = s P + (b - 128 s) X.
-// The products are exact and the dequantized weight is never rounded; the
-// only roundings are the fp32 accumulation and the output conversion.
+//     sum_k x_k (s q_k + b) = s P + (b - 128 s) X,
+// s P with one FMA per output element, the bias terms of 4 groups at a time
+// with one fp32 MFMA (a contraction over the groups).  The products are exact
+// and the dequantized weight is never rounded; the only roundings are the
+// fp32 accumulation and the output conversion.
 #include "common.h"
 #include "launch.h"
 
@@ -397,6 +399,16 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
     for (int m = 0; m < MT; ++m)
 #pragma unroll
       for (int j = 0; j < kNS; ++j) acc[m][j] = zero4();
+    // The bias term of the affine, sum_g (b - 128 s)_g X_g, is a contraction
+    // over the groups; blocks of 4 groups go through one fp32 MFMA
+    // (v_mfma_f32_16x16x4_f32: lane (ln, lq) gives X of row ln and the
+    // correction of column ln for the block's group lq).
+    float xsel[MT];    // X of row ln, tile m, of the block's group lq (0 where not yet set)
+    float ccsel[kNS];  // b - 128 s of column ln, subtile j, of the block's group lq
+#pragma unroll
+    for (int m = 0; m < MT; ++m) xsel[m] = 0.f;
+#pragma unroll
+    for (int j = 0; j < kNS; ++j) ccsel[j] = 0.f;
 
     int c_loc = 0;  // index of the compute cursor's item in this workgroup's sequence
     Item cinfo = decode(item_of(0));
@@ -404,8 +416,9 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
     int cg = crole.gk0;
 
     // one group of the current item from slot `sl`, for the MT row tiles; the
-    // weights are unpacked once for all of them
-    auto compute = [&](Slot<MT>& sl) __attribute__((always_inline)) {
+    // weights are unpacked once for all of them.  kq: the group's place in its
+    // block of 4.
+    auto compute = [&](Slot<MT>& sl, int kq) __attribute__((always_inline)) {
       const bool t2 = cinfo.rows > 16;  // uniform: a second row tile to compute
       u32x4_t a[MT][2];  // operands: lane (ln, lq) holds row ln, columns 16 lq .. 16 lq + 15
       if constexpr (MODE == MODE_DOWN) {
@@ -440,29 +453,44 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       }
-      f32x4_t X[MT];
+      const bool mine = lq == kq;  // this lane group holds the group's place in the block
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
         if (m > 0 && !t2) continue;
-        X[m] = mfma16x16x32(a[m][0], ones, zero4());
-        X[m] = mfma16x16x32(a[m][1], ones, X[m]);
+        // ones as the A operand: every row of the result holds the row sums, so
+        // lane (ln, lq) gets X of activation row ln
+        f32x4_t X = mfma16x16x32(ones, a[m][0], zero4());
+        X = mfma16x16x32(ones, a[m][1], X);
+        xsel[m] = mine ? X[0] : xsel[m];
       }
 #pragma unroll
       for (int j = 0; j < kNS; ++j) {
         const uint32_t sb = sl.s[j >> 2][j & 3];
         const float sc = __uint_as_float(sb << 16);
         const float cc = __uint_as_float(sb & 0xffff0000u) - 128.0f * sc;
-        const u32x4_t b0 = unpack_offset_codes(sl.w[j >> 1][(j & 1) * 2], kc);
-        const u32x4_t b1 = unpack_offset_codes(sl.w[j >> 1][(j & 1) * 2 + 1], kc);
+        ccsel[j] = mine ? cc : ccsel[j];
+        u32x4_t b0, b1;
+        unpack_offset_code_pair(sl.w[j >> 1][(j & 1) * 2], sl.w[j >> 1][(j & 1) * 2 + 1], kc, b0, b1);
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
           if (m > 0 && !t2) continue;
           f32x4_t P = mfma16x16x32(a[m][0], b0, zero4());
           P = mfma16x16x32(a[m][1], b1, P);
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            acc[m][j][i] = __builtin_fmaf(cc, X[m][i], __builtin_fmaf(sc, P[i], acc[m][j][i]));
+          for (int i = 0; i < 4; ++i) acc[m][j][i] = __builtin_fmaf(sc, P[i], acc[m][j][i]);
         }
+      }
+    };
+    // adds the bias terms of the groups collected since the last call
+    auto flush_bias = [&]() __attribute__((always_inline)) {
+      const bool t2 = cinfo.rows > 16;
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        if (m > 0 && !t2) continue;
+#pragma unroll
+        for (int j = 0; j < kNS; ++j)
+          acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(xsel[m], ccsel[j], acc[m][j], 0, 0, 0);
+        xsel[m] = 0.f;
       }
     };
 
@@ -596,7 +624,11 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
     auto step = [&](auto d_tag) __attribute__((always_inline)) {
       constexpr int d = decltype(d_tag)::value;
       fence_slot(ring[d]);
-      if (!done && !cinfo.zero && crole.blk < p.nblk) compute(ring[d]);
+      if (!done && !cinfo.zero && crole.blk < p.nblk) {
+        const int kq = (cg - crole.gk0) & 3;
+        compute(ring[d], kq);
+        if (kq == 3 || cg + 1 == crole.gk1) flush_bias();
+      }
       issue(ring[d]);
       asm volatile("" ::: "memory");  // keeps the slots' loads in ring order
       advance_load();

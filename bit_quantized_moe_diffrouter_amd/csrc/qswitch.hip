@@ -24,16 +24,17 @@
 // 64 columns already in operand order, written by the gate_up epilogue): two
 // coalesced 1 KB loads per tile and group.
 //
-// Work items.  An item is (expert e, chunk of up to 32 sorted rows of e, tile
-// of NW weight blocks).  A persistent grid walks the items, derived on the
-// device from expert_offsets (no host synchronisation).  A chunk of at most 16
-// rows is one 16-row MFMA tile, a larger one two; a wave computes every tile
-// of its chunk from one unpacking of the weights (a one-tile chunk skips the
-// second tile's arithmetic).  The 4 waves of a workgroup split the contraction
-// KW ways and the blocks NW ways (KW*NW = 4); each wave streams its operands
-// straight into registers through a ring of slots that runs on across items.
-// The K-split partial sums meet once per item in LDS, in a fixed order.
-//
+// Work items.  An item is (expert e, chunk of up to 32 sorted rows of e, one
+// 128-row weight block).  A persistent grid derives the items on the device
+// from expert_offsets (no host synchronisation).  A chunk of at most 16 rows
+// is one 16-row MFMA tile, a larger one two; a wave computes every tile of its
+// chunk from one unpacking of the weights (a one-tile chunk skips the second
+// tile's arithmetic).  Each wave (or, for the long gate_up contraction, each
+// pair of waves splitting it in two) walks its own items and writes their
+// outputs itself, so after the prologue no workgroup barrier is needed; a wave
+// streams its operands straight into registers through a ring of slots that
+// runs on across its items.
+
 // Arithmetic per group: P = sum_k x_k (128 + q_k) and, against a ones operand,
 // X = sum_k x_k come from the MFMA; the group's affine is applied in fp32:
 //     sum_k x_k (s q_k + b) = s P + (b - 128 s) X,
@@ -56,25 +57,15 @@ constexpr int kBM = 32;            // sorted rows per chunk (at most two 16-row 
 constexpr int kMaxBuckets = 257;   // experts (<= 256) + the dropped bucket of the down pass
 constexpr int kNS = 8;             // 16-row subtiles per tiled block
 constexpr int kXcds = 8;           // accelerator dies; workgroup b runs on die b % 8
-constexpr int kRingMax = 2;
-constexpr int kMaxWgItems = 64;    // gate_up: items of one workgroup (token table in LDS)        // ring slots: two-tile slots fill the register file at 2 waves/SIMD
+constexpr int kMT = 2;             // row tiles held per slot and accumulator set
+constexpr int kWaveLds = kMT * 16 * 128 * 2;  // LDS per wave: two 16-row tiles of 128 bf16 columns
 
 struct Item {
   int e;     // expert whose weights are used (0 for the dropped bucket)
   int r0;    // first sorted row
   int rows;  // rows of the chunk, 1..32
-  int tile;  // block tile
+  int blk;   // weight block (within the expert)
   int zero;  // down pass, dropped bucket: the rows are written as zeros
-};
-
-// What one wave does for one item: the 4 waves split (K part, block), K
-// 4 / NBI ways; each wave computes all row tiles of the chunk (one or two
-// 16-row tiles) against a whole 128-row block (8 subtiles).
-struct Role {
-  int nk;   // K parts of the item
-  int kp;   // this wave's K part
-  int blk;  // weight block (within the expert)
-  int gk0, gk1;  // groups [gk0, gk1) of the contraction
 };
 
 // One ring slot: operands of one quantization group for one wave and MT row tiles.
@@ -96,6 +87,13 @@ __device__ __forceinline__ void fence_slot(Slot<MT>& sl) {
   for (int m = 0; m < MT; ++m) asm volatile("" : "+v"(sl.a[m][0]), "+v"(sl.a[m][1])::"memory");
 }
 
+// Orders a wave's own LDS stores before its later loads.
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Calls f(0), f(1), ... with compile-time indices.
 template <class F, int... I>
 __device__ __forceinline__ void run_steps(F& f, std::integer_sequence<int, I...>) {
@@ -104,19 +102,32 @@ __device__ __forceinline__ void run_steps(F& f, std::integer_sequence<int, I...>
 
 }  // namespace
 
-template <int MODE, int NBI, int D>
+// Work items and workers.  An item is (chunk of up to 32 sorted rows of one
+// bucket, one 128-row weight block) over the whole contraction.  A worker is
+// one wave (KS = 1) or a pair of waves of one workgroup that split the
+// contraction in two (KS = 2); every worker walks its own items, so after the
+// prologue no wave waits for another except a pair's partner.  A wave streams
+// its part of the block's units (contiguous in HBM) through a register ring
+// that runs on across its items, computes every row tile of the chunk from one
+// unpacking of the weights, and at the item's end writes the outputs itself
+// (KS = 2: the second wave hands its partial sums to the first through LDS).
+template <int MODE, int KS, int D>
 __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
-  constexpr int BCOLS = (MODE == MODE_GATE_UP) ? 64 : 128;  // output columns per block
-
-  extern __shared__ __attribute__((aligned(16))) uint8_t qmm_lds[];  // partial sums [wave][m][kNS][64] f32x4
+  static_assert(KS == 1 || (KS == 2 && MODE == MODE_GATE_UP), "the K-split pair is for the gate_up pass");
+  constexpr int MT = kMT;
+  extern __shared__ __attribute__((aligned(16))) uint8_t qmm_lds[];  // kWaveLds bytes per wave
   __shared__ int s_cum2[kMaxBuckets + 1];  // prefix per bucket of its two-tile chunks
   __shared__ int s_cum1[kMaxBuckets + 1];  // prefix per bucket of its one-tile chunk (0 or 1)
   __shared__ int s_lo[kMaxBuckets];       // clamped segment [lo, hi) of each bucket
   __shared__ int s_hi[kMaxBuckets];
   __shared__ int s_tcum[kMaxBuckets + 1];  // switch modes: first activation tile of each expert
   __shared__ int s_scan[kWaves];
-  __shared__ int s_dst[2][kBM];           // down pass: assignment id of each chunk row
-  __shared__ int s_tok[(MODE == MODE_GATE_UP) ? kMaxWgItems : 1][kBM];  // gate_up: token of each chunk row
+  // down pass: assignment id of each chunk row, per wave and item (mod 4).  The
+  // load cursor writes an item's entry when it enters the item; with a ring of
+  // D <= min(2, G) slots it enters item c + 2 at the earliest during item c's
+  // last step (when G <= D), never item c + 4 before item c is finished.
+  __shared__ int s_dst[kWaves][4][kBM];
+  __shared__ int s_flag[kWaves / 2][2];    // KS = 2: items of each pair produced by its second wave, consumed by its first
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar branches below)
@@ -124,11 +135,10 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
   const int K = p.K, G = K / kGroup;
   const int A = p.rows_total;
 
-  // ---- work items.  A chunk is 32 sorted rows of one bucket (the last chunk of
-  // a bucket may be shorter); chunks of more than 16 rows cost two tiles, the
-  // others one.  Items are ranked two-tile chunks first, then one-tile ones
-  // (tile-minor), and workgroup b takes ranks b, 2 grid - 1 - b, 2 grid + b, ...
-  // (a boustrophedon over the cost-sorted list), which evens out the work.
+  // ---- chunks.  A chunk is 32 sorted rows of one bucket (the last chunk of a
+  // bucket may be shorter); chunks of more than 16 rows cost two tiles, the
+  // others one.  Items are ranked two-tile chunks first, then one-tile ones,
+  // blocks minor.
   const int nb = (MODE == MODE_DOWN) ? p.E + 1 : p.E;
   int total2, total1;
   if constexpr (MODE == MODE_DENSE) {
@@ -167,30 +177,38 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
       s_cum2[0] = 0;
       s_cum1[0] = 0;
     }
-    __syncthreads();
+    if (tid < kWaves) (&s_flag[0][0])[tid] = 0;
+    __syncthreads();  // the last workgroup barrier: from here on every worker runs on its own
   }
   total2 = __builtin_amdgcn_readfirstlane(total2);
   total1 = __builtin_amdgcn_readfirstlane(total1);
-  // Items are ranked two-tile chunks first (the costlier ones), then one-tile
-  // chunks; the workgroup at position q takes ranks q, 2 grid - 1 - q,
-  // 2 grid + q, ... (a boustrophedon over the cost-sorted list, which evens out
-  // the work).  Workgroups are dealt to the 8 XCDs round-robin; positions are
-  // numbered XCD by XCD, so consecutive ranks -- the column tiles of one chunk,
-  // which read the same activation tiles -- run on one XCD and share its L2.
-  const int total_items = __builtin_amdgcn_readfirstlane((total2 + total1) * p.ntiles);
+
+  // ---- worker slots.  The grid's workers form grid * 4 / KS slots; the worker
+  // of slot s takes ranks s, 2S - 1 - s, 2S + s, ... (S slots: a boustrophedon over the
+  // cost-sorted list).  Slot s sits at workgroup position s % grid; positions
+  // are numbered XCD by XCD (workgroup b runs on die b % 8), so consecutive
+  // ranks -- the blocks of one chunk, which read the same activations -- run on
+  // one XCD and share its L2.  Within a workgroup the slot's role s / grid is
+  // rotated by the position, so the costly first ranks spread over the SIMDs.
+  const int total_items = __builtin_amdgcn_readfirstlane((total2 + total1) * p.nblk);
   const int grid = (int)gridDim.x, b = (int)blockIdx.x;
-  const int gb = (grid % kXcds == 0) ? (b % kXcds) * (grid / kXcds) + b / kXcds : b;
-  auto item_of = [&](int j) __attribute__((always_inline)) {  // rank of this workgroup's j-th item
-    return j * grid + ((j & 1) ? grid - 1 - gb : gb);
+  const int pos = (grid % kXcds == 0) ? (b % kXcds) * (grid / kXcds) + b / kXcds : b;
+  constexpr int kWorkers = kWaves / KS;     // workers per workgroup
+  const int worker = wave / KS, kp = wave % KS;  // kp: this wave's half of the contraction (KS = 2)
+  const int gk0 = kp * G / KS, gk1 = (kp + 1) * G / KS;  // groups [gk0, gk1) of this wave
+  const int nslots = grid * kWorkers;
+  const int slot = ((worker + pos) & (kWorkers - 1)) * grid + pos;
+  auto item_of = [&](int j) __attribute__((always_inline)) {  // rank of this wave's j-th item
+    return j * nslots + ((j & 1) ? nslots - 1 - slot : slot);
   };
   auto has_item = [&](int j) __attribute__((always_inline)) { return item_of(j) < total_items; };
-  if (!has_item(0)) return;  // uniform: no barrier follows for this workgroup
+  if (!has_item(0)) return;  // no workgroup barrier follows; a pair leaves together
 
-  // item rank -> (expert, rows, tile); wave-uniform
-  auto decode_raw = [&](int item) __attribute__((always_inline)) {
+  // item rank -> (expert, rows, block); wave-uniform
+  auto decode = [&](int item) __attribute__((always_inline)) {
     Item it;
-    const int chunk = item / p.ntiles;
-    it.tile = item - chunk * p.ntiles;
+    const int chunk = item / p.nblk;
+    it.blk = item - chunk * p.nblk;
     if constexpr (MODE == MODE_DENSE) {
       it.e = 0;
       it.zero = 0;
@@ -213,49 +231,13 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
       it.zero = (MODE == MODE_DOWN) && (e >= p.E);
       it.e = it.zero ? 0 : e;
     }
-    return it;
-  };
-  auto decode = [&](int item) __attribute__((always_inline)) {
-    Item it = decode_raw(item);
     it.e = __builtin_amdgcn_readfirstlane(it.e);
     it.r0 = __builtin_amdgcn_readfirstlane(it.r0);
     it.rows = __builtin_amdgcn_readfirstlane(it.rows);
-    it.tile = __builtin_amdgcn_readfirstlane(it.tile);
+    it.blk = __builtin_amdgcn_readfirstlane(it.blk);
     it.zero = __builtin_amdgcn_readfirstlane(it.zero);
     return it;
   };
-  // K parts per item: kWaves / NBI, fewer only for a contraction of fewer
-  // groups.  The launcher takes NBI = 1 only when G >= 12, so nk is 1, 2 or 4
-  // and the divisions by it below are shifts.
-  auto role_of = [&](const Item& it) __attribute__((always_inline)) {
-    Role r;
-    r.nk = min(kWaves / NBI, G);
-    if (wave < r.nk * NBI) {
-      r.kp = wave % r.nk;
-      r.blk = it.tile * NBI + wave / r.nk;
-      r.gk0 = r.kp * G / r.nk;
-      r.gk1 = (r.kp + 1) * G / r.nk;
-    } else {  // spare wave (contraction shorter than the K split): streams, never stores
-      r.kp = 0;
-      r.blk = 0x7fffffff;
-      r.gk0 = 0;
-      r.gk1 = G;
-    }
-    return r;
-  };
-  // gate_up: the token of every row of this workgroup's items, once (the
-  // launcher keeps a workgroup's items within kMaxWgItems)
-  if constexpr (MODE == MODE_GATE_UP) {
-    int nj = 0;
-    while (nj < kMaxWgItems && has_item(nj)) ++nj;
-    for (int t = tid; t < nj * kBM; t += kThreads) {
-      const Item it = decode_raw(item_of(t / kBM));
-      const int a = p.assign[it.r0 + min(t % kBM, it.rows - 1)];
-      s_tok[t / kBM][t % kBM] = (a >= 0 && a < A) ? a / p.ktop : 0;
-    }
-    __syncthreads();
-  }
-
   // activation tile of row tile m of an item (switch modes); a tile past the
   // buffers (inconsistent offsets) reads tile 0 and is never stored
   auto tile_of = [&](const Item& it, int m) __attribute__((always_inline)) {
@@ -267,391 +249,359 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
       return (tau >= 0 && tau < p.max_tiles) ? tau : -1;
     }
   };
-  // owner (K part) of subtile j among the waves of one block: gate_up keeps
-  // gate j and up j + 4 together; the other modes give each K part a run of
-  // kNS / nk contiguous subtiles
-  auto owner_of = [&](int j, int nk) __attribute__((always_inline)) {
-    return (MODE == MODE_GATE_UP) ? (j & 3) & (nk - 1) : (j * nk) >> 3;  // nk in {1, 2, 4}
+
+  // ---- load cursor: the item and group whose operands are issued next
+  const uint8_t* const wbytes = (const uint8_t*)p.w;
+  const uint8_t* const abytes = (const uint8_t*)p.a;
+  const uint32_t arow = K * 2;                     // gate_up, dense: bytes per activation row
+  const uint32_t c_off = lane * 16;                // code bytes of this lane in a unit
+  const uint32_t s_off = 4096 + ln * 16;           // scale bytes of this lane in a unit
+  // chunk row of this lane's activation load (m, h): row 8 h + lane / 8 of tile
+  // m; a one-tile chunk reads its tile twice
+  auto row_of = [&](const Item& it, int m, int h) __attribute__((always_inline)) {
+    const int mm = (it.rows > 16) ? m : 0;
+    return min(16 * mm + 8 * h + (lane >> 3), it.rows - 1);
   };
-
-  // Slots and accumulators hold two row tiles; a one-tile chunk reads tile 0
-  // twice and skips the second tile's arithmetic.
-  auto body = [&](auto mt_tag) __attribute__((always_inline)) {
-    constexpr int MT = decltype(mt_tag)::value;
-    constexpr int DR = (D > kRingMax) ? kRingMax : D;  // ring depth
-    // ---- load cursor (per wave): the item and group whose operands are issued next
-    const uint8_t* const wbytes = (const uint8_t*)p.w;
-    const uint8_t* const abytes = (const uint8_t*)p.a;
-    const uint32_t arow = K * 2;                     // gate_up, dense: bytes per activation row
-    const uint32_t c_off = lane * 16;                // code bytes of this lane in a unit
-    const uint32_t s_off = 4096 + ln * 16;           // scale bytes of this lane in a unit
-    Item linfo = decode(item_of(0));
-    Role lrole = role_of(linfo);
-    int lg = lrole.gk0;
-    int n_j = 1;  // index (in this workgroup's sequence) of the item after the load cursor's
-    bool n_valid = has_item(n_j);
-    Item ninfo = n_valid ? decode(item_of(n_j)) : linfo;
-    const uint8_t* l_wbase;  // unit (expert, block, group 0) of this wave
-    // per row tile m and half h: gate_up, dense: offset of the lane's 16 bytes
-    // (row 8 h + lane / 8 of the tile, columns 8 (lane % 8) .. + 7 of a group)
-    // in the activation rows; down: of the lane's operand words in the tile's
-    // group-0 block (h = 1 unused)
-    uint32_t l_aoff[MT][2];
-    int l_loc = 0;           // items the load cursor has entered (s_dst parity)
-    // Down pass: assignment id of chunk row lane % 32 of the item after the load
-    // cursor's, loaded at the end of every step (so the item switch uses a value
-    // loaded at least a step before).
-    int pf_raw = 0;
-
-    auto set_weight_base = [&](const Item& it, const Role& r) __attribute__((always_inline)) {
-      const int blk = min(r.blk, p.nblk - 1);  // past the last block: any valid one (never stored)
-      l_wbase = wbytes + ((size_t)it.e * p.nblk + blk) * (size_t)G * kTiledUnit;
-    };
-    auto raw_assign = [&](const Item& it) __attribute__((always_inline)) {
-      if constexpr (MODE == MODE_DOWN) {
-        return p.assign[min(it.r0 + (lane & 31), A - 1)];
-      } else {
-        return 0;
-      }
-    };
-    auto put_dst = [&](int loc, const Item& it, int raw) __attribute__((always_inline)) {  // down only
-      const int lr = lane & 31;
-      s_dst[loc & 1][lr] = (lr < it.rows && raw >= 0 && raw < A) ? raw : -1;
-    };
-    auto set_act_offset = [&](const Item& it, int j) __attribute__((always_inline)) {
-#pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        const int mm = (it.rows > 16) ? m : 0;  // a one-tile chunk reads its tile twice
-        if constexpr (MODE == MODE_DOWN) {
-          const int tau = max(tile_of(it, mm), 0);
-          l_aoff[m][0] = (uint32_t)tau * (uint32_t)(G * kActBlock) + lane * 16;
-          l_aoff[m][1] = 0;
-        } else {
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int rr = min(16 * mm + 8 * h + (lane >> 3), it.rows - 1);  // row of the chunk
-            int src;
-            if constexpr (MODE == MODE_GATE_UP) src = s_tok[min(j, kMaxWgItems - 1)][rr];
-            else src = it.r0 + rr;
-            l_aoff[m][h] = (uint32_t)src * arow + (lane & 7) * 16;
-          }
-        }
-      }
-    };
-    {
-      const int raw0 = raw_assign(linfo);
-      pf_raw = raw_assign(ninfo);
-      set_weight_base(linfo, lrole);
-      set_act_offset(linfo, 0);
-      if constexpr (MODE == MODE_DOWN) put_dst(0, linfo, raw0);
-    }
-
-    auto issue = [&](Slot<MT>& sl) __attribute__((always_inline)) {
-      const uint8_t* u = l_wbase + (size_t)lg * kTiledUnit;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sl.w[i] = *(const u32x4_t*)(u + c_off + i * 1024);
-#pragma unroll
-      for (int h = 0; h < 2; ++h) sl.s[h] = *(const u32x4_t*)(u + s_off + h * 256);
-#pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        if constexpr (MODE == MODE_DOWN) {  // one coalesced kilobyte per operand register
-          const uint8_t* ab = abytes + l_aoff[m][0] + (uint32_t)lg * kActBlock;
-          sl.a[m][0] = *(const u32x4_t*)(ab);
-          sl.a[m][1] = *(const u32x4_t*)(ab + kActBlock / 2);
-        } else {  // 8 rows x 128 bytes per load; compute puts them in operand order
-#pragma unroll
-          for (int h = 0; h < 2; ++h) sl.a[m][h] = *(const u32x4_t*)(abytes + l_aoff[m][h] + (uint32_t)lg * 128);
-        }
-      }
-    };
-    auto advance_load = [&]() __attribute__((always_inline)) {
-      if (++lg < lrole.gk1) return;
-      if (!n_valid) {  // past the last item: keep re-reading the last item's groups (never used)
-        lg = lrole.gk0;
-        return;
-      }
-      linfo = ninfo;
-      lrole = role_of(linfo);
-      lg = lrole.gk0;
-      set_weight_base(linfo, lrole);
-      set_act_offset(linfo, n_j);
-      ++l_loc;
-      if constexpr (MODE == MODE_DOWN) put_dst(l_loc, linfo, pf_raw);
-      ++n_j;
-      n_valid = has_item(n_j);
-      if (n_valid) ninfo = decode(item_of(n_j));
-    };
-
-    Slot<MT> ring[DR];
-#pragma unroll
-    for (int d = 0; d < DR; ++d) {
-      issue(ring[d]);
-      asm volatile("" ::: "memory");  // keeps the slots' loads in ring order
-      advance_load();
-      if constexpr (MODE == MODE_DOWN) pf_raw = raw_assign(ninfo);
-    }
-
-    const u32x4_t ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
-    const OffsetCodeConsts kc = offset_code_consts();
-
-    f32x4_t acc[MT][kNS];
+  // Assignment ids an item needs, loaded when the load cursor enters the item
+  // before it: gate_up, of this lane's four activation rows; down, of chunk
+  // row lane % 32.
+  auto load_ids = [&](const Item& it, int (&ids)[MT][2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
-      for (int j = 0; j < kNS; ++j) acc[m][j] = zero4();
-    // The bias term of the affine, sum_g (b - 128 s)_g X_g, is a contraction
-    // over the groups; blocks of 4 groups go through one fp32 MFMA
-    // (v_mfma_f32_16x16x4_f32: lane (ln, lq) gives X of row ln and the
-    // correction of column ln for the block's group lq).
-    float xsel[MT];    // X of row ln, tile m, of the block's group lq (0 where not yet set)
-    float ccsel[kNS];  // b - 128 s of column ln, subtile j, of the block's group lq
-#pragma unroll
-    for (int m = 0; m < MT; ++m) xsel[m] = 0.f;
-#pragma unroll
-    for (int j = 0; j < kNS; ++j) ccsel[j] = 0.f;
-
-    int c_loc = 0;  // index of the compute cursor's item in this workgroup's sequence
-    Item cinfo = decode(item_of(0));
-    Role crole = role_of(cinfo);
-    int cg = crole.gk0;
-
-    // one group of the current item from slot `sl`, for the MT row tiles; the
-    // weights are unpacked once for all of them.  kq: the group's place in its
-    // block of 4.
-    auto compute = [&](Slot<MT>& sl, int kq) __attribute__((always_inline)) {
-      const bool t2 = cinfo.rows > 16;  // uniform: a second row tile to compute
-      u32x4_t a[MT][2];  // operands: lane (ln, lq) holds row ln, columns 16 lq .. 16 lq + 15
-      if constexpr (MODE == MODE_DOWN) {
-#pragma unroll
-        for (int m = 0; m < MT; ++m) a[m][0] = sl.a[m][0], a[m][1] = sl.a[m][1];
-      } else {
-        // through this wave's own slice of the partial-sum buffer (free while
-        // steps run): row r's 16-byte chunk c sits at slot c ^ swz(r), so both
-        // the 8-lanes-per-row writes and the operand reads are conflict free
-        uint8_t* const scr = qmm_lds + wave * (2 * kNS * 64 * 16);
-        auto swz = [](int r) __attribute__((always_inline)) { return ((r & 1) << 2) | ((r >> 1) & 3); };
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-          if (m > 0 && !t2) continue;
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const int r = 8 * h + (lane >> 3);
-            *(u32x4_t*)(scr + m * 2048 + r * 128 + ((lane & 7) ^ swz(r)) * 16) = sl.a[m][h];
-          }
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-          if (m > 0 && !t2) continue;
-#pragma unroll
-          for (int h = 0; h < 2; ++h)
-            a[m][h] = *(const u32x4_t*)(scr + m * 2048 + ln * 128 + ((2 * lq + h) ^ swz(ln)) * 16);
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      for (int h = 0; h < 2; ++h) {
+        if constexpr (MODE == MODE_GATE_UP) ids[m][h] = p.assign[it.r0 + row_of(it, m, h)];
+        else if constexpr (MODE == MODE_DOWN) ids[m][h] = (m == 0 && h == 0) ? p.assign[min(it.r0 + (lane & 31), A - 1)] : 0;
+        else ids[m][h] = 0;
       }
-      const bool mine = lq == kq;  // this lane group holds the group's place in the block
+  };
+  Item linfo = decode(item_of(0));
+  int lg = gk0;
+  int n_j = 1;  // index (in this wave's sequence) of the item after the load cursor's
+  bool n_valid = has_item(n_j);
+  Item ninfo = n_valid ? decode(item_of(n_j)) : linfo;
+  int ids_cur[MT][2], ids_next[MT][2];
+  load_ids(linfo, ids_cur);
+  load_ids(ninfo, ids_next);
+  const uint8_t* l_wbase;  // unit (expert, block, group 0) of the load cursor's item
+  // per row tile m and half h: gate_up, dense: offset of the lane's 16 bytes
+  // (row 8 h + lane / 8 of the tile, columns 8 (lane % 8) .. + 7 of a group)
+  // in the activation rows; down: of the lane's operand words in the tile's
+  // group-0 block (h = 1 unused)
+  uint32_t l_aoff[MT][2];
+  int l_loc = 0;  // items the load cursor has entered (s_dst entry)
+
+  auto enter_item = [&](const Item& it) __attribute__((always_inline)) {
+    l_wbase = wbytes + ((size_t)it.e * p.nblk + it.blk) * (size_t)G * kTiledUnit;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      if constexpr (MODE == MODE_DOWN) {
+        const int tau = max(tile_of(it, (it.rows > 16) ? m : 0), 0);
+        l_aoff[m][0] = (uint32_t)tau * (uint32_t)(G * kActBlock) + lane * 16;
+        l_aoff[m][1] = 0;
+      } else {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          int src;
+          if constexpr (MODE == MODE_GATE_UP) {
+            const int a = ids_cur[m][h];
+            src = (a >= 0 && a < A) ? a / p.ktop : 0;
+          } else {
+            src = it.r0 + row_of(it, m, h);
+          }
+          l_aoff[m][h] = (uint32_t)src * arow + (lane & 7) * 16;
+        }
+      }
+    }
+    if constexpr (MODE == MODE_DOWN) {
+      const int lr = lane & 31, raw = ids_cur[0][0];
+      s_dst[wave][l_loc & 3][lr] = (lr < it.rows && raw >= 0 && raw < A) ? raw : -1;
+    }
+  };
+  enter_item(linfo);
+
+  auto issue = [&](Slot<MT>& sl) __attribute__((always_inline)) {
+    const uint8_t* u = l_wbase + (size_t)lg * kTiledUnit;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sl.w[i] = *(const u32x4_t*)(u + c_off + i * 1024);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) sl.s[h] = *(const u32x4_t*)(u + s_off + h * 256);
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      if constexpr (MODE == MODE_DOWN) {  // one coalesced kilobyte per operand register
+        const uint8_t* ab = abytes + l_aoff[m][0] + (uint32_t)lg * kActBlock;
+        sl.a[m][0] = *(const u32x4_t*)(ab);
+        sl.a[m][1] = *(const u32x4_t*)(ab + kActBlock / 2);
+      } else {  // 8 rows x 128 bytes per load; compute puts them in operand order
+#pragma unroll
+        for (int h = 0; h < 2; ++h) sl.a[m][h] = *(const u32x4_t*)(abytes + l_aoff[m][h] + (uint32_t)lg * 128);
+      }
+    }
+  };
+  auto advance_load = [&]() __attribute__((always_inline)) {
+    if (++lg < gk1) return;
+    lg = gk0;
+    if (!n_valid) return;  // past the last item: keep re-reading its groups (never used)
+    linfo = ninfo;
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) ids_cur[m][h] = ids_next[m][h];
+    ++l_loc;
+    enter_item(linfo);
+    ++n_j;
+    n_valid = has_item(n_j);
+    if (n_valid) {
+      ninfo = decode(item_of(n_j));
+      load_ids(ninfo, ids_next);
+    }
+  };
+
+  Slot<MT> ring[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    issue(ring[d]);
+    asm volatile("" ::: "memory");  // keeps the slots' loads in ring order
+    advance_load();
+  }
+
+  const u32x4_t ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+  const OffsetCodeConsts kc = offset_code_consts();
+
+  f32x4_t acc[MT][kNS];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int j = 0; j < kNS; ++j) acc[m][j] = zero4();
+  // The bias term of the affine, sum_g (b - 128 s)_g X_g, is a contraction
+  // over the groups; blocks of 4 groups go through one fp32 MFMA
+  // (v_mfma_f32_16x16x4_f32: lane (ln, lq) gives X of row ln and the
+  // correction of column ln for the block's group lq).
+  float xsel[MT];    // X of row ln, tile m, of the block's group lq (0 where not yet set)
+  float ccsel[kNS];  // b - 128 s of column ln, subtile j, of the block's group lq
+#pragma unroll
+  for (int m = 0; m < MT; ++m) xsel[m] = 0.f;
+#pragma unroll
+  for (int j = 0; j < kNS; ++j) ccsel[j] = 0.f;
+
+  int c_j = 0;  // index of the compute cursor's item in this wave's sequence
+  Item cinfo = decode(item_of(0));
+  int cg = gk0;
+  uint8_t* const wlds = qmm_lds + (size_t)wave * kWaveLds;  // this wave's LDS
+
+  // one group of the current item from slot `sl`, for the MT row tiles; the
+  // weights are unpacked once for all of them.  kq: the group's place in its
+  // block of 4.
+  auto compute = [&](Slot<MT>& sl, int kq) __attribute__((always_inline)) {
+    const bool t2 = cinfo.rows > 16;  // uniform: a second row tile to compute
+    u32x4_t a[MT][2];  // operands: lane (ln, lq) holds row ln, columns 16 lq .. 16 lq + 15
+    if constexpr (MODE == MODE_DOWN) {
+#pragma unroll
+      for (int m = 0; m < MT; ++m) a[m][0] = sl.a[m][0], a[m][1] = sl.a[m][1];
+    } else {
+      // through this wave's LDS: row r's 16-byte chunk c sits at slot c ^ swz(r),
+      // so both the 8-lanes-per-row writes and the operand reads are conflict free
+      auto swz = [](int r) __attribute__((always_inline)) { return ((r & 1) << 2) | ((r >> 1) & 3); };
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
         if (m > 0 && !t2) continue;
-        // ones as the A operand: every row of the result holds the row sums, so
-        // lane (ln, lq) gets X of activation row ln
-        f32x4_t X = mfma16x16x32(ones, a[m][0], zero4());
-        X = mfma16x16x32(ones, a[m][1], X);
-        xsel[m] = mine ? X[0] : xsel[m];
-      }
 #pragma unroll
-      for (int j = 0; j < kNS; ++j) {
-        const uint32_t sb = sl.s[j >> 2][j & 3];
-        const float sc = __uint_as_float(sb << 16);
-        const float cc = __uint_as_float(sb & 0xffff0000u) - 128.0f * sc;
-        ccsel[j] = mine ? cc : ccsel[j];
-        u32x4_t b0, b1;
-        unpack_offset_code_pair(sl.w[j >> 1][(j & 1) * 2], sl.w[j >> 1][(j & 1) * 2 + 1], kc, b0, b1);
+        for (int h = 0; h < 2; ++h) {
+          const int r = 8 * h + (lane >> 3);
+          *(u32x4_t*)(wlds + m * 2048 + r * 128 + ((lane & 7) ^ swz(r)) * 16) = sl.a[m][h];
+        }
+      }
+      wave_lds_fence();
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        if (m > 0 && !t2) continue;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          a[m][h] = *(const u32x4_t*)(wlds + m * 2048 + ln * 128 + ((2 * lq + h) ^ swz(ln)) * 16);
+      }
+      wave_lds_fence();
+    }
+    const bool mine = lq == kq;  // this lane group holds the group's place in the block
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      if (m > 0 && !t2) continue;
+      // ones as the A operand: every row of the result holds the row sums, so
+      // lane (ln, lq) gets X of activation row ln
+      f32x4_t X = mfma16x16x32(ones, a[m][0], zero4());
+      X = mfma16x16x32(ones, a[m][1], X);
+      xsel[m] = mine ? X[0] : xsel[m];
+    }
+#pragma unroll
+    for (int j = 0; j < kNS; ++j) {
+      const uint32_t sb = sl.s[j >> 2][j & 3];
+      const float sc = __uint_as_float(sb << 16);
+      const float cc = __uint_as_float(sb & 0xffff0000u) - 128.0f * sc;
+      ccsel[j] = mine ? cc : ccsel[j];
+      u32x4_t b0, b1;
+      unpack_offset_code_pair(sl.w[j >> 1][(j & 1) * 2], sl.w[j >> 1][(j & 1) * 2 + 1], kc, b0, b1);
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        if (m > 0 && !t2) continue;
+        f32x4_t P = mfma16x16x32(a[m][0], b0, zero4());
+        P = mfma16x16x32(a[m][1], b1, P);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[m][j][i] = __builtin_fmaf(sc, P[i], acc[m][j][i]);
+      }
+    }
+  };
+  // adds the bias terms of the groups collected since the last call
+  auto flush_bias = [&]() __attribute__((always_inline)) {
+    const bool t2 = cinfo.rows > 16;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      if (m > 0 && !t2) continue;
+#pragma unroll
+      for (int j = 0; j < kNS; ++j)
+        acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(xsel[m], ccsel[j], acc[m][j], 0, 0, 0);
+      xsel[m] = 0.f;
+    }
+  };
+
+  // Bounded wait on a pair flag: a protocol slip cannot hang the GPU (after
+  // about 10^8 cycles the wave goes on, with wrong results).
+  auto pair_wait = [&](int* f, int v) __attribute__((always_inline)) {
+    for (int it = 0; it < (1 << 21); ++it) {
+      if (__hip_atomic_load(f, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= v) return;
+      __builtin_amdgcn_s_sleep(1);
+    }
+  };
+  (void)pair_wait;
+
+  // End of the compute cursor's item: the wave stages its outputs in its LDS
+  // as bf16 and writes them with 16-byte stores.
+  auto finish_item = [&]() __attribute__((always_inline)) {
+    const bool t2 = cinfo.rows > 16;
+    const int blk = cinfo.blk;
+    if constexpr (KS == 2) {
+      // The second wave of the pair parks its partial sums for item c_j once
+      // the first has consumed item c_j - 1; the first adds them after its own
+      // (K order) and writes the outputs.
+      f32x4_t* const red = (f32x4_t*)(qmm_lds + kWaves * kWaveLds) + worker * (MT * kNS * 64);
+      int* const produced = &s_flag[worker][0];
+      int* const consumed = &s_flag[worker][1];
+      if (kp == 1) {
+        pair_wait(consumed, c_j);
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
           if (m > 0 && !t2) continue;
-          f32x4_t P = mfma16x16x32(a[m][0], b0, zero4());
-          P = mfma16x16x32(a[m][1], b1, P);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[m][j][i] = __builtin_fmaf(sc, P[i], acc[m][j][i]);
+          for (int j = 0; j < kNS; ++j) red[(m * kNS + j) * 64 + lane] = acc[m][j];
         }
+        __hip_atomic_store(produced, c_j + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      } else {
+        pair_wait(produced, c_j + 1);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+          if (m > 0 && !t2) continue;
+#pragma unroll
+          for (int j = 0; j < kNS; ++j) {
+            const f32x4_t o = red[(m * kNS + j) * 64 + lane];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[m][j][i] += o[i];
+          }
+        }
+        __hip_atomic_store(consumed, c_j + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
       }
-    };
-    // adds the bias terms of the groups collected since the last call
-    auto flush_bias = [&]() __attribute__((always_inline)) {
-      const bool t2 = cinfo.rows > 16;
+    }
+    if (kp != 0) {
+      // second wave of a pair: no outputs
+    } else if constexpr (MODE == MODE_GATE_UP) {
+      // gate j and up j + 4 -> columns 16 j .. 16 j + 15 of group blk of the
+      // activation tiles: column 16 q + 8 h + i of tile row r sits at byte
+      // h * 1024 + (16 q + r) * 16 + 2 i of the tile's block
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        if (m > 0 && !t2) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            *(uint16_t*)(wlds + m * 2048 + (ln >> 3) * 1024 + (16 * j + 4 * lq + i) * 16 + (ln & 7) * 2) =
+                f32_to_bf16_bits(gelu_tanh(acc[m][j][i]) * acc[m][j + 4][i]);
+      }
+      wave_lds_fence();
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        if (m > 0 && !t2) continue;
+        const int tau = tile_of(cinfo, m);
+        if (tau < 0) continue;
+        uint8_t* const dst = (uint8_t*)p.out + ((size_t)tau * (p.Nout / 64) + blk) * kActBlock + lane * 16;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) *(u32x4_t*)(dst + h * 1024) = *(const u32x4_t*)(wlds + m * 2048 + h * 1024 + lane * 16);
+      }
+    } else {
+      // bf16 [16 rows][128 columns] per row tile; a store covers 4 rows
+      uint16_t* const stg = (uint16_t*)wlds;
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
         if (m > 0 && !t2) continue;
 #pragma unroll
         for (int j = 0; j < kNS; ++j)
-          acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(xsel[m], ccsel[j], acc[m][j], 0, 0, 0);
-        xsel[m] = 0.f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            stg[m * 2048 + (4 * lq + i) * 128 + 16 * j + ln] = cinfo.zero ? (uint16_t)0 : f32_to_bf16_bits(acc[m][j][i]);
       }
-    };
-
-    // End of the current item.  Each wave parks in LDS the partial sums of the
-    // subtiles that other waves own; after a barrier every owner adds the K
-    // parts of its subtiles in K order (its own part straight from registers),
-    // stages the results in the part of its own LDS slice that nobody parked
-    // into, and writes them with 16-byte stores.
-    auto finish_item = [&]() __attribute__((always_inline)) {
-      f32x4_t* red = (f32x4_t*)qmm_lds;
-      const int nk = crole.nk, kp = crole.kp, blk = crole.blk;
-      const bool t2 = cinfo.rows > 16;
-      const bool member = wave < nk * NBI;  // not a spare wave
-      auto slot_of = [&](int w, int m, int j) __attribute__((always_inline)) {
-        return ((w * 2 + m) * kNS + j) * 64 + lane;
-      };
-      if (member) {
+      wave_lds_fence();
+      const int c = lane & 15;
+      const int col = blk * 128 + 8 * c;  // a block past the last output column (N % 128 == 64) has none there
 #pragma unroll
-        for (int m = 0; m < MT; ++m)
+      for (int m = 0; m < MT; ++m) {
+        if (m > 0 && !t2) continue;
 #pragma unroll
-          for (int j = 0; j < kNS; ++j)
-            if ((m == 0 || t2) && owner_of(j, nk) != kp) red[slot_of(wave, m, j)] = acc[m][j];
-      }
-      __syncthreads();
-      const int wbase = wave - kp;  // wave of K part 0 with the same block
-      // K parts of subtile j in K order; `mine` is this wave's part
-      auto ksum = [&](int m, int j, f32x4_t mine) __attribute__((always_inline)) {
-        f32x4_t v = (kp == 0) ? mine : red[slot_of(wbase, m, j)];
-        for (int q = 1; q < nk; ++q) {
-          const f32x4_t t = (q == kp) ? mine : red[slot_of(wbase + q, m, j)];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) v[i] += t[i];
-        }
-        return v;
-      };
-      uint8_t* const own = qmm_lds + (size_t)wave * (2 * kNS * 1024);  // this wave's slice
-      if (member && blk < p.nblk) {
-        if constexpr (MODE == MODE_GATE_UP) {
-          // gate j and up j + 4 -> 16 columns of mid, which the down pass reads as
-          // group blk of activation tile tau: column 16 j + c of tile row r sits at
-          // byte (c / 8) * 1024 + (r + 16 j) * 16 + (c % 8) * 2 of the block
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            if (owner_of(j, nk) != kp || cinfo.zero) continue;
-            uint8_t* const stg = own + j * 1024;  // slot (0, j): owned, so never parked
-#pragma unroll
-            for (int m = 0; m < MT; ++m) {
-              if (m > 0 && !t2) continue;
-              const f32x4_t g = ksum(m, j, acc[m][j]), u = ksum(m, j + 4, acc[m][j + 4]);
-#pragma unroll
-              for (int i = 0; i < 4; ++i)
-                *(uint16_t*)(stg + m * 512 + (4 * lq + i) * 32 + ln * 2) = f32_to_bf16_bits(gelu_tanh(g[i]) * u[i]);
-            }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            const int m = lane >> 5, r = lane & 15, h = (lane >> 4) & 1;
-            const int tau = (m == 0 || t2) ? tile_of(cinfo, m) : -1;
-            if (tau >= 0) {
-              const u32x4_t v = *(const u32x4_t*)(stg + m * 512 + r * 32 + h * 16);
-              *(u32x4_t*)((uint8_t*)p.out + ((size_t)tau * (p.Nout / 64) + blk) * kActBlock + h * (kActBlock / 2) +
-                          (r + 16 * j) * 16) = v;
-            }
-          }
-        } else if constexpr (MODE == MODE_DOWN) {
-          // subtiles [j0, j0 + 8/nk) are this wave's: W = 128 / nk contiguous
-          // columns, staged per row tile as bf16 [16 rows][W] in slots (m, j0 ..)
-          const int lgnk = nk >> 1;  // log2 nk for nk in {1, 2}
-          const int per = kNS >> lgnk, j0 = kp * per, W = 16 * per;
-#pragma unroll
-          for (int m = 0; m < MT; ++m) {
-            if (m > 0 && !t2) continue;
-            uint16_t* const stg = (uint16_t*)(own + (m * kNS + j0) * 1024);
-#pragma unroll
-            for (int j = 0; j < kNS; ++j) {
-              if (owner_of(j, nk) != kp) continue;
-              const f32x4_t v = ksum(m, j, acc[m][j]);
-#pragma unroll
-              for (int i = 0; i < 4; ++i)
-                stg[(4 * lq + i) * W + 16 * (j - j0) + ln] = cinfo.zero ? (uint16_t)0 : f32_to_bf16_bits(v[i]);
-            }
-          }
-          __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-          __builtin_amdgcn_wave_barrier();
-          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-          const int lgcpr = 4 - lgnk, rpi = 64 >> lgcpr;  // 16-byte chunks per row (W / 8), rows per store
-#pragma unroll
-          for (int m = 0; m < MT; ++m) {
-            if (m > 0 && !t2) continue;
-            const uint16_t* const stg = (const uint16_t*)(own + (m * kNS + j0) * 1024);
-            for (int r0 = 0; r0 < 16; r0 += rpi) {
-              const int r = r0 + (lane >> lgcpr), c = lane & ((1 << lgcpr) - 1);
-              const int a = s_dst[c_loc & 1][16 * m + r];
-              // a block past the last output row (H % 128 == 64) has no columns there
-              if (a >= 0 && blk * BCOLS + 16 * j0 + 8 * c < p.Nout)
-                *(u32x4_t*)((uint16_t*)p.out + (size_t)a * p.Nout + blk * BCOLS + 16 * j0 + 8 * c) =
-                    *(const u32x4_t*)(stg + r * W + 8 * c);
-            }
-          }
-        } else {
-#pragma unroll
-          for (int m = 0; m < MT; ++m) {
-            if (m > 0 && !t2) continue;
-#pragma unroll
-            for (int j = 0; j < kNS; ++j) {
-              if (owner_of(j, nk) != kp) continue;
-              const int col = blk * BCOLS + 16 * j + ln;
-              const f32x4_t v = ksum(m, j, acc[m][j]);
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const int lr = 16 * m + 4 * lq + i;
-                if (lr < cinfo.rows && col < p.Nout)
-                  ((uint16_t*)p.out)[(size_t)(cinfo.r0 + lr) * p.Nout + col] = f32_to_bf16_bits(v[i]);
-              }
-            }
-          }
+        for (int q = 0; q < 4; ++q) {
+          const int r = 4 * q + (lane >> 4), lr = 16 * m + r;
+          int row;
+          if constexpr (MODE == MODE_DOWN) row = s_dst[wave][c_j & 3][lr];
+          else row = (lr < cinfo.rows) ? cinfo.r0 + lr : -1;
+          if (row >= 0 && col < p.Nout)
+            *(u32x4_t*)((uint16_t*)p.out + (size_t)row * p.Nout + col) = *(const u32x4_t*)(stg + m * 2048 + r * 128 + 8 * c);
         }
       }
+    }
+    wave_lds_fence();  // the staging reads are done before the LDS is written again
 #pragma unroll
-      for (int m = 0; m < MT; ++m)
+    for (int m = 0; m < MT; ++m)
 #pragma unroll
-        for (int j = 0; j < kNS; ++j) acc[m][j] = zero4();
-      __syncthreads();  // partial-sum buffer free again
-    };
-
-    // One ring step on slot d: compute the current group, refill the slot.  Every
-    // step issues its loads, also after the last item (compute is skipped then):
-    // the loop has a single exit at the end of a block of D steps and the wait
-    // before each slot always counts the loads of the D - 1 slots issued after it.
-    bool done = false;
-    auto step = [&](auto d_tag) __attribute__((always_inline)) {
-      constexpr int d = decltype(d_tag)::value;
-      fence_slot(ring[d]);
-      if (!done && !cinfo.zero && crole.blk < p.nblk) {
-        const int kq = (cg - crole.gk0) & 3;
-        compute(ring[d], kq);
-        if (kq == 3 || cg + 1 == crole.gk1) flush_bias();
-      }
-      issue(ring[d]);
-      asm volatile("" ::: "memory");  // keeps the slots' loads in ring order
-      advance_load();
-      if constexpr (MODE == MODE_DOWN) pf_raw = raw_assign(ninfo);
-      if (done || ++cg < crole.gk1) return;
-      finish_item();
-      if (!has_item(c_loc + 1)) {
-        done = true;
-        return;
-      }
-      ++c_loc;
-      cinfo = decode(item_of(c_loc));
-      crole = role_of(cinfo);
-      cg = crole.gk0;
-    };
-    do {
-      run_steps(step, std::make_integer_sequence<int, DR>{});
-    } while (!done);
-    // the loads issued past the end are consumed here (they complete before the wave ends)
-#pragma unroll
-    for (int d = 0; d < DR; ++d) fence_slot(ring[d]);
+      for (int j = 0; j < kNS; ++j) acc[m][j] = zero4();
   };
-  body(std::integral_constant<int, 2>{});
+
+  // One ring step on slot d: compute the current group, refill the slot.  Every
+  // step issues its loads, also after the last item (compute is skipped then):
+  // the loop has a single exit at the end of a block of D steps and the wait
+  // before each slot always counts the loads of the D - 1 slots issued after it.
+  bool done = false;
+  auto step = [&](auto d_tag) __attribute__((always_inline)) {
+    constexpr int d = decltype(d_tag)::value;
+    fence_slot(ring[d]);
+    if (!done && !cinfo.zero) {
+      const int kq = (cg - gk0) & 3;
+      compute(ring[d], kq);
+      if (kq == 3 || cg + 1 == gk1) flush_bias();
+    }
+    issue(ring[d]);
+    asm volatile("" ::: "memory");  // keeps the slots' loads in ring order
+    advance_load();
+    if (done || ++cg < gk1) return;
+    finish_item();
+    if (!has_item(c_j + 1)) {
+      done = true;
+      return;
+    }
+    ++c_j;
+    cinfo = decode(item_of(c_j));
+    cg = gk0;
+  };
+  do {
+    run_steps(step, std::make_integer_sequence<int, D>{});
+  } while (!done);
+  // the loads issued past the end are consumed here (they complete before the wave ends)
+#pragma unroll
+  for (int d = 0; d < D; ++d) fence_slot(ring[d]);
 }
 
 // ---------------------------------------------------------------- weight tiling
@@ -743,43 +693,36 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 // ------------------------------------------------------------------ launchers
 namespace {
 
-template <int MODE, int NBI, int D>
+template <int MODE, int KS, int D>
 hipError_t launch_cfg(SwitchArgs a, int extra_buckets, int num_cu, hipStream_t stream) {
-  a.ntiles = (a.nblk + NBI - 1) / NBI;
-  const size_t lds = (size_t)kWaves * 2 * kNS * 64 * 16;  // partial sums of every wave and row tile
+  a.ntiles = a.nblk;
+  // per wave: staging; KS = 2: per pair, the partial sums of the second wave
+  const size_t lds = (size_t)kWaves * kWaveLds + (KS == 2 ? (size_t)(kWaves / 2) * kMT * kNS * 64 * 16 : 0);
   long long chunks;
   if (MODE == MODE_DENSE)
     chunks = (a.rows_total + kBM - 1) / kBM;
   else
     chunks = (a.rows_total + kBM - 1) / kBM + (long long)std::min(a.E, a.rows_total) + extra_buckets;
-  const long long items = chunks * a.ntiles;
+  const long long items = chunks * a.nblk;
   long long grid = std::min(items, (long long)num_cu * 2);
-  if (MODE == MODE_GATE_UP) grid = std::max(grid, (items + kMaxWgItems - 1) / kMaxWgItems);
   if (grid < 1) grid = 1;
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&qmm_kernel<MODE, NBI, D>),
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&qmm_kernel<MODE, KS, D>),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((qmm_kernel<MODE, NBI, D>), dim3((unsigned)grid), dim3(kThreads), lds, stream, a);
+  hipLaunchKernelGGL((qmm_kernel<MODE, KS, D>), dim3((unsigned)grid), dim3(kThreads), lds, stream, a);
   return hipGetLastError();
 }
 
-// Blocks per item and ring depth: one block per item when a single-tile chunk
-// still leaves each of the 4 K parts at least 3 groups, else two; the ring is
-// as deep as the fewest groups a wave owns allow (at most 4), so the load
-// cursor is never more than one item ahead of the compute cursor.
+// gate_up with a long contraction (at least 8 groups) splits it over a wave
+// pair.  Ring depth: two slots, one when a wave's part of the contraction is a
+// single group (the down pass's row table relies on the load cursor never
+// reaching item c + 4 before item c is finished).
 template <int MODE>
 hipError_t launch_mode(SwitchArgs a, int extra_buckets, int num_cu, hipStream_t stream) {
   const int G = a.K / 64;
-  const int nbi = (G >= 12) ? 1 : 2;
-  const int depth = std::min(4, std::max(1, G / (kWaves / nbi)));  // groups of the smallest K part
-  if (nbi == 1) {
-    if (depth >= 4) return launch_cfg<MODE, 1, 4>(a, extra_buckets, num_cu, stream);
-    return launch_cfg<MODE, 1, 3>(a, extra_buckets, num_cu, stream);
-  }
-  if (depth >= 4) return launch_cfg<MODE, 2, 4>(a, extra_buckets, num_cu, stream);
-  if (depth == 3) return launch_cfg<MODE, 2, 3>(a, extra_buckets, num_cu, stream);
-  if (depth == 2) return launch_cfg<MODE, 2, 2>(a, extra_buckets, num_cu, stream);
-  return launch_cfg<MODE, 2, 1>(a, extra_buckets, num_cu, stream);
+  if (MODE == MODE_GATE_UP && G >= 8) return launch_cfg<MODE, (MODE == MODE_GATE_UP) ? 2 : 1, 2>(a, extra_buckets, num_cu, stream);
+  if (G >= 2) return launch_cfg<MODE, 1, 2>(a, extra_buckets, num_cu, stream);
+  return launch_cfg<MODE, 1, 1>(a, extra_buckets, num_cu, stream);
 }
 
 }  // namespace

@@ -279,7 +279,12 @@ def test_layer_deterministic_bitwise():
     assert torch.equal(y1.view(torch.uint16), y2.view(torch.uint16))
 
 
-@pytest.mark.parametrize("T,H,E,k,I", [(1, 64, 1, 1, 64), (37, 192, 12, 3, 192), (9, 256, 8, 8, 64)])
+# (45, 576, 12, 4, 320): gate_up's contraction of 9 groups is split 4 + 5 over a
+# wave pair, and the down output ends in a half block (576 = 4.5 x 128);
+# (200, 512, 6, 4, 128): experts of ~130 rows, several chunks each, many items
+# per worker.
+@pytest.mark.parametrize("T,H,E,k,I", [(1, 64, 1, 1, 64), (37, 192, 12, 3, 192), (9, 256, 8, 8, 64),
+                                       (45, 576, 12, 4, 320), (200, 512, 6, 4, 128)])
 def test_layer_ragged_and_degenerate(T, H, E, k, I):
     import bit_quantized_moe_diffrouter_amd as q
     say(f"[layer ragged] T={T} H={H} E={E} k={k} I={I}")

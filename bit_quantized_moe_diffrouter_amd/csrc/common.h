@@ -57,11 +57,11 @@ __device__ __forceinline__ OffsetCodeConsts offset_code_consts() {
   k.expo = e;
   return k;
 }
-__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t smask, uint32_t vor) {
-  uint32_t r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(smask), "v"(vor));
-  return r;
-}
+// (a & smask) | vor: selected as one v_and_or_b32.  Written in C, not as
+// inline asm, so that the compiler sees the VGPR it writes: an MFMA that reads
+// a VALU result needs two wait states, which the compiler inserts only for
+// instructions it knows about.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t smask, uint32_t vor) { return (a & smask) | vor; }
 __device__ __forceinline__ void unpack_offset_code_pair(uint32_t w0, uint32_t w1, const OffsetCodeConsts& k,
                                                         u32x4_t& b0, u32x4_t& b1) {
   const u32x2_t pr = {w0, w1};

@@ -148,8 +148,9 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
   } else {
     // bucket b < E is expert b's segment; bucket E (down only) holds the dropped rows
     auto counts_of = [&](int b, int& one, int& tl) __attribute__((always_inline)) {
-      const int lo = min(max(p.offsets[b], 0), A);
-      const int hi = (b < p.E) ? min(max(p.offsets[b + 1], lo), A) : A;
+      const int o0 = p.offsets[b], o1 = p.offsets[min(b + 1, p.E)];  // both loads in flight together
+      const int lo = min(max(o0, 0), A);
+      const int hi = (b < p.E) ? min(max(o1, lo), A) : A;
       s_lo[b] = lo;
       s_hi[b] = hi;
       const int n = hi - lo, rem = n % kBM;
@@ -281,9 +282,8 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
   bool n_valid = has_item(n_j);
   Item ninfo = n_valid ? decode(item_of(n_j)) : linfo;
   int ids_cur[MT][2], ids_next[MT][2];
-  load_ids(linfo, ids_cur);
-  load_ids(ninfo, ids_next);
-  const uint8_t* l_wbase;  // unit (expert, block, group 0) of the load cursor's item
+  // unit (expert, block, group 0) of the load cursor's item
+  const uint8_t* l_wbase = wbytes + ((size_t)linfo.e * p.nblk + linfo.blk) * (size_t)G * kTiledUnit;
   // per row tile m and half h: gate_up, dense: offset of the lane's 16 bytes
   // (row 8 h + lane / 8 of the tile, columns 8 (lane % 8) .. + 7 of a group)
   // in the activation rows; down: of the lane's operand words in the tile's
@@ -318,14 +318,23 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
       s_dst[wave][l_loc & 3][lr] = (lr < it.rows && raw >= 0 && raw < A) ? raw : -1;
     }
   };
-  enter_item(linfo);
 
-  auto issue = [&](Slot<MT>& sl) __attribute__((always_inline)) {
-    const uint8_t* u = l_wbase + (size_t)lg * kTiledUnit;
+  // Codes and scales of group g.  Each weight byte is read once; in the gate_up
+  // pass the loads carry the non-temporal hint, which keeps the weight stream
+  // from displacing in L2 the activation rows every block of a chunk re-reads
+  // (3 us at 256 tokens; no gain in the down pass).
+  auto issue_w = [&](Slot<MT>& sl, int g) __attribute__((always_inline)) {
+    const uint8_t* u = l_wbase + (size_t)g * kTiledUnit;
+    auto ld = [](const uint8_t* a) __attribute__((always_inline)) {
+      if constexpr (MODE == MODE_GATE_UP) return __builtin_nontemporal_load((const u32x4_t*)a);
+      else return *(const u32x4_t*)a;
+    };
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sl.w[i] = *(const u32x4_t*)(u + c_off + i * 1024);
+    for (int i = 0; i < 4; ++i) sl.w[i] = ld(u + c_off + i * 1024);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) sl.s[h] = *(const u32x4_t*)(u + s_off + h * 256);
+    for (int h = 0; h < 2; ++h) sl.s[h] = ld(u + s_off + h * 256);
+  };
+  auto issue_a = [&](Slot<MT>& sl) __attribute__((always_inline)) {  // activations of group lg
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
       if constexpr (MODE == MODE_DOWN) {  // one coalesced kilobyte per operand register
@@ -337,6 +346,10 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
         for (int h = 0; h < 2; ++h) sl.a[m][h] = *(const u32x4_t*)(abytes + l_aoff[m][h] + (uint32_t)lg * 128);
       }
     }
+  };
+  auto issue = [&](Slot<MT>& sl) __attribute__((always_inline)) {
+    issue_w(sl, lg);
+    issue_a(sl);
   };
   auto advance_load = [&]() __attribute__((always_inline)) {
     if (++lg < gk1) return;
@@ -357,6 +370,9 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
     }
   };
 
+  load_ids(linfo, ids_cur);
+  load_ids(ninfo, ids_next);
+  enter_item(linfo);
   Slot<MT> ring[D];
 #pragma unroll
   for (int d = 0; d < D; ++d) {

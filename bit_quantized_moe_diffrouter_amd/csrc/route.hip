@@ -215,12 +215,22 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const RouteArgs p) {
   __shared__ __align__(16) unsigned long long s_key[4][64 * NI];
   __shared__ float s_sv[4][16];
   __shared__ int s_se[4][16];
+  __shared__ float s_pes[4][16];
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const int t = blockIdx.x * 4 + wv;
   if (t >= p.T) return;  // whole wave leaves; only wave-level syncs below
   const int E = p.E, T = p.T;
 
+  // per_expert_scale and the logit offset of this lane's experts, loaded with
+  // the partials (not after the ranking: one round trip fewer)
+  float pes_v[NI], bias_v[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int e = lane + 64 * i;
+    pes_v[i] = (e < E) ? bf16_bits_to_f32(p.pes[e]) : 0.f;
+    bias_v[i] = (e < E && p.logit_bias) ? p.logit_bias[e] : 0.f;
+  }
   // The logit kernel works on the un-normalised row: the norm is one positive
   // factor per token, 1 / sqrt(mean(x^2) + eps), applied here.  All partial
   // loads of a batch are issued before any is summed (fixed q order).
@@ -259,7 +269,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const RouteArgs p) {
     key[i] = 0;
     if (e < E) {
       float s = part[i] * rs;
-      if (p.logit_bias) s += p.logit_bias[e];
+      if (p.logit_bias) s += bias_v[i];
       if (p.logits_out) p.logits_out[(size_t)t * E + e] = s;
       v[i] = (s != s) ? -INFINITY : s;  // NaN never wins
       key[i] = select_key(v[i], e);
@@ -284,6 +294,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const RouteArgs p) {
     if (key[i] != 0 && rank[i] < p.k) {
       s_sv[wv][rank[i]] = v[i];
       s_se[wv][rank[i]] = lane + 64 * i;
+      s_pes[wv][rank[i]] = pes_v[i];
     }
   wave_lds_sync();
 
@@ -293,7 +304,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const RouteArgs p) {
     for (int j = 0; j < p.k; ++j) sum += expf(s_sv[wv][j] - m);
     const int e = s_se[wv][lane];
     const float pj = expf(s_sv[wv][lane] - m) / sum;
-    const float pes = bf16_bits_to_f32(p.pes[e]);
+    const float pes = s_pes[wv][lane];
     p.indices[(size_t)t * p.k + lane] = e;
     p.weights[(size_t)t * p.k + lane] = pj * pes;
   }

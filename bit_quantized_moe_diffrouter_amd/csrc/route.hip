@@ -28,11 +28,14 @@ constexpr int kRKS = 4;              // groups per LDS stage
 constexpr int kRRowB = kRKS * 128 + 16;
 }  // namespace
 
+// K parts of the logit kernel: enough (token tile, K part) workgroups to fill
+// the chip at small T, and at least 4 at large T, where a single part per tile
+// would walk all groups in latency-bound stages one after another.
 int route_ksplit(int T, int H) {
   const int G = H / kGroup;
   const int tiles = (T + kTT - 1) / kTT;
   int ks = 256 / (tiles > 0 ? tiles : 1);
-  if (ks < 1) ks = 1;
+  if (ks < 4) ks = 4;
   if (ks > G) ks = G;
   return ks;
 }

@@ -173,6 +173,24 @@ def test_sort_large_random_and_dropped():
     np.testing.assert_array_equal(sa_g[nv:], np.nonzero(~valid)[0])
 
 
+
+@pytest.mark.parametrize("T,k,E", [(4100, 8, 128), (9000, 4, 7)])
+def test_sort_beyond_the_lds_cache(T, k, E):
+    """More than 32768 assignments: the kernel recomputes buckets and ranks
+    instead of keeping them in LDS (stable order and offsets as before)."""
+    say(f"[sort] beyond the LDS cache: T={T} k={k} E={E}")
+    rng = np.random.default_rng(T)
+    idx = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    idx[rng.random((T, k)) < 0.01] = -3
+    off_g, sa_g = gpu_sort(idx, E)
+    flat = idx.reshape(-1)
+    valid = (flat >= 0) & (flat < E)
+    ids = np.nonzero(valid)[0]
+    np.testing.assert_array_equal(off_g, np.concatenate([[0], np.cumsum(np.bincount(flat[ids], minlength=E))]))
+    np.testing.assert_array_equal(sa_g[:ids.size], ids[np.argsort(flat[ids], kind="stable")])
+    np.testing.assert_array_equal(sa_g[ids.size:], np.nonzero(~valid)[0])
+
+
 # ------------------------------------------------------------------ experts
 def sample_tokens(T, n, seed=5):
     if T <= n:

@@ -37,6 +37,13 @@ X  per assignment: ``g = x_t . W_gu[e]^T``, split at I, ``gelu_tanh(gate) * up``
                                    gelu_approx(gate) * up: [vision page] DiffVisionMLP)
 L  dense 4-bit linear ``y = x . W^T``
                                   ([vision page] VisionLinear.forward, quantized arm)
+F  the decoder's feed-forward block around the MoE: plain RMSNorm with its
+   weight used as stored (no 1 + w offset); the parallel dense GeGLU MLP
+   ``down(gelu_tanh(gate x) * up x)``; ``out = (h + N(N1(h1) + N2(h2))) * s``
+   with h1 the dense branch on N0(h), h2 the experts on N0'(h), the router
+   on the raw h                   ([model page] DiffDecoderLayer.forwardWith,
+                                   the file header's note on plain RMSNorm;
+                                   the MLP shape: SelfConditioning, GegluMLP)
 
 Readings where the pages are silent (each is listed in the design doc): group 64,
 codes stored first-in-lowest-bits, scales/biases bf16; eps = 1e-6; router kept
@@ -230,6 +237,12 @@ def expert_rows_bruteforce(x_row: np.ndarray, e: int, gate_up, down, I: int
     return mid, Wd @ mid
 
 
+def _as_f64(x) -> np.ndarray:
+    """bf16 bit patterns (uint16) are decoded; anything else is taken as values."""
+    x = np.asarray(x)
+    return bf16_to_f64(x) if x.dtype == np.uint16 else x.astype(np.float64)
+
+
 def experts_bruteforce(x_bits, indices, weights, gate_up, down, I: int,
                        tokens: Optional[Sequence[int]] = None) -> np.ndarray:
     """X by brute force, per token and per slot in fp64, no sort:
@@ -237,8 +250,9 @@ def experts_bruteforce(x_bits, indices, weights, gate_up, down, I: int,
     ([model page] DiffExperts.forward, final weighted sum over k).
 
     ``tokens`` restricts the computation to those rows (returned in that
-    order).  Each touched expert is dequantized once."""
-    x = bf16_to_f64(x_bits)
+    order).  Each touched expert is dequantized once.  ``x_bits`` may also be
+    an array of values (the feed-forward block passes a norm's output)."""
+    x = _as_f64(x_bits)
     idx = np.asarray(indices)
     w = np.asarray(weights, dtype=np.float32).astype(np.float64)
     T, k = idx.shape
@@ -342,6 +356,59 @@ def moe_layer(x_bits, weights, k: int, I: int, eps: float, grouped: bool = True)
     else:
         y = experts_bruteforce(x_bits, idx, wts, weights.gate_up, weights.down, I)
     return y, idx, wts, logits
+
+
+# ----------------------------------------------------------------------------
+# F: the decoder's feed-forward block
+# ----------------------------------------------------------------------------
+def rms_norm(x, weight_bits, eps: float) -> np.ndarray:
+    """Plain RMSNorm, ``x / sqrt(mean(x^2) + eps) * w`` over the last axis, the
+    stored weight used as is ([model page] header: plain RMSNorm everywhere,
+    no 1 + weight offset; [vision page] manualRms with a weight)."""
+    return rms_norm_noscale(_as_f64(x), eps) * bf16_to_f64(weight_bits)
+
+
+def dense_geglu_mlp(x, gate, up, down, rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    """The dense branch ``down(gelu_tanh(gate . x) * (up . x))`` with three 4-bit
+    linears, fp64 ([model page] DiffDecoderLayer's GegluMLP, the same shape as
+    SelfConditioning's down(geglu(gate(.), up(.))); GeGLU as in the experts)."""
+    x = _as_f64(x)
+    if rows is not None:
+        x = x[list(rows)]
+    g = x @ dequantize(gate.w, gate.scales, gate.biases).T
+    u = x @ dequantize(up.w, up.scales, up.biases).T
+    return (gelu_tanh(g) * u) @ dequantize(down.w, down.scales, down.biases).T
+
+
+def ff_block(h_bits, moe_weights, ffw, k: int, I: int, eps: float,
+             tokens: Optional[Sequence[int]] = None, route_out=None):
+    """The feed-forward half of a decoder layer, fp64 with no intermediate
+    rounding ([model page] DiffDecoderLayer.forwardWith, after the attention
+    residual):
+
+        residual = h
+        h1 = postFfNorm1(mlp(preFfNorm(h)))
+        (indices, weights) = router(h)                 # on the raw residual
+        h2 = postFfNorm2(experts(preFfNorm2(h), indices, weights))
+        out = (residual + postFfNorm(h1 + h2)) * layer_scalar
+
+    ``tokens`` restricts the output rows (routing is per token, so only those
+    tokens are routed); ``route_out`` = (indices, weights) replaces the
+    oracle's own routing.  Returns (out [len(tokens), H], indices, weights)."""
+    h = bf16_to_f64(h_bits)
+    toks = list(range(h.shape[0])) if tokens is None else list(tokens)
+    if route_out is None:
+        r = moe_weights.router
+        idx, wts, _ = route(np.asarray(h_bits)[toks], moe_weights.norm_scale, eps, r.w, r.scales, r.biases,
+                            moe_weights.per_expert_scale, k, moe_weights.logit_bias)
+    else:
+        idx, wts = (np.asarray(route_out[0])[toks], np.asarray(route_out[1])[toks])
+    hs = h[toks]
+    h1 = rms_norm(dense_geglu_mlp(rms_norm(hs, ffw.pre_ff, eps), ffw.gate, ffw.up, ffw.down), ffw.post_ff1, eps)
+    xe = rms_norm(hs, ffw.pre_ff2, eps)
+    h2 = rms_norm(experts_bruteforce(xe, idx, wts, moe_weights.gate_up, moe_weights.down, I), ffw.post_ff2, eps)
+    out = (hs + rms_norm(h1 + h2, ffw.post_ff, eps)) * ffw.layer_scalar
+    return out, idx, wts
 
 
 # ----------------------------------------------------------------------------

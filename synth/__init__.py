@@ -18,6 +18,12 @@ Workload recipe (one line per tensor, in draw order of the weight stream):
 * down codes / scales / biases                                   -> ``[E, H, I/8]`` / ``[E, H, I/64]``
 
 The activations come from an independent stream: ``x ~ N(0, 1)`` -> bf16 ``[T, H]``.
+
+The decoder's feed-forward block (MoE plus the parallel dense GeGLU branch)
+adds, from a stream of its own: the five RMSNorm weights ``~ U[0.8, 1.2]``
+(pre, pre_2, post_1, post_2, post) -> bf16 ``[H]``; the dense gate, up and down
+4-bit weights (same recipe as above) ``[I_d, H/8]``, ``[I_d, H/8]``,
+``[H, I_d/8]``; and ``layer_scalar ~ U[0.5, 1.5]`` rounded to bf16.
 The skewed-routing workload adds a per-expert logit offset
 ``tau * ln p_e`` with ``p_e`` proportional to ``rank_e ** -1.1`` (Zipf, s = 1.1)
 and ``rank`` a seeded permutation of ``1..E``.
@@ -198,3 +204,43 @@ def make_qlinear_inputs(cfg: QLinearConfig) -> QLinearInputs:
     rng = np.random.default_rng(cfg.seed_w)
     W = random_qtensor(rng, (cfg.N,), cfg.K)
     return QLinearInputs(cfg, make_activations(cfg.M, cfg.K, cfg.seed_x), W)
+
+
+# ----------------------------------------------------------------------------
+# the decoder's feed-forward block: MoE + parallel dense GeGLU MLP
+# ----------------------------------------------------------------------------
+@dataclass
+class FFConfig:
+    name: str
+    moe: MoEConfig
+    I_dense: int       # width of the dense GeGLU branch (not printed by the pages)
+    seed_ff: int
+
+
+@dataclass
+class FFWeights:
+    pre_ff: np.ndarray      # bf16 bits [H]: norm before the dense branch
+    pre_ff2: np.ndarray     # bf16 bits [H]: norm before the experts
+    post_ff1: np.ndarray    # bf16 bits [H]: norm after the dense branch
+    post_ff2: np.ndarray    # bf16 bits [H]: norm after the experts
+    post_ff: np.ndarray     # bf16 bits [H]: norm of the sum
+    gate: QTensor           # [I_d, H/8]
+    up: QTensor             # [I_d, H/8]
+    down: QTensor           # [H, I_d/8]
+    layer_scalar: float     # a bf16 value
+
+
+FF_TINY = FFConfig("ff_tiny_16tok_h256", TINY, I_dense=192, seed_ff=5)
+FF_CANVAS = FFConfig("ff_canvas_256tok_h2816", CANVAS, I_dense=2112, seed_ff=6)
+FF_CONFIGS = {c.name: c for c in (FF_TINY, FF_CANVAS)}
+
+
+def make_ff_weights(cfg: FFConfig) -> FFWeights:
+    rng = np.random.default_rng(cfg.seed_ff)
+    H, Id = cfg.moe.H, cfg.I_dense
+    norms = [to_bf16_bits(rng.uniform(0.8, 1.2, size=H).astype(np.float32)) for _ in range(5)]
+    gate = random_qtensor(rng, (Id,), H)
+    up = random_qtensor(rng, (Id,), H)
+    down = random_qtensor(rng, (H,), Id)
+    scalar = float(bf16_bits_as_f32(to_bf16_bits(np.float32(rng.uniform(0.5, 1.5))).reshape(1))[0])
+    return FFWeights(*norms, gate, up, down, scalar)

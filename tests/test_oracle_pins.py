@@ -335,3 +335,95 @@ def test_bf16_roundtrip_and_rounding():
     bits = O.f64_to_bf16_bits(v)
     # 1 + 2^-8 is a tie between 1 and 1 + 2^-7 -> even (1.0); 1 + 3*2^-8 -> 1 + 2^-6
     np.testing.assert_array_equal(O.bf16_to_f64(bits), [1.0, 1.0, 1.0 + 2 ** -6, -2.5, 3.140625])
+
+
+# ----------------------------------------------------------------------------
+# F: the decoder's feed-forward block
+# ----------------------------------------------------------------------------
+def test_rms_norm_weighted_closed_form():
+    """A constant row c*1 normalises to c / sqrt(c^2 + eps) before the weight;
+    the stored weight multiplies as is (a 1 + w offset would double these)."""
+    eps = 1e-6
+    w = np.array([0.5, 1.0, 1.5, 2.0] * 16, dtype=np.float32)
+    for c in (3.0, -0.25, 1e-4):
+        x = np.full((1, 64), c)
+        y = O.rms_norm(x, bf16(w), eps)
+        np.testing.assert_allclose(y[0], c / math.sqrt(c * c + eps) * w.astype(np.float64), rtol=1e-12)
+    # a worked row: x = (3, 4, 0, 0), mean(x^2) = 25/4, so r = x / 2.5 (eps 0)
+    y = O.rms_norm(np.array([[3.0, 4.0, 0.0, 0.0]]), bf16([1.0, 2.0, 1.0, 1.0]), 0.0)
+    np.testing.assert_allclose(y, [[1.2, 3.2, 0.0, 0.0]], rtol=1e-12)
+
+
+def test_rms_norm_scale_invariant_and_zero_row():
+    rng = np.random.default_rng(40)
+    x = rng.standard_normal((3, 128))
+    w = bf16(rng.uniform(0.8, 1.2, 128))
+    # exact invariance with eps = 0 (eps shifts it by about eps / mean(x^2))
+    np.testing.assert_allclose(O.rms_norm(37.0 * x, w, 0.0), O.rms_norm(x, w, 0.0), rtol=1e-12)
+    assert np.all(O.rms_norm(np.zeros((1, 128)), w, 1e-6) == 0.0)
+
+
+def test_dense_geglu_mlp_integer_worked_example():
+    """Integer weights (W = q - 8) and x in eighths: gate, up and down by plain
+    numpy; swapping gate and up, or transposing a weight, changes the result."""
+    rng = np.random.default_rng(41)
+    H, Id = 128, 64
+    cg, cu = rng.integers(0, 16, size=(Id, H)), rng.integers(0, 16, size=(Id, H))
+    cd = rng.integers(0, 16, size=(H, Id))
+    gate = synth.QTensor(*integer_qtensor(cg))
+    up = synth.QTensor(*integer_qtensor(cu))
+    down = synth.QTensor(*integer_qtensor(cd))
+    xf = rng.integers(-2, 3, size=(4, H)).astype(np.float64) * 0.125
+    y = O.dense_geglu_mlp(bf16(xf), gate, up, down)
+    g = xf @ (cg - 8.0).T
+    u = xf @ (cu - 8.0).T
+    ref = (0.5 * g * (1 + np.tanh(math.sqrt(2 / math.pi) * (g + 0.044715 * g ** 3))) * u) @ (cd - 8.0).T
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-9)
+    swapped = O.dense_geglu_mlp(bf16(xf), up, gate, down)
+    assert np.abs(swapped - ref).max() > 1.0
+
+
+def test_ff_block_with_zero_branches_is_scaled_residual():
+    """All codes 8 with bias -8*scale make every 4-bit weight zero: both
+    branches vanish, their norms map 0 to 0, and out = h * layer_scalar."""
+    cfg = synth.FF_TINY
+    inp = synth.make_moe_inputs(cfg.moe)
+    ffw = synth.make_ff_weights(cfg)
+    eights = lambda qt: synth.QTensor(np.full_like(qt.w, 0x88888888), qt.scales, qt.biases)
+    wt = inp.weights
+    zero_moe = synth.MoEWeights(wt.norm_scale, wt.router, wt.per_expert_scale, eights(wt.gate_up),
+                                eights(wt.down), wt.logit_bias)
+    zero_ff = synth.FFWeights(ffw.pre_ff, ffw.pre_ff2, ffw.post_ff1, ffw.post_ff2, ffw.post_ff,
+                              eights(ffw.gate), eights(ffw.up), eights(ffw.down), ffw.layer_scalar)
+    out, _, _ = O.ff_block(inp.x, zero_moe, zero_ff, cfg.moe.k, cfg.moe.I, cfg.moe.eps)
+    np.testing.assert_array_equal(out, O.bf16_to_f64(inp.x) * ffw.layer_scalar)
+
+
+def test_ff_block_residual_raw_branches_scale_invariant():
+    """Scaling h by a > 0 leaves the routing (its own norm) and both branches
+    (they see normalised copies) unchanged, while the residual enters raw:
+    out(a h) - a s h == out(h) - s h."""
+    cfg = synth.FF_TINY
+    inp = synth.make_moe_inputs(cfg.moe)
+    ffw = synth.make_ff_weights(cfg)
+    s = ffw.layer_scalar
+    h = O.bf16_to_f64(inp.x)
+    h4 = bf16(4.0 * h)  # exact: a power of two
+    out1, idx1, _ = O.ff_block(inp.x, inp.weights, ffw, cfg.moe.k, cfg.moe.I, cfg.moe.eps)
+    out4, idx4, _ = O.ff_block(h4, inp.weights, ffw, cfg.moe.k, cfg.moe.I, cfg.moe.eps)
+    np.testing.assert_array_equal(idx1, idx4)
+    np.testing.assert_allclose(out4 - 4.0 * s * h, out1 - s * h, rtol=1e-6, atol=1e-6)
+
+
+def test_ff_block_rows_and_given_routing():
+    """Selected rows equal the full block's rows; feeding back the block's own
+    routing reproduces it."""
+    cfg = synth.FF_TINY
+    inp = synth.make_moe_inputs(cfg.moe)
+    ffw = synth.make_ff_weights(cfg)
+    full, idx, w = O.ff_block(inp.x, inp.weights, ffw, cfg.moe.k, cfg.moe.I, cfg.moe.eps)
+    rows = [3, 11, 0]
+    part, _, _ = O.ff_block(inp.x, inp.weights, ffw, cfg.moe.k, cfg.moe.I, cfg.moe.eps, tokens=rows)
+    np.testing.assert_allclose(part, full[rows], rtol=1e-12, atol=1e-12)
+    again, _, _ = O.ff_block(inp.x, inp.weights, ffw, cfg.moe.k, cfg.moe.I, cfg.moe.eps, route_out=(idx, w))
+    np.testing.assert_allclose(again, full, rtol=1e-12, atol=1e-12)

@@ -27,6 +27,7 @@ __all__ = [
     "moe_route", "moe_route_workspace", "moe_sort", "qswitch_mid_bytes",
     "qswitch_gate_up_geglu",
     "qswitch_down_combine", "qswitch_down_combine_workspace", "qlinear", "moe_layer",
+    "ff_prenorm", "qlinear_geglu", "ff_combine", "FFParams", "ff_block",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -74,6 +75,9 @@ _SIGNATURES = {
     "qswitch_down_combine_workspace": (_SZ, [_I, _I, _I, _I]),
     "qswitch_down_combine": (ctypes.c_int, [_P, _I, _I, _I, _QP, _I, _P, _P, _P, _P, _P, _SZ, _I, _P]),
     "qlinear": (ctypes.c_int, [_P, _I, _QP, _P, _P]),
+    "qlinear_geglu": (ctypes.c_int, [_P, _I, _QP, _P, _P]),
+    "ff_prenorm": (ctypes.c_int, [_P, _I, _I, _P, _P, ctypes.c_float, _P, _P, _P]),
+    "ff_combine": (ctypes.c_int, [_P, _P, _P, _I, _I, _P, _P, _P, ctypes.c_float, ctypes.c_float, _P, _P]),
     "qmoe_tiled_weight_bytes": (_SZ, [_I, _I, _I, _I]),
     "qmoe_tile_weight": (ctypes.c_int, [_QP, _I, _P, _SZ, _P]),
 }
@@ -332,3 +336,82 @@ def moe_layer(x_router: torch.Tensor, x_expert: torch.Tensor, p: MoEParams, k: i
     mid = qswitch_gate_up_geglu(x_expert, p.gate_up, p.I, k, off, sa)
     y = qswitch_down_combine(mid, x_expert.shape[0], k, p.down, w, off, sa, deterministic=deterministic)
     return y, idx, w, off, sa, mid
+
+
+# ----------------------------------------------------------------------------
+# the decoder's feed-forward block around the MoE
+# ----------------------------------------------------------------------------
+def ff_prenorm(h: torch.Tensor, w_dense: torch.Tensor, w_moe: torch.Tensor, eps: float):
+    """Both pre-norms from one read of h: returns (rms(h) * w_dense, rms(h) * w_moe), bf16 [T, H]."""
+    _need(h, "h", 2)
+    T, H = (int(v) for v in h.shape)
+    _need(w_dense, "w_dense", 2, (H,))
+    _need(w_moe, "w_moe", 2, (H,))
+    xa = torch.empty((T, H), dtype=torch.bfloat16, device=h.device)
+    xb = torch.empty((T, H), dtype=torch.bfloat16, device=h.device)
+    _check(lib().ff_prenorm(_ptr(h), T, H, _ptr(w_dense), _ptr(w_moe), float(eps), _ptr(xa), _ptr(xb), _stream()))
+    return xa, xb
+
+
+def qlinear_geglu(x: torch.Tensor, W: "TiledWeight", y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """gelu_tanh(x . gate^T) * (x . up^T) against the fused [gate; up] weight
+    (tiled with split = N): returns bf16 [M, N]."""
+    M = int(x.shape[0])
+    _need(x, "x", 2)
+    if y is None:
+        y = torch.empty((M, W.split), dtype=torch.bfloat16, device=x.device)
+    d = W.desc()
+    _check(lib().qlinear_geglu(_ptr(x), M, ctypes.byref(d), _ptr(y), _stream()))
+    return y
+
+
+def ff_combine(h: torch.Tensor, dense_out: torch.Tensor, moe_out: torch.Tensor, w_post1: torch.Tensor,
+               w_post2: torch.Tensor, w_post: torch.Tensor, eps: float, layer_scalar: float,
+               out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """(h + rms(rms(dense_out) w_post1 + rms(moe_out) w_post2) w_post) * layer_scalar, bf16 [T, H]."""
+    _need(h, "h", 2)
+    T, H = (int(v) for v in h.shape)
+    _need(dense_out, "dense_out", 2, (T, H))
+    _need(moe_out, "moe_out", 2, (T, H))
+    for t, n in ((w_post1, "w_post1"), (w_post2, "w_post2"), (w_post, "w_post")):
+        _need(t, n, 2, (H,))
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=h.device)
+    _check(lib().ff_combine(_ptr(h), _ptr(dense_out), _ptr(moe_out), T, H, _ptr(w_post1), _ptr(w_post2),
+                            _ptr(w_post), float(eps), float(layer_scalar), _ptr(out), _stream()))
+    return out
+
+
+@dataclass
+class FFParams:
+    """Device-resident weights of the feed-forward block (besides the MoE's)."""
+
+    pre_ff: torch.Tensor      # bf16 [H]  preFfNorm (dense branch)
+    pre_ff2: torch.Tensor     # bf16 [H]  preFfNorm2 (experts)
+    post_ff1: torch.Tensor    # bf16 [H]
+    post_ff2: torch.Tensor    # bf16 [H]
+    post_ff: torch.Tensor     # bf16 [H]
+    gate_up: TiledWeight      # [2 I_dense, H]: gate rows then up rows, tiled with split = I_dense
+    down: TiledWeight         # [H, I_dense], tiled with split = 0
+    layer_scalar: float
+
+    @classmethod
+    def from_rows(cls, pre_ff, pre_ff2, post_ff1, post_ff2, post_ff, gate: QuantWeight, up: QuantWeight,
+                  down: QuantWeight, layer_scalar: float) -> "FFParams":
+        """Stacks gate over up and tiles both linears (once, when the layer is loaded)."""
+        if gate.rows != up.rows or gate.in_features != up.in_features:
+            raise ValueError("gate and up must have the same shape")
+        fused = QuantWeight(torch.cat([gate.w, up.w], dim=-2).contiguous(),
+                            torch.cat([gate.scales, up.scales], dim=-2).contiguous(),
+                            torch.cat([gate.biases, up.biases], dim=-2).contiguous())
+        return cls(pre_ff, pre_ff2, post_ff1, post_ff2, post_ff, fused.tiled(gate.rows), down.tiled(0),
+                   float(layer_scalar))
+
+
+def ff_block(h: torch.Tensor, moe: MoEParams, ff: FFParams, k: int, eps: float, deterministic: int = 1):
+    """The feed-forward half of a decoder layer: returns (out bf16 [T, H], indices, weights)."""
+    xa, xb = ff_prenorm(h, ff.pre_ff, ff.pre_ff2, eps)
+    dense = qlinear(qlinear_geglu(xa, ff.gate_up), ff.down)
+    y, idx, w, _, _, _ = moe_layer(h, xb, moe, k, eps, deterministic)
+    out = ff_combine(h, dense, y, ff.post_ff1, ff.post_ff2, ff.post_ff, eps, ff.layer_scalar)
+    return out, idx, w

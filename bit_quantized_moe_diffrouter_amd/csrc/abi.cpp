@@ -322,4 +322,65 @@ int qlinear(const uint16_t* x, int32_t M, const qmoe_qweight* W, uint16_t* y, hi
   return launched(qmoe::launch_dense(a, ncu, stream), "qlinear");
 }
 
+int qlinear_geglu(const uint16_t* x, int32_t M, const qmoe_qweight* W, uint16_t* y, hipStream_t stream) {
+  REQUIRE(M >= 0, QMOE_ERR_INVALID, "qlinear_geglu: M=%d < 0", M);
+  REQUIRE(W != nullptr, QMOE_ERR_INVALID, "qlinear_geglu: null weight descriptor");
+  const int K = W->in, N = W->split;
+  REQUIRE(K > 0 && K % 64 == 0, QMOE_ERR_INVALID, "qlinear_geglu: K=%d must be a positive multiple of 64", K);
+  REQUIRE(N > 0 && N % 64 == 0, QMOE_ERR_INVALID, "qlinear_geglu: split=%d must be a positive multiple of 64", N);
+  if (int rc = check_qweight(W, "qlinear_geglu W", 1, 2 * N, K, QMOE_LAYOUT_TILED, N)) return rc;
+  if (M == 0) return ok();
+  REQUIRE_PTR(x, 16, "qlinear_geglu x");
+  REQUIRE_PTR(y, 16, "qlinear_geglu y");
+  REQUIRE((long long)M * K * 2 < (1LL << 32), QMOE_ERR_UNSUPPORTED, "qlinear_geglu: activation bytes reach 2^32");
+  int ncu = 0;
+  if (int rc = num_cu_current(&ncu)) return rc;
+  qmoe::SwitchArgs a{};
+  a.a = x;
+  a.w = W->w;
+  a.nblk = qmoe::tiled_blocks(2 * N, N);
+  a.out = y;
+  a.K = K;
+  a.Nout = N;
+  a.E = 1;
+  a.ktop = 1;
+  a.rows_total = M;
+  return launched(qmoe::launch_dense_geglu(a, ncu, stream), "qlinear_geglu");
+}
+
+int ff_prenorm(const uint16_t* h, int32_t T, int32_t H, const uint16_t* w_dense, const uint16_t* w_moe, float eps,
+               uint16_t* x_dense, uint16_t* x_moe, hipStream_t stream) {
+  REQUIRE(T >= 0, QMOE_ERR_INVALID, "ff_prenorm: T=%d < 0", T);
+  REQUIRE(H > 0 && H % 8 == 0, QMOE_ERR_INVALID, "ff_prenorm: H=%d must be a positive multiple of 8", H);
+  REQUIRE(std::isfinite(eps) && eps >= 0.f, QMOE_ERR_INVALID, "ff_prenorm: eps must be finite and >= 0");
+  if (T == 0) return ok();
+  REQUIRE_PTR(h, 16, "ff_prenorm h");
+  REQUIRE_PTR(w_dense, 16, "ff_prenorm w_dense");
+  REQUIRE_PTR(w_moe, 16, "ff_prenorm w_moe");
+  REQUIRE_PTR(x_dense, 16, "ff_prenorm x_dense");
+  REQUIRE_PTR(x_moe, 16, "ff_prenorm x_moe");
+  REQUIRE(T <= (1 << 30) / 4, QMOE_ERR_UNSUPPORTED, "ff_prenorm: T=%d too large", T);
+  return launched(qmoe::launch_ff_prenorm(h, T, H, w_dense, w_moe, eps, x_dense, x_moe, stream), "ff_prenorm");
+}
+
+int ff_combine(const uint16_t* h, const uint16_t* dense_out, const uint16_t* moe_out, int32_t T, int32_t H,
+               const uint16_t* w_post1, const uint16_t* w_post2, const uint16_t* w_post, float eps,
+               float layer_scalar, uint16_t* out, hipStream_t stream) {
+  REQUIRE(T >= 0, QMOE_ERR_INVALID, "ff_combine: T=%d < 0", T);
+  REQUIRE(H > 0 && H % 8 == 0, QMOE_ERR_INVALID, "ff_combine: H=%d must be a positive multiple of 8", H);
+  REQUIRE(std::isfinite(eps) && eps >= 0.f, QMOE_ERR_INVALID, "ff_combine: eps must be finite and >= 0");
+  if (T == 0) return ok();
+  REQUIRE_PTR(h, 16, "ff_combine h");
+  REQUIRE_PTR(dense_out, 16, "ff_combine dense_out");
+  REQUIRE_PTR(moe_out, 16, "ff_combine moe_out");
+  REQUIRE_PTR(w_post1, 16, "ff_combine w_post1");
+  REQUIRE_PTR(w_post2, 16, "ff_combine w_post2");
+  REQUIRE_PTR(w_post, 16, "ff_combine w_post");
+  REQUIRE_PTR(out, 16, "ff_combine out");
+  REQUIRE(T <= (1 << 30) / 4, QMOE_ERR_UNSUPPORTED, "ff_combine: T=%d too large", T);
+  return launched(qmoe::launch_ff_combine(h, dense_out, moe_out, T, H, w_post1, w_post2, w_post, eps, layer_scalar,
+                                          out, stream),
+                  "ff_combine");
+}
+
 }  // extern "C"

@@ -64,6 +64,18 @@ struct SwitchArgs {
 hipError_t launch_gate_up_geglu(SwitchArgs a, int num_cu, hipStream_t stream);
 hipError_t launch_down(SwitchArgs a, int num_cu, hipStream_t stream);
 hipError_t launch_dense(SwitchArgs a, int num_cu, hipStream_t stream);
+// dense rows against a fused gate|up weight (tiled with split = Nout), GeGLU,
+// row-major bf16 [rows_total, Nout] out
+hipError_t launch_dense_geglu(SwitchArgs a, int num_cu, hipStream_t stream);
 hipError_t launch_combine(const uint16_t* D, const float* w, int T, int k, int H, uint16_t* y, hipStream_t stream);
+
+// ---------------------------------------------------------------- feed-forward block norms
+// xa = rms(h) * wa, xb = rms(h) * wb (bf16 [T, H] each, H % 8 == 0)
+hipError_t launch_ff_prenorm(const uint16_t* h, int T, int H, const uint16_t* wa, const uint16_t* wb, float eps,
+                             uint16_t* xa, uint16_t* xb, hipStream_t stream);
+// out = (res + rms(rms(h1) w1 + rms(h2) w2) w) * scalar (bf16 [T, H], H % 8 == 0)
+hipError_t launch_ff_combine(const uint16_t* res, const uint16_t* h1, const uint16_t* h2, int T, int H,
+                             const uint16_t* w1, const uint16_t* w2, const uint16_t* w, float eps, float scalar,
+                             uint16_t* out, hipStream_t stream);
 
 }  // namespace qmoe

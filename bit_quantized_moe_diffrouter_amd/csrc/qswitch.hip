@@ -47,7 +47,10 @@
 
 namespace qmoe {
 
-enum : int { MODE_GATE_UP = 0, MODE_DOWN = 1, MODE_DENSE = 2 };
+// gate_up + GeGLU and down over sorted expert rows; the dense linear; the
+// dense linear with a fused gate|up weight and the GeGLU (the decoder's dense
+// MLP branch, first half)
+enum : int { MODE_GATE_UP = 0, MODE_DOWN = 1, MODE_DENSE = 2, MODE_DENSE_GEGLU = 3 };
 
 namespace {
 
@@ -115,6 +118,7 @@ template <int MODE, int KS, int D>
 __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
   static_assert(KS == 1 || (KS == 2 && MODE == MODE_GATE_UP), "the K-split pair is for the gate_up pass");
   constexpr int MT = kMT;
+  constexpr bool kRows = MODE == MODE_DENSE || MODE == MODE_DENSE_GEGLU;  // plain rows 0..M-1, no buckets
   extern __shared__ __attribute__((aligned(16))) uint8_t qmm_lds[];  // kWaveLds bytes per wave
   __shared__ int s_cum2[kMaxBuckets + 1];  // prefix per bucket of its two-tile chunks
   __shared__ int s_cum1[kMaxBuckets + 1];  // prefix per bucket of its one-tile chunk (0 or 1)
@@ -141,7 +145,7 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
   // blocks minor.
   const int nb = (MODE == MODE_DOWN) ? p.E + 1 : p.E;
   int total2, total1;
-  if constexpr (MODE == MODE_DENSE) {
+  if constexpr (kRows) {
     const int rem = A % kBM;
     total2 = A / kBM + (rem > 16 ? 1 : 0);
     total1 = (rem > 0 && rem <= 16) ? 1 : 0;
@@ -210,7 +214,7 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
     Item it;
     const int chunk = item / p.nblk;
     it.blk = item - chunk * p.nblk;
-    if constexpr (MODE == MODE_DENSE) {
+    if constexpr (kRows) {
       it.e = 0;
       it.zero = 0;
       it.r0 = chunk * kBM;  // the only possible one-tile chunk is the last one
@@ -242,7 +246,7 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
   // activation tile of row tile m of an item (switch modes); a tile past the
   // buffers (inconsistent offsets) reads tile 0 and is never stored
   auto tile_of = [&](const Item& it, int m) __attribute__((always_inline)) {
-    if constexpr (MODE == MODE_DENSE) {
+    if constexpr (kRows) {
       return 0;
     } else {
       if (it.zero) return 0;
@@ -326,7 +330,7 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
   auto issue_w = [&](Slot<MT>& sl, int g) __attribute__((always_inline)) {
     const uint8_t* u = l_wbase + (size_t)g * kTiledUnit;
     auto ld = [](const uint8_t* a) __attribute__((always_inline)) {
-      if constexpr (MODE == MODE_GATE_UP) return __builtin_nontemporal_load((const u32x4_t*)a);
+      if constexpr (MODE == MODE_GATE_UP || MODE == MODE_DENSE_GEGLU) return __builtin_nontemporal_load((const u32x4_t*)a);
       else return *(const u32x4_t*)a;
     };
 #pragma unroll
@@ -550,6 +554,32 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) *(u32x4_t*)(dst + h * 1024) = *(const u32x4_t*)(wlds + m * 2048 + h * 1024 + lane * 16);
       }
+    } else if constexpr (MODE == MODE_DENSE_GEGLU) {
+      // gate j and up j + 4 -> columns 64 blk + 16 j .. + 15 of the row-major
+      // output: bf16 [16 rows][64 columns] per row tile, a store covers 8 rows
+      uint16_t* const stg = (uint16_t*)wlds;
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        if (m > 0 && !t2) continue;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            stg[m * 1024 + (4 * lq + i) * 64 + 16 * j + ln] = f32_to_bf16_bits(gelu_tanh(acc[m][j][i]) * acc[m][j + 4][i]);
+      }
+      wave_lds_fence();
+      const int c = lane & 7;
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        if (m > 0 && !t2) continue;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          const int r = 8 * q + (lane >> 3), lr = 16 * m + r;
+          if (lr < cinfo.rows)
+            *(u32x4_t*)((uint16_t*)p.out + (size_t)(cinfo.r0 + lr) * p.Nout + blk * 64 + 8 * c) =
+                *(const u32x4_t*)(stg + m * 1024 + r * 64 + 8 * c);
+        }
+      }
     } else {
       // bf16 [16 rows][128 columns] per row tile; a store covers 4 rows
       uint16_t* const stg = (uint16_t*)wlds;
@@ -715,7 +745,7 @@ hipError_t launch_cfg(SwitchArgs a, int extra_buckets, int num_cu, hipStream_t s
   // per wave: staging; KS = 2: per pair, the partial sums of the second wave
   const size_t lds = (size_t)kWaves * kWaveLds + (KS == 2 ? (size_t)(kWaves / 2) * kMT * kNS * 64 * 16 : 0);
   long long chunks;
-  if (MODE == MODE_DENSE)
+  if (MODE == MODE_DENSE || MODE == MODE_DENSE_GEGLU)
     chunks = (a.rows_total + kBM - 1) / kBM;
   else
     chunks = (a.rows_total + kBM - 1) / kBM + (long long)std::min(a.E, a.rows_total) + extra_buckets;
@@ -751,6 +781,9 @@ hipError_t launch_down(SwitchArgs a, int num_cu, hipStream_t stream) {
 }
 hipError_t launch_dense(SwitchArgs a, int num_cu, hipStream_t stream) {
   return launch_mode<MODE_DENSE>(a, 0, num_cu, stream);
+}
+hipError_t launch_dense_geglu(SwitchArgs a, int num_cu, hipStream_t stream) {
+  return launch_mode<MODE_DENSE_GEGLU>(a, 0, num_cu, stream);
 }
 hipError_t launch_combine(const uint16_t* D, const float* w, int T, int k, int H, uint16_t* y, hipStream_t stream) {
   const long long n = (long long)T * (H / 8);

@@ -14,6 +14,10 @@
  *   qswitch_gate_up_geglu fused gate_up switch linear, split, GeGLU
  *   qswitch_down_combine  down switch linear + weighted sum over k per token
  *   qlinear               dense 4-bit linear
+ *   ff_prenorm, qlinear_geglu, ff_combine
+ *                         the decoder's feed-forward block around the MoE
+ *                         (pre-norms, dense GeGLU branch, post-norms and
+ *                         residual)
  *
  * Conventions shared by every call
  * --------------------------------
@@ -264,6 +268,69 @@ int qswitch_down_combine(const void* mid, int32_t T, int32_t k, int32_t I,
  * ---------------------------------------------------------------------- */
 int qlinear(const uint16_t* x, int32_t M, const qmoe_qweight* W, uint16_t* y,
             hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * The decoder's feed-forward block around the MoE (model.ts page,
+ * DiffDecoderLayer.forwardWith, after the attention residual):
+ *
+ *   h1  = postFfNorm1(mlp(preFfNorm(h)))           dense GeGLU branch
+ *   h2  = postFfNorm2(experts(preFfNorm2(h)))      the MoE layer above; the
+ *                                                  router (moe_route) takes
+ *                                                  the raw h
+ *   out = (h + postFfNorm(h1 + h2)) * layer_scalar
+ *
+ * mlp(x) = down(gelu_approx(gate . x) * (up . x)) with three 4-bit linears.
+ * Every norm is a plain RMSNorm, x / sqrt(mean(x^2) + eps) * w, the stored
+ * weight used as is (model.ts page, header note on the checkpoint: no 1 + w
+ * offset).  One block is
+ *   ff_prenorm -> qlinear_geglu -> qlinear (down)      dense branch
+ *   moe_route(h) -> moe_sort -> qswitch_gate_up_geglu -> qswitch_down_combine
+ *   ff_combine
+ * with bf16 tensors between the calls and fp32 arithmetic inside each.
+ * ---------------------------------------------------------------------- */
+
+/* ff_prenorm -- both pre-norms of the block from one read of h:
+ *   x_dense = rms(h) * w_dense   (preFfNorm),  x_moe = rms(h) * w_moe
+ *   (preFfNorm2),  rms(h) = 1 / sqrt(mean over H of h^2 + eps)
+ *
+ *   h                bf16 [T, H]; H % 8 == 0
+ *   w_dense, w_moe   bf16 [H]
+ *   x_dense, x_moe   bf16 [T, H] (out); must not overlap h
+ * Every pointer here is 16-byte aligned.  eps >= 0 (an all-zero row with
+ * eps = 0 gives NaN, as the formula does). */
+int ff_prenorm(const uint16_t* h, int32_t T, int32_t H, const uint16_t* w_dense,
+               const uint16_t* w_moe, float eps, uint16_t* x_dense, uint16_t* x_moe,
+               hipStream_t stream);
+
+/* qlinear_geglu -- the first half of the dense branch: gate and up
+ * QuantizedLinears in one pass over the fused weight [gate; up] and the GeGLU
+ * (model.ts page, DiffDecoderLayer's mlp; gelu_approx(gate) * up as in the
+ * vision.ts page, DiffVisionMLP):
+ *   y[m, i] = gelu_tanh(g) * u,  g = x[m] . dequant(gate)[i],
+ *                                u = x[m] . dequant(up)[i]   (fp32 accumulate)
+ *
+ *   x        bf16 [M, K]
+ *   W        experts = 1, rows = 2N, in = K (rows 0..N-1 gate, N..2N-1 up);
+ *            K % 64 == 0, N % 64 == 0; layout QMOE_LAYOUT_TILED with split = N
+ *   y (out)  bf16 [M, N]
+ * The down projection is qlinear on y. */
+int qlinear_geglu(const uint16_t* x, int32_t M, const qmoe_qweight* W, uint16_t* y,
+                  hipStream_t stream);
+
+/* ff_combine -- the post-norms, the residual add and the layer scalar:
+ *   s   = rms(dense_out) * w_post1 + rms(moe_out) * w_post2
+ *   out = (h + rms(s) * w_post) * layer_scalar
+ *
+ *   h                 bf16 [T, H] residual (the block's input); H % 8 == 0
+ *   dense_out         bf16 [T, H] the dense branch before postFfNorm1
+ *   moe_out           bf16 [T, H] the experts' output before postFfNorm2
+ *   w_post1, w_post2, w_post   bf16 [H]
+ *   out (out)         bf16 [T, H]; must not overlap the inputs
+ * Every pointer here is 16-byte aligned; eps as in ff_prenorm. */
+int ff_combine(const uint16_t* h, const uint16_t* dense_out, const uint16_t* moe_out, int32_t T,
+               int32_t H, const uint16_t* w_post1, const uint16_t* w_post2,
+               const uint16_t* w_post, float eps, float layer_scalar, uint16_t* out,
+               hipStream_t stream);
 
 #ifdef __cplusplus
 }

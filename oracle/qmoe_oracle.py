@@ -368,16 +368,21 @@ def rms_norm(x, weight_bits, eps: float) -> np.ndarray:
     return rms_norm_noscale(_as_f64(x), eps) * bf16_to_f64(weight_bits)
 
 
-def dense_geglu_mlp(x, gate, up, down, rows: Optional[Sequence[int]] = None) -> np.ndarray:
-    """The dense branch ``down(gelu_tanh(gate . x) * (up . x))`` with three 4-bit
-    linears, fp64 ([model page] DiffDecoderLayer's GegluMLP, the same shape as
-    SelfConditioning's down(geglu(gate(.), up(.))); GeGLU as in the experts)."""
+def dense_geglu(x, gate, up, rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    """First half of the dense branch, ``gelu_tanh(gate . x) * (up . x)``, fp64."""
     x = _as_f64(x)
     if rows is not None:
         x = x[list(rows)]
     g = x @ dequantize(gate.w, gate.scales, gate.biases).T
     u = x @ dequantize(up.w, up.scales, up.biases).T
-    return (gelu_tanh(g) * u) @ dequantize(down.w, down.scales, down.biases).T
+    return gelu_tanh(g) * u
+
+
+def dense_geglu_mlp(x, gate, up, down, rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    """The dense branch ``down(gelu_tanh(gate . x) * (up . x))`` with three 4-bit
+    linears, fp64 ([model page] DiffDecoderLayer's GegluMLP, the same shape as
+    SelfConditioning's down(geglu(gate(.), up(.))); GeGLU as in the experts)."""
+    return dense_geglu(x, gate, up, rows) @ dequantize(down.w, down.scales, down.biases).T
 
 
 def ff_block(h_bits, moe_weights, ffw, k: int, I: int, eps: float,

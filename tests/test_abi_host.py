@@ -29,7 +29,7 @@ def header_functions():
 def test_exports_every_declared_function(L):
     names = header_functions()
     assert set(names) >= {"moe_route", "moe_sort", "qswitch_gate_up_geglu", "qswitch_down_combine",
-                          "qlinear", "qmoe_last_error"}
+                          "qlinear", "qmoe_last_error", "ff_prenorm", "qlinear_geglu", "ff_combine"}
     for n in names:
         assert hasattr(L, n), f"{n} is declared in qmoe.h but not exported"
 
@@ -148,6 +148,49 @@ def test_qlinear_validation(L):
     bad = qw(1, 1152, 1152, layout=0)
     assert L.qlinear(A16, 8, ctypes.byref(bad), A16, None) == INVALID
     assert L.qlinear(A16, 8, None, A16, None) == INVALID
+
+
+def test_qlinear_geglu_validation(L):
+    d = qw(1, 2 * 192, 256, layout=1, split=192)
+    assert L.qlinear_geglu(None, 0, ctypes.byref(d), None, None) == 0
+    assert L.qlinear_geglu(A16, -1, ctypes.byref(d), A16, None) == INVALID
+    for bad in (qw(1, 2 * 192, 256, layout=1, split=0),      # not tiled as a fused pair
+                qw(1, 2 * 192, 256, layout=1, split=128),    # rows != 2 * split
+                qw(1, 2 * 160, 256, layout=1, split=160),    # split not a multiple of 64
+                qw(1, 2 * 192, 200, layout=1, split=192),    # K not a multiple of 64
+                qw(2, 2 * 192, 256, layout=1, split=192),    # not dense
+                qw(1, 2 * 192, 256, layout=0, split=192)):   # row-major codes
+        assert L.qlinear_geglu(A16, 8, ctypes.byref(bad), A16, None) == INVALID, err(L)
+    assert L.qlinear_geglu(A16 + 8, 8, ctypes.byref(d), A16, None) == INVALID
+    assert "aligned" in err(L)
+    assert L.qlinear_geglu(A16, 8, ctypes.byref(d), None, None) == INVALID
+    assert L.qlinear_geglu(A16, 8, ctypes.byref(qw(1, 384, 256, bits=8, layout=1, split=192)), A16,
+                           None) == UNSUPPORTED
+
+
+def test_ff_norm_validation(L):
+    f = ctypes.c_float
+    pre = lambda T=4, H=256, h=A16, wa=A16, wb=A16, eps=1e-6, xa=A16, xb=A16: L.ff_prenorm(
+        h, T, H, wa, wb, f(eps), xa, xb, None)
+    assert pre(T=0, h=None) == 0
+    assert pre(T=-1) == INVALID
+    assert pre(H=252) == INVALID
+    assert "multiple of 8" in err(L)
+    assert pre(eps=-1.0) == INVALID
+    assert pre(eps=float("nan")) == INVALID
+    assert pre(h=None) == INVALID
+    assert pre(wb=A16 + 2) == INVALID
+    assert pre(xa=None) == INVALID
+
+    comb = lambda T=4, H=256, h=A16, d=A16, m=A16, w1=A16, w2=A16, w=A16, eps=1e-6, out=A16: L.ff_combine(
+        h, d, m, T, H, w1, w2, w, f(eps), f(1.0), out, None)
+    assert comb(T=0, h=None, out=None) == 0
+    assert comb(T=-3) == INVALID
+    assert comb(H=0) == INVALID
+    assert comb(eps=float("inf")) == INVALID
+    assert comb(m=None) == INVALID
+    assert comb(w2=A16 + 4) == INVALID
+    assert comb(out=None) == INVALID
 
 
 def test_route_rejects_tiled_proj(L):

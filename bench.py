@@ -16,6 +16,9 @@ Prints ONE JSON line (rank 0):
              second pass of K steps (events between kernels add a few
              microseconds of idle time per call, so they stay out of `value`)
   cpu_baseline  the CPU oracle timed on this host on a bounded sample
+  ff_block   diagnostic, not the metric: the decoder's feed-forward block
+             around the same MoE layer (pre-norms, dense GeGLU branch, the
+             layer, post-norms and residual) on the same tokens
 
 Two helper modes serve the committed profiles (see profiles/):
   --copy-probe        one plain 256 MiB device copy, five times (the known-size
@@ -57,6 +60,7 @@ def parse():
                     help="diagnostic override; the reported line is defined on the canvas workload")
     ap.add_argument("--weight-sets", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ff-block", action="store_true", help="skip the feed-forward block diagnostic")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--summarize", metavar="DIR")
@@ -188,6 +192,76 @@ def cpu_baseline(cfg, inp, seconds):
     return {"value": cfg.T / t, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"full {cfg.T}-token layer (route + grouped fp32 experts), {len(times)} run(s), "
                       f"median {t:.2f} s; host has {os.cpu_count()} logical CPUs"}
+
+
+def ff_block_timing(q, torch, synth, ffc, h, sets, K, warmup, t, buf):
+    """Diagnostic: the decoder's whole feed-forward block around the MoE
+    (ff_prenorm, qlinear_geglu, qlinear, the four MoE calls, ff_combine) on the
+    same tokens, K blocks with HIP events between the calls.  The dense
+    branch's weights are cloned to 32 distinct buffers (about 290 MB) and
+    rotated with the MoE weight sets, so neither is served from the Infinity
+    Cache of the previous block."""
+    import dataclasses
+    cfg, Id = ffc.moe, ffc.I_dense
+    T, H, k, E, I = cfg.T, cfg.H, cfg.k, cfg.E, cfg.I
+    fw = synth.make_ff_weights(ffc)
+    qw = lambda m: q.QuantWeight(t(m.w), t(m.scales), t(m.biases))
+    base = q.FFParams.from_rows(t(fw.pre_ff), t(fw.pre_ff2), t(fw.post_ff1), t(fw.post_ff2), t(fw.post_ff),
+                                qw(fw.gate), qw(fw.up), qw(fw.down), fw.layer_scalar)
+    reps = [dataclasses.replace(base, gate_up=dataclasses.replace(base.gate_up, buf=base.gate_up.buf.clone()),
+                                down=dataclasses.replace(base.down, buf=base.down.buf.clone()))
+            for _ in range(32)]
+    dev = h.device
+    xa = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    xb = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    gmid = torch.empty((T, Id), dtype=torch.bfloat16, device=dev)
+    dense = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    b = buf
+
+    def block(i, ev=None):
+        p, f = sets[i % len(sets)], reps[i % len(reps)]
+        mark = (lambda j: ev[j].record()) if ev is not None else (lambda j: None)
+        mark(0)
+        q.ff_prenorm(h, f.pre_ff, f.pre_ff2, cfg.eps, xa, xb)
+        mark(1)
+        q.qlinear_geglu(xa, f.gate_up, gmid)
+        mark(2)
+        q.qlinear(gmid, f.down, dense)
+        mark(3)
+        q.moe_route(h, p.norm_scale, cfg.eps, p.router, p.per_expert_scale, k, p.logit_bias,
+                    indices=b["idx"], weights=b["wts"], workspace=b["ws_r"])
+        q.moe_sort(b["idx"], E, b["off"], b["sa"])
+        q.qswitch_gate_up_geglu(xb, p.gate_up, I, k, b["off"], b["sa"], mid=b["mid"])
+        q.qswitch_down_combine(b["mid"], T, k, p.down, b["wts"], b["off"], b["sa"], y=b["y"],
+                               workspace=b["ws_d"], deterministic=1)
+        mark(4)
+        q.ff_combine(h, dense, b["y"], f.post_ff1, f.post_ff2, f.post_ff, cfg.eps, f.layer_scalar, out)
+        mark(5)
+
+    for i in range(warmup):
+        block(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        block(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(K)]
+    for i in range(K):
+        block(i, evs[i])
+    torch.cuda.synchronize()
+    names = ["ff_prenorm", "qlinear_geglu", "qlinear_down", "moe_layer", "ff_combine"]
+    mean_us = {n: float(np.mean([ev[j].elapsed_time(ev[j + 1]) * 1e3 for ev in evs])) for j, n in enumerate(names)}
+    wgu = 2 * Id * (H // 2 + 4 * (H // 64))
+    wdn = H * (Id // 2 + 4 * (Id // 64))
+    geglu_alg = wgu + T * H * 2 + T * Id * 2
+    down_alg = wdn + T * Id * 2 + T * H * 2
+    return {"workload": ffc.name, "dense_intermediate": Id, "blocks": K,
+            "us_per_block": wall / K * 1e6, "tokens_per_s": T * K / wall, "call_mean_us": mean_us,
+            "qlinear_geglu_GBs": geglu_alg / (mean_us["qlinear_geglu"] * 1e-6) / 1e9,
+            "qlinear_down_GBs": down_alg / (mean_us["qlinear_down"] * 1e-6) / 1e9,
+            "dense_weight_bytes": wgu + wdn}
 
 
 def main():
@@ -325,6 +399,10 @@ def main():
                   "call_sum_us": float(sum(mean_us.values()))},
         "cpu_baseline": None,
     }
+    ffc = next((f for f in synth.FF_CONFIGS.values() if f.moe.name == cfg.name), None)
+    if ffc is not None and not args.no_ff_block:
+        out["ff_block"] = ff_block_timing(q, torch, synth, ffc, x, sets, K, args.warmup, t,
+                                          dict(idx=idx, wts=wts, off=off, sa=sa, mid=mid, y=y, ws_r=ws_r, ws_d=ws_d))
     if not args.no_cpu_baseline:
         inp = synth.MoEInputs(cfg, x_host, host_first)
         out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)

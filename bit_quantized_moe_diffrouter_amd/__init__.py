@@ -341,14 +341,19 @@ def moe_layer(x_router: torch.Tensor, x_expert: torch.Tensor, p: MoEParams, k: i
 # ----------------------------------------------------------------------------
 # the decoder's feed-forward block around the MoE
 # ----------------------------------------------------------------------------
-def ff_prenorm(h: torch.Tensor, w_dense: torch.Tensor, w_moe: torch.Tensor, eps: float):
+def ff_prenorm(h: torch.Tensor, w_dense: torch.Tensor, w_moe: torch.Tensor, eps: float,
+               xa: Optional[torch.Tensor] = None, xb: Optional[torch.Tensor] = None):
     """Both pre-norms from one read of h: returns (rms(h) * w_dense, rms(h) * w_moe), bf16 [T, H]."""
     _need(h, "h", 2)
     T, H = (int(v) for v in h.shape)
     _need(w_dense, "w_dense", 2, (H,))
     _need(w_moe, "w_moe", 2, (H,))
-    xa = torch.empty((T, H), dtype=torch.bfloat16, device=h.device)
-    xb = torch.empty((T, H), dtype=torch.bfloat16, device=h.device)
+    if xa is None:
+        xa = torch.empty((T, H), dtype=torch.bfloat16, device=h.device)
+    if xb is None:
+        xb = torch.empty((T, H), dtype=torch.bfloat16, device=h.device)
+    _need(xa, "xa", 2, (T, H))
+    _need(xb, "xb", 2, (T, H))
     _check(lib().ff_prenorm(_ptr(h), T, H, _ptr(w_dense), _ptr(w_moe), float(eps), _ptr(xa), _ptr(xb), _stream()))
     return xa, xb
 
@@ -377,6 +382,7 @@ def ff_combine(h: torch.Tensor, dense_out: torch.Tensor, moe_out: torch.Tensor, 
         _need(t, n, 2, (H,))
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=h.device)
+    _need(out, "out", 2, (T, H))
     _check(lib().ff_combine(_ptr(h), _ptr(dense_out), _ptr(moe_out), T, H, _ptr(w_post1), _ptr(w_post2),
                             _ptr(w_post), float(eps), float(layer_scalar), _ptr(out), _stream()))
     return out

@@ -61,7 +61,12 @@ constexpr int kMaxBuckets = 257;   // experts (<= 256) + the dropped bucket of t
 constexpr int kNS = 8;             // 16-row subtiles per tiled block
 constexpr int kXcds = 8;           // accelerator dies; workgroup b runs on die b % 8
 constexpr int kMT = 2;             // row tiles held per slot and accumulator set
-constexpr int kWaveLds = kMT * 16 * 128 * 2;  // LDS per wave: two 16-row tiles of 128 bf16 columns
+// LDS per wave: staging of two 16-row tiles, 64 bf16 columns wide (activation
+// rows in; gate_up and dense GeGLU outputs) or 128 wide (down and dense outputs)
+constexpr int wave_lds_bytes(int mode) {
+  return (mode == MODE_DOWN || mode == MODE_DENSE) ? kMT * 16 * 128 * 2 : kMT * 16 * 64 * 2;
+}
+constexpr int kRedBytes = kMT * kNS * 64 * 16;  // one wave's fp32 accumulators (K-split hand-over)
 
 struct Item {
   int e;     // expert whose weights are used (0 for the dropped bucket)
@@ -107,19 +112,22 @@ __device__ __forceinline__ void run_steps(F& f, std::integer_sequence<int, I...>
 
 // Work items and workers.  An item is (chunk of up to 32 sorted rows of one
 // bucket, one 128-row weight block) over the whole contraction.  A worker is
-// one wave (KS = 1) or a pair of waves of one workgroup that split the
-// contraction in two (KS = 2); every worker walks its own items, so after the
-// prologue no wave waits for another except a pair's partner.  A wave streams
-// its part of the block's units (contiguous in HBM) through a register ring
-// that runs on across its items, computes every row tile of the chunk from one
-// unpacking of the weights, and at the item's end writes the outputs itself
-// (KS = 2: the second wave hands its partial sums to the first through LDS).
+// one wave (KS = 1) or KS = 2 or 4 waves of one workgroup that split the
+// contraction into KS contiguous parts; every worker walks its own items, so
+// after the prologue no wave waits for another except within its worker.  A
+// wave streams its part of the block's units (contiguous in HBM) through a
+// register ring that runs on across its items, computes every row tile of the
+// chunk from one unpacking of the weights, and at the item's end the worker's
+// first wave writes the outputs (KS > 1: the other waves hand it their
+// partial sums through LDS, which it adds in contraction order).
 template <int MODE, int KS, int D>
 __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
-  static_assert(KS == 1 || (KS == 2 && MODE == MODE_GATE_UP), "the K-split pair is for the gate_up pass");
+  static_assert(KS == 1 || KS == 2 || KS == 4, "a worker is 1, 2 or 4 waves");
+  constexpr int kWaveLds = wave_lds_bytes(MODE);
   constexpr int MT = kMT;
   constexpr bool kRows = MODE == MODE_DENSE || MODE == MODE_DENSE_GEGLU;  // plain rows 0..M-1, no buckets
-  extern __shared__ __attribute__((aligned(16))) uint8_t qmm_lds[];  // kWaveLds bytes per wave
+  // kWaveLds bytes per wave, then (KS > 1) kRedBytes per wave that is not the first of its worker
+  extern __shared__ __attribute__((aligned(16))) uint8_t qmm_lds[];
   __shared__ int s_cum2[kMaxBuckets + 1];  // prefix per bucket of its two-tile chunks
   __shared__ int s_cum1[kMaxBuckets + 1];  // prefix per bucket of its one-tile chunk (0 or 1)
   __shared__ int s_lo[kMaxBuckets];       // clamped segment [lo, hi) of each bucket
@@ -131,7 +139,9 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
   // D <= min(2, G) slots it enters item c + 2 at the earliest during item c's
   // last step (when G <= D), never item c + 4 before item c is finished.
   __shared__ int s_dst[kWaves][4][kBM];
-  __shared__ int s_flag[kWaves / 2][2];    // KS = 2: items of each pair produced by its second wave, consumed by its first
+  // KS > 1, per wave that is not the first of its worker: items whose partial
+  // sums it has handed over [0], and the first wave has taken [1]
+  __shared__ int s_flag[kWaves][2];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar branches below)
@@ -149,6 +159,10 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
     const int rem = A % kBM;
     total2 = A / kBM + (rem > 16 ? 1 : 0);
     total1 = (rem > 0 && rem <= 16) ? 1 : 0;
+    if constexpr (KS > 1) {
+      if (tid < 2 * kWaves) (&s_flag[0][0])[tid] = 0;
+      __syncthreads();  // the only workgroup barrier of these modes
+    }
   } else {
     // bucket b < E is expert b's segment; bucket E (down only) holds the dropped rows
     auto counts_of = [&](int b, int& one, int& tl) __attribute__((always_inline)) {
@@ -182,7 +196,7 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
       s_cum2[0] = 0;
       s_cum1[0] = 0;
     }
-    if (tid < kWaves) (&s_flag[0][0])[tid] = 0;
+    if (tid < 2 * kWaves) (&s_flag[0][0])[tid] = 0;
     __syncthreads();  // the last workgroup barrier: from here on every worker runs on its own
   }
   total2 = __builtin_amdgcn_readfirstlane(total2);
@@ -199,7 +213,7 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
   const int grid = (int)gridDim.x, b = (int)blockIdx.x;
   const int pos = (grid % kXcds == 0) ? (b % kXcds) * (grid / kXcds) + b / kXcds : b;
   constexpr int kWorkers = kWaves / KS;     // workers per workgroup
-  const int worker = wave / KS, kp = wave % KS;  // kp: this wave's half of the contraction (KS = 2)
+  const int worker = wave / KS, kp = wave % KS;  // kp: this wave's part of the contraction
   const int gk0 = kp * G / KS, gk1 = (kp + 1) * G / KS;  // groups [gk0, gk1) of this wave
   const int nslots = grid * kWorkers;
   const int slot = ((worker + pos) & (kWorkers - 1)) * grid + pos;
@@ -482,7 +496,7 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
     }
   };
 
-  // Bounded wait on a pair flag: a protocol slip cannot hang the GPU (after
+  // Bounded wait on a hand-over flag: a protocol slip cannot hang the GPU (after
   // about 10^8 cycles the wave goes on, with wrong results).
   auto pair_wait = [&](int* f, int v) __attribute__((always_inline)) {
     for (int it = 0; it < (1 << 21); ++it) {
@@ -497,39 +511,43 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
   auto finish_item = [&]() __attribute__((always_inline)) {
     const bool t2 = cinfo.rows > 16;
     const int blk = cinfo.blk;
-    if constexpr (KS == 2) {
-      // The second wave of the pair parks its partial sums for item c_j once
-      // the first has consumed item c_j - 1; the first adds them after its own
-      // (K order) and writes the outputs.
-      f32x4_t* const red = (f32x4_t*)(qmm_lds + kWaves * kWaveLds) + worker * (MT * kNS * 64);
-      int* const produced = &s_flag[worker][0];
-      int* const consumed = &s_flag[worker][1];
-      if (kp == 1) {
-        pair_wait(consumed, c_j);
+    if constexpr (KS > 1) {
+      // Every other wave of the worker parks its partial sums for item c_j
+      // once the first has taken its sums of item c_j - 1; the first adds them
+      // after its own in contraction order (kp = 1, 2, ...) and writes the
+      // outputs.
+      f32x4_t* const red0 = (f32x4_t*)(qmm_lds + kWaves * kWaveLds) + worker * (KS - 1) * (MT * kNS * 64);
+      if (kp != 0) {
+        f32x4_t* const red = red0 + (kp - 1) * (MT * kNS * 64);
+        pair_wait(&s_flag[wave][1], c_j);
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
           if (m > 0 && !t2) continue;
 #pragma unroll
           for (int j = 0; j < kNS; ++j) red[(m * kNS + j) * 64 + lane] = acc[m][j];
         }
-        __hip_atomic_store(produced, c_j + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        __hip_atomic_store(&s_flag[wave][0], c_j + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
       } else {
-        pair_wait(produced, c_j + 1);
+#pragma unroll 1
+        for (int q = 1; q < KS; ++q) {  // kept a loop: unrolled, the LDS reads of all parts would be hoisted
+          const f32x4_t* const red = red0 + (q - 1) * (MT * kNS * 64);
+          pair_wait(&s_flag[wave + q][0], c_j + 1);
 #pragma unroll
-        for (int m = 0; m < MT; ++m) {
-          if (m > 0 && !t2) continue;
+          for (int m = 0; m < MT; ++m) {
+            if (m > 0 && !t2) continue;
 #pragma unroll
-          for (int j = 0; j < kNS; ++j) {
-            const f32x4_t o = red[(m * kNS + j) * 64 + lane];
+            for (int j = 0; j < kNS; ++j) {
+              const f32x4_t o = red[(m * kNS + j) * 64 + lane];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[m][j][i] += o[i];
+              for (int i = 0; i < 4; ++i) acc[m][j][i] += o[i];
+            }
           }
+          __hip_atomic_store(&s_flag[wave + q][1], c_j + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
         }
-        __hip_atomic_store(consumed, c_j + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
       }
     }
     if (kp != 0) {
-      // second wave of a pair: no outputs
+      // not the first wave of its worker: no outputs
     } else if constexpr (MODE == MODE_GATE_UP) {
       // gate j and up j + 4 -> columns 16 j .. 16 j + 15 of group blk of the
       // activation tiles: column 16 q + 8 h + i of tile row r sits at byte
@@ -739,17 +757,25 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 // ------------------------------------------------------------------ launchers
 namespace {
 
+// Items a launch can hold (every one of the A rows in its own bucket's
+// chunks, at most one partial chunk per bucket).
+template <int MODE>
+long long max_items(const SwitchArgs& a, int extra_buckets) {
+  long long chunks = (a.rows_total + kBM - 1) / kBM;
+  if (MODE == MODE_GATE_UP || MODE == MODE_DOWN) chunks += (long long)std::min(a.E, a.rows_total) + extra_buckets;
+  return chunks * a.nblk;
+}
+
+template <int MODE, int KS>
+constexpr size_t lds_bytes() {
+  return (size_t)kWaves * wave_lds_bytes(MODE) + (size_t)(kWaves / KS) * (KS - 1) * kRedBytes;
+}
+
 template <int MODE, int KS, int D>
 hipError_t launch_cfg(SwitchArgs a, int extra_buckets, int num_cu, hipStream_t stream) {
   a.ntiles = a.nblk;
-  // per wave: staging; KS = 2: per pair, the partial sums of the second wave
-  const size_t lds = (size_t)kWaves * kWaveLds + (KS == 2 ? (size_t)(kWaves / 2) * kMT * kNS * 64 * 16 : 0);
-  long long chunks;
-  if (MODE == MODE_DENSE || MODE == MODE_DENSE_GEGLU)
-    chunks = (a.rows_total + kBM - 1) / kBM;
-  else
-    chunks = (a.rows_total + kBM - 1) / kBM + (long long)std::min(a.E, a.rows_total) + extra_buckets;
-  const long long items = chunks * a.nblk;
+  constexpr size_t lds = lds_bytes<MODE, KS>();
+  const long long items = max_items<MODE>(a, extra_buckets);
   long long grid = std::min(items, (long long)num_cu * 2);
   if (grid < 1) grid = 1;
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&qmm_kernel<MODE, KS, D>),
@@ -759,14 +785,35 @@ hipError_t launch_cfg(SwitchArgs a, int extra_buckets, int num_cu, hipStream_t s
   return hipGetLastError();
 }
 
-// gate_up with a long contraction (at least 8 groups) splits it over a wave
-// pair.  Ring depth: two slots, one when a wave's part of the contraction is a
-// single group (the down pass's row table relies on the load cursor never
-// reaching item c + 4 before item c is finished).
+// Contraction split.  The gate_up pass with at least 8 groups splits it in two
+// (its items then fill the chip at the canvas's 2048 rows).  A launch whose
+// items give fewer than one wave per SIMD (small batches, the dense linears
+// at a few hundred rows) splits it in two or four, as long as every wave keeps
+// at least two groups: a wave's loads in flight are bounded by its ring, so
+// fewer items need more waves per item to keep HBM busy.  Four-way splits of
+// the down and dense passes hold 86 KB of LDS per workgroup (one per CU), and
+// are taken only when the items fit one workgroup per CU.  Ring depth: two
+// slots, one when a wave's part of the contraction is a single group (the
+// down pass's row table relies on the load cursor never reaching item c + 4
+// before item c is finished).
+template <int MODE>
+int choose_ks(const SwitchArgs& a, int extra_buckets, int num_cu) {
+  const int G = a.K / 64;
+  const long long items = max_items<MODE>(a, extra_buckets);
+  const long long simds = 4LL * num_cu;
+  constexpr size_t kStaticLds = 8192;  // the kernel's own __shared__ arrays, rounded up
+  const bool four_fits = 2 * (lds_bytes<MODE, 4>() + kStaticLds) <= 160 * 1024 || items <= num_cu;
+  int ks = (MODE == MODE_GATE_UP && G >= 8) ? 2 : 1;
+  while (ks < 4 && items * ks < simds && G >= 4 * ks && (ks == 1 || four_fits)) ks *= 2;
+  return ks;
+}
+
 template <int MODE>
 hipError_t launch_mode(SwitchArgs a, int extra_buckets, int num_cu, hipStream_t stream) {
   const int G = a.K / 64;
-  if (MODE == MODE_GATE_UP && G >= 8) return launch_cfg<MODE, (MODE == MODE_GATE_UP) ? 2 : 1, 2>(a, extra_buckets, num_cu, stream);
+  const int ks = choose_ks<MODE>(a, extra_buckets, num_cu);
+  if (ks == 4) return launch_cfg<MODE, 4, 2>(a, extra_buckets, num_cu, stream);
+  if (ks == 2) return launch_cfg<MODE, 2, 2>(a, extra_buckets, num_cu, stream);
   if (G >= 2) return launch_cfg<MODE, 1, 2>(a, extra_buckets, num_cu, stream);
   return launch_cfg<MODE, 1, 1>(a, extra_buckets, num_cu, stream);
 }

@@ -112,23 +112,40 @@ def _pmc_per_dispatch(d, counter, match):
     return (sum(v) / len(v) if v else float("nan")), len(v)
 
 
-def summarize(d):
+def _kt_table(d, title, cmd, notes):
     import csv
     import glob
-    cmd_kt = ("rocprofv3 --kernel-trace --stats -d DIR/kt -o kt --output-format csv -- "
-              "python3 bench.py --steps 60 --warmup 10 --no-cpu-baseline")
-    stats = glob.glob(os.path.join(d, "kt", "**", "*kernel_stats.csv"), recursive=True)
-    lines = ["# Kernel durations, canvas workload (256 tokens, H 2816, 128 experts, top-8, I 704)", "",
-             "Command (from the repository root, TMPDIR=/tmp):", "", "    " + cmd_kt, "",
-             "rocprofv3 kernel-trace statistics; every dispatch of the run (warm-up, the timed",
-             "pass and the event pass).  qmm_kernel<0,...> is qswitch_gate_up_geglu,",
-             "qmm_kernel<1,...> the down switch linear of qswitch_down_combine.", "",
-             "| kernel | calls | average us | min us | max us | share |", "|---|---|---|---|---|---|"]
+    stats = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
+    lines = [f"# {title}", "", "Command (from the repository root, TMPDIR=/tmp):", "", "    " + cmd, ""] + notes + [
+        "", "| kernel | calls | average us | min us | max us | share |", "|---|---|---|---|---|---|"]
     for r in sorted(csv.DictReader(open(stats[0])), key=lambda r: -float(r["TotalDurationNs"])):
         lines.append(f"| `{r['Name'][:70]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |")
+    return lines
+
+
+def summarize(d):
+    import glob
+    kt = "rocprofv3 --kernel-trace --stats -d DIR/{d} -o kt --output-format csv -- python3 bench.py {a}"
+    lines = _kt_table(os.path.join(d, "kt"),
+                      "Kernel durations, canvas workload (256 tokens, H 2816, 128 experts, top-8, I 704)",
+                      kt.format(d="kt", a="--steps 60 --warmup 10 --no-cpu-baseline --no-ff-block"),
+                      ["rocprofv3 kernel-trace statistics; every dispatch of the run (warm-up, the timed",
+                       "pass and the event pass).  qmm_kernel<0,...> is qswitch_gate_up_geglu,",
+                       "qmm_kernel<1,...> the down switch linear of qswitch_down_combine."])
     out_kt = os.path.join(ROOT, "profiles", "switch_kernels_canvas_kernel_trace.md")
     open(out_kt, "w").write("\n".join(lines) + "\n")
+    if glob.glob(os.path.join(d, "kt_ff", "**", "*kernel_stats.csv"), recursive=True):
+        ff = _kt_table(os.path.join(d, "kt_ff"),
+                       "Kernel durations, feed-forward block around the canvas MoE layer (256 tokens, "
+                       "H 2816, dense GeGLU width 2112)",
+                       kt.format(d="kt_ff", a="--steps 60 --warmup 10 --no-cpu-baseline"),
+                       ["The same run as the canvas line plus the feed-forward block diagnostic, so the",
+                        "MoE kernels appear twice as often.  qmm_kernel<3,...> is qlinear_geglu (dense",
+                        "gate|up + GeGLU), qmm_kernel<2,...> qlinear (the dense down projection);",
+                        "ff_prenorm_kernel and ff_combine_kernel are the five RMSNorms, the residual",
+                        "and the layer scalar."])
+        open(os.path.join(ROOT, "profiles", "ff_block_canvas_kernel_trace.md"), "w").write("\n".join(ff) + "\n")
 
     fetch, nf = _pmc_per_dispatch(os.path.join(d, "fetch"), "FETCH_SIZE", lambda n: "qmm_kernel<0" in n)
     write, nw = _pmc_per_dispatch(os.path.join(d, "write"), "WRITE_SIZE", lambda n: "qmm_kernel<0" in n)
@@ -141,8 +158,8 @@ def summarize(d):
     cmd = ("rocprofv3 --pmc {c} -d DIR/{d} -o p --output-format csv -- python3 bench.py {a}")
     txt = ["# HBM traffic of qswitch_gate_up_geglu (qmm_kernel<0,...>), canvas workload",
            "# Commands (from the repository root, TMPDIR=/tmp), one counter per run:",
-           "#   " + cmd.format(c="FETCH_SIZE", d="fetch", a="--steps 20 --warmup 5 --no-cpu-baseline"),
-           "#   " + cmd.format(c="WRITE_SIZE", d="write", a="--steps 20 --warmup 5 --no-cpu-baseline"),
+           "#   " + cmd.format(c="FETCH_SIZE", d="fetch", a="--steps 20 --warmup 5 --no-cpu-baseline --no-ff-block"),
+           "#   " + cmd.format(c="WRITE_SIZE", d="write", a="--steps 20 --warmup 5 --no-cpu-baseline --no-ff-block"),
            "#   " + cmd.format(c="FETCH_SIZE", d="copy_fetch", a="--copy-probe"),
            "#   " + cmd.format(c="WRITE_SIZE", d="copy_write", a="--copy-probe"),
            "# FETCH_SIZE / WRITE_SIZE are KiB per dispatch; each is scaled by what the same",

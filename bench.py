@@ -16,6 +16,8 @@ Prints ONE JSON line (rank 0):
              second pass of K steps (events between kernels add a few
              microseconds of idle time per call, so they stay out of `value`)
   cpu_baseline  the CPU oracle timed on this host on a bounded sample
+  decode_unsorted  diagnostic, not the metric: the small-batch arm (route +
+             the two unsorted calls) at 1 and 7 tokens on the same weights
   ff_block   diagnostic, not the metric: the decoder's feed-forward block
              around the same MoE layer (pre-norms, dense GeGLU branch, the
              layer, post-norms and residual) on the same tokens
@@ -61,6 +63,7 @@ def parse():
     ap.add_argument("--weight-sets", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ff-block", action="store_true", help="skip the feed-forward block diagnostic")
+    ap.add_argument("--no-decode", action="store_true", help="skip the small-batch (unsorted arm) diagnostic")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--summarize", metavar="DIR")
@@ -129,7 +132,7 @@ def summarize(d):
     kt = "rocprofv3 --kernel-trace --stats -d DIR/{d} -o kt --output-format csv -- python3 bench.py {a}"
     lines = _kt_table(os.path.join(d, "kt"),
                       "Kernel durations, canvas workload (256 tokens, H 2816, 128 experts, top-8, I 704)",
-                      kt.format(d="kt", a="--steps 60 --warmup 10 --no-cpu-baseline --no-ff-block"),
+                      kt.format(d="kt", a="--steps 60 --warmup 10 --no-cpu-baseline --no-ff-block --no-decode"),
                       ["rocprofv3 kernel-trace statistics; every dispatch of the run (warm-up, the timed",
                        "pass and the event pass).  qmm_kernel<0,...> is qswitch_gate_up_geglu,",
                        "qmm_kernel<1,...> the down switch linear of qswitch_down_combine."])
@@ -139,13 +142,26 @@ def summarize(d):
         ff = _kt_table(os.path.join(d, "kt_ff"),
                        "Kernel durations, feed-forward block around the canvas MoE layer (256 tokens, "
                        "H 2816, dense GeGLU width 2112)",
-                       kt.format(d="kt_ff", a="--steps 60 --warmup 10 --no-cpu-baseline"),
+                       kt.format(d="kt_ff", a="--steps 60 --warmup 10 --no-cpu-baseline --no-decode"),
                        ["The same run as the canvas line plus the feed-forward block diagnostic, so the",
                         "MoE kernels appear twice as often.  qmm_kernel<3,...> is qlinear_geglu (dense",
                         "gate|up + GeGLU), qmm_kernel<2,...> qlinear (the dense down projection);",
                         "ff_prenorm_kernel and ff_combine_kernel are the five RMSNorms, the residual",
                         "and the layer scalar."])
         open(os.path.join(ROOT, "profiles", "ff_block_canvas_kernel_trace.md"), "w").write("\n".join(ff) + "\n")
+    if glob.glob(os.path.join(d, "kt_dec", "**", "*kernel_stats.csv"), recursive=True):
+        dec = _kt_table(os.path.join(d, "kt_dec"),
+                        "Kernel durations, small-batch arm at 1 and 7 tokens (canvas weights: H 2816, "
+                        "128 experts, top-8, I 704)",
+                        kt.format(d="kt_dec", a="--steps 60 --warmup 10 --no-cpu-baseline --no-ff-block"),
+                        ["The same run as the canvas line plus the decode diagnostic (moe_route and the",
+                         "two unsorted calls, 60 + 10 + 48 layers at each of 1 and 7 tokens), so the",
+                         "router kernels also count the decode layers.  qswitch_unsorted_kernel<0,...> is",
+                         "the gate_up pass and unsorted_geglu_kernel its part sum + GeGLU;",
+                         "qswitch_unsorted_kernel<1,...> the down pass and unsorted_combine_kernel its",
+                         "part sum + weighted sum over k.  Both token counts are pooled in one row per",
+                         "kernel; the bench line's decode_unsorted object has them apart."])
+        open(os.path.join(ROOT, "profiles", "unsorted_decode_kernel_trace.md"), "w").write("\n".join(dec) + "\n")
 
     fetch, nf = _pmc_per_dispatch(os.path.join(d, "fetch"), "FETCH_SIZE", lambda n: "qmm_kernel<0" in n)
     write, nw = _pmc_per_dispatch(os.path.join(d, "write"), "WRITE_SIZE", lambda n: "qmm_kernel<0" in n)
@@ -158,8 +174,8 @@ def summarize(d):
     cmd = ("rocprofv3 --pmc {c} -d DIR/{d} -o p --output-format csv -- python3 bench.py {a}")
     txt = ["# HBM traffic of qswitch_gate_up_geglu (qmm_kernel<0,...>), canvas workload",
            "# Commands (from the repository root, TMPDIR=/tmp), one counter per run:",
-           "#   " + cmd.format(c="FETCH_SIZE", d="fetch", a="--steps 20 --warmup 5 --no-cpu-baseline --no-ff-block"),
-           "#   " + cmd.format(c="WRITE_SIZE", d="write", a="--steps 20 --warmup 5 --no-cpu-baseline --no-ff-block"),
+           "#   " + cmd.format(c="FETCH_SIZE", d="fetch", a="--steps 20 --warmup 5 --no-cpu-baseline --no-ff-block --no-decode"),
+           "#   " + cmd.format(c="WRITE_SIZE", d="write", a="--steps 20 --warmup 5 --no-cpu-baseline --no-ff-block --no-decode"),
            "#   " + cmd.format(c="FETCH_SIZE", d="copy_fetch", a="--copy-probe"),
            "#   " + cmd.format(c="WRITE_SIZE", d="copy_write", a="--copy-probe"),
            "# FETCH_SIZE / WRITE_SIZE are KiB per dispatch; each is scaled by what the same",
@@ -279,6 +295,66 @@ def ff_block_timing(q, torch, synth, ffc, h, sets, K, warmup, t, buf):
             "qlinear_geglu_GBs": geglu_alg / (mean_us["qlinear_geglu"] * 1e-6) / 1e9,
             "qlinear_down_GBs": down_alg / (mean_us["qlinear_down"] * 1e-6) / 1e9,
             "dense_weight_bytes": wgu + wdn}
+
+
+def decode_timing(q, torch, synth, sets, K, warmup, tokens=(1, 7)):
+    """Diagnostic: the small-batch arm (moe_route + the two unsorted calls) at
+    decode batch sizes on the canvas weights, K layers each with HIP events
+    between the calls.  Sixteen token sets and the three weight sets rotate,
+    so most experts' weights come from HBM."""
+    cfg = synth.CANVAS
+    k, E, H, I = cfg.k, cfg.E, cfg.H, cfg.I
+    dev = torch.device("cuda:0")
+    gu_b, dn_b = expert_bytes(cfg)
+    out = {}
+    for T in tokens:
+        xs = [torch.from_numpy(synth.make_activations(T, H, 1000 + j)).to(dev) for j in range(16)]
+        ws = q.unsorted_workspace(T, k, H, I)
+        idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+        wts = torch.empty((T, k), dtype=torch.float32, device=dev)
+        ws_r = torch.empty(max(1, q.moe_route_workspace(T, H, E)), dtype=torch.uint8, device=dev)
+        mid = torch.empty((T * k, I), dtype=torch.bfloat16, device=dev)
+        y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        touched = []
+
+        def layer(i, ev=None):
+            x, p = xs[i % 16], sets[i % len(sets)]
+            mark = (lambda j: ev[j].record()) if ev is not None else (lambda j: None)
+            mark(0)
+            q.moe_route(x, p.norm_scale, cfg.eps, p.router, p.per_expert_scale, k, p.logit_bias,
+                        indices=idx, weights=wts, workspace=ws_r)
+            mark(1)
+            q.qswitch_gate_up_geglu_unsorted(x, p.gate_up, I, idx, ws, mid)
+            mark(2)
+            q.qswitch_down_combine_unsorted(mid, T, k, p.down, idx, wts, ws, y)
+            mark(3)
+
+        for i in range(48):
+            layer(i)
+            if i < 16 * len(sets):
+                torch.cuda.synchronize()
+                touched.append(len(set(idx.cpu().numpy().reshape(-1).tolist())))
+        for i in range(warmup):
+            layer(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(K):
+            layer(i)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+        for i in range(K):
+            layer(i, evs[i])
+        torch.cuda.synchronize()
+        names = ["moe_route", "qswitch_gate_up_geglu_unsorted", "qswitch_down_combine_unsorted"]
+        mean_us = {n: float(np.mean([ev[j].elapsed_time(ev[j + 1]) * 1e3 for ev in evs])) for j, n in enumerate(names)}
+        n_touch = float(np.mean(touched))
+        alg = n_touch * (gu_b + dn_b) + router_bytes(cfg) + 2 * T * H * 2
+        us = wall / K * 1e6
+        out[f"T{T}"] = {"tokens": T, "us_per_layer": us, "tokens_per_s": T / (us * 1e-6),
+                        "experts_touched": n_touch, "alg_bytes": alg, "achieved_GBs": alg / (us * 1e-6) / 1e9,
+                        "call_mean_us": mean_us}
+    return out
 
 
 def main():
@@ -416,6 +492,8 @@ def main():
                   "call_sum_us": float(sum(mean_us.values()))},
         "cpu_baseline": None,
     }
+    if cfg.name == synth.CANVAS.name and not args.no_decode:
+        out["decode_unsorted"] = decode_timing(q, torch, synth, sets, K, args.warmup)
     ffc = next((f for f in synth.FF_CONFIGS.values() if f.moe.name == cfg.name), None)
     if ffc is not None and not args.no_ff_block:
         out["ff_block"] = ff_block_timing(q, torch, synth, ffc, x, sets, K, args.warmup, t,

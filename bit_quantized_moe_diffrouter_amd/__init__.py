@@ -28,6 +28,8 @@ __all__ = [
     "qswitch_gate_up_geglu",
     "qswitch_down_combine", "qswitch_down_combine_workspace", "qlinear", "moe_layer",
     "ff_prenorm", "qlinear_geglu", "ff_combine", "FFParams", "ff_block",
+    "qswitch_unsorted_workspace", "unsorted_workspace", "qswitch_gate_up_geglu_unsorted",
+    "qswitch_down_combine_unsorted", "moe_layer_unsorted",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -76,6 +78,9 @@ _SIGNATURES = {
     "qswitch_down_combine": (ctypes.c_int, [_P, _I, _I, _I, _QP, _I, _P, _P, _P, _P, _P, _SZ, _I, _P]),
     "qlinear": (ctypes.c_int, [_P, _I, _QP, _P, _P]),
     "qlinear_geglu": (ctypes.c_int, [_P, _I, _QP, _P, _P]),
+    "qswitch_unsorted_workspace": (_SZ, [_I, _I, _I, _I]),
+    "qswitch_gate_up_geglu_unsorted": (ctypes.c_int, [_P, _I, _I, _QP, _I, _I, _P, _P, _P, _SZ, _P]),
+    "qswitch_down_combine_unsorted": (ctypes.c_int, [_P, _I, _I, _I, _QP, _I, _P, _P, _P, _P, _SZ, _P]),
     "ff_prenorm": (ctypes.c_int, [_P, _I, _I, _P, _P, ctypes.c_float, _P, _P, _P]),
     "ff_combine": (ctypes.c_int, [_P, _P, _P, _I, _I, _P, _P, _P, ctypes.c_float, ctypes.c_float, _P, _P]),
     "qmoe_tiled_weight_bytes": (_SZ, [_I, _I, _I, _I]),
@@ -421,3 +426,65 @@ def ff_block(h: torch.Tensor, moe: MoEParams, ff: FFParams, k: int, eps: float, 
     y, idx, w, _, _, _ = moe_layer(h, xb, moe, k, eps, deterministic)
     out = ff_combine(h, dense, y, ff.post_ff1, ff.post_ff2, ff.post_ff, eps, ff.layer_scalar)
     return out, idx, w
+
+
+# ----------------------------------------------------------------------------
+# the unsorted small-batch arm
+# ----------------------------------------------------------------------------
+def qswitch_unsorted_workspace(T: int, k: int, H: int, I: int) -> int:
+    return int(lib().qswitch_unsorted_workspace(T, k, H, I))
+
+
+def unsorted_workspace(T: int, k: int, H: int, I: int, device="cuda") -> torch.Tensor:
+    """Scratch for the unsorted calls (fp32 partial sums; any contents)."""
+    n = qswitch_unsorted_workspace(T, k, H, I)
+    if n == 0:
+        raise ValueError(f"no unsorted workspace for T={T} k={k} H={H} I={I}")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def qswitch_gate_up_geglu_unsorted(x_expert: torch.Tensor, gate_up: "TiledWeight", I: int, indices: torch.Tensor,
+                                   workspace: torch.Tensor, mid_rows: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """gate_up + split + GeGLU per assignment, no sort: returns mid_rows bf16 [T*k, I]."""
+    _need(x_expert, "x_expert", 2)
+    _need(indices, "indices", 4)
+    T, H = (int(v) for v in x_expert.shape)
+    k = int(indices.shape[-1])
+    if mid_rows is None:
+        mid_rows = torch.empty((T * k, I), dtype=torch.bfloat16, device=x_expert.device)
+    _need(mid_rows, "mid_rows", 2, (T * k, I))
+    d = gate_up.desc()
+    _check(lib().qswitch_gate_up_geglu_unsorted(_ptr(x_expert), T, H, ctypes.byref(d), I, k, _ptr(indices),
+                                                _ptr(mid_rows), _ptr(workspace), _nbytes(workspace), _stream()))
+    return mid_rows
+
+
+def qswitch_down_combine_unsorted(mid_rows: torch.Tensor, T: int, k: int, down: "TiledWeight", indices: torch.Tensor,
+                                  weights: torch.Tensor, workspace: torch.Tensor,
+                                  y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """down per assignment + weighted sum over k, no sort: returns y bf16 [T, H]."""
+    _need(mid_rows, "mid_rows", 2)
+    _need(indices, "indices", 4)
+    _need(weights, "weights", 4)
+    I = int(mid_rows.shape[-1])
+    H = down.rows
+    if y is None:
+        y = torch.empty((T, H), dtype=torch.bfloat16, device=mid_rows.device)
+    _need(y, "y", 2, (T, H))
+    d = down.desc()
+    _check(lib().qswitch_down_combine_unsorted(_ptr(mid_rows), T, k, I, ctypes.byref(d), H, _ptr(indices),
+                                               _ptr(weights), _ptr(y), _ptr(workspace), _nbytes(workspace),
+                                               _stream()))
+    return y
+
+
+def moe_layer_unsorted(x_router: torch.Tensor, x_expert: torch.Tensor, p: MoEParams, k: int, eps: float,
+                       workspace: Optional[torch.Tensor] = None):
+    """The small-batch arm: route, then the two unsorted calls.  Returns (y, indices, weights, mid_rows)."""
+    T, H = (int(v) for v in x_expert.shape)
+    if workspace is None:
+        workspace = unsorted_workspace(T, k, H, p.I, device=x_expert.device)
+    idx, w = moe_route(x_router, p.norm_scale, eps, p.router, p.per_expert_scale, k, p.logit_bias)
+    mid = qswitch_gate_up_geglu_unsorted(x_expert, p.gate_up, p.I, idx, workspace)
+    y = qswitch_down_combine_unsorted(mid, T, k, p.down, idx, w, workspace)
+    return y, idx, w, mid

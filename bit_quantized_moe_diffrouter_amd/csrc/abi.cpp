@@ -3,6 +3,7 @@
 // so a call that returns an error has done nothing on the device.
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdarg>
@@ -95,6 +96,16 @@ int launched(hipError_t err, const char* what) {
 }
 
 constexpr long long kMaxAssign = 1LL << 24;
+constexpr long long kMaxUnsortedAssign = 4096;  // the unsorted path is sized for small batches
+
+// Workspace of the unsorted pair: the partial sums of the larger of the two
+// passes (fp32), written by the first kernel of a call and read by its second.
+size_t unsorted_bytes(long long T, int k, int H, int I) {
+  const long long A = T * k;
+  const qmoe::UnsortedPlan gu = qmoe::unsorted_plan(A, qmoe::tiled_blocks(2 * I, I), H / 64);
+  const qmoe::UnsortedPlan dn = qmoe::unsorted_plan(A, qmoe::tiled_blocks(H, 0), I / 64);
+  return (size_t)std::max(gu.partials, dn.partials) * sizeof(float);
+}
 
 }  // namespace
 
@@ -381,6 +392,91 @@ int ff_combine(const uint16_t* h, const uint16_t* dense_out, const uint16_t* moe
   return launched(qmoe::launch_ff_combine(h, dense_out, moe_out, T, H, w_post1, w_post2, w_post, eps, layer_scalar,
                                           out, stream),
                   "ff_combine");
+}
+
+}  // extern "C"
+
+extern "C" {
+
+size_t qswitch_unsorted_workspace(int32_t T, int32_t k, int32_t H, int32_t I) {
+  if (T <= 0 || k <= 0 || H <= 0 || I <= 0 || H % 64 != 0 || I % 64 != 0) return 0;
+  if ((long long)T * k > kMaxUnsortedAssign) return 0;
+  return unsorted_bytes(T, k, H, I);
+}
+
+}  // extern "C"
+
+namespace {
+// Shared validation of the two unsorted calls; fills the common arguments.
+int unsorted_common(const char* fn, int32_t T, int32_t k, int32_t H, int32_t I, const qmoe_qweight* W, int rows,
+                    int in, int split, const int32_t* indices, void* workspace, size_t ws_bytes,
+                    qmoe::UnsortedArgs* a) {
+  REQUIRE(T >= 0, QMOE_ERR_INVALID, "%s: T=%d < 0", fn, T);
+  REQUIRE(H > 0 && H % 64 == 0, QMOE_ERR_INVALID, "%s: H=%d must be a positive multiple of 64", fn, H);
+  REQUIRE(I > 0 && I % 64 == 0, QMOE_ERR_INVALID, "%s: I=%d must be a positive multiple of 64", fn, I);
+  REQUIRE(k >= 1 && k <= 16, QMOE_ERR_UNSUPPORTED, "%s: k=%d outside [1, 16]", fn, k);
+  REQUIRE((long long)T * k <= kMaxUnsortedAssign, QMOE_ERR_UNSUPPORTED,
+          "%s: T*k=%lld above %lld (use the sorted calls)", fn, (long long)T * k, kMaxUnsortedAssign);
+  REQUIRE(W != nullptr, QMOE_ERR_INVALID, "%s: null weight descriptor", fn);
+  const int E = W->experts;
+  REQUIRE(E >= 1 && E <= 256, QMOE_ERR_UNSUPPORTED, "%s: E=%d outside [1, 256]", fn, E);
+  if (T == 0) return QMOE_OK;
+  char what[96];
+  snprintf(what, sizeof(what), "%s weight", fn);
+  if (int rc = check_qweight(W, what, E, rows, in, QMOE_LAYOUT_TILED, split)) return rc;
+  REQUIRE_PTR(indices, 4, "indices");
+  REQUIRE_PTR(workspace, 16, "workspace");
+  const size_t need = unsorted_bytes(T, k, H, I);
+  REQUIRE(ws_bytes >= need, QMOE_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws_bytes);
+  a->w = W->w;
+  a->indices = indices;
+  a->part = (float*)workspace;
+  a->A = T * k;
+  a->k = k;
+  a->E = E;
+  a->K = in;
+  a->G = in / 64;
+  a->nblk = qmoe::tiled_blocks(rows, split);
+  const qmoe::UnsortedPlan pl = qmoe::unsorted_plan(a->A, a->nblk, a->G);
+  a->S = pl.S;
+  a->gpw = pl.gpw;
+  return QMOE_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int qswitch_gate_up_geglu_unsorted(const uint16_t* x_expert, int32_t T, int32_t H, const qmoe_qweight* gate_up,
+                                   int32_t I, int32_t k, const int32_t* indices, uint16_t* mid_rows,
+                                   void* workspace, size_t ws_bytes, hipStream_t stream) {
+  const char* fn = "qswitch_gate_up_geglu_unsorted";
+  qmoe::UnsortedArgs a{};
+  if (int rc = unsorted_common(fn, T, k, H, I, gate_up, 2 * I, H, I, indices, workspace, ws_bytes, &a)) return rc;
+  if (T == 0) return ok();
+  REQUIRE_PTR(x_expert, 16, "x_expert");
+  REQUIRE_PTR(mid_rows, 16, "mid_rows");
+  a.x = x_expert;
+  a.out = mid_rows;
+  a.Nout = I;
+  return launched(qmoe::launch_unsorted(qmoe::UNSORTED_GATE_UP, a, stream), fn);
+}
+
+int qswitch_down_combine_unsorted(const uint16_t* mid_rows, int32_t T, int32_t k, int32_t I,
+                                  const qmoe_qweight* down, int32_t H, const int32_t* indices,
+                                  const float* weights, uint16_t* y, void* workspace, size_t ws_bytes,
+                                  hipStream_t stream) {
+  const char* fn = "qswitch_down_combine_unsorted";
+  qmoe::UnsortedArgs a{};
+  if (int rc = unsorted_common(fn, T, k, H, I, down, H, I, 0, indices, workspace, ws_bytes, &a)) return rc;
+  if (T == 0) return ok();
+  REQUIRE_PTR(mid_rows, 16, "mid_rows");
+  REQUIRE_PTR(weights, 4, "weights");
+  REQUIRE_PTR(y, 16, "y");
+  a.x = mid_rows;
+  a.weights = weights;
+  a.out = y;
+  a.Nout = H;
+  return launched(qmoe::launch_unsorted(qmoe::UNSORTED_DOWN, a, stream), fn);
 }
 
 }  // extern "C"

@@ -69,6 +69,26 @@ hipError_t launch_dense(SwitchArgs a, int num_cu, hipStream_t stream);
 hipError_t launch_dense_geglu(SwitchArgs a, int num_cu, hipStream_t stream);
 hipError_t launch_combine(const uint16_t* D, const float* w, int T, int k, int H, uint16_t* y, hipStream_t stream);
 
+// ---------------------------------------------------------------- unsorted small-batch switch linears
+enum : int { UNSORTED_GATE_UP = 0, UNSORTED_DOWN = 1 };
+struct UnsortedArgs {
+  const uint16_t* x;        // gate_up: bf16 [T, K] tokens; down: bf16 [A, K] mid rows
+  const void* w;            // tiled weight [E, nblk, K/64] units
+  const int32_t* indices;   // [A] expert of each assignment
+  const float* weights;     // [A] routing weights (down)
+  uint16_t* out;            // gate_up: bf16 [A, Nout] mid rows; down: bf16 [T, Nout] y
+  float* part;              // workspace: [A * nblk * S][128] partial sums
+  int A, k, K, G, nblk, E, Nout;
+  int S;    // workgroups per (assignment, block)
+  int gpw;  // groups per wave
+};
+struct UnsortedPlan {
+  int gpw, S;
+  long long partials;  // floats
+};
+UnsortedPlan unsorted_plan(long long A, int nblk, int G);
+hipError_t launch_unsorted(int mode, UnsortedArgs a, hipStream_t stream);
+
 // ---------------------------------------------------------------- feed-forward block norms
 // xa = rms(h) * wa, xb = rms(h) * wb (bf16 [T, H] each, H % 8 == 0)
 hipError_t launch_ff_prenorm(const uint16_t* h, int T, int H, const uint16_t* wa, const uint16_t* wb, float eps,

@@ -30,12 +30,15 @@ constexpr int kRRowB = kRKS * 128 + 16;
 
 // K parts of the logit kernel: enough (token tile, K part) workgroups to fill
 // the chip at small T, and at least 4 at large T, where a single part per tile
-// would walk all groups in latency-bound stages one after another.
+// would walk all groups in latency-bound stages one after another; at most
+// 16, the parts the top-k kernel sums with one round of loads (more parts at
+// a few tokens cost the top-k kernel more than they save the logit kernel).
 int route_ksplit(int T, int H) {
   const int G = H / kGroup;
   const int tiles = (T + kTT - 1) / kTT;
   int ks = 256 / (tiles > 0 ? tiles : 1);
   if (ks < 4) ks = 4;
+  if (ks > 16) ks = 16;
   if (ks > G) ks = G;
   return ks;
 }

@@ -14,6 +14,8 @@
  *   qswitch_gate_up_geglu fused gate_up switch linear, split, GeGLU
  *   qswitch_down_combine  down switch linear + weighted sum over k per token
  *   qlinear               dense 4-bit linear
+ *   qswitch_gate_up_geglu_unsorted, qswitch_down_combine_unsorted
+ *                         the small-batch arm without the sort
  *   ff_prenorm, qlinear_geglu, ff_combine
  *                         the decoder's feed-forward block around the MoE
  *                         (pre-norms, dense GeGLU branch, post-norms and
@@ -255,6 +257,47 @@ int qswitch_down_combine(const void* mid, int32_t T, int32_t k, int32_t I,
                          const int32_t* sorted_assign, const float* weights, uint16_t* y,
                          void* workspace, size_t ws_bytes, int32_t deterministic,
                          hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Unsorted small-batch arm (model.ts page, DiffExperts.forward: below 64
+ * assignments the flat indices are not sorted and the gather matmuls read
+ * each assignment's expert directly; the model's decode layers use this arm
+ * when canvas length times top-k is under 64).  Same results as the sorted
+ * calls up to fp32 summation order:
+ *
+ *   qswitch_gate_up_geglu_unsorted:  mid_rows[a] = gelu_tanh(g) * u,
+ *       (g, u) = x_expert[a / k] . dequant(gate_up[indices[a]])^T split at I
+ *   qswitch_down_combine_unsorted:   d_a = bf16(mid_rows[a] . dequant(down[e_a])^T),
+ *       y[t] = sum_j weights[t, j] * d_{t k + j}   (fp32, j order, bf16 out)
+ *
+ *   x_expert    bf16 [T, H]
+ *   gate_up     experts = E, rows = 2I, in = H, tiled with split = I
+ *   down        experts = E, rows = H, in = I, tiled with split = 0
+ *   indices     int32 [T, k] (moe_route's output); an index outside [0, E)
+ *               drops its assignment: its mid row is zero and y leaves it out
+ *   mid_rows    bf16 [T*k, I], row a = assignment t*k + j (plain row-major;
+ *               not the activation tiles of the sorted calls)
+ *   weights     fp32 [T, k]
+ *   y (out)     bf16 [T, H]
+ *   workspace   qswitch_unsorted_workspace(T, k, H, I) bytes of device
+ *               scratch (fp32 partial sums), 16-byte aligned, any contents;
+ *               one buffer serves both calls.  Calls that share a workspace
+ *               must not overlap in time.
+ *
+ * H % 64 == 0, I % 64 == 0, 1 <= k <= 16, E <= 256, T*k <= 4096 (larger
+ * batches: the sorted calls; qswitch_unsorted_workspace returns 0 for sizes
+ * it does not accept).  The result does not depend on how the work is split;
+ * it is bitwise reproducible run to run.
+ * ---------------------------------------------------------------------- */
+size_t qswitch_unsorted_workspace(int32_t T, int32_t k, int32_t H, int32_t I);
+int qswitch_gate_up_geglu_unsorted(const uint16_t* x_expert, int32_t T, int32_t H,
+                                   const qmoe_qweight* gate_up, int32_t I, int32_t k,
+                                   const int32_t* indices, uint16_t* mid_rows, void* workspace,
+                                   size_t ws_bytes, hipStream_t stream);
+int qswitch_down_combine_unsorted(const uint16_t* mid_rows, int32_t T, int32_t k, int32_t I,
+                                  const qmoe_qweight* down, int32_t H, const int32_t* indices,
+                                  const float* weights, uint16_t* y, void* workspace,
+                                  size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * qlinear -- dense 4-bit QuantizedLinear (vision.ts page, VisionLinear.forward,

@@ -136,7 +136,11 @@ PREFILL = MoEConfig("moe_prefill_4096tok_h2816_e128_top8", T=4096, H=2816, E=128
 SKEW = MoEConfig("moe_canvas_skew_256tok_zipf1.1", T=256, H=2816, E=128, k=8, I=704,
                  seed_w=2, seed_x=2, zipf_tau=0.1)
 
-CONFIGS = {c.name: c for c in (TINY, QLINEAR_VISION, CANVAS, PREFILL, SKEW)}
+# decode-sized batches on the canvas weights: the unsorted arm's regime (T*k < 64)
+DECODE_1 = MoEConfig("moe_decode_1tok_h2816_e128_top8", T=1, H=2816, E=128, k=8, I=704, seed_w=2, seed_x=5)
+DECODE_7 = MoEConfig("moe_decode_7tok_h2816_e128_top8", T=7, H=2816, E=128, k=8, I=704, seed_w=2, seed_x=6)
+
+CONFIGS = {c.name: c for c in (TINY, QLINEAR_VISION, CANVAS, PREFILL, SKEW, DECODE_1, DECODE_7)}
 
 
 @dataclass

@@ -29,7 +29,8 @@ def header_functions():
 def test_exports_every_declared_function(L):
     names = header_functions()
     assert set(names) >= {"moe_route", "moe_sort", "qswitch_gate_up_geglu", "qswitch_down_combine",
-                          "qlinear", "qmoe_last_error", "ff_prenorm", "qlinear_geglu", "ff_combine"}
+                          "qlinear", "qmoe_last_error", "ff_prenorm", "qlinear_geglu", "ff_combine",
+                          "qswitch_gate_up_geglu_unsorted", "qswitch_down_combine_unsorted"}
     for n in names:
         assert hasattr(L, n), f"{n} is declared in qmoe.h but not exported"
 
@@ -193,6 +194,43 @@ def test_ff_norm_validation(L):
     assert comb(out=None) == INVALID
 
 
+def test_unsorted_workspace_sizes(L):
+    # T=1, k=8, canvas: gate_up plan 1 group per wave, 11 workgroups per (assignment, block)
+    # T=1: one group per wave; gate_up 11 workgroups per (assignment, block), down 3
+    assert L.qswitch_unsorted_workspace(1, 8, 2816, 704) == max(8 * 11 * 11, 8 * 22 * 3) * 128 * 4
+    assert L.qswitch_unsorted_workspace(512, 8, 2816, 704) > 0
+    assert L.qswitch_unsorted_workspace(513, 8, 2816, 704) == 0      # T*k above 4096
+    assert L.qswitch_unsorted_workspace(1, 8, 2800, 704) == 0        # H % 64
+    assert L.qswitch_unsorted_workspace(0, 8, 2816, 704) == 0
+
+
+def test_unsorted_validation(L):
+    ws = L.qswitch_unsorted_workspace(2, 4, 256, 128)
+    gu = qw(8, 256, 256, layout=1, split=128)
+    dn = qw(8, 256, 128, layout=1)
+    g = lambda T=2, H=256, I=128, k=4, d=gu, x=A16, idx=A16, mid=A16, w=A16, n=ws: \
+        L.qswitch_gate_up_geglu_unsorted(x, T, H, ctypes.byref(d), I, k, idx, mid, w, n, None)
+    dcall = lambda T=2, H=256, I=128, k=4, d=dn, mid=A16, idx=A16, wt=A16, y=A16, w=A16, n=ws: \
+        L.qswitch_down_combine_unsorted(mid, T, k, I, ctypes.byref(d), H, idx, wt, y, w, n, None)
+    assert g(T=0, x=None, mid=None) == 0
+    assert g(T=-1) == INVALID
+    assert g(H=200) == INVALID
+    assert g(k=17) == UNSUPPORTED
+    assert g(T=1025) == UNSUPPORTED
+    assert "sorted calls" in err(L)
+    assert g(d=qw(8, 256, 256, layout=1, split=0)) == INVALID       # not tiled as a fused pair
+    assert g(d=qw(300, 256, 256, layout=1, split=128)) == UNSUPPORTED
+    assert g(idx=None) == INVALID
+    assert g(w=A16 + 8) == INVALID                                   # workspace not 16-byte aligned
+    assert g(n=ws - 1) == WORKSPACE
+    assert g(mid=None) == INVALID
+    assert dcall(T=0, mid=None, y=None) == 0
+    assert dcall(d=qw(8, 256, 128, layout=1, split=64)) == INVALID
+    assert dcall(wt=None) == INVALID
+    assert dcall(y=A16 + 8) == INVALID
+    assert dcall(n=0) == WORKSPACE
+
+
 def test_route_rejects_tiled_proj(L):
     d = qw(1, 8, 256, layout=1)
     assert L.moe_route(A16, 16, 256, A16, 1e-6, ctypes.byref(d), A16, None, 2, A16, A16, None, A16, 1 << 30,
@@ -224,3 +262,4 @@ def test_route_workspace_size(L):
     assert L.moe_route_workspace(4096, 2816, 128) == 4 * 4096 * 129 * 4
     assert L.moe_route_workspace(16, 256, 8) == 4 * 16 * 9 * 4
     assert L.moe_route_workspace(0, 256, 8) == 0
+    assert L.moe_route_workspace(1, 2816, 128) == 16 * 1 * 129 * 4   # at most 16 parts

@@ -1,0 +1,182 @@
+"""GPU parity of the unsorted small-batch arm (gate_up + GeGLU per assignment,
+down + weighted sum over k) against the CPU oracle, through the C ABI.
+
+Bars as on the sorted path: mid rows and y from the GPU's mid within a
+per-row relative error of 1e-2, the whole layer within 2e-2; the unsorted
+and sorted calls on the same routing agree within 1e-2 (they differ only in
+fp32 summation order and so in an occasional bf16 rounding); repeated calls
+are bitwise equal, whatever the workspace held before."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from _util import bf16_host, dev_params, dev_tensor, ensure_built, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ensure_built()
+    torch.cuda.init()
+
+
+_cache = {}
+
+
+def canvas_weights():
+    if "w" not in _cache:
+        _cache["w"] = synth.make_moe_weights(synth.CANVAS)
+    return _cache["w"]
+
+
+def inputs(cfg):
+    if cfg.name not in _cache:
+        w = canvas_weights() if cfg.H == 2816 else None
+        _cache[cfg.name] = synth.make_moe_inputs(cfg, w)
+    return _cache[cfg.name]
+
+
+def params(cfg):
+    key = ("dev", cfg.H, cfg.E, cfg.I, cfg.seed_w)
+    if key not in _cache:
+        _cache[key] = dev_params(inputs(cfg).weights)
+    return _cache[key]
+
+
+def oracle_route(inp):
+    cfg, wt = inp.cfg, inp.weights
+    r = wt.router
+    return O.route(inp.x, wt.norm_scale, cfg.eps, r.w, r.scales, r.biases, wt.per_expert_scale, cfg.k,
+                   wt.logit_bias)
+
+
+def run_unsorted(inp, idx, w, ws=None):
+    import bit_quantized_moe_diffrouter_amd as q
+    cfg = inp.cfg
+    p = params(cfg)
+    x = dev_tensor(inp.x)
+    idx_d = dev_tensor(np.ascontiguousarray(idx, dtype=np.int32))
+    w_d = dev_tensor(np.ascontiguousarray(w, dtype=np.float32))
+    if ws is None:
+        ws = q.unsorted_workspace(cfg.T, cfg.k, cfg.H, cfg.I)
+    mid = q.qswitch_gate_up_geglu_unsorted(x, p.gate_up, cfg.I, idx_d, ws)
+    y = q.qswitch_down_combine_unsorted(mid, cfg.T, cfg.k, p.down, idx_d, w_d, ws)
+    torch.cuda.synchronize()
+    return bf16_host(y), bf16_host(mid), ws
+
+
+CFGS = [synth.DECODE_1, synth.DECODE_7, synth.TINY]
+
+
+@pytest.mark.parametrize("cfg", CFGS, ids=lambda c: c.name)
+def test_unsorted_mid_and_y_parity(cfg):
+    say(f"[unsorted] {cfg.name}")
+    inp = inputs(cfg)
+    idx, w, _ = oracle_route(inp)
+    y, mid, ws = run_unsorted(inp, idx, w)
+    A = cfg.T * cfg.k
+    rows = list(range(A)) if A <= 64 else list(range(0, A, max(1, A // 48)))
+    ref_mid = O.expert_mid_bruteforce(inp.x, idx, inp.weights.gate_up, cfg.I, rows)
+    e_mid = O.rowwise_rel_err(mid[rows], ref_mid)
+    toks = list(range(min(cfg.T, 16)))
+    ref_y = O.down_combine_from_mid(mid, idx, w, inp.weights.down, toks)
+    e_y = O.rowwise_rel_err(y[toks], ref_y)
+    say(f"  mid rel err {e_mid:.3e}, y (from GPU mid) rel err {e_y:.3e}")
+    assert e_mid <= 1e-2
+    assert e_y <= 1e-2
+
+
+@pytest.mark.parametrize("cfg", [synth.DECODE_1, synth.DECODE_7], ids=lambda c: c.name)
+def test_unsorted_layer_parity(cfg):
+    """Route + the two unsorted calls against the oracle's experts on the GPU's routing."""
+    import bit_quantized_moe_diffrouter_amd as q
+    say(f"[unsorted layer] {cfg.name}")
+    inp = inputs(cfg)
+    p = params(cfg)
+    x = dev_tensor(inp.x)
+    y, idx, w, _ = q.moe_layer_unsorted(x, x, p, cfg.k, cfg.eps)
+    torch.cuda.synchronize()
+    idx_g, w_g = idx.cpu().numpy(), w.cpu().numpy()
+    ref = O.experts_bruteforce(inp.x, idx_g, w_g, inp.weights.gate_up, inp.weights.down, cfg.I)
+    err = O.rowwise_rel_err(bf16_host(y), ref)
+    say(f"  layer rel err {err:.3e}")
+    assert err <= 2e-2
+    idx_r, _, lg_r = oracle_route(inp)
+    ok = O.gap_kth(lg_r, cfg.k) >= 1e-5
+    assert all(set(idx_g[t]) == set(idx_r[t]) for t in np.nonzero(ok)[0])
+
+
+@pytest.mark.parametrize("cfg", [synth.DECODE_7, synth.TINY], ids=lambda c: c.name)
+def test_unsorted_matches_sorted(cfg):
+    import bit_quantized_moe_diffrouter_amd as q
+    say(f"[unsorted vs sorted] {cfg.name}")
+    inp = inputs(cfg)
+    p = params(cfg)
+    idx, w, _ = oracle_route(inp)
+    y_u, _, _ = run_unsorted(inp, idx, w)
+    x = dev_tensor(inp.x)
+    idx_d = dev_tensor(idx.astype(np.int32))
+    off, sa = q.moe_sort(idx_d, cfg.E)
+    mid = q.qswitch_gate_up_geglu(x, p.gate_up, cfg.I, cfg.k, off, sa)
+    y_s = q.qswitch_down_combine(mid, cfg.T, cfg.k, p.down, dev_tensor(w.astype(np.float32)), off, sa)
+    torch.cuda.synchronize()
+    err = O.rowwise_rel_err(y_u, bf16_host(y_s))
+    say(f"  unsorted vs sorted rel diff {err:.3e}")
+    assert err <= 1e-2
+
+
+def test_unsorted_bitwise_reproducible_and_workspace_reuse():
+    """Two calls give the same bits; one workspace (filled with garbage first)
+    serves calls of different sizes in turn."""
+    import bit_quantized_moe_diffrouter_amd as q
+    big, small = synth.DECODE_7, synth.DECODE_1
+    ws = q.unsorted_workspace(big.T, big.k, big.H, big.I)
+    ws.fill_(0xA5)
+    inp_b, inp_s = inputs(big), inputs(small)
+    ib, wb, _ = oracle_route(inp_b)
+    is_, ws_, _ = oracle_route(inp_s)
+    y1, m1, _ = run_unsorted(inp_b, ib, wb, ws)
+    ys, _, _ = run_unsorted(inp_s, is_, ws_, ws)
+    y2, m2, _ = run_unsorted(inp_b, ib, wb, ws)
+    assert np.array_equal(y1, y2) and np.array_equal(m1, m2)
+    ys_fresh, _, _ = run_unsorted(inp_s, is_, ws_)
+    assert np.array_equal(ys, ys_fresh)
+
+
+@pytest.mark.parametrize("T,H,E,k,I", [(3, 192, 5, 3, 128), (1, 64, 1, 1, 64), (9, 320, 16, 7, 192),
+                                       (4, 1024, 32, 16, 320)])
+def test_unsorted_ragged_and_degenerate(T, H, E, k, I):
+    cfg = synth.MoEConfig(f"u_T{T}_H{H}_E{E}_k{k}_I{I}", T=T, H=H, E=E, k=k, I=I, seed_w=T + H, seed_x=E + I)
+    say(f"[unsorted ragged] {cfg.name}")
+    inp = inputs(cfg)
+    idx, w, _ = oracle_route(inp)
+    y, mid, ws = run_unsorted(inp, idx, w)
+    ref = O.experts_bruteforce(inp.x, idx, w, inp.weights.gate_up, inp.weights.down, I)
+    err = O.rowwise_rel_err(y, ref)
+    say(f"  rel err {err:.3e}")
+    assert err <= 2e-2
+
+
+def test_unsorted_dropped_indices():
+    """An index outside [0, E) drops its assignment: zero mid row, left out of y."""
+    cfg = synth.DECODE_7
+    inp = inputs(cfg)
+    idx, w, _ = oracle_route(inp)
+    idx = idx.copy()
+    idx[0, 3] = cfg.E + 5
+    idx[2, 0] = -1
+    idx[4, :] = cfg.E     # a token with no assignment left: y row is zero
+    y, mid, _ = run_unsorted(inp, idx, w)
+    assert not mid[0 * cfg.k + 3].any() and not mid[2 * cfg.k].any()
+    assert not y[4].any()
+    keep = (idx >= 0) & (idx < cfg.E)
+    idx_ok = np.where(keep, idx, 0)
+    w_ok = np.where(keep, w, 0.0).astype(np.float32)
+    toks = [0, 1, 2, 3, 5]
+    ref = O.experts_bruteforce(inp.x, idx_ok, w_ok, inp.weights.gate_up, inp.weights.down, cfg.I, tokens=toks)
+    assert O.rowwise_rel_err(y[toks], ref) <= 2e-2

@@ -180,3 +180,49 @@ def test_unsorted_dropped_indices():
     toks = [0, 1, 2, 3, 5]
     ref = O.experts_bruteforce(inp.x, idx_ok, w_ok, inp.weights.gate_up, inp.weights.down, cfg.I, tokens=toks)
     assert O.rowwise_rel_err(y[toks], ref) <= 2e-2
+
+
+def test_unsorted_layer_in_hip_graph():
+    """The small-batch layer (route + the two unsorted calls) captured in a HIP
+    graph: every replay, with eager work and synchronisations in between,
+    gives the eager result bit for bit (the calls enqueue only kernels)."""
+    import bit_quantized_moe_diffrouter_amd as q
+    cfg = synth.DECODE_7
+    inp = inputs(cfg)
+    p = params(cfg)
+    T, k, H, I, E = cfg.T, cfg.k, cfg.H, cfg.I, cfg.E
+    xs = [dev_tensor(inp.x), dev_tensor(synth.make_activations(T, H, 77))]
+    ws = q.unsorted_workspace(T, k, H, I)
+    ws_r = torch.empty(q.moe_route_workspace(T, H, E), dtype=torch.uint8, device="cuda")
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    wts = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    mid = torch.empty((T * k, I), dtype=torch.bfloat16, device="cuda")
+    ys = [torch.empty((T, H), dtype=torch.bfloat16, device="cuda") for _ in xs]
+
+    def layers():
+        for x, y in zip(xs, ys):
+            q.moe_route(x, p.norm_scale, cfg.eps, p.router, p.per_expert_scale, k, None, indices=idx, weights=wts,
+                        workspace=ws_r)
+            q.qswitch_gate_up_geglu_unsorted(x, p.gate_up, I, idx, ws, mid)
+            q.qswitch_down_combine_unsorted(mid, T, k, p.down, idx, wts, ws, y)
+
+    layers()
+    torch.cuda.synchronize()
+    eager = [y.clone() for y in ys]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layers()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        layers()
+    for rep in range(3):
+        for y in ys:
+            y.fill_(0)
+        q.moe_sort(idx, E)          # unrelated eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for y, e in zip(ys, eager):
+            assert torch.equal(y, e), f"replay {rep} differs from the eager result"

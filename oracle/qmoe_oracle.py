@@ -37,6 +37,9 @@ X  per assignment: ``g = x_t . W_gu[e]^T``, split at I, ``gelu_tanh(gate) * up``
                                    gelu_approx(gate) * up: [vision page] DiffVisionMLP)
 L  dense 4-bit linear ``y = x . W^T``
                                   ([vision page] VisionLinear.forward, quantized arm)
+H  the tied LM head: ``cap * tanh(bf16(x . E^T) / cap)``, fp32 out
+                                  ([model page] logitsFromHidden, the softcap
+                                   default in the constructor)
 F  the decoder's feed-forward block around the MoE: plain RMSNorm with its
    weight used as stored (no 1 + w offset); the parallel dense GeGLU MLP
    ``down(gelu_tanh(gate x) * up x)``; ``out = (h + N(N1(h1) + N2(h2))) * s``
@@ -45,7 +48,7 @@ F  the decoder's feed-forward block around the MoE: plain RMSNorm with its
                                    the file header's note on plain RMSNorm;
                                    the MLP shape: SelfConditioning, GegluMLP)
 
-Readings where the pages are silent (each is listed in the design doc): group 64,
+Readings where the pages are silent: group 64,
 codes stored first-in-lowest-bits, scales/biases bf16; eps = 1e-6; router kept
 in fp32/fp64 without the pages' intermediate bf16 roundings; ties to the lower
 expert index; stable sort; tanh-form GELU.
@@ -86,7 +89,7 @@ def unpack_codes(words: np.ndarray) -> np.ndarray:
     Code c of a row sits in word c // 8 at bits 4*(c % 8) .. 4*(c % 8) + 3
     (first code in the lowest bits).  The pages show the packed weight as a
     uint32 array ([vision page] VisionLinear.weightDtype) but not the field
-    order; this reading is stated in the design doc and pinned by a golden file.
+    order; this reading is pinned by a golden file.
     """
     w = np.asarray(words, dtype=np.uint32)
     shifts = (4 * np.arange(8, dtype=np.uint32)).reshape((1,) * w.ndim + (8,))
@@ -414,6 +417,30 @@ def ff_block(h_bits, moe_weights, ffw, k: int, I: int, eps: float,
     h2 = rms_norm(experts_bruteforce(xe, idx, wts, moe_weights.gate_up, moe_weights.down, I), ffw.post_ff2, eps)
     out = (hs + rms_norm(h1 + h2, ffw.post_ff, eps)) * ffw.layer_scalar
     return out, idx, wts
+
+
+# ----------------------------------------------------------------------------
+# H: the tied LM head and its softcap
+# ----------------------------------------------------------------------------
+def softcap(z, cap: float) -> np.ndarray:
+    """``cap * tanh(z / cap)`` in fp64 ([model page] logitsFromHidden: a tanh
+    softcap of the fp32-widened logits, cap = finalLogitSoftcapping, 30 when
+    the config leaves it out)."""
+    z = np.asarray(z, dtype=np.float64)
+    return cap * np.tanh(z / cap)
+
+
+def lm_head_softcap(x_bits, words, scales, biases, cap: float,
+                    rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    """The tied head ([model page] logitsFromHidden): the embedding's 4-bit
+    weight used as a linear, ``z = x . dequant(E)^T``, returned in the input's
+    dtype (bf16, rounded to nearest even) as the quantized matmul returns it,
+    then widened and softcapped.  ``rows`` restricts the output rows."""
+    x = bf16_to_f64(x_bits)
+    if rows is not None:
+        x = x[list(rows)]
+    z = x @ dequantize(words, scales, biases).T
+    return softcap(bf16_to_f64(f64_to_bf16_bits(z)), cap)
 
 
 # ----------------------------------------------------------------------------

@@ -427,3 +427,45 @@ def test_ff_block_rows_and_given_routing():
     np.testing.assert_allclose(part, full[rows], rtol=1e-12, atol=1e-12)
     again, _, _ = O.ff_block(inp.x, inp.weights, ffw, cfg.moe.k, cfg.moe.I, cfg.moe.eps, route_out=(idx, w))
     np.testing.assert_allclose(again, full, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------- H: tied head + softcap
+def test_softcap_closed_forms():
+    cap = 30.0
+    z = np.array([-1e6, -45.0, -1.0, 0.0, 0.3, 1.0, 45.0, 1e6])
+    y = O.softcap(z, cap)
+    assert np.all(np.abs(y) < cap + 1e-12)
+    assert np.allclose(O.softcap(-z, cap), -y, rtol=0, atol=0)          # odd
+    assert y[0] == -cap and y[-1] == cap                                 # saturates at +-cap
+    # tanh(atanh(1/2)) = 1/2: the point where the cap halves
+    assert abs(O.softcap(cap * math.atanh(0.5), cap) - cap / 2) < 1e-12
+    # small z: z - z^3 / (3 cap^2) + 2 z^5 / (15 cap^4)
+    s = 0.01 * cap
+    assert abs(O.softcap(s, cap) - (s - s ** 3 / (3 * cap ** 2) + 2 * s ** 5 / (15 * cap ** 4))) < 1e-12
+
+
+def test_lm_head_with_huge_cap_is_the_bf16_qlinear():
+    rng = np.random.default_rng(21)
+    W = synth.random_qtensor(rng, (48,), 128)
+    x = synth.make_activations(5, 128, seed=3)
+    ref = O.bf16_to_f64(O.f64_to_bf16_bits(O.qlinear(x, W.w, W.scales, W.biases)))
+    got = O.lm_head_softcap(x, W.w, W.scales, W.biases, cap=1e12)
+    assert np.allclose(got, ref, rtol=1e-15, atol=0)
+    rows = [4, 0, 2]
+    assert np.array_equal(O.lm_head_softcap(x, W.w, W.scales, W.biases, 30.0, rows=rows),
+                          O.lm_head_softcap(x, W.w, W.scales, W.biases, 30.0)[rows])
+
+
+def test_lm_head_rounds_to_bf16_before_the_cap():
+    """A logit of 257 (not a bf16 value) is returned as 256 by the quantized
+    matmul and only then capped: 30 tanh(256 / 30), not 30 tanh(257 / 30)."""
+    # one row of 64 codes 1, scale 1, bias 0 -> weight row of ones; x: 64 values summing to 257
+    words = np.full((1, 8), 0x11111111, dtype=np.uint32)
+    scales = O.f64_to_bf16_bits(np.ones((1, 1)))
+    biases = O.f64_to_bf16_bits(np.zeros((1, 1)))
+    xv = np.full((1, 64), 4.0)
+    xv[0, 0] = 5.0                                        # 63 * 4 + 5 = 257
+    x = O.f64_to_bf16_bits(xv)
+    got = O.lm_head_softcap(x, words, scales, biases, 30.0)
+    assert abs(got[0, 0] - 30.0 * math.tanh(256.0 / 30.0)) < 1e-12
+    assert abs(got[0, 0] - 30.0 * math.tanh(257.0 / 30.0)) > 1e-8

@@ -18,6 +18,8 @@ Prints ONE JSON line (rank 0):
   cpu_baseline  the CPU oracle timed on this host on a bounded sample
   decode_unsorted  diagnostic, not the metric: the small-batch arm (route +
              the two unsorted calls) at 1 and 7 tokens on the same weights
+  lm_head    diagnostic, not the metric: the tied LM head with its softcap,
+             256 rows x 2816 -> 262,144 (fp32 logits)
   ff_block   diagnostic, not the metric: the decoder's feed-forward block
              around the same MoE layer (pre-norms, dense GeGLU branch, the
              layer, post-norms and residual) on the same tokens
@@ -64,6 +66,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ff-block", action="store_true", help="skip the feed-forward block diagnostic")
     ap.add_argument("--no-decode", action="store_true", help="skip the small-batch (unsorted arm) diagnostic")
+    ap.add_argument("--no-head", action="store_true", help="skip the LM-head diagnostic")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--summarize", metavar="DIR")
@@ -378,6 +381,37 @@ def decode_timing(q, torch, synth, sets, K, warmup, tokens=(1, 7)):
     return out
 
 
+def lm_head_timing(q, torch, synth, K, warmup, vocab=262144, rows=256, hidden=2816, cap=30.0):
+    """Diagnostic: the tied LM head with its softcap (qlinear_softcap) on the
+    canvas rows, vocabulary 262,144 (its 4-bit weight, 415 MB, exceeds the
+    Infinity Cache, so every call streams it from HBM)."""
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(31)
+    W = synth.random_qtensor(rng, (vocab,), hidden)
+    Wt = q.QuantWeight(torch.from_numpy(W.w).to(dev), torch.from_numpy(W.scales).to(dev),
+                       torch.from_numpy(W.biases).to(dev)).tiled(0)
+    del W
+    x = torch.from_numpy(synth.make_activations(rows, hidden, 32)).to(dev)
+    y = torch.empty((rows, vocab), dtype=torch.float32, device=dev)
+    n = max(4, K // 10)
+    for _ in range(max(2, warmup // 10)):
+        q.qlinear_softcap(x, Wt, cap, y)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in evs:
+        a.record()
+        q.qlinear_softcap(x, Wt, cap, y)
+        b.record()
+    torch.cuda.synchronize()
+    us = float(np.mean([a.elapsed_time(b) * 1e3 for a, b in evs]))
+    flops = 2.0 * rows * vocab * hidden
+    wbytes = vocab * (hidden // 2 + 4 * (hidden // 64))
+    hbm = wbytes + rows * hidden * 2 + rows * vocab * 4
+    return {"rows": rows, "vocab": vocab, "hidden": hidden, "calls": n, "mean_launch_us": us,
+            "tflops": flops / (us * 1e-6) / 1e12, "mfma_frac": flops / (us * 1e-6) / (MFMA_BF16_PEAK_TFLOPS * 1e12),
+            "hbm_bytes": hbm, "achieved_GBs": hbm / (us * 1e-6) / 1e9, "hbm_frac": hbm / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+
+
 def main():
     args = parse()
     if args.summarize:
@@ -515,6 +549,8 @@ def main():
     }
     if cfg.name == synth.CANVAS.name and not args.no_decode:
         out["decode_unsorted"] = decode_timing(q, torch, synth, sets, K, args.warmup)
+    if cfg.name == synth.CANVAS.name and not args.no_head:
+        out["lm_head"] = lm_head_timing(q, torch, synth, K, args.warmup)
     ffc = next((f for f in synth.FF_CONFIGS.values() if f.moe.name == cfg.name), None)
     if ffc is not None and not args.no_ff_block:
         out["ff_block"] = ff_block_timing(q, torch, synth, ffc, x, sets, K, args.warmup, t,

@@ -27,7 +27,7 @@ __all__ = [
     "moe_route", "moe_route_workspace", "moe_sort", "qswitch_mid_bytes",
     "qswitch_gate_up_geglu",
     "qswitch_down_combine", "qswitch_down_combine_workspace", "qlinear", "moe_layer",
-    "ff_prenorm", "qlinear_geglu", "ff_combine", "FFParams", "ff_block",
+    "ff_prenorm", "qlinear_geglu", "ff_combine", "FFParams", "ff_block", "qlinear_softcap",
     "qswitch_unsorted_workspace", "unsorted_workspace", "qswitch_gate_up_geglu_unsorted",
     "qswitch_down_combine_unsorted", "moe_layer_unsorted",
 ]
@@ -78,6 +78,7 @@ _SIGNATURES = {
     "qswitch_down_combine": (ctypes.c_int, [_P, _I, _I, _I, _QP, _I, _P, _P, _P, _P, _P, _SZ, _I, _P]),
     "qlinear": (ctypes.c_int, [_P, _I, _QP, _P, _P]),
     "qlinear_geglu": (ctypes.c_int, [_P, _I, _QP, _P, _P]),
+    "qlinear_softcap": (ctypes.c_int, [_P, _I, _QP, ctypes.c_float, _P, _P]),
     "qswitch_unsorted_workspace": (_SZ, [_I, _I, _I, _I]),
     "qswitch_gate_up_geglu_unsorted": (ctypes.c_int, [_P, _I, _I, _QP, _I, _I, _P, _P, _P, _SZ, _P]),
     "qswitch_down_combine_unsorted": (ctypes.c_int, [_P, _I, _I, _I, _QP, _I, _P, _P, _P, _P, _SZ, _P]),
@@ -488,3 +489,19 @@ def moe_layer_unsorted(x_router: torch.Tensor, x_expert: torch.Tensor, p: MoEPar
     mid = qswitch_gate_up_geglu_unsorted(x_expert, p.gate_up, p.I, idx, workspace)
     y = qswitch_down_combine_unsorted(mid, T, k, p.down, idx, w, workspace)
     return y, idx, w, mid
+
+
+# ----------------------------------------------------------------------------
+# the tied LM head
+# ----------------------------------------------------------------------------
+def qlinear_softcap(x: torch.Tensor, W: "TiledWeight", cap: float = 30.0,
+                    y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """cap * tanh(bf16(x . dequant(W)^T) / cap): returns fp32 [M, N]."""
+    M = int(x.shape[0])
+    _need(x, "x", 2)
+    if y is None:
+        y = torch.empty((M, W.rows), dtype=torch.float32, device=x.device)
+    _need(y, "y", 4, (M, W.rows))
+    d = W.desc()
+    _check(lib().qlinear_softcap(_ptr(x), M, ctypes.byref(d), float(cap), _ptr(y), _stream()))
+    return y

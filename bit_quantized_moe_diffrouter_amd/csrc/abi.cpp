@@ -333,6 +333,34 @@ int qlinear(const uint16_t* x, int32_t M, const qmoe_qweight* W, uint16_t* y, hi
   return launched(qmoe::launch_dense(a, ncu, stream), "qlinear");
 }
 
+int qlinear_softcap(const uint16_t* x, int32_t M, const qmoe_qweight* W, float cap, float* y, hipStream_t stream) {
+  REQUIRE(M >= 0, QMOE_ERR_INVALID, "qlinear_softcap: M=%d < 0", M);
+  REQUIRE(W != nullptr, QMOE_ERR_INVALID, "qlinear_softcap: null weight descriptor");
+  REQUIRE(std::isfinite(cap) && cap > 0.f, QMOE_ERR_INVALID, "qlinear_softcap: cap must be finite and > 0");
+  const int N = W->rows, K = W->in;
+  REQUIRE(K > 0 && K % 64 == 0, QMOE_ERR_INVALID, "qlinear_softcap: K=%d must be a positive multiple of 64", K);
+  REQUIRE(N > 0 && N % 16 == 0, QMOE_ERR_INVALID, "qlinear_softcap: N=%d must be a positive multiple of 16", N);
+  if (int rc = check_qweight(W, "qlinear_softcap W", 1, N, K, QMOE_LAYOUT_TILED, 0)) return rc;
+  if (M == 0) return ok();
+  REQUIRE_PTR(x, 16, "qlinear_softcap x");
+  REQUIRE_PTR(y, 16, "qlinear_softcap y");
+  REQUIRE((long long)M * K * 2 < (1LL << 32), QMOE_ERR_UNSUPPORTED, "qlinear_softcap: activation bytes reach 2^32");
+  int ncu = 0;
+  if (int rc = num_cu_current(&ncu)) return rc;
+  qmoe::SwitchArgs a{};
+  a.a = x;
+  a.w = W->w;
+  a.nblk = qmoe::tiled_blocks(N, 0);
+  a.out = y;
+  a.K = K;
+  a.Nout = N;
+  a.E = 1;
+  a.ktop = 1;
+  a.rows_total = M;
+  a.cap = cap;
+  return launched(qmoe::launch_dense_softcap(a, ncu, stream), "qlinear_softcap");
+}
+
 int qlinear_geglu(const uint16_t* x, int32_t M, const qmoe_qweight* W, uint16_t* y, hipStream_t stream) {
   REQUIRE(M >= 0, QMOE_ERR_INVALID, "qlinear_geglu: M=%d < 0", M);
   REQUIRE(W != nullptr, QMOE_ERR_INVALID, "qlinear_geglu: null weight descriptor");

@@ -60,6 +60,7 @@ struct SwitchArgs {
   int rows_total;  // dense: M; switch: A = T*k
   int ntiles;      // column tiles per row chunk (set by the launcher)
   int max_tiles;   // switch: activation tiles the input and output buffers hold
+  float cap;       // softcap of the LM-head mode
 };
 hipError_t launch_gate_up_geglu(SwitchArgs a, int num_cu, hipStream_t stream);
 hipError_t launch_down(SwitchArgs a, int num_cu, hipStream_t stream);
@@ -67,6 +68,9 @@ hipError_t launch_dense(SwitchArgs a, int num_cu, hipStream_t stream);
 // dense rows against a fused gate|up weight (tiled with split = Nout), GeGLU,
 // row-major bf16 [rows_total, Nout] out
 hipError_t launch_dense_geglu(SwitchArgs a, int num_cu, hipStream_t stream);
+// dense rows against the tied head's weight; fp32 [rows_total, Nout] out,
+// cap * tanh(bf16(logit) / cap)
+hipError_t launch_dense_softcap(SwitchArgs a, int num_cu, hipStream_t stream);
 hipError_t launch_combine(const uint16_t* D, const float* w, int T, int k, int H, uint16_t* y, hipStream_t stream);
 
 // ---------------------------------------------------------------- unsorted small-batch switch linears

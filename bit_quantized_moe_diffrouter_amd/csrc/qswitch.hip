@@ -49,8 +49,9 @@ namespace qmoe {
 
 // gate_up + GeGLU and down over sorted expert rows; the dense linear; the
 // dense linear with a fused gate|up weight and the GeGLU (the decoder's dense
-// MLP branch, first half)
-enum : int { MODE_GATE_UP = 0, MODE_DOWN = 1, MODE_DENSE = 2, MODE_DENSE_GEGLU = 3 };
+// MLP branch, first half); the dense linear as the tied LM head, its bf16
+// logits widened and softcapped to fp32
+enum : int { MODE_GATE_UP = 0, MODE_DOWN = 1, MODE_DENSE = 2, MODE_DENSE_GEGLU = 3, MODE_DENSE_SOFTCAP = 4 };
 
 namespace {
 
@@ -64,7 +65,8 @@ constexpr int kMT = 2;             // row tiles held per slot and accumulator se
 // LDS per wave: staging of two 16-row tiles, 64 bf16 columns wide (activation
 // rows in; gate_up and dense GeGLU outputs) or 128 wide (down and dense outputs)
 constexpr int wave_lds_bytes(int mode) {
-  return (mode == MODE_DOWN || mode == MODE_DENSE) ? kMT * 16 * 128 * 2 : kMT * 16 * 64 * 2;
+  return (mode == MODE_DOWN || mode == MODE_DENSE || mode == MODE_DENSE_SOFTCAP) ? kMT * 16 * 128 * 2
+                                                                                 : kMT * 16 * 64 * 2;
 }
 constexpr int kRedBytes = kMT * kNS * 64 * 16;  // one wave's fp32 accumulators (K-split hand-over)
 
@@ -125,7 +127,8 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
   static_assert(KS == 1 || KS == 2 || KS == 4, "a worker is 1, 2 or 4 waves");
   constexpr int kWaveLds = wave_lds_bytes(MODE);
   constexpr int MT = kMT;
-  constexpr bool kRows = MODE == MODE_DENSE || MODE == MODE_DENSE_GEGLU;  // plain rows 0..M-1, no buckets
+  // plain rows 0..M-1, no buckets
+  constexpr bool kRows = MODE == MODE_DENSE || MODE == MODE_DENSE_GEGLU || MODE == MODE_DENSE_SOFTCAP;
   // kWaveLds bytes per wave, then (KS > 1) kRedBytes per wave that is not the first of its worker
   extern __shared__ __attribute__((aligned(16))) uint8_t qmm_lds[];
   __shared__ int s_cum2[kMaxBuckets + 1];  // prefix per bucket of its two-tile chunks
@@ -344,7 +347,8 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
   auto issue_w = [&](Slot<MT>& sl, int g) __attribute__((always_inline)) {
     const uint8_t* u = l_wbase + (size_t)g * kTiledUnit;
     auto ld = [](const uint8_t* a) __attribute__((always_inline)) {
-      if constexpr (MODE == MODE_GATE_UP || MODE == MODE_DENSE_GEGLU) return __builtin_nontemporal_load((const u32x4_t*)a);
+      if constexpr (MODE == MODE_GATE_UP || MODE == MODE_DENSE_GEGLU || MODE == MODE_DENSE_SOFTCAP)
+        return __builtin_nontemporal_load((const u32x4_t*)a);
       else return *(const u32x4_t*)a;
     };
 #pragma unroll
@@ -598,6 +602,32 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
                 *(const u32x4_t*)(stg + m * 1024 + r * 64 + 8 * c);
         }
       }
+    } else if constexpr (MODE == MODE_DENSE_SOFTCAP) {
+      // logits rounded to bf16 (the quantized matmul's output type), widened,
+      // cap * tanh(z / cap); fp32 [16 rows][128 columns] per row tile staged
+      // one tile at a time, a store covers 2 rows
+      float* const stg = (float*)wlds;
+      const int c = lane & 31;
+      const int col = blk * 128 + 4 * c;
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        if (m > 0 && !t2) continue;
+        if (m > 0) wave_lds_fence();  // the previous tile's staging reads are done
+#pragma unroll
+        for (int j = 0; j < kNS; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float z = bf16_bits_to_f32(f32_to_bf16_bits(acc[m][j][i]));
+            stg[(4 * lq + i) * 128 + 16 * j + ln] = p.cap * tanhf(z / p.cap);
+          }
+        wave_lds_fence();
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int r = 2 * q + (lane >> 5), lr = 16 * m + r;
+          if (lr < cinfo.rows && col < p.Nout)
+            *(u32x4_t*)((float*)p.out + (size_t)(cinfo.r0 + lr) * p.Nout + col) = *(const u32x4_t*)(stg + r * 128 + 4 * c);
+        }
+      }
     } else {
       // bf16 [16 rows][128 columns] per row tile; a store covers 4 rows
       uint16_t* const stg = (uint16_t*)wlds;
@@ -831,6 +861,9 @@ hipError_t launch_dense(SwitchArgs a, int num_cu, hipStream_t stream) {
 }
 hipError_t launch_dense_geglu(SwitchArgs a, int num_cu, hipStream_t stream) {
   return launch_mode<MODE_DENSE_GEGLU>(a, 0, num_cu, stream);
+}
+hipError_t launch_dense_softcap(SwitchArgs a, int num_cu, hipStream_t stream) {
+  return launch_mode<MODE_DENSE_SOFTCAP>(a, 0, num_cu, stream);
 }
 hipError_t launch_combine(const uint16_t* D, const float* w, int T, int k, int H, uint16_t* y, hipStream_t stream) {
   const long long n = (long long)T * (H / 8);

@@ -16,6 +16,7 @@
  *   qlinear               dense 4-bit linear
  *   qswitch_gate_up_geglu_unsorted, qswitch_down_combine_unsorted
  *                         the small-batch arm without the sort
+ *   qlinear_softcap       the tied LM head with its fp32 tanh softcap
  *   ff_prenorm, qlinear_geglu, ff_combine
  *                         the decoder's feed-forward block around the MoE
  *                         (pre-norms, dense GeGLU branch, post-norms and
@@ -311,6 +312,23 @@ int qswitch_down_combine_unsorted(const uint16_t* mid_rows, int32_t T, int32_t k
  * ---------------------------------------------------------------------- */
 int qlinear(const uint16_t* x, int32_t M, const qmoe_qweight* W, uint16_t* y,
             hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * qlinear_softcap -- the tied LM head (model.ts page, logitsFromHidden): the
+ * embedding's 4-bit weight used as a linear, its logits returned in bf16 as
+ * the quantized matmul returns them, widened to fp32 and softcapped:
+ *   y[m, v] = cap * tanh(bf16(x[m] . dequant(E)[v]) / cap)      (fp32 out)
+ * cap is the model's final-logit softcapping (30 when the config leaves it
+ * out, model.ts page, the decoder constructor).
+ *
+ *   x        bf16 [M, K]
+ *   W        experts = 1, rows = N (vocabulary), in = K;  K % 64 == 0,
+ *            N % 16 == 0; layout QMOE_LAYOUT_TILED, split = 0
+ *   cap      finite, > 0
+ *   y (out)  fp32 [M, N]
+ * ---------------------------------------------------------------------- */
+int qlinear_softcap(const uint16_t* x, int32_t M, const qmoe_qweight* W, float cap, float* y,
+                    hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * The decoder's feed-forward block around the MoE (model.ts page,

@@ -30,7 +30,8 @@ def test_exports_every_declared_function(L):
     names = header_functions()
     assert set(names) >= {"moe_route", "moe_sort", "qswitch_gate_up_geglu", "qswitch_down_combine",
                           "qlinear", "qmoe_last_error", "ff_prenorm", "qlinear_geglu", "ff_combine",
-                          "qswitch_gate_up_geglu_unsorted", "qswitch_down_combine_unsorted"}
+                          "qswitch_gate_up_geglu_unsorted", "qswitch_down_combine_unsorted",
+                          "qlinear_softcap"}
     for n in names:
         assert hasattr(L, n), f"{n} is declared in qmoe.h but not exported"
 
@@ -149,6 +150,20 @@ def test_qlinear_validation(L):
     bad = qw(1, 1152, 1152, layout=0)
     assert L.qlinear(A16, 8, ctypes.byref(bad), A16, None) == INVALID
     assert L.qlinear(A16, 8, None, A16, None) == INVALID
+
+
+def test_qlinear_softcap_validation(L):
+    f = ctypes.c_float
+    d = qw(1, 4096, 256, layout=1)
+    assert L.qlinear_softcap(None, 0, ctypes.byref(d), f(30.0), None, None) == 0
+    assert L.qlinear_softcap(A16, -1, ctypes.byref(d), f(30.0), A16, None) == INVALID
+    for cap in (0.0, -30.0, float("inf"), float("nan")):
+        assert L.qlinear_softcap(A16, 4, ctypes.byref(d), f(cap), A16, None) == INVALID
+    assert "cap" in err(L)
+    assert L.qlinear_softcap(A16, 4, ctypes.byref(qw(1, 4100, 256, layout=1)), f(30.0), A16, None) == INVALID
+    assert L.qlinear_softcap(A16, 4, ctypes.byref(qw(1, 4096, 256, layout=1, split=2048)), f(30.0), A16,
+                             None) == INVALID
+    assert L.qlinear_softcap(A16, 4, ctypes.byref(d), f(30.0), A16 + 4, None) == INVALID
 
 
 def test_qlinear_geglu_validation(L):

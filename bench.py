@@ -20,6 +20,8 @@ Prints ONE JSON line (rank 0):
              the two unsorted calls) at 1 and 7 tokens on the same weights
   lm_head    diagnostic, not the metric: the tied LM head with its softcap,
              256 rows x 2816 -> 262,144 (fp32 logits)
+  vision_qlinears  diagnostic, not the metric: the vision tower's 4-bit
+             linears, 27 blocks at 2520 x 1152
   ff_block   diagnostic, not the metric: the decoder's feed-forward block
              around the same MoE layer (pre-norms, dense GeGLU branch, the
              layer, post-norms and residual) on the same tokens
@@ -67,6 +69,7 @@ def parse():
     ap.add_argument("--no-ff-block", action="store_true", help="skip the feed-forward block diagnostic")
     ap.add_argument("--no-decode", action="store_true", help="skip the small-batch (unsorted arm) diagnostic")
     ap.add_argument("--no-head", action="store_true", help="skip the LM-head diagnostic")
+    ap.add_argument("--no-vision", action="store_true", help="skip the vision-tower linears diagnostic")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--summarize", metavar="DIR")
@@ -412,6 +415,48 @@ def lm_head_timing(q, torch, synth, K, warmup, vocab=262144, rows=256, hidden=28
             "hbm_bytes": hbm, "achieved_GBs": hbm / (us * 1e-6) / 1e9, "hbm_frac": hbm / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
 
 
+def vision_timing(q, torch, synth, passes=3, blocks=27, rows=2520, hidden=1152, mlp=4304):
+    """Diagnostic: the vision tower's 4-bit linears at their geometry, 27
+    blocks x (q, k, v, o: 1152 -> 1152; gate|up fused with GeGLU: 1152 ->
+    4304) on 2520 patch rows, each block with its own weights (231 MB in all).
+    Attention and the bf16 down projection are not part of this library."""
+    dev = torch.device("cuda:0")
+    rng = np.random.default_rng(51)
+    qw = lambda n: q.QuantWeight(*(torch.from_numpy(a).to(dev) for a in
+                                   (lambda t: (t.w, t.scales, t.biases))(synth.random_qtensor(rng, (n,), hidden))))
+    weights = []
+    for _ in range(blocks):
+        proj = [qw(hidden).tiled(0) for _ in range(4)]
+        g, u = qw(mlp), qw(mlp)
+        gu = q.QuantWeight(torch.cat([g.w, u.w]), torch.cat([g.scales, u.scales]),
+                           torch.cat([g.biases, u.biases])).tiled(mlp)
+        weights.append((proj, gu))
+    x = torch.from_numpy(synth.make_activations(rows, hidden, 52)).to(dev)
+    outs = [torch.empty((rows, hidden), dtype=torch.bfloat16, device=dev) for _ in range(4)]
+    mid = torch.empty((rows, mlp), dtype=torch.bfloat16, device=dev)
+
+    def tower():
+        for proj, gu in weights:
+            for W, y in zip(proj, outs):
+                q.qlinear(x, W, y)
+            q.qlinear_geglu(x, gu, mid)
+
+    tower()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(passes + 1)]
+    ev[0].record()
+    for i in range(passes):
+        tower()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    us = float(np.mean([ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(passes)]))
+    flops = 2.0 * rows * hidden * (4 * hidden + 2 * mlp) * blocks
+    wbytes = (4 * hidden + 2 * mlp) * (hidden // 2 + 4 * (hidden // 64)) * blocks
+    return {"blocks": blocks, "rows": rows, "hidden": hidden, "mlp": mlp, "us_per_tower": us,
+            "tflops": flops / (us * 1e-6) / 1e12, "mfma_frac": flops / (us * 1e-6) / (MFMA_BF16_PEAK_TFLOPS * 1e12),
+            "weight_bytes": wbytes}
+
+
 def main():
     args = parse()
     if args.summarize:
@@ -551,6 +596,8 @@ def main():
         out["decode_unsorted"] = decode_timing(q, torch, synth, sets, K, args.warmup)
     if cfg.name == synth.CANVAS.name and not args.no_head:
         out["lm_head"] = lm_head_timing(q, torch, synth, K, args.warmup)
+    if cfg.name == synth.CANVAS.name and not args.no_vision:
+        out["vision_qlinears"] = vision_timing(q, torch, synth)
     ffc = next((f for f in synth.FF_CONFIGS.values() if f.moe.name == cfg.name), None)
     if ffc is not None and not args.no_ff_block:
         out["ff_block"] = ff_block_timing(q, torch, synth, ffc, x, sets, K, args.warmup, t,

@@ -283,7 +283,7 @@ int qswitch_down_combine(const void* mid, int32_t T, int32_t k, int32_t I, const
 
 size_t qmoe_tiled_weight_bytes(int32_t experts, int32_t rows, int32_t in, int32_t split) {
   if (experts <= 0 || rows <= 0 || in <= 0 || in % 64 != 0 || split < 0) return 0;
-  if (split > 0 && (split % 64 != 0 || rows != 2 * split)) return 0;
+  if (split > 0 && (split % 16 != 0 || rows != 2 * split)) return 0;
   return (size_t)experts * (size_t)qmoe::tiled_blocks(rows, split) * (size_t)(in / 64) * (size_t)qmoe::kTiledUnit;
 }
 
@@ -294,8 +294,8 @@ int qmoe_tile_weight(const qmoe_qweight* src, int32_t split, void* dst, size_t d
   REQUIRE(src->in > 0 && src->in % 64 == 0, QMOE_ERR_INVALID, "qmoe_tile_weight: in=%d must be a positive multiple of 64",
           src->in);
   REQUIRE(split >= 0, QMOE_ERR_INVALID, "qmoe_tile_weight: split=%d < 0", split);
-  REQUIRE(split == 0 || (split % 64 == 0 && src->rows == 2 * split), QMOE_ERR_INVALID,
-          "qmoe_tile_weight: split=%d needs rows == 2*split and split %% 64 == 0 (rows=%d)", split, src->rows);
+  REQUIRE(split == 0 || (split % 16 == 0 && src->rows == 2 * split), QMOE_ERR_INVALID,
+          "qmoe_tile_weight: split=%d needs rows == 2*split and split %% 16 == 0 (rows=%d)", split, src->rows);
   if (int rc = check_qweight(src, "qmoe_tile_weight src", src->experts, src->rows, src->in)) return rc;
   REQUIRE((long long)src->experts * src->rows * (src->in / 8) < (1LL << 31), QMOE_ERR_UNSUPPORTED,
           "qmoe_tile_weight: more than 2^31 code words");
@@ -366,7 +366,7 @@ int qlinear_geglu(const uint16_t* x, int32_t M, const qmoe_qweight* W, uint16_t*
   REQUIRE(W != nullptr, QMOE_ERR_INVALID, "qlinear_geglu: null weight descriptor");
   const int K = W->in, N = W->split;
   REQUIRE(K > 0 && K % 64 == 0, QMOE_ERR_INVALID, "qlinear_geglu: K=%d must be a positive multiple of 64", K);
-  REQUIRE(N > 0 && N % 64 == 0, QMOE_ERR_INVALID, "qlinear_geglu: split=%d must be a positive multiple of 64", N);
+  REQUIRE(N > 0 && N % 16 == 0, QMOE_ERR_INVALID, "qlinear_geglu: split=%d must be a positive multiple of 16", N);
   if (int rc = check_qweight(W, "qlinear_geglu W", 1, 2 * N, K, QMOE_LAYOUT_TILED, N)) return rc;
   if (M == 0) return ok();
   REQUIRE_PTR(x, 16, "qlinear_geglu x");

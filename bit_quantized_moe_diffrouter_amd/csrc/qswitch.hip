@@ -597,7 +597,7 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
           const int r = 8 * q + (lane >> 3), lr = 16 * m + r;
-          if (lr < cinfo.rows)
+          if (lr < cinfo.rows && blk * 64 + 8 * c < p.Nout)  // the last block may be partly past the width
             *(u32x4_t*)((uint16_t*)p.out + (size_t)(cinfo.r0 + lr) * p.Nout + blk * 64 + 8 * c) =
                 *(const u32x4_t*)(stg + m * 1024 + r * 64 + 8 * c);
         }
@@ -699,9 +699,14 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
 }
 
 // ---------------------------------------------------------------- weight tiling
-// Weight row of block b, subtile j, row n (split > 0: gate rows then up rows).
+// Weight row of block b, subtile j, row n (split > 0: gate rows then up rows;
+// past the gate half's end, -1: read as zero).
 __device__ __forceinline__ int tiled_row(int b, int j, int n, int split) {
-  if (split > 0) return (j < 4) ? 64 * b + 16 * j + n : split + 64 * b + 16 * (j - 4) + n;
+  if (split > 0) {
+    const int c = 64 * b + 16 * (j & 3) + n;  // column of the pair
+    if (c >= split) return -1;
+    return (j < 4) ? c : split + c;
+  }
   return 128 * b + 16 * j + n;
 }
 
@@ -736,7 +741,7 @@ __global__ __launch_bounds__(256) void tile_weight_kernel(const uint32_t* __rest
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const int row = tiled_row(b, 2 * i + t, n, split);
-      if (row < rows) {
+      if (row >= 0 && row < rows) {
         const uint32_t* src = w + ((size_t)e * rows + row) * KW + g * 8 + 2 * kq;
         out[2 * t] = operand_word(src[0]);
         out[2 * t + 1] = operand_word(src[1]);
@@ -747,7 +752,7 @@ __global__ __launch_bounds__(256) void tile_weight_kernel(const uint32_t* __rest
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const int row = tiled_row(b, 4 * h + jj, n, split);
-      if (row < rows) {
+      if (row >= 0 && row < rows) {
         const size_t si = ((size_t)e * rows + row) * G + g;
         out[jj] = (uint32_t)s[si] | ((uint32_t)bi[si] << 16);
       }
@@ -871,7 +876,7 @@ hipError_t launch_combine(const uint16_t* D, const float* w, int T, int k, int H
   hipLaunchKernelGGL(combine_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, D, w, T, k, H, y);
   return hipGetLastError();
 }
-int tiled_blocks(int rows, int split) { return split > 0 ? split / 64 : (rows + 127) / 128; }
+int tiled_blocks(int rows, int split) { return split > 0 ? (split + 63) / 64 : (rows + 127) / 128; }
 hipError_t launch_tile_weight(const uint32_t* w, const uint16_t* s, const uint16_t* b, int E, int rows, int K,
                               int split, uint8_t* dst, hipStream_t stream) {
   const int nblk = tiled_blocks(rows, split);

@@ -110,12 +110,14 @@ const char* qmoe_last_error(void);
  * vision.ts page, VisionLinear).  Done once when the weights are loaded.
  *
  * Tiled layout: units of 4608 bytes, unit index ((e * nblk + b) * (in/64) + g)
- * for expert e, row block b (nblk blocks of 128 rows), group g.  Block b holds
- * 8 subtiles of 16 rows; row n of subtile j is weight row
+ * for expert e, row block b, group g; nblk = ceil(rows / 128) blocks for
+ * split == 0, ceil(split / 64) for a fused pair.  Block b holds 8 subtiles of
+ * 16 rows; row n of subtile j is weight row
  *   split == 0:  128 b + 16 j + n
- *   split  > 0:  j < 4: 64 b + 16 j + n;  j >= 4: split + 64 b + 16 (j-4) + n
+ *   split  > 0:  with c = 64 b + 16 (j % 4) + n:  j < 4: c;  j >= 4: split + c
  * (so a fused gate|up weight keeps gate row c and up row split + c in one
- * block); rows past `rows` read as zero.  Bytes [0, 4096) of a unit: for
+ * block); rows past `rows`, and for a fused pair every c >= split, read as
+ * zero.  Bytes [0, 4096) of a unit: for
  * i = 0..3 and lane L = 0..63 (n = L % 16, q = L / 16), 16 bytes at
  * 1024 i + 16 L = two code words of subtile 2i then two of subtile 2i+1 of
  * row n: word 2q and word 2q+1 of the group (codes 16q .. 16q+15), each with
@@ -124,7 +126,8 @@ const char* qmoe_last_error(void);
  * 4096 + 256 h + 16 n = (scale, bias) bf16 pairs of subtiles 4h .. 4h+3, row n.
  *
  *   src        layout QMOE_LAYOUT_ROWS, in % 64 == 0
- *   split      0, or rows/2 for a fused pair (split % 64 == 0)
+ *   split      0, or rows/2 for a fused pair (split % 16 == 0; the switch
+ *              calls need split % 64 == 0 since their I is a multiple of 64)
  *   dst        device buffer of qmoe_tiled_weight_bytes(...) bytes, 16-byte
  *              aligned, owned by the caller (the tiled weight's `w`)
  * qmoe_tiled_weight_bytes returns 0 for sizes it does not accept.
@@ -372,7 +375,7 @@ int ff_prenorm(const uint16_t* h, int32_t T, int32_t H, const uint16_t* w_dense,
  *
  *   x        bf16 [M, K]
  *   W        experts = 1, rows = 2N, in = K (rows 0..N-1 gate, N..2N-1 up);
- *            K % 64 == 0, N % 64 == 0; layout QMOE_LAYOUT_TILED with split = N
+ *            K % 64 == 0, N % 16 == 0; layout QMOE_LAYOUT_TILED with split = N
  *   y (out)  bf16 [M, N]
  * The down projection is qlinear on y. */
 int qlinear_geglu(const uint16_t* x, int32_t M, const qmoe_qweight* W, uint16_t* y,

@@ -172,7 +172,7 @@ def test_qlinear_geglu_validation(L):
     assert L.qlinear_geglu(A16, -1, ctypes.byref(d), A16, None) == INVALID
     for bad in (qw(1, 2 * 192, 256, layout=1, split=0),      # not tiled as a fused pair
                 qw(1, 2 * 192, 256, layout=1, split=128),    # rows != 2 * split
-                qw(1, 2 * 160, 256, layout=1, split=160),    # split not a multiple of 64
+                qw(1, 2 * 72, 256, layout=1, split=72),      # split not a multiple of 16
                 qw(1, 2 * 192, 200, layout=1, split=192),    # K not a multiple of 64
                 qw(2, 2 * 192, 256, layout=1, split=192),    # not dense
                 qw(1, 2 * 192, 256, layout=0, split=192)):   # row-major codes
@@ -259,7 +259,9 @@ def test_tile_weight_sizes_and_validation(L):
     assert L.qmoe_tiled_weight_bytes(1, 1152, 1152, 0) == 1 * 9 * 18 * 4608
     assert L.qmoe_tiled_weight_bytes(1, 48, 192, 0) == 1 * 1 * 3 * 4608  # rows padded to a block
     assert L.qmoe_tiled_weight_bytes(8, 256, 100, 0) == 0
-    assert L.qmoe_tiled_weight_bytes(8, 200, 256, 100) == 0  # split must be rows / 2, a multiple of 64
+    assert L.qmoe_tiled_weight_bytes(8, 200, 256, 100) == 0  # split must be rows / 2, a multiple of 16
+    # a fused pair whose width is a multiple of 16 only (the vision MLP's 4304): 68 blocks of 64 columns
+    assert L.qmoe_tiled_weight_bytes(1, 2 * 4304, 1152, 4304) == 68 * 18 * 4608
     src = qw(8, 256, 256)
     need = L.qmoe_tiled_weight_bytes(8, 256, 256, 128)
     assert L.qmoe_tile_weight(ctypes.byref(src), 128, A16, need - 1, None) == INVALID

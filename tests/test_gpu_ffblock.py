@@ -116,7 +116,8 @@ def test_ff_norms_of_a_zero_branch_row_use_eps():
 
 
 # ---------------------------------------------------------------- dense GeGLU
-@pytest.mark.parametrize("M,K,N", [(16, 256, 192), (37, 320, 128), (1, 64, 64), (100, 1152, 448), (65, 128, 576)])
+@pytest.mark.parametrize("M,K,N", [(16, 256, 192), (37, 320, 128), (1, 64, 64), (100, 1152, 448), (65, 128, 576),
+                                   (33, 192, 48), (70, 256, 208)])
 def test_qlinear_geglu_parity(M, K, N):
     import bit_quantized_moe_diffrouter_amd as q
     say(f"[qlinear_geglu] M={M} K={K} N={N}")
@@ -196,3 +197,25 @@ def test_ff_block_dense_branch_matches_the_oracle_branch():
     err = O.rowwise_rel_err(bf16_host(dense), ref)
     say(f"  dense branch rel err {err:.3e}")
     assert err <= BLOCK_TOL
+
+
+def test_qlinear_geglu_vision_mlp_width_sampled_rows():
+    """The vision tower's MLP gate|up at its geometry: 2520 x 1152 -> 4304, a
+    width that is a multiple of 16 but not of 64 (the last tiled block is
+    three-quarters empty); sampled rows, every column."""
+    import bit_quantized_moe_diffrouter_amd as q
+    M, K, N = 2520, 1152, 4304
+    say(f"[qlinear_geglu] vision MLP {M}x{K} -> {N}")
+    rng = np.random.default_rng(41)
+    gate = synth.random_qtensor(rng, (N,), K)
+    up = synth.random_qtensor(rng, (N,), K)
+    x = synth.make_activations(M, K, seed=42)
+    fused = q.QuantWeight(torch.cat([dev_tensor(gate.w), dev_tensor(up.w)]),
+                          torch.cat([dev_tensor(gate.scales), dev_tensor(up.scales)]),
+                          torch.cat([dev_tensor(gate.biases), dev_tensor(up.biases)])).tiled(N)
+    y = q.qlinear_geglu(dev_tensor(x), fused)
+    torch.cuda.synchronize()
+    rows = [0, 1, 31, 32, 1000, 2495, 2519]
+    err = O.rowwise_rel_err(bf16_host(y)[rows], O.dense_geglu(x, gate, up, rows=rows))
+    say(f"  rel err {err:.3e}")
+    assert err <= GEGLU_TOL

@@ -397,16 +397,18 @@ def tiled_reference(w, s, b, split):
     from its definition: a pure rearrangement of codes, scales and biases."""
     E, rows, KW = w.shape
     G = KW // 8
-    nblk = split // 64 if split else -(-rows // 128)
+    nblk = -(-split // 64) if split else -(-rows // 128)
     out = np.zeros((E, nblk, G, 4608), dtype=np.uint8)
     n = np.arange(16)
     for blk in range(nblk):
         for j in range(8):
             if split:
-                r = (64 * blk + 16 * j + n) if j < 4 else (split + 64 * blk + 16 * (j - 4) + n)
+                c = 64 * blk + 16 * (j % 4) + n
+                r = c if j < 4 else split + c
+                ok = (c < split) & (r < rows)
             else:
                 r = 128 * blk + 16 * j + n
-            ok = r < rows
+                ok = r < rows
             rr = np.where(ok, r, 0)
             for q in range(4):  # lane L = 16 q + n: words 2q, 2q+1 of the group
                 for t in range(2):
@@ -430,7 +432,7 @@ def tiled_reference(w, s, b, split):
 
 
 @pytest.mark.parametrize("E,rows,K,split", [(3, 256, 192, 128), (2, 200, 128, 0), (1, 48, 64, 0),
-                                           (2, 1408, 2816, 704)])
+                                           (2, 1408, 2816, 704), (1, 96, 128, 48), (2, 416, 64, 208)])
 def test_tile_weight_layout_bitwise(E, rows, K, split):
     import bit_quantized_moe_diffrouter_amd as q
     say(f"[tile] E={E} rows={rows} K={K} split={split}")

@@ -101,3 +101,25 @@ def test_head_with_huge_cap_is_the_bf16_qlinear():
     a = capped.cpu().numpy().astype(np.float64)
     b = bf16_host(plain)
     assert np.allclose(a, b, rtol=1e-6, atol=0)
+
+
+@pytest.mark.parametrize("M,K", [(100, 128), (17, 192), (64, 64)])
+def test_head_wide_ragged_rows_sampled(M, K):
+    """A wide head (131,072 rows of weights, enough items to fill the chip
+    without splitting the contraction) at ragged row counts: 100 (three full
+    32-row chunks and one of 4 rows), 17 (a second tile holding one row), 64;
+    sampled columns, every row."""
+    import bit_quantized_moe_diffrouter_amd as q
+    N = 131072
+    say(f"[head] wide M={M} K={K} N={N}")
+    rng = np.random.default_rng(M + K)
+    W = synth.random_qtensor(rng, (N,), K)
+    x = synth.make_activations(M, K, seed=M * 3 + 1)
+    y = q.qlinear_softcap(dev_tensor(x), dev_qweight(W).tiled(0), 30.0)
+    torch.cuda.synchronize()
+    cols = sorted(np.random.default_rng(M).choice(N, size=384, replace=False).tolist()) + [N - 1]
+    got = y[:, cols].cpu().numpy().astype(np.float64)
+    ref = O.lm_head_softcap(x, W.w[cols], W.scales[cols], W.biases[cols], 30.0)
+    err = O.rowwise_rel_err(got, ref)
+    say(f"  rel err {err:.3e}")
+    assert err <= 1e-2

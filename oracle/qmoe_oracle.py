@@ -40,6 +40,9 @@ L  dense 4-bit linear ``y = x . W^T``
 H  the tied LM head: ``cap * tanh(bf16(x . E^T) / cap)``, fp32 out
                                   ([model page] logitsFromHidden, the softcap
                                    default in the constructor)
+C  self-conditioning embedding: ``bf16(bf16(softmax(z) . E) * embed_scale)``
+   with the table E used without transposing
+                                  ([model page] #embedCanvas)
 F  the decoder's feed-forward block around the MoE: plain RMSNorm with its
    weight used as stored (no 1 + w offset); the parallel dense GeGLU MLP
    ``down(gelu_tanh(gate x) * up x)``; ``out = (h + N(N1(h1) + N2(h2))) * s``
@@ -441,6 +444,30 @@ def lm_head_softcap(x_bits, words, scales, biases, cap: float,
         x = x[list(rows)]
     z = x @ dequantize(words, scales, biases).T
     return softcap(bf16_to_f64(f64_to_bf16_bits(z)), cap)
+
+
+# ----------------------------------------------------------------------------
+# C: the self-conditioning embedding (probabilities times the embedding table)
+# ----------------------------------------------------------------------------
+def softmax_rows_bf16(logits) -> np.ndarray:
+    """Precise softmax over the last axis in fp64, cast to bf16 bit patterns
+    ([model page] #embedCanvas: softmaxAxis(scLogits, -1, precise) then
+    astype to the embeddings' dtype)."""
+    return f64_to_bf16_bits(precise_softmax(logits))
+
+
+def embed_matmul_t(probs_bits, words, scales, biases, scale: float,
+                   rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    """``bf16(bf16(p . dequant(E)) * scale)`` with E the embedding table
+    [V, H] used without transposing ([model page] #embedCanvas: the quantized
+    matmul with transpose = false returns bf16, then mulScalar by embed_scale):
+    probabilities [L, V] bf16 -> [L, H], fp64 inside each step.  ``rows``
+    restricts the output rows."""
+    p = bf16_to_f64(probs_bits)
+    if rows is not None:
+        p = p[list(rows)]
+    se = bf16_to_f64(f64_to_bf16_bits(p @ dequantize(words, scales, biases)))
+    return bf16_to_f64(f64_to_bf16_bits(se * np.float64(np.float32(scale))))
 
 
 # ----------------------------------------------------------------------------

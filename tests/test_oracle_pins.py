@@ -469,3 +469,41 @@ def test_lm_head_rounds_to_bf16_before_the_cap():
     got = O.lm_head_softcap(x, words, scales, biases, 30.0)
     assert abs(got[0, 0] - 30.0 * math.tanh(256.0 / 30.0)) < 1e-12
     assert abs(got[0, 0] - 30.0 * math.tanh(257.0 / 30.0)) > 1e-8
+
+
+# ---------------------------------------------------------------------------- C: self-conditioning embedding
+def test_embed_matmul_t_one_hot_probabilities_pick_a_row():
+    """Logits with one value far above the rest give a probability of exactly
+    1 there and 0 elsewhere, so the product is that row of the dequantized
+    table, rounded to bf16, times the scale, rounded again."""
+    rng = np.random.default_rng(31)
+    V, H, L = 96, 128, 3
+    W = synth.random_qtensor(rng, (V,), H)
+    logits = rng.standard_normal((L, V))
+    hot = [5, 0, 95]
+    for l, v in enumerate(hot):
+        logits[l, v] += 2000.0
+    p = O.softmax_rows_bf16(logits)
+    assert np.array_equal(O.bf16_to_f64(p).sum(axis=1), np.ones(L))
+    scale = math.sqrt(2816.0)
+    got = O.embed_matmul_t(p, W.w, W.scales, W.biases, scale)
+    Wd = O.dequantize(W.w, W.scales, W.biases)
+    for l, v in enumerate(hot):
+        row = O.bf16_to_f64(O.f64_to_bf16_bits(Wd[v]))
+        want = O.bf16_to_f64(O.f64_to_bf16_bits(row * np.float32(scale)))
+        assert np.array_equal(got[l], want)
+
+
+def test_embed_matmul_t_uniform_probabilities_give_column_means():
+    """Equal logits over V = 2^k entries give probabilities of exactly 2^-k,
+    so the product is the table's column sums times 2^-k."""
+    rng = np.random.default_rng(32)
+    V, H = 256, 64
+    W = synth.random_qtensor(rng, (V,), H)
+    p = O.softmax_rows_bf16(np.zeros((2, V)))
+    assert np.all(O.bf16_to_f64(p) == 2.0 ** -8)
+    got = O.embed_matmul_t(p, W.w, W.scales, W.biases, 1.0)
+    cols = O.dequantize(W.w, W.scales, W.biases).sum(axis=0) * 2.0 ** -8
+    want = O.bf16_to_f64(O.f64_to_bf16_bits(cols))
+    assert np.array_equal(got[0], want) and np.array_equal(got[1], want)
+    assert np.array_equal(O.embed_matmul_t(p, W.w, W.scales, W.biases, 1.0, rows=[1]), got[[1]])

@@ -19,7 +19,8 @@ Prints ONE JSON line (rank 0):
   decode_unsorted  diagnostic, not the metric: the small-batch arm (route +
              the two unsorted calls) at 1 and 7 tokens on the same weights
   lm_head    diagnostic, not the metric: the tied LM head with its softcap,
-             256 rows x 2816 -> 262,144 (fp32 logits)
+             256 rows x 2816 -> 262,144 (fp32 logits), and the self-conditioning
+             signal on the same table (softmax to bf16, untransposed product)
   vision_qlinears  diagnostic, not the metric: the vision tower's 4-bit
              linears, 27 blocks at 2520 x 1152
   ff_block   diagnostic, not the metric: the decoder's feed-forward block
@@ -391,9 +392,11 @@ def lm_head_timing(q, torch, synth, K, warmup, vocab=262144, rows=256, hidden=28
     dev = torch.device("cuda:0")
     rng = np.random.default_rng(31)
     W = synth.random_qtensor(rng, (vocab,), hidden)
-    Wt = q.QuantWeight(torch.from_numpy(W.w).to(dev), torch.from_numpy(W.scales).to(dev),
-                       torch.from_numpy(W.biases).to(dev)).tiled(0)
-    del W
+    Wq = q.QuantWeight(torch.from_numpy(W.w).to(dev), torch.from_numpy(W.scales).to(dev),
+                       torch.from_numpy(W.biases).to(dev))
+    Wt = Wq.tiled(0)
+    WtT = Wq.tiled_t()  # the same table for the untransposed self-conditioning product
+    del W, Wq
     x = torch.from_numpy(synth.make_activations(rows, hidden, 32)).to(dev)
     y = torch.empty((rows, vocab), dtype=torch.float32, device=dev)
     n = max(4, K // 10)
@@ -410,9 +413,37 @@ def lm_head_timing(q, torch, synth, K, warmup, vocab=262144, rows=256, hidden=28
     flops = 2.0 * rows * vocab * hidden
     wbytes = vocab * (hidden // 2 + 4 * (hidden // 64))
     hbm = wbytes + rows * hidden * 2 + rows * vocab * 4
-    return {"rows": rows, "vocab": vocab, "hidden": hidden, "calls": n, "mean_launch_us": us,
+    head = {"rows": rows, "vocab": vocab, "hidden": hidden, "calls": n, "mean_launch_us": us,
             "tflops": flops / (us * 1e-6) / 1e12, "mfma_frac": flops / (us * 1e-6) / (MFMA_BF16_PEAK_TFLOPS * 1e12),
             "hbm_bytes": hbm, "achieved_GBs": hbm / (us * 1e-6) / 1e9, "hbm_frac": hbm / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+    # the self-conditioning signal on the same table: softmax of fp32 logits
+    # [rows, vocab] to bf16, then probabilities times the untransposed table
+    z = y  # the head's softcapped logits serve as self-conditioning logits
+    probs = torch.empty((rows, vocab), dtype=torch.bfloat16, device=dev)
+    se = torch.empty((rows, hidden), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(int(q.lib().embed_matmul_t_workspace(rows, vocab, hidden)), dtype=torch.uint8, device=dev)
+    scale = float(np.sqrt(hidden))
+    for _ in range(2):
+        q.softmax_rows_bf16(z, probs)
+        q.embed_matmul_t(probs, WtT, scale, se, ws)
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n)]
+    for e in ev:
+        e[0].record()
+        q.softmax_rows_bf16(z, probs)
+        e[1].record()
+        q.embed_matmul_t(probs, WtT, scale, se, ws)
+        e[2].record()
+    torch.cuda.synchronize()
+    us_sm = float(np.mean([e[0].elapsed_time(e[1]) * 1e3 for e in ev]))
+    us_mm = float(np.mean([e[1].elapsed_time(e[2]) * 1e3 for e in ev]))
+    sm_bytes = rows * vocab * (4 * 2 + 2)  # two passes over the fp32 logits, bf16 out
+    head["self_conditioning"] = {
+        "softmax_us": us_sm, "softmax_GBs": sm_bytes / (us_sm * 1e-6) / 1e9,
+        "product_us": us_mm, "product_tflops": flops / (us_mm * 1e-6) / 1e12,
+        "product_mfma_frac": flops / (us_mm * 1e-6) / (MFMA_BF16_PEAK_TFLOPS * 1e12),
+        "product_hbm_GBs": (wbytes + rows * vocab * 2) / (us_mm * 1e-6) / 1e9}
+    return head
 
 
 def vision_timing(q, torch, synth, passes=3, blocks=27, rows=2520, hidden=1152, mlp=4304):

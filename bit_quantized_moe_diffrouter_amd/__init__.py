@@ -28,6 +28,7 @@ __all__ = [
     "qswitch_gate_up_geglu",
     "qswitch_down_combine", "qswitch_down_combine_workspace", "qlinear", "moe_layer",
     "ff_prenorm", "qlinear_geglu", "ff_combine", "FFParams", "ff_block", "qlinear_softcap",
+    "TiledTWeight", "softmax_rows_bf16", "embed_matmul_t", "self_condition_embed",
     "qswitch_unsorted_workspace", "unsorted_workspace", "qswitch_gate_up_geglu_unsorted",
     "qswitch_down_combine_unsorted", "moe_layer_unsorted",
 ]
@@ -79,6 +80,11 @@ _SIGNATURES = {
     "qlinear": (ctypes.c_int, [_P, _I, _QP, _P, _P]),
     "qlinear_geglu": (ctypes.c_int, [_P, _I, _QP, _P, _P]),
     "qlinear_softcap": (ctypes.c_int, [_P, _I, _QP, ctypes.c_float, _P, _P]),
+    "qmoe_tiled_weight_t_bytes": (_SZ, [_I, _I]),
+    "qmoe_tile_weight_t": (ctypes.c_int, [_QP, _P, _SZ, _P]),
+    "softmax_rows_bf16": (ctypes.c_int, [_P, _I, _I, _P, _P]),
+    "embed_matmul_t_workspace": (_SZ, [_I, _I, _I]),
+    "embed_matmul_t": (ctypes.c_int, [_P, _I, _QP, ctypes.c_float, _P, _P, _SZ, _P]),
     "qswitch_unsorted_workspace": (_SZ, [_I, _I, _I, _I]),
     "qswitch_gate_up_geglu_unsorted": (ctypes.c_int, [_P, _I, _I, _QP, _I, _I, _P, _P, _P, _SZ, _P]),
     "qswitch_down_combine_unsorted": (ctypes.c_int, [_P, _I, _I, _I, _QP, _I, _P, _P, _P, _P, _SZ, _P]),
@@ -173,6 +179,16 @@ class QuantWeight:
     def from_numpy(cls, w, scales, biases, device="cuda") -> "QuantWeight":
         return cls(torch.from_numpy(w).to(device), torch.from_numpy(scales).to(device),
                    torch.from_numpy(biases).to(device))
+
+    def tiled_t(self) -> "TiledTWeight":
+        """The re-laid copy the untransposed product reads (qmoe_tile_weight_t)."""
+        n = int(lib().qmoe_tiled_weight_t_bytes(self.rows, self.in_features))
+        if n == 0 or self.experts != 1 or self.w.dim() != 2:
+            raise ValueError(f"cannot tile a [{self.rows}, {self.in_features}] table for the untransposed product")
+        buf = torch.empty(n, dtype=torch.uint8, device=self.w.device)
+        d = self.desc()
+        _check(lib().qmoe_tile_weight_t(ctypes.byref(d), _ptr(buf), n, _stream()))
+        return TiledTWeight(buf, self.rows, self.in_features)
 
     def tiled(self, split: int = 0) -> "TiledWeight":
         """The tiled copy the switch linears and qlinear read (qmoe_tile_weight)."""
@@ -505,3 +521,53 @@ def qlinear_softcap(x: torch.Tensor, W: "TiledWeight", cap: float = 30.0,
     d = W.desc()
     _check(lib().qlinear_softcap(_ptr(x), M, ctypes.byref(d), float(cap), _ptr(y), _stream()))
     return y
+
+
+# ----------------------------------------------------------------------------
+# the self-conditioning embedding
+# ----------------------------------------------------------------------------
+@dataclass
+class TiledTWeight:
+    """An embedding table [rows, in] re-laid for the untransposed product (qmoe_tile_weight_t)."""
+
+    buf: torch.Tensor
+    rows: int
+    in_features: int
+
+    def desc(self) -> QWeightDesc:
+        _need(self.buf, "tiled table", 1)
+        return QWeightDesc(self.buf.data_ptr(), None, None, 1, self.rows, self.in_features, 4, 64, 2, 0)
+
+
+def softmax_rows_bf16(z: torch.Tensor, probs: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Precise row softmax of fp32 logits, cast to bf16: returns bf16 [L, V]."""
+    _need(z, "z", 4)
+    L, V = (int(v) for v in z.shape)
+    if probs is None:
+        probs = torch.empty((L, V), dtype=torch.bfloat16, device=z.device)
+    _need(probs, "probs", 2, (L, V))
+    _check(lib().softmax_rows_bf16(_ptr(z), L, V, _ptr(probs), _stream()))
+    return probs
+
+
+def embed_matmul_t(probs: torch.Tensor, W: TiledTWeight, scale: float, out: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """bf16(bf16(probs . dequant(E)) * scale) with the table E [V, H] used
+    without transposing: returns bf16 [L, H]."""
+    _need(probs, "probs", 2)
+    L = int(probs.shape[0])
+    if out is None:
+        out = torch.empty((L, W.in_features), dtype=torch.bfloat16, device=probs.device)
+    _need(out, "out", 2, (L, W.in_features))
+    if workspace is None:
+        workspace = torch.empty(max(1, int(lib().embed_matmul_t_workspace(L, W.rows, W.in_features))),
+                                dtype=torch.uint8, device=probs.device)
+    d = W.desc()
+    _check(lib().embed_matmul_t(_ptr(probs), L, ctypes.byref(d), float(scale), _ptr(out), _ptr(workspace),
+                                _nbytes(workspace), _stream()))
+    return out
+
+
+def self_condition_embed(sc_logits: torch.Tensor, W: TiledTWeight, scale: float) -> torch.Tensor:
+    """The self-conditioning signal: softmax of the logits to bf16, times the table, times scale."""
+    return embed_matmul_t(softmax_rows_bf16(sc_logits), W, scale)

@@ -64,6 +64,10 @@ int check_qweight(const qmoe_qweight* q, const char* what, int experts, int rows
     REQUIRE_PTR(q->w, 16, "tiled weight");
     return QMOE_OK;
   }
+  if (layout == QMOE_LAYOUT_TILED_T) {
+    REQUIRE_PTR(q->w, 16, "tiled table");
+    return QMOE_OK;
+  }
   REQUIRE_PTR(q->w, 16, "weight codes");
   REQUIRE_PTR(q->scales, 2, "weight scales");
   REQUIRE_PTR(q->biases, 2, "weight biases");
@@ -505,6 +509,62 @@ int qswitch_down_combine_unsorted(const uint16_t* mid_rows, int32_t T, int32_t k
   a.out = y;
   a.Nout = H;
   return launched(qmoe::launch_unsorted(qmoe::UNSORTED_DOWN, a, stream), fn);
+}
+
+}  // extern "C"
+
+extern "C" {
+
+size_t qmoe_tiled_weight_t_bytes(int32_t V, int32_t H) {
+  if (V <= 0 || H <= 0 || V % 32 != 0 || H % 64 != 0) return 0;
+  return (size_t)(H / 64) * (size_t)(V / 32) * 1152;
+}
+
+int qmoe_tile_weight_t(const qmoe_qweight* src, void* dst, size_t dst_bytes, hipStream_t stream) {
+  REQUIRE(src != nullptr, QMOE_ERR_INVALID, "qmoe_tile_weight_t: null weight descriptor");
+  const int V = src->rows, H = src->in;
+  REQUIRE(V > 0 && V % 32 == 0, QMOE_ERR_INVALID, "qmoe_tile_weight_t: rows=%d must be a positive multiple of 32", V);
+  REQUIRE(H > 0 && H % 64 == 0, QMOE_ERR_INVALID, "qmoe_tile_weight_t: in=%d must be a positive multiple of 64", H);
+  if (int rc = check_qweight(src, "qmoe_tile_weight_t src", 1, V, H, QMOE_LAYOUT_ROWS)) return rc;
+  REQUIRE_PTR(dst, 16, "qmoe_tile_weight_t dst");
+  const size_t need = qmoe_tiled_weight_t_bytes(V, H);
+  REQUIRE(dst_bytes >= need, QMOE_ERR_INVALID, "qmoe_tile_weight_t: dst of %zu bytes needed, %zu given", need, dst_bytes);
+  return launched(qmoe::launch_tile_weight_t(src->w, src->scales, src->biases, V, H, (uint8_t*)dst, stream),
+                  "qmoe_tile_weight_t");
+}
+
+int softmax_rows_bf16(const float* z, int32_t L, int32_t V, uint16_t* probs, hipStream_t stream) {
+  REQUIRE(L >= 0, QMOE_ERR_INVALID, "softmax_rows_bf16: L=%d < 0", L);
+  REQUIRE(V > 0 && V % 4 == 0, QMOE_ERR_INVALID, "softmax_rows_bf16: V=%d must be a positive multiple of 4", V);
+  if (L == 0) return ok();
+  REQUIRE_PTR(z, 16, "softmax_rows_bf16 z");
+  REQUIRE_PTR(probs, 16, "softmax_rows_bf16 probs");
+  return launched(qmoe::launch_softmax_rows_bf16(z, L, V, probs, stream), "softmax_rows_bf16");
+}
+
+size_t embed_matmul_t_workspace(int32_t L, int32_t V, int32_t H) {
+  if (L <= 0 || V <= 0 || H <= 0 || V % 32 != 0 || H % 64 != 0) return 0;
+  return (size_t)qmoe::embed_t_splits(L, V, H) * (size_t)L * (size_t)H * sizeof(float);
+}
+
+int embed_matmul_t(const uint16_t* probs, int32_t L, const qmoe_qweight* W, float scale, uint16_t* out,
+                   void* workspace, size_t ws_bytes, hipStream_t stream) {
+  REQUIRE(L >= 0, QMOE_ERR_INVALID, "embed_matmul_t: L=%d < 0", L);
+  REQUIRE(W != nullptr, QMOE_ERR_INVALID, "embed_matmul_t: null weight descriptor");
+  REQUIRE(std::isfinite(scale), QMOE_ERR_INVALID, "embed_matmul_t: scale must be finite");
+  const int V = W->rows, H = W->in;
+  REQUIRE(V > 0 && V % 32 == 0, QMOE_ERR_INVALID, "embed_matmul_t: rows=%d must be a positive multiple of 32", V);
+  REQUIRE(H > 0 && H % 64 == 0, QMOE_ERR_INVALID, "embed_matmul_t: in=%d must be a positive multiple of 64", H);
+  if (int rc = check_qweight(W, "embed_matmul_t W", 1, V, H, QMOE_LAYOUT_TILED_T)) return rc;
+  if (L == 0) return ok();
+  REQUIRE_PTR(probs, 16, "embed_matmul_t probs");
+  REQUIRE_PTR(out, 16, "embed_matmul_t out");
+  REQUIRE_PTR(workspace, 16, "embed_matmul_t workspace");
+  const size_t need = embed_matmul_t_workspace(L, V, H);
+  REQUIRE(ws_bytes >= need, QMOE_ERR_WORKSPACE, "embed_matmul_t: workspace of %zu bytes needed, %zu given", need,
+          ws_bytes);
+  return launched(qmoe::launch_embed_t(probs, L, V, H, W->w, scale, (float*)workspace, out, stream),
+                  "embed_matmul_t");
 }
 
 }  // extern "C"

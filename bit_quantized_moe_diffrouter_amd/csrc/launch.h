@@ -93,6 +93,15 @@ struct UnsortedPlan {
 UnsortedPlan unsorted_plan(long long A, int nblk, int G);
 hipError_t launch_unsorted(int mode, UnsortedArgs a, hipStream_t stream);
 
+// ---------------------------------------------------------------- self-conditioning embedding
+// the untransposed table's tiling, 1152-byte units per (64-column group, 32-row chunk)
+hipError_t launch_tile_weight_t(const uint32_t* w, const uint16_t* s, const uint16_t* b, int V, int H, uint8_t* dst,
+                                hipStream_t stream);
+int embed_t_splits(int L, int V, int H);  // row ranges summed by the second kernel (workspace: splits * L * H fp32)
+hipError_t launch_embed_t(const uint16_t* probs, int L, int V, int H, const void* wt, float scale, float* part,
+                          uint16_t* out, hipStream_t stream);
+hipError_t launch_softmax_rows_bf16(const float* z, int L, int V, uint16_t* probs, hipStream_t stream);
+
 // ---------------------------------------------------------------- feed-forward block norms
 // xa = rms(h) * wa, xb = rms(h) * wb (bf16 [T, H] each, H % 8 == 0)
 hipError_t launch_ff_prenorm(const uint16_t* h, int T, int H, const uint16_t* wa, const uint16_t* wb, float eps,

@@ -17,6 +17,9 @@
  *   qswitch_gate_up_geglu_unsorted, qswitch_down_combine_unsorted
  *                         the small-batch arm without the sort
  *   qlinear_softcap       the tied LM head with its fp32 tanh softcap
+ *   softmax_rows_bf16, embed_matmul_t
+ *                         the self-conditioning embedding (probabilities
+ *                         times the untransposed 4-bit table)
  *   ff_prenorm, qlinear_geglu, ff_combine
  *                         the decoder's feed-forward block around the MoE
  *                         (pre-norms, dense GeGLU branch, post-norms and
@@ -71,6 +74,7 @@ extern "C" {
 /* Weight layouts (qmoe_qweight.layout). */
 #define QMOE_LAYOUT_ROWS 0  /* row-major codes + separate scale/bias arrays   */
 #define QMOE_LAYOUT_TILED 1 /* the tiled buffer written by qmoe_tile_weight   */
+#define QMOE_LAYOUT_TILED_T 2 /* the buffer written by qmoe_tile_weight_t     */
 
 /* A 4-bit group-quantized weight (one dense matrix, or `experts` stacked
  * matrices for a switch linear) of `rows` output rows and `in` inputs.
@@ -332,6 +336,44 @@ int qlinear(const uint16_t* x, int32_t M, const qmoe_qweight* W, uint16_t* y,
  * ---------------------------------------------------------------------- */
 int qlinear_softcap(const uint16_t* x, int32_t M, const qmoe_qweight* W, float cap, float* y,
                     hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * The self-conditioning embedding (model.ts page, #embedCanvas): the
+ * precise softmax of the self-conditioning logits cast to bf16, times the
+ * embedding table's 4-bit weight used WITHOUT transposing, returned in bf16,
+ * times embed_scale (sqrt(hidden) in the model):
+ *
+ *   softmax_rows_bf16:  probs[l, v] = bf16( exp(z - max) / sum exp(z - max) )
+ *                       (fp32 inside)
+ *   embed_matmul_t:     out[l, h] = bf16( bf16( sum_v probs[l, v] E[v, h] )
+ *                                         * scale ),  E[v, h] = s q + b
+ *
+ * In the product each term is formed as bf16(p s) (128 + q) - 128 bf16(p s)
+ * + bf16(p b) with fp32 sums (the pages' quantized matmul rounds the
+ * dequantized table to bf16 instead; both round each term once).
+ *
+ * qmoe_tile_weight_t -- re-lays the table [V, H] (experts = 1, rows = V,
+ * in = H, layout QMOE_LAYOUT_ROWS; V % 32 == 0, H % 64 == 0) for the product:
+ * units of 1152 bytes, unit index g * (V/32) + c for 64-column group g and
+ * 32-row chunk c.  Bytes [0, 1024): lane L = 16 kq + n (n = L % 16) holds at
+ * 16 L four words; word j has the codes of rows 32 c + 8 kq + t (t = 0..7)
+ * at column 64 g + 16 j + n, code t = 2p at bits 4p and t = 2p + 1 at bits
+ * 16 + 4p.  Bytes [1024, 1152): the 32 rows' (scale, bias) bf16 pairs of
+ * group g, row 32 c + r at 1024 + 4 r.  The result is described by a
+ * qmoe_qweight with layout QMOE_LAYOUT_TILED_T, rows = V, in = H, w = dst.
+ *
+ *   z           fp32 [L, V], V % 4 == 0          (softmax_rows_bf16)
+ *   probs       bf16 [L, V], V % 32 == 0         (embed_matmul_t input)
+ *   W           layout QMOE_LAYOUT_TILED_T, experts = 1, rows = V, in = H
+ *   out (out)   bf16 [L, H]
+ *   workspace   embed_matmul_t_workspace(L, V, H) bytes (fp32 partial sums)
+ * ---------------------------------------------------------------------- */
+size_t qmoe_tiled_weight_t_bytes(int32_t V, int32_t H);
+int qmoe_tile_weight_t(const qmoe_qweight* src, void* dst, size_t dst_bytes, hipStream_t stream);
+int softmax_rows_bf16(const float* z, int32_t L, int32_t V, uint16_t* probs, hipStream_t stream);
+size_t embed_matmul_t_workspace(int32_t L, int32_t V, int32_t H);
+int embed_matmul_t(const uint16_t* probs, int32_t L, const qmoe_qweight* W, float scale, uint16_t* out,
+                   void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * The decoder's feed-forward block around the MoE (model.ts page,

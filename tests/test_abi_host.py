@@ -31,7 +31,7 @@ def test_exports_every_declared_function(L):
     assert set(names) >= {"moe_route", "moe_sort", "qswitch_gate_up_geglu", "qswitch_down_combine",
                           "qlinear", "qmoe_last_error", "ff_prenorm", "qlinear_geglu", "ff_combine",
                           "qswitch_gate_up_geglu_unsorted", "qswitch_down_combine_unsorted",
-                          "qlinear_softcap"}
+                          "qlinear_softcap", "softmax_rows_bf16", "embed_matmul_t", "qmoe_tile_weight_t"}
     for n in names:
         assert hasattr(L, n), f"{n} is declared in qmoe.h but not exported"
 
@@ -164,6 +164,31 @@ def test_qlinear_softcap_validation(L):
     assert L.qlinear_softcap(A16, 4, ctypes.byref(qw(1, 4096, 256, layout=1, split=2048)), f(30.0), A16,
                              None) == INVALID
     assert L.qlinear_softcap(A16, 4, ctypes.byref(d), f(30.0), A16 + 4, None) == INVALID
+
+
+def test_embed_matmul_t_validation(L):
+    f = ctypes.c_float
+    assert L.qmoe_tiled_weight_t_bytes(262144, 2816) == 44 * 8192 * 1152
+    assert L.qmoe_tiled_weight_t_bytes(100, 2816) == 0 and L.qmoe_tiled_weight_t_bytes(256, 100) == 0
+    ws = L.embed_matmul_t_workspace(16, 1024, 256)
+    assert ws > 0 and ws % (16 * 256 * 4) == 0
+    d = qw(1, 1024, 256, layout=2)
+    e = lambda Lr=16, W=d, p=A16, sc=1.0, o=A16, w=A16, n=ws: L.embed_matmul_t(p, Lr, ctypes.byref(W), f(sc), o, w, n,
+                                                                             None)
+    assert e(Lr=0, p=None, o=None) == 0
+    assert e(Lr=-1) == INVALID
+    assert e(W=qw(1, 1000, 256, layout=2)) == INVALID      # rows % 32
+    assert e(W=qw(1, 1024, 256, layout=1)) == INVALID      # not the untransposed tiling
+    assert e(W=qw(2, 1024, 256, layout=2)) == INVALID      # one table
+    assert e(sc=float("nan")) == INVALID
+    assert e(o=A16 + 2) == INVALID
+    assert e(n=ws - 1) == WORKSPACE
+    assert L.softmax_rows_bf16(A16, 4, 1022, A16, None) == INVALID
+    assert L.softmax_rows_bf16(None, 4, 1024, A16, None) == INVALID
+    assert L.softmax_rows_bf16(None, 0, 1024, None, None) == 0
+    src = qw(1, 1024, 256)
+    assert L.qmoe_tile_weight_t(ctypes.byref(src), A16, L.qmoe_tiled_weight_t_bytes(1024, 256) - 1, None) == INVALID
+    assert L.qmoe_tile_weight_t(ctypes.byref(qw(1, 1024, 256, layout=1)), A16, 1 << 30, None) == INVALID
 
 
 def test_qlinear_geglu_validation(L):

@@ -1,0 +1,116 @@
+"""GPU parity of the self-conditioning embedding: the row softmax to bf16 and
+the product of probabilities with the untransposed 4-bit table, against the
+CPU oracle.
+
+Bars: probabilities within one bf16 step of the oracle's (the GPU's fp32
+exp and sum against fp64); the product within the layer's per-row relative
+error of 2e-2: each term p s and p b is rounded once to bf16 on the GPU (the
+pages round the dequantized table instead, the same order of error), the
+output is rounded twice (the product, then the scaled product), and the sum
+over the table's rows cancels (the dequantized values are centred near
+zero), which lifts a per-term 2^-9 to about 1e-2 of a row's largest output;
+a one-hot probability row reproduces the table's row bit for bit."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from _util import bf16_host, dev_qweight, dev_tensor, ensure_built, say
+
+pytestmark = pytest.mark.gpu
+
+SCALE = math.sqrt(2816.0)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ensure_built()
+    torch.cuda.init()
+
+
+def probs_on_gpu(z):
+    import bit_quantized_moe_diffrouter_amd as q
+    p = q.softmax_rows_bf16(dev_tensor(np.ascontiguousarray(z, dtype=np.float32)))
+    torch.cuda.synchronize()
+    return p.view(torch.uint16).cpu().numpy()
+
+
+@pytest.mark.parametrize("L,V", [(8, 4096), (3, 1024), (1, 262144)])
+def test_softmax_rows_bf16_parity(L, V):
+    say(f"[softmax] L={L} V={V}")
+    rng = np.random.default_rng(L + V)
+    z = (rng.standard_normal((L, V)) * 3).astype(np.float32)
+    if L >= 3:
+        z[1, 17] += 2000.0        # one-hot row
+        z[2, :] = 0.5             # constant row
+    got = O.bf16_to_f64(probs_on_gpu(z))
+    ref = O.bf16_to_f64(O.softmax_rows_bf16(z.astype(np.float64)))
+    assert np.all(np.abs(got - ref) <= 2.0 ** -7 * np.abs(ref) + 1e-30)
+    assert np.allclose(got.sum(axis=1), 1.0, atol=1e-2)
+    if L >= 3:
+        assert got[1, 17] == 1.0 and np.count_nonzero(got[1]) == 1
+
+
+def run_product(p_bits, W, scale):
+    import bit_quantized_moe_diffrouter_amd as q
+    Wt = dev_qweight(W).tiled_t()
+    out = q.embed_matmul_t(dev_tensor(p_bits), Wt, scale)
+    torch.cuda.synchronize()
+    return bf16_host(out)
+
+
+@pytest.mark.parametrize("L,V,H", [(16, 1024, 256), (37, 512, 128), (300, 256, 192), (1, 64, 64)])
+def test_embed_matmul_t_parity(L, V, H):
+    say(f"[embed_t] L={L} V={V} H={H}")
+    rng = np.random.default_rng(L * 7 + V + H)
+    W = synth.random_qtensor(rng, (V,), H)
+    p = O.softmax_rows_bf16(rng.standard_normal((L, V)) * 2)
+    got = run_product(p, W, SCALE)
+    ref = O.embed_matmul_t(p, W.w, W.scales, W.biases, SCALE)
+    err = O.rowwise_rel_err(got, ref)
+    say(f"  rel err {err:.3e}")
+    assert err <= 2e-2
+
+
+def test_embed_matmul_t_one_hot_rows_are_table_rows():
+    V, H, L = 512, 128, 4
+    rng = np.random.default_rng(7)
+    W = synth.random_qtensor(rng, (V,), H)
+    z = rng.standard_normal((L, V))
+    hot = [0, 31, 32, 511]
+    for l, v in enumerate(hot):
+        z[l, v] += 2000.0
+    p = O.softmax_rows_bf16(z)
+    got = run_product(p, W, SCALE)
+    ref = O.embed_matmul_t(p, W.w, W.scales, W.biases, SCALE)
+    assert np.array_equal(got, ref)
+
+
+def test_embed_matmul_t_full_vocab_sampled():
+    """256 rows against the full 262,144-row table (probabilities from the
+    GPU's softmax); every output of two column groups, four rows."""
+    import bit_quantized_moe_diffrouter_amd as q
+    L, V, H = 256, 262144, 2816
+    say(f"[embed_t] {L} x {V} -> {H}")
+    rng = np.random.default_rng(61)
+    W = synth.random_qtensor(rng, (V,), H)
+    z = dev_tensor((rng.standard_normal((L, V)) * 4).astype(np.float32))
+    Wt = dev_qweight(W).tiled_t()
+    probs = q.softmax_rows_bf16(z)
+    out = q.embed_matmul_t(probs, Wt, SCALE)
+    torch.cuda.synchronize()
+    rows = [0, 100, 200, 255]
+    p_bits = probs.cpu().view(torch.uint16).numpy()[rows]
+    got = bf16_host(out)[rows]
+    for g in (0, H // 64 - 1):
+        cols = slice(64 * g, 64 * g + 64)
+        ref = O.embed_matmul_t(p_bits, W.w[:, 8 * g:8 * g + 8], W.scales[:, g:g + 1], W.biases[:, g:g + 1], SCALE)
+        err = O.rowwise_rel_err(got[:, cols], ref)
+        say(f"  group {g}: rel err {err:.3e}")
+        assert err <= 2e-2
+    assert bool(torch.isfinite(out.float()).all())

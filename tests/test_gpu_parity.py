@@ -119,7 +119,8 @@ def test_route_weights_sum_to_one_before_per_expert_scale():
     assert np.abs(s - 1.0).max() <= 1e-6
 
 
-@pytest.mark.parametrize("T,H,E,k", [(37, 320, 40, 5), (5, 128, 16, 16), (33, 256, 200, 1), (3, 64, 1, 1)])
+@pytest.mark.parametrize("T,H,E,k", [(37, 320, 40, 5), (5, 128, 16, 16), (33, 256, 200, 1), (3, 64, 1, 1),
+                                     (21, 192, 256, 16)])
 def test_route_ragged_and_degenerate(T, H, E, k):
     say(f"[route ragged] T={T} H={H} E={E} k={k}")
     cfg = synth.MoEConfig("ragged", T=T, H=H, E=E, k=k, I=64, seed_w=7, seed_x=8)
@@ -174,7 +175,7 @@ def test_sort_large_random_and_dropped():
 
 
 
-@pytest.mark.parametrize("T,k,E", [(4100, 8, 128), (9000, 4, 7)])
+@pytest.mark.parametrize("T,k,E", [(4100, 8, 128), (9000, 4, 7), (18750, 16, 256)])
 def test_sort_beyond_the_lds_cache(T, k, E):
     """More than 32768 assignments: the kernel recomputes buckets and ranks
     instead of keeping them in LDS (stable order and offsets as before)."""
@@ -302,7 +303,8 @@ def test_layer_deterministic_bitwise():
 # (200, 512, 6, 4, 128): experts of ~130 rows, several chunks each, many items
 # per worker.
 @pytest.mark.parametrize("T,H,E,k,I", [(1, 64, 1, 1, 64), (37, 192, 12, 3, 192), (9, 256, 8, 8, 64),
-                                       (45, 576, 12, 4, 320), (200, 512, 6, 4, 128)])
+                                       (45, 576, 12, 4, 320), (200, 512, 6, 4, 128),
+                                       (40, 128, 256, 16, 64)])  # the largest E and k: 257 buckets in down
 def test_layer_ragged_and_degenerate(T, H, E, k, I):
     import bit_quantized_moe_diffrouter_amd as q
     say(f"[layer ragged] T={T} H={H} E={E} k={k} I={I}")

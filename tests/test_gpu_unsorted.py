@@ -226,3 +226,18 @@ def test_unsorted_layer_in_hip_graph():
         torch.cuda.synchronize()
         for y, e in zip(ys, eager):
             assert torch.equal(y, e), f"replay {rep} differs from the eager result"
+
+
+def test_unsorted_largest_batch_and_experts():
+    """The arm's largest batch (T*k = 4096) with the largest E and k (256, 16)."""
+    T, H, E, k, I = 256, 128, 256, 16, 64
+    cfg = synth.MoEConfig(f"u_T{T}_H{H}_E{E}_k{k}_I{I}", T=T, H=H, E=E, k=k, I=I, seed_w=71, seed_x=72)
+    say(f"[unsorted max] {cfg.name}")
+    inp = inputs(cfg)
+    idx, w, _ = oracle_route(inp)
+    y, mid, _ = run_unsorted(inp, idx, w)
+    toks = [0, 1, 100, 255]
+    ref = O.experts_bruteforce(inp.x, idx, w, inp.weights.gate_up, inp.weights.down, I, tokens=toks)
+    err = O.rowwise_rel_err(y[toks], ref)
+    say(f"  rel err {err:.3e}")
+    assert err <= 2e-2

@@ -42,6 +42,8 @@
 // with one fp32 MFMA (a contraction over the groups).  The products are exact
 // and the dequantized weight is never rounded; the only roundings are the
 // fp32 accumulation and the output conversion.
+#include <atomic>
+
 #include "common.h"
 #include "launch.h"
 
@@ -792,6 +794,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
 // ------------------------------------------------------------------ launchers
 namespace {
 
+constexpr int kMaxDevices = 64;
+
 // Items a launch can hold (every one of the A rows in its own bucket's
 // chunks, at most one partial chunk per bucket).
 template <int MODE>
@@ -813,9 +817,17 @@ hipError_t launch_cfg(SwitchArgs a, int extra_buckets, int num_cu, hipStream_t s
   const long long items = max_items<MODE>(a, extra_buckets);
   long long grid = std::min(items, (long long)num_cu * 2);
   if (grid < 1) grid = 1;
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&qmm_kernel<MODE, KS, D>),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (attr != hipSuccess) return attr;
+  // the dynamic-LDS limit is raised once per device (the attribute belongs to
+  // the device's copy of the kernel)
+  static std::atomic<int> attr_done[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
+  if (!attr_done[dev].load(std::memory_order_acquire)) {
+    const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&qmm_kernel<MODE, KS, D>),
+                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (attr != hipSuccess) return attr;
+    attr_done[dev].store(1, std::memory_order_release);
+  }
   hipLaunchKernelGGL((qmm_kernel<MODE, KS, D>), dim3((unsigned)grid), dim3(kThreads), lds, stream, a);
   return hipGetLastError();
 }

@@ -305,3 +305,40 @@ def test_route_workspace_size(L):
     assert L.moe_route_workspace(16, 256, 8) == 4 * 16 * 9 * 4
     assert L.moe_route_workspace(0, 256, 8) == 0
     assert L.moe_route_workspace(1, 2816, 128) == 16 * 1 * 129 * 4   # at most 16 parts
+
+
+C_CALLER = r"""
+#include <stdio.h>
+#include <string.h>
+#include "qmoe.h"
+
+int main(void) {
+    qmoe_qweight w;
+    memset(&w, 0, sizeof w);
+    if (qswitch_mid_bytes(256, 8, 704, 128) != (size_t)(128 + 128) * 11 * 2048) return 2;
+    if (moe_route_workspace(0, 256, 8) != 0) return 3;
+    if (qlinear(NULL, 4, &w, NULL, 0) != QMOE_ERR_INVALID) return 4;
+    if (strstr(qmoe_last_error(), "qlinear") == NULL) return 5;
+    puts(qmoe_last_error());
+    return 0;
+}
+"""
+
+
+def test_header_is_plain_c_and_links(L, tmp_path):
+    """A C11 program includes the header, links the library and reaches its
+    validation: the boundary needs no C++ or torch on the caller's side."""
+    import shutil
+    import subprocess
+    if shutil.which("gcc") is None or not os.path.isdir("/opt/rocm/include"):
+        pytest.skip("gcc or the ROCm headers are not available")
+    lib_dir = os.path.dirname(L._name)
+    src, exe = tmp_path / "caller.c", tmp_path / "caller"
+    src.write_text(C_CALLER)
+    cmd = ["gcc", "-std=c11", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(ROOT, "include"), "-I", "/opt/rocm/include", str(src), "-o", str(exe),
+           "-L", lib_dir, "-lqmoe", f"-Wl,-rpath,{lib_dir}"]
+    subprocess.run(cmd, check=True, capture_output=True, timeout=120)
+    run = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert run.returncode == 0, (run.returncode, run.stdout, run.stderr)
+    assert "qlinear" in run.stdout

@@ -23,6 +23,8 @@ Prints ONE JSON line (rank 0):
              signal on the same table (softmax to bf16, untransposed product)
   vision_qlinears  diagnostic, not the metric: the vision tower's 4-bit
              linears, 27 blocks at 2520 x 1152
+  other_workloads  diagnostic, not the metric: the same layer on the 4096-token
+             prefill and on the Zipf-skewed 256-token canvas
   ff_block   diagnostic, not the metric: the decoder's feed-forward block
              around the same MoE layer (pre-norms, dense GeGLU branch, the
              layer, post-norms and residual) on the same tokens
@@ -70,6 +72,7 @@ def parse():
     ap.add_argument("--no-ff-block", action="store_true", help="skip the feed-forward block diagnostic")
     ap.add_argument("--no-decode", action="store_true", help="skip the small-batch (unsorted arm) diagnostic")
     ap.add_argument("--no-head", action="store_true", help="skip the LM-head diagnostic")
+    ap.add_argument("--no-other", action="store_true", help="skip the prefill and skewed-canvas diagnostic")
     ap.add_argument("--no-vision", action="store_true", help="skip the vision-tower linears diagnostic")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-probe", action="store_true")
@@ -139,7 +142,7 @@ def summarize(d):
     kt = "rocprofv3 --kernel-trace --stats -d DIR/{d} -o kt --output-format csv -- python3 bench.py {a}"
     lines = _kt_table(os.path.join(d, "kt"),
                       "Kernel durations, canvas workload (256 tokens, H 2816, 128 experts, top-8, I 704)",
-                      kt.format(d="kt", a="--steps 60 --warmup 10 --no-cpu-baseline --no-ff-block --no-decode"),
+                      kt.format(d="kt", a="--steps 60 --warmup 10 --no-cpu-baseline --no-ff-block --no-decode --no-other"),
                       ["rocprofv3 kernel-trace statistics; every dispatch of the run (warm-up, the timed",
                        "pass and the event pass).  qmm_kernel<0,...> is qswitch_gate_up_geglu,",
                        "qmm_kernel<1,...> the down switch linear of qswitch_down_combine."])
@@ -149,7 +152,7 @@ def summarize(d):
         ff = _kt_table(os.path.join(d, "kt_ff"),
                        "Kernel durations, feed-forward block around the canvas MoE layer (256 tokens, "
                        "H 2816, dense GeGLU width 2112)",
-                       kt.format(d="kt_ff", a="--steps 60 --warmup 10 --no-cpu-baseline --no-decode"),
+                       kt.format(d="kt_ff", a="--steps 60 --warmup 10 --no-cpu-baseline --no-decode --no-other"),
                        ["The same run as the canvas line plus the feed-forward block diagnostic, so the",
                         "MoE kernels appear twice as often.  qmm_kernel<3,...> is qlinear_geglu (dense",
                         "gate|up + GeGLU), qmm_kernel<2,...> qlinear (the dense down projection);",
@@ -160,7 +163,7 @@ def summarize(d):
         dec = _kt_table(os.path.join(d, "kt_dec"),
                         "Kernel durations, small-batch arm at 1 and 7 tokens (canvas weights: H 2816, "
                         "128 experts, top-8, I 704)",
-                        kt.format(d="kt_dec", a="--steps 60 --warmup 10 --no-cpu-baseline --no-ff-block"),
+                        kt.format(d="kt_dec", a="--steps 60 --warmup 10 --no-cpu-baseline --no-ff-block --no-other"),
                         ["The same run as the canvas line plus the decode diagnostic (moe_route and the",
                          "two unsorted calls, 60 + 10 + 48 layers at each of 1 and 7 tokens), so the",
                          "router kernels also count the decode layers.  qswitch_unsorted_kernel<0,...> is",
@@ -169,6 +172,21 @@ def summarize(d):
                          "part sum + weighted sum over k.  Both token counts are pooled in one row per",
                          "kernel; the bench line's decode_unsorted object has them apart."])
         open(os.path.join(ROOT, "profiles", "unsorted_decode_kernel_trace.md"), "w").write("\n".join(dec) + "\n")
+
+    for name, wl, title in (
+            ("kt_prefill", "moe_prefill_4096tok_h2816_e128_top8",
+             "Kernel durations, prefill workload (4096 tokens, H 2816, 128 experts, top-8, I 704)"),
+            ("kt_skew", "moe_canvas_skew_256tok_zipf1.1",
+             "Kernel durations, Zipf-skewed canvas (256 tokens, per-expert logit offset 0.1 ln p, p ~ rank^-1.1)")):
+        if glob.glob(os.path.join(d, name, "**", "*kernel_stats.csv"), recursive=True):
+            steps = "--steps 20 --warmup 3" if "prefill" in wl else "--steps 60 --warmup 10"
+            tab = _kt_table(os.path.join(d, name), title,
+                            kt.format(d=name, a=f"--workload {wl} {steps} --no-cpu-baseline"),
+                            ["The four layer calls only (the diagnostics run on the canvas workload alone).",
+                             "qmm_kernel<0,...> is qswitch_gate_up_geglu, qmm_kernel<1,...> the down switch",
+                             "linear of qswitch_down_combine."])
+            out_name = "switch_kernels_" + ("prefill" if "prefill" in wl else "skew") + "_kernel_trace.md"
+            open(os.path.join(ROOT, "profiles", out_name), "w").write("\n".join(tab) + "\n")
 
     fetch, nf = _pmc_per_dispatch(os.path.join(d, "fetch"), "FETCH_SIZE", lambda n: "qmm_kernel<0" in n)
     write, nw = _pmc_per_dispatch(os.path.join(d, "write"), "WRITE_SIZE", lambda n: "qmm_kernel<0" in n)
@@ -181,8 +199,8 @@ def summarize(d):
     cmd = ("rocprofv3 --pmc {c} -d DIR/{d} -o p --output-format csv -- python3 bench.py {a}")
     txt = ["# HBM traffic of qswitch_gate_up_geglu (qmm_kernel<0,...>), canvas workload",
            "# Commands (from the repository root, TMPDIR=/tmp), one counter per run:",
-           "#   " + cmd.format(c="FETCH_SIZE", d="fetch", a="--steps 20 --warmup 5 --no-cpu-baseline --no-ff-block --no-decode"),
-           "#   " + cmd.format(c="WRITE_SIZE", d="write", a="--steps 20 --warmup 5 --no-cpu-baseline --no-ff-block --no-decode"),
+           "#   " + cmd.format(c="FETCH_SIZE", d="fetch", a="--steps 20 --warmup 5 --no-cpu-baseline --no-ff-block --no-decode --no-other"),
+           "#   " + cmd.format(c="WRITE_SIZE", d="write", a="--steps 20 --warmup 5 --no-cpu-baseline --no-ff-block --no-decode --no-other"),
            "#   " + cmd.format(c="FETCH_SIZE", d="copy_fetch", a="--copy-probe"),
            "#   " + cmd.format(c="WRITE_SIZE", d="copy_write", a="--copy-probe"),
            "# FETCH_SIZE / WRITE_SIZE are KiB per dispatch; each is scaled by what the same",
@@ -234,6 +252,117 @@ def cpu_baseline(cfg, inp, seconds):
                       f"median {t:.2f} s; host has {os.cpu_count()} logical CPUs"}
 
 
+LAYER_CALLS = ["moe_route", "moe_sort", "qswitch_gate_up_geglu", "qswitch_down_combine"]
+
+
+def make_layer_step(q, torch, cfg, x):
+    """The layer's four calls on preallocated outputs and workspaces (the
+    library allocates nothing); step(p, ev) records ev[0..4] around the calls."""
+    T, k, E, H, I = cfg.T, cfg.k, cfg.E, cfg.H, cfg.I
+    dev = x.device
+    buf = dict(idx=torch.empty((T, k), dtype=torch.int32, device=dev),
+               wts=torch.empty((T, k), dtype=torch.float32, device=dev),
+               off=torch.empty(E + 1, dtype=torch.int32, device=dev),
+               sa=torch.empty(T * k, dtype=torch.int32, device=dev),
+               mid=torch.empty(q.qswitch_mid_bytes(T, k, I, E), dtype=torch.uint8, device=dev),
+               y=torch.empty((T, H), dtype=torch.bfloat16, device=dev),
+               ws_r=torch.empty(max(1, q.moe_route_workspace(T, H, E)), dtype=torch.uint8, device=dev),
+               ws_s=torch.empty(max(1, q.moe_sort_workspace(T, k, E)), dtype=torch.uint8, device=dev),
+               ws_d=torch.empty(max(1, q.qswitch_down_combine_workspace(T, k, H, 1)), dtype=torch.uint8, device=dev))
+    idx, wts, off, sa, mid, y = (buf[n] for n in ("idx", "wts", "off", "sa", "mid", "y"))
+
+    def step(p, ev=None):
+        if ev is not None:
+            ev[0].record()
+        q.moe_route(x, p.norm_scale, cfg.eps, p.router, p.per_expert_scale, k, p.logit_bias,
+                    indices=idx, weights=wts, workspace=buf["ws_r"])
+        if ev is not None:
+            ev[1].record()
+        q.moe_sort(idx, E, off, sa, workspace=buf["ws_s"])
+        if ev is not None:
+            ev[2].record()
+        q.qswitch_gate_up_geglu(x, p.gate_up, I, k, off, sa, mid=mid)
+        if ev is not None:
+            ev[3].record()
+        q.qswitch_down_combine(mid, T, k, p.down, wts, off, sa, y=y, workspace=buf["ws_d"], deterministic=1)
+        if ev is not None:
+            ev[4].record()
+
+    return step, buf
+
+
+def time_layer(torch, step, sets, K, warmup, off):
+    """Wall time of K steps (weight sets rotated, no events inside), then the
+    per-call mean times (us) from a second pass of K steps with HIP events
+    between the calls on the launch stream.  Returns (wall_s, mean_us,
+    experts touched per set)."""
+    touched = []
+    for p in sets:
+        step(p)
+        torch.cuda.synchronize()
+        touched.append(int((torch.diff(off.cpu()) > 0).sum()))
+    for i in range(warmup):
+        step(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
+    torch.cuda.synchronize()
+    for i in range(K):
+        step(sets[i % len(sets)], evs[i])
+    torch.cuda.synchronize()
+    per = {n: [] for n in LAYER_CALLS}
+    for ev in evs:
+        for j, n in enumerate(LAYER_CALLS):
+            per[n].append(ev[j].elapsed_time(ev[j + 1]) * 1e3)
+    return wall, {n: float(np.mean(v)) for n, v in per.items()}, touched
+
+
+def other_workloads_timing(q, torch, synth, sets, K, warmup, t):
+    """Diagnostic: the same four calls on the 4096-token prefill and on the
+    Zipf-skewed 256-token canvas, with the canvas's weight sets (same shapes;
+    the skewed canvas adds its per-expert logit offset to each set).  Prefill
+    is priced against the bf16 MFMA peak (its contraction, not its bytes,
+    bounds it); the skewed canvas against HBM like the canvas."""
+    import dataclasses
+    res = {}
+    for cfg in (synth.PREFILL, synth.SKEW):
+        T, k, H, I = cfg.T, cfg.k, cfg.H, cfg.I
+        A = T * k
+        x = t(synth.make_activations(T, H, cfg.seed_x))
+        run_sets = sets
+        if cfg.zipf_tau:
+            bias = t(synth.zipf_logit_bias(cfg.E, cfg.zipf_tau, cfg.zipf_perm_seed))
+            run_sets = [dataclasses.replace(p, logit_bias=bias) for p in sets]
+        step, buf = make_layer_step(q, torch, cfg, x)
+        n = max(10, K // 10) if T > 1024 else K
+        wall, mean_us, touched = time_layer(torch, step, run_sets, n, max(3, warmup // 10), buf["off"])
+        gu_b, dn_b = expert_bytes(cfg)
+        n_touch = float(np.mean(touched))
+        gu_us = mean_us["qswitch_gate_up_geglu"]
+        gu_flops = 2.0 * A * 2 * I * H
+        gu_bytes = n_touch * gu_b + T * H * 2 + A * I * 2
+        layer_flops = 2.0 * A * (2 * I * H + H * I) + 2.0 * T * cfg.E * H
+        layer_bytes = n_touch * (gu_b + dn_b) + router_bytes(cfg) + 2 * T * H * 2
+        ms = wall / n * 1e3
+        res[cfg.name] = {
+            "steps": n, "tokens_per_s": T * n / wall, "ms_per_layer": ms, "experts_touched": n_touch,
+            "call_mean_us": mean_us,
+            "gate_up": {"TFLOPs": gu_flops / (gu_us * 1e-6) / 1e12,
+                        "mfma_frac": gu_flops / (gu_us * 1e-6) / (MFMA_BF16_PEAK_TFLOPS * 1e12),
+                        "GBs": gu_bytes / (gu_us * 1e-6) / 1e9,
+                        "hbm_frac": gu_bytes / (gu_us * 1e-6) / 1e9 / HBM_PEAK_GBS},
+            "layer": {"mfma_frac": layer_flops / (ms * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12),
+                      "hbm_frac": layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        }
+        del step, buf, x
+    return res
+
+
+
 def ff_block_timing(q, torch, synth, ffc, h, sets, K, warmup, t, buf):
     """Diagnostic: the decoder's whole feed-forward block around the MoE
     (ff_prenorm, qlinear_geglu, qlinear, the four MoE calls, ff_combine) on the
@@ -271,7 +400,7 @@ def ff_block_timing(q, torch, synth, ffc, h, sets, K, warmup, t, buf):
         mark(3)
         q.moe_route(h, p.norm_scale, cfg.eps, p.router, p.per_expert_scale, k, p.logit_bias,
                     indices=b["idx"], weights=b["wts"], workspace=b["ws_r"])
-        q.moe_sort(b["idx"], E, b["off"], b["sa"])
+        q.moe_sort(b["idx"], E, b["off"], b["sa"], workspace=b["ws_s"])
         q.qswitch_gate_up_geglu(xb, p.gate_up, I, k, b["off"], b["sa"], mid=b["mid"])
         q.qswitch_down_combine(b["mid"], T, k, p.down, b["wts"], b["off"], b["sa"], y=b["y"],
                                workspace=b["ws_d"], deterministic=1)
@@ -527,65 +656,9 @@ def main():
     x = t(x_host)
     T, k, E, H, I = cfg.T, cfg.k, cfg.E, cfg.H, cfg.I
     A = T * k
-    # preallocated outputs and workspaces (the library allocates nothing)
-    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
-    wts = torch.empty((T, k), dtype=torch.float32, device=dev)
-    off = torch.empty(E + 1, dtype=torch.int32, device=dev)
-    sa = torch.empty(A, dtype=torch.int32, device=dev)
-    mid = torch.empty(q.qswitch_mid_bytes(T, k, I, E), dtype=torch.uint8, device=dev)
-    y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-    ws_r = torch.empty(max(1, q.moe_route_workspace(T, H, E)), dtype=torch.uint8, device=dev)
-    ws_d = torch.empty(max(1, q.qswitch_down_combine_workspace(T, k, H, 1)), dtype=torch.uint8, device=dev)
-
-    def step(p, ev=None):
-        if ev is not None:
-            ev[0].record()
-        q.moe_route(x, p.norm_scale, cfg.eps, p.router, p.per_expert_scale, k, p.logit_bias,
-                    indices=idx, weights=wts, workspace=ws_r)
-        if ev is not None:
-            ev[1].record()
-        q.moe_sort(idx, E, off, sa)
-        if ev is not None:
-            ev[2].record()
-        q.qswitch_gate_up_geglu(x, p.gate_up, I, k, off, sa, mid=mid)
-        if ev is not None:
-            ev[3].record()
-        q.qswitch_down_combine(mid, T, k, p.down, wts, off, sa, y=y, workspace=ws_d, deterministic=1)
-        if ev is not None:
-            ev[4].record()
-
-    # touched experts per weight set (routing is a function of x and the router)
-    touched = []
-    for p in sets:
-        step(p)
-        torch.cuda.synchronize()
-        touched.append(int((torch.diff(off.cpu()) > 0).sum()))
-
-    for i in range(args.warmup):
-        step(sets[i % len(sets)])
-    torch.cuda.synchronize()
-
+    step, buf = make_layer_step(q, torch, cfg, x)
+    wall, mean_us, touched = time_layer(torch, step, sets, args.steps, args.warmup, buf["off"])
     K = args.steps
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        step(sets[i % len(sets)])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
-    # per-call times: the same K steps again with events between the calls
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
-    torch.cuda.synchronize()
-    for i in range(K):
-        step(sets[i % len(sets)], evs[i])
-    torch.cuda.synchronize()
-
-    names = ["moe_route", "moe_sort", "qswitch_gate_up_geglu", "qswitch_down_combine"]
-    per = {n: [] for n in names}
-    for ev in evs:
-        for j, n in enumerate(names):
-            per[n].append(ev[j].elapsed_time(ev[j + 1]) * 1e3)  # us
-    mean_us = {n: float(np.mean(v)) for n, v in per.items()}
 
     gu_b, dn_b = expert_bytes(cfg)
     n_touch = float(np.mean(touched))
@@ -625,6 +698,8 @@ def main():
     }
     if cfg.name == synth.CANVAS.name and not args.no_decode:
         out["decode_unsorted"] = decode_timing(q, torch, synth, sets, K, args.warmup)
+    if cfg.name == synth.CANVAS.name and not args.no_other:
+        out["other_workloads"] = other_workloads_timing(q, torch, synth, sets, K, args.warmup, t)
     if cfg.name == synth.CANVAS.name and not args.no_head:
         out["lm_head"] = lm_head_timing(q, torch, synth, K, args.warmup)
     if cfg.name == synth.CANVAS.name and not args.no_vision:
@@ -632,7 +707,7 @@ def main():
     ffc = next((f for f in synth.FF_CONFIGS.values() if f.moe.name == cfg.name), None)
     if ffc is not None and not args.no_ff_block:
         out["ff_block"] = ff_block_timing(q, torch, synth, ffc, x, sets, K, args.warmup, t,
-                                          dict(idx=idx, wts=wts, off=off, sa=sa, mid=mid, y=y, ws_r=ws_r, ws_d=ws_d))
+                                          buf)
     if not args.no_cpu_baseline:
         inp = synth.MoEInputs(cfg, x_host, host_first)
         out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)

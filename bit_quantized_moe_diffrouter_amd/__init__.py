@@ -24,7 +24,7 @@ import torch
 
 __all__ = [
     "QMoEError", "QuantWeight", "TiledWeight", "MoEParams", "lib", "library_path",
-    "moe_route", "moe_route_workspace", "moe_sort", "qswitch_mid_bytes",
+    "moe_route", "moe_route_workspace", "moe_sort", "moe_sort_workspace", "qswitch_mid_bytes",
     "qswitch_gate_up_geglu",
     "qswitch_down_combine", "qswitch_down_combine_workspace", "qlinear", "moe_layer",
     "ff_prenorm", "qlinear_geglu", "ff_combine", "FFParams", "ff_block", "qlinear_softcap",
@@ -247,9 +247,17 @@ def moe_route(x_router: torch.Tensor, norm_scale: torch.Tensor, eps: float, proj
     return indices, weights
 
 
+def moe_sort_workspace(T: int, k: int, E: int) -> int:
+    """Bytes of the sort's workspace (0 below 8192 assignments)."""
+    return int(lib().moe_sort_workspace(T, k, E))
+
+
 def moe_sort(indices: torch.Tensor, E: int, expert_offsets: Optional[torch.Tensor] = None,
-             sorted_assign: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """Token-by-expert sort: returns (expert_offsets int32 [E+1], sorted_assign int32 [T*k])."""
+             sorted_assign: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+             slices: bool = True) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Token-by-expert sort: returns (expert_offsets int32 [E+1], sorted_assign int32 [T*k]).
+    A workspace is allocated when none is given and the input is large enough
+    for the slice sort; slices=False passes none, so one workgroup sorts."""
     T, k = indices.shape
     _need(indices, "indices", 4)
     dev = indices.device
@@ -257,8 +265,14 @@ def moe_sort(indices: torch.Tensor, E: int, expert_offsets: Optional[torch.Tenso
         expert_offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
     if sorted_assign is None:
         sorted_assign = torch.empty(T * k, dtype=torch.int32, device=dev)
-    _check(lib().moe_sort(_ptr(indices), T, k, E, _ptr(expert_offsets), _ptr(sorted_assign), None, 0,
-                          _stream()))
+    if not slices:
+        workspace = None
+    elif workspace is None:
+        need = moe_sort_workspace(T, k, E)
+        if need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _check(lib().moe_sort(_ptr(indices), T, k, E, _ptr(expert_offsets), _ptr(sorted_assign),
+                          None if workspace is None else _ptr(workspace), _nbytes(workspace), _stream()))
     return expert_offsets, sorted_assign
 
 

@@ -171,12 +171,13 @@ int moe_route(const uint16_t* x_router, int32_t T, int32_t H, const uint16_t* no
   return launched(qmoe::launch_route(a, stream), "moe_route");
 }
 
-size_t moe_sort_workspace(int32_t, int32_t, int32_t) { return 0; }
+size_t moe_sort_workspace(int32_t T, int32_t k, int32_t E) {
+  if (T <= 0 || k <= 0 || E < 1 || E > 256 || (long long)T * k > kMaxAssign) return 0;
+  return qmoe::sort_workspace_bytes(T * k, E);
+}
 
 int moe_sort(const int32_t* indices, int32_t T, int32_t k, int32_t E, int32_t* expert_offsets,
              int32_t* sorted_assign, void* workspace, size_t ws_bytes, hipStream_t stream) {
-  (void)workspace;
-  (void)ws_bytes;
   REQUIRE(T >= 0, QMOE_ERR_INVALID, "moe_sort: T=%d < 0", T);
   REQUIRE(k >= 1, QMOE_ERR_INVALID, "moe_sort: k=%d < 1", k);
   REQUIRE(E >= 1 && E <= 256, QMOE_ERR_UNSUPPORTED, "moe_sort: E=%d outside [1, 256]", E);
@@ -185,7 +186,9 @@ int moe_sort(const int32_t* indices, int32_t T, int32_t k, int32_t E, int32_t* e
   REQUIRE_PTR(indices, 4, "moe_sort indices");
   REQUIRE_PTR(expert_offsets, 4, "moe_sort expert_offsets");
   REQUIRE_PTR(sorted_assign, 4, "moe_sort sorted_assign");
-  return launched(qmoe::launch_sort(indices, T * k, E, expert_offsets, sorted_assign, stream), "moe_sort");
+  if (workspace != nullptr) REQUIRE_PTR(workspace, 4, "moe_sort workspace");
+  return launched(qmoe::launch_sort(indices, T * k, E, expert_offsets, sorted_assign, workspace, ws_bytes, stream),
+                  "moe_sort");
 }
 
 size_t qswitch_mid_bytes(int32_t T, int32_t k, int32_t I, int32_t E) {

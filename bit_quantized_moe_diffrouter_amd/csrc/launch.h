@@ -28,8 +28,11 @@ int route_ksplit(int T, int H);
 hipError_t launch_route(const RouteArgs& a, hipStream_t stream);
 
 // ---------------------------------------------------------------- sort
-hipError_t launch_sort(const int32_t* indices, int A, int E, int32_t* offsets, int32_t* sorted_assign,
-                       hipStream_t stream);
+// Workspace of the slice sort (0 below 8192 assignments); with less, the
+// one-workgroup sort runs.
+size_t sort_workspace_bytes(int A, int E);
+hipError_t launch_sort(const int32_t* indices, int A, int E, int32_t* offsets, int32_t* sorted_assign, void* ws,
+                       size_t ws_bytes, hipStream_t stream);
 
 // ---------------------------------------------------------------- switch / dense linears
 // Bytes of one tiled unit: (expert, block of 128 weight rows, 64-wide group) ->

@@ -184,9 +184,18 @@ int moe_route(const uint16_t* x_router, int32_t T, int32_t H, const uint16_t* no
  *                      ascending within an expert (stable)
  *
  * An index outside [0, E) is dropped: it is counted nowhere and offsets[E]
- * is then below T*k (the later calls process only offsets[E] rows).
- * E <= 256; T*k <= 2^24.  No workspace is needed (moe_sort_workspace returns
- * 0); the arguments are kept so the size can grow without an ABI change.
+ * is then below T*k (the later calls process only offsets[E] rows); the
+ * dropped ids fill sorted_assign[offsets[E] .. T*k) in ascending order.
+ * E <= 256; T*k <= 2^24.
+ *
+ *   workspace          device, 4-byte aligned, moe_sort_workspace(T, k, E)
+ *                      bytes (0 below 8192 assignments; about 1 KB per slice
+ *                      of at least 1024 assignments, at most 256 slices).
+ *                      With it, 8192 and more assignments are sorted by two
+ *                      kernels over many workgroups (slice histograms, then
+ *                      each slice placed at its offsets); with a null or
+ *                      smaller workspace one workgroup sorts the whole input.
+ *                      Both give the same output.  The call overwrites it.
  * ---------------------------------------------------------------------- */
 size_t moe_sort_workspace(int32_t T, int32_t k, int32_t E);
 int moe_sort(const int32_t* indices, int32_t T, int32_t k, int32_t E, int32_t* expert_offsets,

@@ -78,7 +78,20 @@ def test_sort_validation(L):
     assert L.moe_sort(A16, 1 << 22, 8, 8, A16, A16, None, 0, None) == UNSUPPORTED
     assert L.moe_sort(None, 4, 2, 8, A16, A16, None, 0, None) == INVALID
     assert L.moe_sort(A16, 4, 2, 8, A16 + 2, A16, None, 0, None) == INVALID
+    assert L.moe_sort(A16, 4, 2, 8, A16, A16, A16 + 2, 64, None) == INVALID   # misaligned workspace
+
+
+def test_sort_workspace_sizes(L):
+    # 0 below 8192 assignments; above, one (E+1)-int histogram per slice, slices
+    # a multiple of 1024 assignments and at most 256 of them
     assert L.moe_sort_workspace(256, 8, 128) == 0
+    assert L.moe_sort_workspace(1023, 8, 128) == 0
+    assert L.moe_sort_workspace(1024, 8, 128) == 8 * 129 * 4
+    assert L.moe_sort_workspace(4096, 8, 128) == 32 * 129 * 4
+    assert L.moe_sort_workspace(18750, 16, 256) == 147 * 257 * 4       # slices of 2048
+    assert L.moe_sort_workspace(1 << 21, 8, 256) == 256 * 257 * 4      # 2^24: slices of 65536
+    assert L.moe_sort_workspace(0, 8, 128) == 0
+    assert L.moe_sort_workspace(1 << 22, 8, 128) == 0                  # above the limit
 
 
 def gate_up(L, T=16, H=256, I=128, k=2, E=8, rows=None, inp=None, x=A16, mid=A16, mid_bytes=1 << 30, layout=1,

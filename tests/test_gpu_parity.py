@@ -132,9 +132,9 @@ def test_route_ragged_and_degenerate(T, H, E, k):
 
 
 # ------------------------------------------------------------------------- sort
-def gpu_sort(idx, E):
+def gpu_sort(idx, E, slices=True):
     import bit_quantized_moe_diffrouter_amd as q
-    off, sa = q.moe_sort(dev_tensor(idx.astype(np.int32)), E)
+    off, sa = q.moe_sort(dev_tensor(idx.astype(np.int32)), E, slices=slices)
     torch.cuda.synchronize()
     return off.cpu().numpy(), sa.cpu().numpy()
 
@@ -149,12 +149,13 @@ def test_sort_parity(cfg):
     np.testing.assert_array_equal(sa_g, sa_r)
 
 
-def test_sort_large_random_and_dropped():
-    say("[sort] random 3000x8 over 256 experts, with out-of-range indices")
+@pytest.mark.parametrize("slices", [True, False], ids=["slices", "one_workgroup"])
+def test_sort_large_random_and_dropped(slices):
+    say(f"[sort] random 3000x8 over 256 experts, with out-of-range indices (slices={slices})")
     rng = np.random.default_rng(21)
     T, k, E = 3000, 8, 256
     idx = rng.integers(0, E, size=(T, k)).astype(np.int32)
-    off_g, sa_g = gpu_sort(idx, E)
+    off_g, sa_g = gpu_sort(idx, E, slices)
     off_r, sa_r = O.sort_assignments(idx, E)
     np.testing.assert_array_equal(off_g, off_r)
     np.testing.assert_array_equal(sa_g, sa_r)
@@ -162,7 +163,7 @@ def test_sort_large_random_and_dropped():
     bad[5, 3] = -1
     bad[17, 0] = E
     bad[2999, 7] = 1 << 20
-    off_g, sa_g = gpu_sort(bad, E)
+    off_g, sa_g = gpu_sort(bad, E, slices)
     flat = bad.reshape(-1)
     valid = (flat >= 0) & (flat < E)
     ids = np.nonzero(valid)[0]
@@ -175,21 +176,58 @@ def test_sort_large_random_and_dropped():
 
 
 
-@pytest.mark.parametrize("T,k,E", [(4100, 8, 128), (9000, 4, 7), (18750, 16, 256)])
-def test_sort_beyond_the_lds_cache(T, k, E):
-    """More than 32768 assignments: the kernel recomputes buckets and ranks
-    instead of keeping them in LDS (stable order and offsets as before)."""
-    say(f"[sort] beyond the LDS cache: T={T} k={k} E={E}")
-    rng = np.random.default_rng(T)
-    idx = rng.integers(0, E, size=(T, k)).astype(np.int32)
-    idx[rng.random((T, k)) < 0.01] = -3
-    off_g, sa_g = gpu_sort(idx, E)
+def check_sort(idx, E, off_g, sa_g):
     flat = idx.reshape(-1)
     valid = (flat >= 0) & (flat < E)
     ids = np.nonzero(valid)[0]
     np.testing.assert_array_equal(off_g, np.concatenate([[0], np.cumsum(np.bincount(flat[ids], minlength=E))]))
     np.testing.assert_array_equal(sa_g[:ids.size], ids[np.argsort(flat[ids], kind="stable")])
     np.testing.assert_array_equal(sa_g[ids.size:], np.nonzero(~valid)[0])
+
+
+@pytest.mark.parametrize("slices", [True, False], ids=["slices", "one_workgroup"])
+@pytest.mark.parametrize("T,k,E", [(4100, 8, 128), (9000, 4, 7), (18750, 16, 256)])
+def test_sort_beyond_the_lds_cache(T, k, E, slices):
+    """More than 32768 assignments.  One workgroup recomputes buckets and
+    ranks instead of keeping them in LDS; the slice sort cuts the input into
+    33, 36 and 147 slices (of 1024, 1024 and 2048 assignments).  Stable order
+    and offsets as before."""
+    say(f"[sort] beyond the LDS cache: T={T} k={k} E={E} slices={slices}")
+    rng = np.random.default_rng(T)
+    idx = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    idx[rng.random((T, k)) < 0.01] = -3
+    off_g, sa_g = gpu_sort(idx, E, slices)
+    check_sort(idx, E, off_g, sa_g)
+
+
+@pytest.mark.parametrize("T,k,E,hot", [(1024, 8, 128, 1.0), (1025, 8, 128, 0.9), (2000, 8, 1, 0.0)])
+def test_sort_slices_threshold_and_hot_expert(T, k, E, hot):
+    """At and just past the slice sort's threshold (8192 assignments: 8 and 9
+    slices, the last one 8 assignments long), with one expert taking all or
+    90 % of the assignments (every slice's histogram lands in one LDS bucket),
+    and with a single expert; the two sorts give the same bits."""
+    say(f"[sort] threshold T={T} k={k} E={E} hot={hot}")
+    rng = np.random.default_rng(T + E)
+    idx = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    idx[rng.random((T, k)) < hot] = E // 2
+    idx[0, 0] = -1
+    off_s, sa_s = gpu_sort(idx, E, True)
+    off_1, sa_1 = gpu_sort(idx, E, False)
+    np.testing.assert_array_equal(off_s, off_1)
+    np.testing.assert_array_equal(sa_s, sa_1)
+    check_sort(idx, E, off_s, sa_s)
+
+
+def test_sort_slices_beyond_the_lds_cache():
+    """9,000,000 assignments: 252 slices of 35,840, each past its LDS cache,
+    so each slice recomputes buckets and ranks in its scatter pass."""
+    T, k, E = 562500, 16, 256
+    say(f"[sort] slices beyond the LDS cache: T={T} k={k} E={E}")
+    rng = np.random.default_rng(99)
+    idx = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    idx[rng.random((T, k)) < 0.001] = E + 1
+    off_g, sa_g = gpu_sort(idx, E, True)
+    check_sort(idx, E, off_g, sa_g)
 
 
 # ------------------------------------------------------------------ experts

@@ -120,8 +120,12 @@ def test_route_weights_sum_to_one_before_per_expert_scale():
 
 
 @pytest.mark.parametrize("T,H,E,k", [(37, 320, 40, 5), (5, 128, 16, 16), (33, 256, 200, 1), (3, 64, 1, 1),
-                                     (21, 192, 256, 16)])
+                                     (21, 192, 256, 16), (1100, 320, 40, 5), (1030, 192, 256, 16),
+                                     (1024, 64, 1, 1)])
 def test_route_ragged_and_degenerate(T, H, E, k):
+    """Ragged token counts (down to a last 16-token tile of 4 or 6 tokens, also
+    past 1024 tokens, where the contraction is split in at most 4 parts), expert
+    counts that are not multiples of 16, single groups and single experts."""
     say(f"[route ragged] T={T} H={H} E={E} k={k}")
     cfg = synth.MoEConfig("ragged", T=T, H=H, E=E, k=k, I=64, seed_w=7, seed_x=8)
     inp = synth.make_moe_inputs(cfg)

@@ -776,13 +776,26 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict
   const int t = (int)(idx / H8), h = (int)(idx - (long long)t * H8) * 8;
   const uint16_t* base = D + (size_t)t * k * H + h;
   float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < k; ++j) {
-    const u32x4_t v = *(const u32x4_t*)(base + (size_t)j * H);
-    const float wj = w[(size_t)t * k + j];
+  // the loads of up to 8 rows are issued before any is summed (few waves per
+  // SIMD at a few hundred tokens, so one round trip per row would be exposed);
+  // the terms are still added in j order
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    u32x4_t v[8];
+    float wj[8];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      s[2 * q] += wj * bf16_lo_f32(v[q]);
-      s[2 * q + 1] += wj * bf16_hi_f32(v[q]);
+    for (int u = 0; u < 8; ++u) {
+      const bool ok = j0 + u < k;
+      v[u] = ok ? *(const u32x4_t*)(base + (size_t)(j0 + u) * H) : u32x4_t{0u, 0u, 0u, 0u};
+      wj[u] = ok ? w[(size_t)t * k + j0 + u] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (j0 + u >= k) break;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        s[2 * q] += wj[u] * bf16_lo_f32(v[u][q]);
+        s[2 * q + 1] += wj[u] * bf16_hi_f32(v[u][q]);
+      }
     }
   }
   u32x4_t o;

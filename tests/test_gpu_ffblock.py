@@ -62,7 +62,9 @@ def sample(n_all, n, seed):
 
 
 # ---------------------------------------------------------------- norms
-@pytest.mark.parametrize("T,H", [(16, 256), (256, 2816), (37, 72), (1, 8), (5, 2824)])
+# rows of up to 4096 columns stay in registers; 4104 and 6144 take the re-reading form
+@pytest.mark.parametrize("T,H", [(16, 256), (256, 2816), (37, 72), (1, 8), (5, 2824), (9, 4096), (7, 4104),
+                                 (3, 6144)])
 def test_ff_prenorm_parity(T, H):
     import bit_quantized_moe_diffrouter_amd as q
     say(f"[ff_prenorm] T={T} H={H}")
@@ -78,7 +80,8 @@ def test_ff_prenorm_parity(T, H):
         assert err <= NORM_TOL
 
 
-@pytest.mark.parametrize("T,H", [(16, 256), (256, 2816), (37, 72), (1, 8)])
+@pytest.mark.parametrize("T,H", [(16, 256), (256, 2816), (37, 72), (1, 8), (5, 2824), (9, 4096), (7, 4104),
+                                 (3, 6144)])
 def test_ff_combine_parity(T, H):
     import bit_quantized_moe_diffrouter_amd as q
     say(f"[ff_combine] T={T} H={H}")

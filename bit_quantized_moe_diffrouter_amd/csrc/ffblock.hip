@@ -133,13 +133,19 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void ff_combine_kernel(
   const int n8 = H / 8;
   const size_t o = (size_t)t * H;
   if constexpr (NC > 0) {
-    u32x4_t A[NC], B[NC];
+    // every load of the row is issued here, before the first sum
+    const u32x4_t z4 = {0u, 0u, 0u, 0u};
+    u32x4_t A[NC], B[NC], GA[NC], GB[NC], X[NC], G[NC];
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
       const int c = lane + 64 * i;
       const bool ok = c < n8;
-      A[i] = ok ? *(const u32x4_t*)(h1 + o + 8 * c) : u32x4_t{0u, 0u, 0u, 0u};
-      B[i] = ok ? *(const u32x4_t*)(h2 + o + 8 * c) : u32x4_t{0u, 0u, 0u, 0u};
+      A[i] = ok ? *(const u32x4_t*)(h1 + o + 8 * c) : z4;
+      B[i] = ok ? *(const u32x4_t*)(h2 + o + 8 * c) : z4;
+      GA[i] = ok ? *(const u32x4_t*)(w1 + 8 * c) : z4;
+      GB[i] = ok ? *(const u32x4_t*)(w2 + 8 * c) : z4;
+      X[i] = ok ? *(const u32x4_t*)(res + o + 8 * c) : z4;
+      G[i] = ok ? *(const u32x4_t*)(w + 8 * c) : z4;
     }
     float s1 = 0.f, s2 = 0.f;
 #pragma unroll
@@ -169,10 +175,7 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void ff_combine_kernel(
     float ss = 0.f;
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
-      const int c = lane + 64 * i;
-      const bool ok = c < n8;
-      const u32x4_t ga = ok ? *(const u32x4_t*)(w1 + 8 * c) : u32x4_t{0u, 0u, 0u, 0u};
-      const u32x4_t gb = ok ? *(const u32x4_t*)(w2 + 8 * c) : u32x4_t{0u, 0u, 0u, 0u};
+      const u32x4_t ga = GA[i], gb = GB[i];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         S[i][2 * q] = bf16_lo_f32(A[i][q]) * r1 * bf16_lo_f32(ga[q]) + bf16_lo_f32(B[i][q]) * r2 * bf16_lo_f32(gb[q]);
@@ -191,7 +194,7 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void ff_combine_kernel(
     for (int i = 0; i < NC; ++i) {
       const int c = lane + 64 * i;
       if (c >= n8) break;
-      const u32x4_t x = *(const u32x4_t*)(res + o + 8 * c), g = *(const u32x4_t*)(w + 8 * c);
+      const u32x4_t x = X[i], g = G[i];
       u32x4_t y;
 #pragma unroll
       for (int q = 0; q < 4; ++q)

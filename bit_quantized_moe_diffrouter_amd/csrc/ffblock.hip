@@ -65,11 +65,16 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void ff_prenorm_kernel(const ui
   const int n8 = H / 8;
   const uint16_t* row = h + (size_t)t * H;
   if constexpr (NC > 0) {
-    u32x4_t v[NC];
+    // the row and both weight vectors are loaded before the first sum
+    const u32x4_t z4 = {0u, 0u, 0u, 0u};
+    u32x4_t v[NC], GA[NC], GB[NC];
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
       const int c = lane + 64 * i;
-      v[i] = (c < n8) ? *(const u32x4_t*)(row + 8 * c) : u32x4_t{0u, 0u, 0u, 0u};
+      const bool ok = c < n8;
+      v[i] = ok ? *(const u32x4_t*)(row + 8 * c) : z4;
+      GA[i] = ok ? *(const u32x4_t*)(wa + 8 * c) : z4;
+      GB[i] = ok ? *(const u32x4_t*)(wb + 8 * c) : z4;
     }
     float ss = 0.f;
 #pragma unroll
@@ -87,8 +92,7 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void ff_prenorm_kernel(const ui
     for (int i = 0; i < NC; ++i) {
       const int c = lane + 64 * i;
       if (c >= n8) break;
-      const u32x4_t ga = *(const u32x4_t*)(wa + 8 * c);
-      const u32x4_t gb = *(const u32x4_t*)(wb + 8 * c);
+      const u32x4_t ga = GA[i], gb = GB[i];
       u32x4_t oa, ob;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {

@@ -25,7 +25,7 @@ import torch
 __all__ = [
     "QMoEError", "QuantWeight", "TiledWeight", "MoEParams", "lib", "library_path",
     "moe_route", "moe_route_workspace", "moe_sort", "moe_sort_workspace", "qswitch_mid_bytes",
-    "qswitch_gate_up_geglu",
+    "qswitch_gate_up_geglu", "device_status",
     "qswitch_down_combine", "qswitch_down_combine_workspace", "qlinear", "moe_layer",
     "ff_prenorm", "qlinear_geglu", "ff_combine", "FFParams", "ff_block", "qlinear_softcap",
     "TiledTWeight", "softmax_rows_bf16", "embed_matmul_t", "self_condition_embed",
@@ -75,6 +75,7 @@ _SIGNATURES = {
     "moe_sort": (ctypes.c_int, [_P, _I, _I, _I, _P, _P, _P, _SZ, _P]),
     "qswitch_mid_bytes": (_SZ, [_I, _I, _I, _I]),
     "qswitch_gate_up_geglu": (ctypes.c_int, [_P, _I, _I, _QP, _I, _I, _P, _P, _P, _SZ, _P]),
+    "qmoe_device_status": (ctypes.c_int, [ctypes.POINTER(ctypes.c_int32), _I]),
     "qswitch_down_combine_workspace": (_SZ, [_I, _I, _I, _I]),
     "qswitch_down_combine": (ctypes.c_int, [_P, _I, _I, _I, _QP, _I, _P, _P, _P, _P, _P, _SZ, _I, _P]),
     "qlinear": (ctypes.c_int, [_P, _I, _QP, _P, _P]),
@@ -299,6 +300,14 @@ def qswitch_gate_up_geglu(x_expert: torch.Tensor, gate_up: "TiledWeight", I: int
     _check(lib().qswitch_gate_up_geglu(_ptr(x_expert), T, H, ctypes.byref(d), I, k, _ptr(expert_offsets),
                                        _ptr(sorted_assign), _ptr(mid), _nbytes(mid), _stream()))
     return mid
+
+
+def device_status(reset: bool = True) -> int:
+    """The device status word (0: no kernel gave up a bounded wait since the
+    last reset).  Synchronises the device."""
+    v = ctypes.c_int32(0)
+    _check(lib().qmoe_device_status(ctypes.byref(v), 1 if reset else 0))
+    return int(v.value)
 
 
 def qswitch_down_combine_workspace(T: int, k: int, H: int, deterministic: int = 1) -> int:

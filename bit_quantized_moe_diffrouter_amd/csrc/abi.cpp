@@ -111,11 +111,32 @@ size_t unsorted_bytes(long long T, int k, int H, int I) {
   return (size_t)std::max(gu.partials, dn.partials) * sizeof(float);
 }
 
+int status_ptr(int** out) {
+  int* s = qmoe::device_status();
+  if (s == nullptr) return fail(QMOE_ERR_HIP, "the device status word is not available");
+  *out = s;
+  return QMOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
 const char* qmoe_last_error(void) { return g_last_error.c_str(); }
+
+int qmoe_device_status(int32_t* value, int32_t reset) {
+  REQUIRE(value != nullptr, QMOE_ERR_INVALID, "qmoe_device_status: null value pointer");
+  int* s = nullptr;
+  if (int rc = status_ptr(&s)) return rc;
+  hipError_t err = hipDeviceSynchronize();
+  if (err == hipSuccess) err = hipMemcpy(value, s, sizeof(int32_t), hipMemcpyDeviceToHost);
+  if (err == hipSuccess && reset) {
+    const int32_t zero = 0;
+    err = hipMemcpy(s, &zero, sizeof(int32_t), hipMemcpyHostToDevice);
+  }
+  if (err != hipSuccess) return fail(QMOE_ERR_HIP, "qmoe_device_status: %s", hipGetErrorString(err));
+  return ok();
+}
 
 size_t moe_route_workspace(int32_t T, int32_t H, int32_t E) {
   if (T <= 0 || H <= 0 || E <= 0 || H % 64 != 0) return 0;

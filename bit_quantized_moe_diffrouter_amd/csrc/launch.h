@@ -64,7 +64,13 @@ struct SwitchArgs {
   int ntiles;      // column tiles per row chunk (set by the launcher)
   int max_tiles;   // switch: activation tiles the input and output buffers hold
   float cap;       // softcap of the LM-head mode
+  int* status;     // device status word (set by the launcher)
 };
+// Device status word: bits a kernel raises when a bounded wait inside a
+// workgroup gave up (its outputs are then wrong).
+constexpr int kStatusSpin = 1;
+// this device's status word (a device address), or null
+int* device_status();
 hipError_t launch_gate_up_geglu(SwitchArgs a, int num_cu, hipStream_t stream);
 hipError_t launch_down(SwitchArgs a, int num_cu, hipStream_t stream);
 hipError_t launch_dense(SwitchArgs a, int num_cu, hipStream_t stream);

@@ -503,12 +503,14 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
   };
 
   // Bounded wait on a hand-over flag: a protocol slip cannot hang the GPU (after
-  // about 10^8 cycles the wave goes on, with wrong results).
+  // about 10^8 cycles the wave goes on, with wrong results, and raises the
+  // device status word's kStatusSpin bit so that the caller can tell).
   auto pair_wait = [&](int* f, int v) __attribute__((always_inline)) {
     for (int it = 0; it < (1 << 21); ++it) {
       if (__hip_atomic_load(f, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) >= v) return;
       __builtin_amdgcn_s_sleep(1);
     }
+    if (lane == 0) __hip_atomic_fetch_or(p.status, kStatusSpin, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
   (void)pair_wait;
 
@@ -809,6 +811,28 @@ namespace {
 
 constexpr int kMaxDevices = 64;
 
+}  // namespace
+
+// One int per device (each device holds its own copy of the module's
+// variables).
+__device__ int g_qmoe_status;
+
+int* device_status() {
+  static int* addr[kMaxDevices];
+  static std::atomic<int> ready[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  if (!ready[dev].load(std::memory_order_acquire)) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(g_qmoe_status)) != hipSuccess || ptr == nullptr) return nullptr;
+    addr[dev] = static_cast<int*>(ptr);
+    ready[dev].store(1, std::memory_order_release);
+  }
+  return addr[dev];
+}
+
+namespace {
+
 // Items a launch can hold (every one of the A rows in its own bucket's
 // chunks, at most one partial chunk per bucket).
 template <int MODE>
@@ -826,6 +850,8 @@ constexpr size_t lds_bytes() {
 template <int MODE, int KS, int D>
 hipError_t launch_cfg(SwitchArgs a, int extra_buckets, int num_cu, hipStream_t stream) {
   a.ntiles = a.nblk;
+  a.status = device_status();
+  if (a.status == nullptr) return hipErrorInvalidSymbol;
   constexpr size_t lds = lds_bytes<MODE, KS>();
   const long long items = max_items<MODE>(a, extra_buckets);
   long long grid = std::min(items, (long long)num_cu * 2);

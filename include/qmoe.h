@@ -106,6 +106,15 @@ typedef struct qmoe_qweight {
  * thread. */
 const char* qmoe_last_error(void);
 
+/* The current device's status word: bits the kernels raise when a bounded
+ * wait inside a workgroup gave up (1) or a workgroup met more sorted rows
+ * than its LDS holds (2); the outputs of such a call are wrong.  0 means no
+ * kernel has raised anything since the last reset.  Waits for the device
+ * (hipDeviceSynchronize), then copies the word to *value and, if reset is
+ * non-zero, clears it.  A debugging and testing aid; not needed for normal
+ * use. */
+int qmoe_device_status(int32_t* value, int32_t reset);
+
 /* ------------------------------------------------------------------------
  * qmoe_tile_weight -- re-lays a row-major 4-bit weight into the tiled layout
  * the switch linears and qlinear read.  A pure permutation of the codes,

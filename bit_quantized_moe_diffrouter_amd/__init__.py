@@ -123,8 +123,15 @@ def _check(rc: int):
         raise QMoEError(rc, lib().qmoe_last_error().decode())
 
 
+def _dptr(t: torch.Tensor) -> int:
+    """Device address of a tensor handed to the library (host tensors refused)."""
+    if not t.is_cuda:
+        raise ValueError(f"a {tuple(t.shape)} {t.dtype} argument must be a device tensor")
+    return t.data_ptr()
+
+
 def _ptr(t: Optional[torch.Tensor]):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    return None if t is None else ctypes.c_void_p(_dptr(t))
 
 
 def _stream():
@@ -132,16 +139,28 @@ def _stream():
 
 
 def _need(t: torch.Tensor, name: str, elem: int, shape=None):
+    """Checks a tensor handed to the library: element size, shape and layout
+    (the C calls take bare pointers, so this is the only size check some
+    arguments get).  Raises before anything is launched; residence on the
+    device is checked when the pointer is taken (_dptr)."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name}: expected a torch.Tensor")
-    if not t.is_cuda:
-        raise ValueError(f"{name}: must be a device tensor")
-    if not t.is_contiguous():
-        raise ValueError(f"{name}: must be contiguous")
     if t.element_size() != elem:
         raise ValueError(f"{name}: element size {t.element_size()}, expected {elem}")
-    if shape is not None and tuple(t.shape) != tuple(shape):
+    if shape is not None and tuple(t.shape) != tuple(int(v) for v in shape):
         raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def _need_opt(t: Optional[torch.Tensor], name: str, elem: int, shape=None):
+    if t is not None:
+        _need(t, name, elem, shape)
+
+
+def _same(a: int, b: int, what: str):
+    if int(a) != int(b):
+        raise ValueError(f"{what}: {a} != {b}")
 
 
 @dataclass
@@ -173,7 +192,7 @@ class QuantWeight:
         lead = tuple(self.w.shape[:-1])
         if tuple(self.scales.shape) != lead + (g,) or tuple(self.biases.shape) != lead + (g,):
             raise ValueError("scales/biases shape does not match the codes")
-        return QWeightDesc(self.w.data_ptr(), self.scales.data_ptr(), self.biases.data_ptr(),
+        return QWeightDesc(_dptr(self.w), _dptr(self.scales), _dptr(self.biases),
                            self.experts, self.rows, self.in_features, 4, 64, LAYOUT_ROWS, 0)
 
     @classmethod
@@ -215,7 +234,7 @@ class TiledWeight:
 
     def desc(self) -> QWeightDesc:
         _need(self.buf, "tiled weight", 1)
-        return QWeightDesc(self.buf.data_ptr(), None, None, self.experts, self.rows, self.in_features, 4, 64,
+        return QWeightDesc(_dptr(self.buf), None, None, self.experts, self.rows, self.in_features, 4, 64,
                            LAYOUT_TILED, self.split)
 
 
@@ -229,10 +248,18 @@ def moe_route(x_router: torch.Tensor, norm_scale: torch.Tensor, eps: float, proj
               weights: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None
               ) -> Tuple[torch.Tensor, torch.Tensor]:
     """DiffRouter: returns (indices int32 [T, k], weights fp32 [T, k])."""
-    T, H = x_router.shape
+    _need(x_router, "x_router", 2)
+    T, H = (int(v) for v in x_router.shape)
     E = proj.rows
     dev = x_router.device
-    _need(x_router, "x_router", 2)
+    _same(proj.in_features, H, "router weight in_features vs x_router.shape[1]")
+    _need(norm_scale, "norm_scale", 2, (H,))
+    _need(per_expert_scale, "per_expert_scale", 2, (E,))
+    _need_opt(logit_bias, "logit_bias (fp32)", 4, (E,))
+    _need_opt(logits_out, "logits_out (fp32)", 4, (T, E))
+    _need_opt(indices, "indices", 4, (T, k))
+    _need_opt(weights, "weights (fp32)", 4, (T, k))
+    _need_opt(workspace, "workspace", 1)
     if indices is None:
         indices = torch.empty((T, k), dtype=torch.int32, device=dev)
     if weights is None:
@@ -259,8 +286,11 @@ def moe_sort(indices: torch.Tensor, E: int, expert_offsets: Optional[torch.Tenso
     """Token-by-expert sort: returns (expert_offsets int32 [E+1], sorted_assign int32 [T*k]).
     A workspace is allocated when none is given and the input is large enough
     for the slice sort; slices=False passes none, so one workgroup sorts."""
-    T, k = indices.shape
     _need(indices, "indices", 4)
+    T, k = (int(v) for v in indices.shape)
+    _need_opt(expert_offsets, "expert_offsets", 4, (E + 1,))
+    _need_opt(sorted_assign, "sorted_assign", 4, (T * k,))
+    _need_opt(workspace, "workspace", 1)
     dev = indices.device
     if expert_offsets is None:
         expert_offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
@@ -291,9 +321,14 @@ def qswitch_gate_up_geglu(x_expert: torch.Tensor, gate_up: "TiledWeight", I: int
                           mid: Optional[torch.Tensor] = None) -> torch.Tensor:
     """gate_up switch linear + split + GeGLU: returns mid, a uint8 buffer of activation tiles
     (I columns, the sorted rows of each expert in 16-row tiles; layout in qmoe.h)."""
-    T, H = x_expert.shape
     _need(x_expert, "x_expert", 2)
+    T, H = (int(v) for v in x_expert.shape)
     E = gate_up.experts
+    _same(gate_up.in_features, H, "gate_up in_features vs x_expert.shape[1]")
+    _same(gate_up.rows, 2 * I, "gate_up rows vs 2 * I")
+    _need(expert_offsets, "expert_offsets", 4, (E + 1,))
+    _need(sorted_assign, "sorted_assign", 4, (T * k,))
+    _need_opt(mid, "mid", 1)
     if mid is None:
         mid = torch.empty(max(1, qswitch_mid_bytes(T, k, I, E)), dtype=torch.uint8, device=x_expert.device)
     d = gate_up.desc()
@@ -322,6 +357,15 @@ def qswitch_down_combine(mid: torch.Tensor, T: int, k: int, down: "TiledWeight",
     activation-tile buffer qswitch_gate_up_geglu wrote."""
     I = down.in_features
     H = down.rows
+    E = down.experts
+    _need(mid, "mid", 1)
+    _need(weights, "weights (fp32)", 4, (T, k))
+    _need(expert_offsets, "expert_offsets", 4, (E + 1,))
+    _need(sorted_assign, "sorted_assign", 4, (T * k,))
+    _need_opt(y, "y", 2, (T, H))
+    _need_opt(workspace, "workspace", 1)
+    if T > 0 and _nbytes(mid) < qswitch_mid_bytes(T, k, I, E):
+        raise ValueError(f"mid: {_nbytes(mid)} bytes, {qswitch_mid_bytes(T, k, I, E)} needed")
     dev = mid.device
     if y is None:
         y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
@@ -339,7 +383,8 @@ def qswitch_down_combine(mid: torch.Tensor, T: int, k: int, down: "TiledWeight",
 def qlinear(x: torch.Tensor, W: "TiledWeight", y: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Dense 4-bit linear y = x . dequant(W)^T: returns bf16 [M, N]."""
     M = int(x.shape[0])
-    _need(x, "x", 2)
+    _need(x, "x", 2, (M, W.in_features))
+    _need_opt(y, "y", 2, (M, W.rows))
     if y is None:
         y = torch.empty((M, W.rows), dtype=torch.bfloat16, device=x.device)
     d = W.desc()
@@ -407,7 +452,8 @@ def qlinear_geglu(x: torch.Tensor, W: "TiledWeight", y: Optional[torch.Tensor] =
     """gelu_tanh(x . gate^T) * (x . up^T) against the fused [gate; up] weight
     (tiled with split = N): returns bf16 [M, N]."""
     M = int(x.shape[0])
-    _need(x, "x", 2)
+    _need(x, "x", 2, (M, W.in_features))
+    _need_opt(y, "y", 2, (M, W.split))
     if y is None:
         y = torch.empty((M, W.split), dtype=torch.bfloat16, device=x.device)
     d = W.desc()
@@ -487,9 +533,12 @@ def qswitch_gate_up_geglu_unsorted(x_expert: torch.Tensor, gate_up: "TiledWeight
                                    workspace: torch.Tensor, mid_rows: Optional[torch.Tensor] = None) -> torch.Tensor:
     """gate_up + split + GeGLU per assignment, no sort: returns mid_rows bf16 [T*k, I]."""
     _need(x_expert, "x_expert", 2)
-    _need(indices, "indices", 4)
     T, H = (int(v) for v in x_expert.shape)
     k = int(indices.shape[-1])
+    _need(indices, "indices", 4, (T, k))
+    _same(gate_up.in_features, H, "gate_up in_features vs x_expert.shape[1]")
+    _same(gate_up.rows, 2 * I, "gate_up rows vs 2 * I")
+    _need(workspace, "workspace", 1)
     if mid_rows is None:
         mid_rows = torch.empty((T * k, I), dtype=torch.bfloat16, device=x_expert.device)
     _need(mid_rows, "mid_rows", 2, (T * k, I))
@@ -503,11 +552,12 @@ def qswitch_down_combine_unsorted(mid_rows: torch.Tensor, T: int, k: int, down: 
                                   weights: torch.Tensor, workspace: torch.Tensor,
                                   y: Optional[torch.Tensor] = None) -> torch.Tensor:
     """down per assignment + weighted sum over k, no sort: returns y bf16 [T, H]."""
-    _need(mid_rows, "mid_rows", 2)
-    _need(indices, "indices", 4)
-    _need(weights, "weights", 4)
-    I = int(mid_rows.shape[-1])
+    I = down.in_features
     H = down.rows
+    _need(mid_rows, "mid_rows", 2, (T * k, I))
+    _need(indices, "indices", 4, (T, k))
+    _need(weights, "weights (fp32)", 4, (T, k))
+    _need(workspace, "workspace", 1)
     if y is None:
         y = torch.empty((T, H), dtype=torch.bfloat16, device=mid_rows.device)
     _need(y, "y", 2, (T, H))
@@ -537,7 +587,7 @@ def qlinear_softcap(x: torch.Tensor, W: "TiledWeight", cap: float = 30.0,
                     y: Optional[torch.Tensor] = None) -> torch.Tensor:
     """cap * tanh(bf16(x . dequant(W)^T) / cap): returns fp32 [M, N]."""
     M = int(x.shape[0])
-    _need(x, "x", 2)
+    _need(x, "x", 2, (M, W.in_features))
     if y is None:
         y = torch.empty((M, W.rows), dtype=torch.float32, device=x.device)
     _need(y, "y", 4, (M, W.rows))
@@ -559,7 +609,7 @@ class TiledTWeight:
 
     def desc(self) -> QWeightDesc:
         _need(self.buf, "tiled table", 1)
-        return QWeightDesc(self.buf.data_ptr(), None, None, 1, self.rows, self.in_features, 4, 64, 2, 0)
+        return QWeightDesc(_dptr(self.buf), None, None, 1, self.rows, self.in_features, 4, 64, 2, 0)
 
 
 def softmax_rows_bf16(z: torch.Tensor, probs: Optional[torch.Tensor] = None) -> torch.Tensor:
@@ -577,8 +627,9 @@ def embed_matmul_t(probs: torch.Tensor, W: TiledTWeight, scale: float, out: Opti
                    workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """bf16(bf16(probs . dequant(E)) * scale) with the table E [V, H] used
     without transposing: returns bf16 [L, H]."""
-    _need(probs, "probs", 2)
     L = int(probs.shape[0])
+    _need(probs, "probs", 2, (L, W.rows))
+    _need_opt(workspace, "workspace", 1)
     if out is None:
         out = torch.empty((L, W.in_features), dtype=torch.bfloat16, device=probs.device)
     _need(out, "out", 2, (L, W.in_features))

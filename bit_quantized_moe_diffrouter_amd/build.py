@@ -1,12 +1,14 @@
 """Builds libqmoe.so (HIP for gfx950) in the package directory with hipcc.
 
 Each kernel translation unit is compiled separately (in parallel), then all
-objects are linked into one shared library.  The library is written to a
+objects are linked into one shared library.  A kernel that spills registers
+to scratch memory fails the build.  The library is written to a
 temporary name and renamed, so a concurrent reader never sees a half-written
 file."""
 from __future__ import annotations
 
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -37,6 +39,28 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libqmoe.so)")
 
 
+# The compiler's per-kernel resource remarks: a kernel that spills registers
+# to scratch memory fails the build (the hot loops are sized to fit).
+RESOURCE_FLAGS = ["-Rpass-analysis=kernel-resource-usage"]
+_REMARK = re.compile(r"remark:\s+(Function Name|SGPRs Spill|VGPRs Spill): (\S+)")
+
+
+def spills(output: str):
+    """(kernel, sgpr_spills, vgpr_spills) for every kernel in the remarks whose
+    spill count is non-zero."""
+    found, name, sgpr = [], None, 0
+    for m in _REMARK.finditer(output):
+        key, val = m.group(1), m.group(2)
+        if key == "Function Name":
+            name, sgpr = val, 0
+        elif key == "SGPRs Spill":
+            sgpr = int(val)
+        else:
+            if sgpr or int(val):
+                found.append((name, sgpr, int(val)))
+    return found
+
+
 def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -44,8 +68,13 @@ def _run(cmd, verbose):
     out = "\n".join(l for l in r.stdout.splitlines() if "is not a recognized feature" not in l)
     if r.returncode != 0:
         raise RuntimeError(f"command failed ({r.returncode}): {' '.join(cmd)}\n{out}")
-    if verbose and out.strip():
-        print(out)
+    bad = spills(out)
+    if bad:
+        raise RuntimeError("register spills in " + ", ".join(f"{n} (SGPR {s}, VGPR {v})" for n, s, v in bad))
+    if verbose:
+        shown = "\n".join(l for l in out.splitlines() if "remark:" not in l)
+        if shown.strip():
+            print(shown)
 
 
 def build(verbose: bool = False) -> str:
@@ -55,7 +84,7 @@ def build(verbose: bool = False) -> str:
     jobs = []
     for src in HIP_SOURCES:
         obj = os.path.join(OBJ, src.replace(".hip", ".o"))
-        jobs.append([hipcc, f"--offload-arch={ARCH}", *COMMON_FLAGS, *DEVICE_FLAGS, "-c",
+        jobs.append([hipcc, f"--offload-arch={ARCH}", *COMMON_FLAGS, *DEVICE_FLAGS, *RESOURCE_FLAGS, "-c",
                      os.path.join(CSRC, src), "-o", obj])
     for src in HOST_SOURCES:
         obj = os.path.join(OBJ, src.replace(".cpp", ".o"))

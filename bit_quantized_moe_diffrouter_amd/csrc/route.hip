@@ -13,7 +13,9 @@
 // 1 / sqrt(mean(x^2) + eps).  A (token tile, k-range) grid fills the chip at
 // 256 tokens; the partial logits go to a workspace and kernel 2 sums them in
 // a fixed order, so the result is run-to-run reproducible.  Kernel 2 runs one
-// wave per token: k rounds of a wave-wide arg-max, then the softmax in fp32.
+// wave per token: each logit's rank is counted against the token's table of
+// ordering keys, the k best land in slots 0..k-1 in descending order, then the
+// softmax in fp32.
 #include <math.h>
 
 #include "common.h"

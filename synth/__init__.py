@@ -13,6 +13,9 @@ Workload recipe (one line per tensor, in draw order of the weight stream):
 * router norm scale ``s[h] ~ U[0.8, 1.2]``                     -> bf16 ``[H]``
 * router projection codes                                        -> u32  ``[E, H/8]``
 * router projection scales ``|N(0, 0.02)|``, biases ``-8*scale`` -> bf16 ``[E, H/64]``
+  (or, with a bias seed, biases drawn independently of the scales from a
+  stream of their own: ``bf16(-scale * U[6, 9.5] + N(0, 0.01))``, so that a
+  kernel which derived the bias from the scale would be caught)
 * ``per_expert_scale ~ U[0.5, 1.5]``                            -> bf16 ``[E]``
 * gate_up codes / scales / biases                                -> ``[E, 2I, H/8]`` / ``[E, 2I, H/64]``
 * down codes / scales / biases                                   -> ``[E, H, I/8]`` / ``[E, H, I/64]``
@@ -58,10 +61,15 @@ def _codes(rng: np.random.Generator, shape) -> np.ndarray:
     return rng.integers(0, 2**32, size=shape, dtype=np.uint32)
 
 
-def _scales_biases(rng: np.random.Generator, shape):
+def _scales_biases(rng: np.random.Generator, shape, bias_rng: Optional[np.random.Generator] = None):
     scales = to_bf16_bits(np.abs(rng.normal(0.0, 0.02, size=shape)).astype(np.float32))
-    # -8 * scale is exact in bfloat16 (power-of-two multiply, sign flip)
-    biases = to_bf16_bits(-8.0 * bf16_bits_as_f32(scales))
+    if bias_rng is None:
+        # -8 * scale is exact in bfloat16 (power-of-two multiply, sign flip)
+        biases = to_bf16_bits(-8.0 * bf16_bits_as_f32(scales))
+    else:
+        u = bias_rng.uniform(6.0, 9.5, size=shape)
+        n = bias_rng.normal(0.0, 0.01, size=shape)
+        biases = to_bf16_bits((-bf16_bits_as_f32(scales) * u + n).astype(np.float32))
     return scales, biases
 
 
@@ -92,11 +100,16 @@ class QTensor:
         return self.w.nbytes + self.scales.nbytes + self.biases.nbytes
 
 
-def random_qtensor(rng: np.random.Generator, lead_shape, in_features: int) -> QTensor:
+def random_qtensor(rng: np.random.Generator, lead_shape, in_features: int,
+                   bias_rng: Optional[np.random.Generator] = None) -> QTensor:
     assert in_features % GROUP == 0
     w = _codes(rng, tuple(lead_shape) + (in_features // 8,))
-    s, b = _scales_biases(rng, tuple(lead_shape) + (in_features // GROUP,))
+    s, b = _scales_biases(rng, tuple(lead_shape) + (in_features // GROUP,), bias_rng)
     return QTensor(w, s, b)
+
+
+def _bias_rng(seed: Optional[int]) -> Optional[np.random.Generator]:
+    return None if seed is None else np.random.default_rng(seed)
 
 
 # ----------------------------------------------------------------------------
@@ -115,6 +128,7 @@ class MoEConfig:
     zipf_tau: Optional[float] = None
     zipf_perm_seed: int = 4
     eps: float = 1e-6
+    bias_seed: Optional[int] = None   # set: biases independent of the scales
 
 
 @dataclass(frozen=True)
@@ -125,6 +139,7 @@ class QLinearConfig:
     K: int
     seed_w: int
     seed_x: int
+    bias_seed: Optional[int] = None
 
 
 TINY = MoEConfig("tiny_16tok_h256_e8_top2", T=16, H=256, E=8, k=2, I=128, seed_w=0, seed_x=0)
@@ -174,12 +189,13 @@ def zipf_logit_bias(E: int, tau: float, perm_seed: int, s: float = 1.1) -> np.nd
 
 def make_moe_weights(cfg: MoEConfig, seed: Optional[int] = None) -> MoEWeights:
     rng = np.random.default_rng(cfg.seed_w if seed is None else seed)
+    brng = _bias_rng(cfg.bias_seed)
     H, E, I = cfg.H, cfg.E, cfg.I
     norm_scale = to_bf16_bits(rng.uniform(0.8, 1.2, size=H).astype(np.float32))
-    router = random_qtensor(rng, (E,), H)
+    router = random_qtensor(rng, (E,), H, brng)
     pes = to_bf16_bits(rng.uniform(0.5, 1.5, size=E).astype(np.float32))
-    gate_up = random_qtensor(rng, (E, 2 * I), H)
-    down = random_qtensor(rng, (E, H), I)
+    gate_up = random_qtensor(rng, (E, 2 * I), H, brng)
+    down = random_qtensor(rng, (E, H), I, brng)
     bias = None
     if cfg.zipf_tau is not None:
         bias = zipf_logit_bias(E, cfg.zipf_tau, cfg.zipf_perm_seed)
@@ -206,7 +222,7 @@ class QLinearInputs:
 
 def make_qlinear_inputs(cfg: QLinearConfig) -> QLinearInputs:
     rng = np.random.default_rng(cfg.seed_w)
-    W = random_qtensor(rng, (cfg.N,), cfg.K)
+    W = random_qtensor(rng, (cfg.N,), cfg.K, _bias_rng(cfg.bias_seed))
     return QLinearInputs(cfg, make_activations(cfg.M, cfg.K, cfg.seed_x), W)
 
 

@@ -355,3 +355,16 @@ def test_header_is_plain_c_and_links(L, tmp_path):
     run = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
     assert run.returncode == 0, (run.returncode, run.stdout, run.stderr)
     assert "qlinear" in run.stdout
+
+
+def test_build_rejects_register_spills():
+    """The build reads the compiler's per-kernel resource remarks and fails on
+    any kernel that spills registers to scratch memory."""
+    from bit_quantized_moe_diffrouter_amd import build
+    tail = " [-Rpass-analysis=kernel-resource-usage]"
+    remarks = "\n".join(f"x.hip:1:1: remark: {l}{tail}" for l in [
+        "Function Name: _ZN4qmoe3fooEv", "    SGPRs Spill: 0", "    VGPRs Spill: 12",
+        "Function Name: _ZN4qmoe3barEv", "    SGPRs Spill: 0", "    VGPRs Spill: 0",
+        "Function Name: _ZN4qmoe3bazEv", "    SGPRs Spill: 3", "    VGPRs Spill: 0"])
+    assert build.spills(remarks) == [("_ZN4qmoe3fooEv", 0, 12), ("_ZN4qmoe3bazEv", 3, 0)]
+    assert "-Rpass-analysis=kernel-resource-usage" in build.RESOURCE_FLAGS

@@ -78,6 +78,11 @@ def gpu_route(inp, p, logits=True):
 
 
 def assert_route_parity(inp, idx_g, w_g, lg_g):
+    """Logits within 2e-6; outside the exempt band the oracle's set and
+    weights; on every token (exempt ones included) a valid top-k of the GPU's
+    own logits -- k distinct experts in descending order whose smallest logit
+    is at least the largest unselected one -- with weights equal to the
+    precise softmax of those selected logits times per_expert_scale."""
     cfg = inp.cfg
     idx_r, w_r, lg_r = oracle_route(inp)
     np.testing.assert_allclose(lg_g, lg_r, rtol=0, atol=2e-6)
@@ -88,10 +93,17 @@ def assert_route_parity(inp, idx_g, w_g, lg_g):
         wg = dict(zip(idx_g[t].tolist(), w_g[t].tolist()))
         for e, wr in zip(idx_r[t].tolist(), w_r[t].tolist()):
             assert abs(wg[e] - wr) <= 1e-5, f"token {t} expert {e}: {wg[e]} vs {wr}"
-    # every row is a valid top-k set of distinct experts, in descending logit order
+    pes = O.bf16_to_f64(inp.weights.per_expert_scale)
     for t in range(cfg.T):
-        assert len(set(idx_g[t].tolist())) == cfg.k
-        assert np.all(np.diff(lg_g[t, idx_g[t]]) <= 0)
+        sel = idx_g[t].tolist()
+        assert len(set(sel)) == cfg.k and all(0 <= e < cfg.E for e in sel)
+        picked = lg_g[t, sel].astype(np.float64)
+        assert np.all(np.diff(picked) <= 0)
+        rest = np.delete(lg_g[t], sel)
+        if rest.size:
+            assert picked.min() >= rest.max(), f"token {t}: selected {picked.min()} < unselected {rest.max()}"
+        ref_w = O.precise_softmax(picked) * pes[sel]
+        np.testing.assert_allclose(w_g[t], ref_w, rtol=0, atol=1e-6, err_msg=f"token {t}")
     return int(exempt.sum())
 
 
@@ -287,10 +299,21 @@ def test_down_combine_parity_from_gpu_mid(cfg):
     assert err <= 1e-2
 
 
+def mixed_routing(inp, idx_g, w_g):
+    """The oracle's own routing, except on tokens inside the exempt band
+    (8th/9th oracle-logit gap below 1e-5), which keep the GPU's."""
+    idx_r, w_r, lg_r = oracle_route(inp)
+    ex = O.gap_kth(lg_r, inp.cfg.k) < GAP_EXEMPT
+    idx_m, w_m = idx_r.copy(), w_r.copy()
+    idx_m[ex], w_m[ex] = idx_g[ex], w_g[ex]
+    return idx_m, w_m, idx_r, ex
+
+
 @pytest.mark.parametrize("cfg", MOE_CFGS, ids=lambda c: c.name)
 def test_layer_parity(cfg):
-    """Whole layer through the four calls against the oracle (exempt tokens use
-    the GPU's own routing in the oracle's expert stage)."""
+    """Whole layer through the four calls against the oracle's whole layer:
+    the oracle routes every token itself, except those inside the exempt band,
+    which take the GPU's routing (there either choice is correct)."""
     import bit_quantized_moe_diffrouter_amd as q
     say(f"[layer] {cfg.name}")
     inp = inputs(cfg)
@@ -299,31 +322,30 @@ def test_layer_parity(cfg):
     y, idx, w, off, sa, mid = q.moe_layer(x, x, p, cfg.k, cfg.eps)
     torch.cuda.synchronize()
     idx_g, w_g = idx.cpu().numpy(), w.cpu().numpy()
+    idx_m, w_m, idx_r, ex = mixed_routing(inp, idx_g, w_g)
+    assert all(set(idx_g[t]) == set(idx_r[t]) for t in np.nonzero(~ex)[0])
     toks = sample_tokens(cfg.T, 32)
-    ref = O.experts_bruteforce(inp.x, idx_g, w_g, inp.weights.gate_up, inp.weights.down, cfg.I, tokens=toks)
+    ref = O.experts_bruteforce(inp.x, idx_m, w_m, inp.weights.gate_up, inp.weights.down, cfg.I, tokens=toks)
     err = O.rowwise_rel_err(bf16_host(y)[toks], ref)
-    say(f"  layer rel err {err:.3e} over {len(toks)} tokens")
+    say(f"  layer rel err {err:.3e} over {len(toks)} tokens ({int(ex.sum())} exempt in all)")
     assert err <= Y_TOL
-    # routing of the same run matches the oracle
-    idx_r, _, lg_r = oracle_route(inp)
-    ok = O.gap_kth(lg_r, cfg.k) >= GAP_EXEMPT
-    assert all(set(idx_g[t]) == set(idx_r[t]) for t in np.nonzero(ok)[0])
 
 
-def test_layer_full_canvas_against_grouped_oracle():
-    """All 256 canvas tokens against the fp32 grouped oracle."""
+@pytest.mark.parametrize("cfg", [synth.CANVAS, synth.PREFILL, synth.SKEW], ids=lambda c: c.name)
+def test_layer_all_tokens_against_grouped_oracle(cfg):
+    """Every token of the canvas, the 4096-token prefill and the skewed canvas
+    against the fp32 grouped oracle (oracle routing outside the exempt band)."""
     import bit_quantized_moe_diffrouter_amd as q
-    cfg = synth.CANVAS
     say(f"[layer all tokens] {cfg.name}")
     inp = inputs(cfg)
     p = params(cfg)
     x = dev_tensor(inp.x)
     y, idx, w, *_ = q.moe_layer(x, x, p, cfg.k, cfg.eps)
     torch.cuda.synchronize()
-    ref = O.experts_grouped(inp.x, idx.cpu().numpy(), w.cpu().numpy(), inp.weights.gate_up,
-                            inp.weights.down, cfg.I)
+    idx_m, w_m, _, ex = mixed_routing(inp, idx.cpu().numpy(), w.cpu().numpy())
+    ref = O.experts_grouped(inp.x, idx_m, w_m, inp.weights.gate_up, inp.weights.down, cfg.I)
     err = O.rowwise_rel_err(bf16_host(y), ref)
-    say(f"  rel err {err:.3e}")
+    say(f"  rel err {err:.3e} over {cfg.T} tokens")
     assert err <= Y_TOL
 
 

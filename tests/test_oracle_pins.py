@@ -507,3 +507,18 @@ def test_embed_matmul_t_uniform_probabilities_give_column_means():
     want = O.bf16_to_f64(O.f64_to_bf16_bits(cols))
     assert np.array_equal(got[0], want) and np.array_equal(got[1], want)
     assert np.array_equal(O.embed_matmul_t(p, W.w, W.scales, W.biases, 1.0, rows=[1]), got[[1]])
+
+
+# ---------------------------------------------------------------------------- inputs
+def test_synth_independent_biases():
+    """The general affine workload: biases not a fixed multiple of the scales,
+    codes and scales identical to the default stream's."""
+    import dataclasses
+    cfg = dataclasses.replace(synth.TINY, bias_seed=101)
+    wt, w0 = synth.make_moe_weights(cfg), synth.make_moe_weights(synth.TINY)
+    np.testing.assert_array_equal(wt.gate_up.w, w0.gate_up.w)
+    np.testing.assert_array_equal(wt.gate_up.scales, w0.gate_up.scales)
+    s = synth.bf16_bits_as_f32(wt.gate_up.scales).astype(np.float64)
+    b = synth.bf16_bits_as_f32(wt.gate_up.biases).astype(np.float64)
+    ratio = b[s > 0] / s[s > 0]
+    assert np.std(ratio) > 1.0 and np.mean(b == -8 * s) < 0.05

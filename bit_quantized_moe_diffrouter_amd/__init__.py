@@ -26,7 +26,7 @@ __all__ = [
     "QMoEError", "QuantWeight", "TiledWeight", "MoEParams", "lib", "library_path",
     "moe_route", "moe_route_workspace", "moe_sort", "moe_sort_workspace", "qswitch_mid_bytes",
     "qswitch_gate_up_geglu", "device_status",
-    "qswitch_down_combine", "qswitch_down_combine_workspace", "qlinear", "moe_layer",
+    "qswitch_down_combine", "qswitch_down_combine_workspace", "qswitch_down_combine_noalloc", "qlinear", "moe_layer",
     "ff_prenorm", "qlinear_geglu", "ff_combine", "FFParams", "ff_block", "qlinear_softcap",
     "TiledTWeight", "softmax_rows_bf16", "embed_matmul_t", "self_condition_embed",
     "qswitch_unsorted_workspace", "unsorted_workspace", "qswitch_gate_up_geglu_unsorted",
@@ -78,6 +78,7 @@ _SIGNATURES = {
     "qmoe_device_status": (ctypes.c_int, [ctypes.POINTER(ctypes.c_int32), _I]),
     "qswitch_down_combine_workspace": (_SZ, [_I, _I, _I, _I]),
     "qswitch_down_combine": (ctypes.c_int, [_P, _I, _I, _I, _QP, _I, _P, _P, _P, _P, _P, _SZ, _I, _P]),
+    "qswitch_down_combine_noalloc": (ctypes.c_int, [_P, _I, _I, _I, _QP, _I, _P, _P, _P, _P, _I, _P]),
     "qlinear": (ctypes.c_int, [_P, _I, _QP, _P, _P]),
     "qlinear_geglu": (ctypes.c_int, [_P, _I, _QP, _P, _P]),
     "qlinear_softcap": (ctypes.c_int, [_P, _I, _QP, ctypes.c_float, _P, _P]),
@@ -377,6 +378,33 @@ def qswitch_down_combine(mid: torch.Tensor, T: int, k: int, down: "TiledWeight",
     _check(lib().qswitch_down_combine(_ptr(mid), T, k, I, ctypes.byref(d), H, _ptr(expert_offsets),
                                       _ptr(sorted_assign), _ptr(weights), _ptr(y), _ptr(workspace), ws_bytes,
                                       int(deterministic), _stream()))
+    return y
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20  # the scratch the library holds per device for the no-allocation calls
+
+
+def qswitch_down_combine_noalloc(mid: torch.Tensor, T: int, k: int, down: "TiledWeight", weights: torch.Tensor,
+                                 expert_offsets: torch.Tensor, sorted_assign: torch.Tensor, y: torch.Tensor,
+                                 deterministic: int = 1) -> torch.Tensor:
+    """qswitch_down_combine with the library's own scratch instead of a
+    workspace: allocates nothing (y is the caller's).  T*k*H*2 bytes of
+    scratch at most NOALLOC_SCRATCH_BYTES; calls overlapping on one device
+    race."""
+    I = down.in_features
+    H = down.rows
+    E = down.experts
+    _need(mid, "mid", 1)
+    _need(weights, "weights (fp32)", 4, (T, k))
+    _need(expert_offsets, "expert_offsets", 4, (E + 1,))
+    _need(sorted_assign, "sorted_assign", 4, (T * k,))
+    _need(y, "y", 2, (T, H))
+    if T > 0 and _nbytes(mid) < qswitch_mid_bytes(T, k, I, E):
+        raise ValueError(f"mid: {_nbytes(mid)} bytes, {qswitch_mid_bytes(T, k, I, E)} needed")
+    d = down.desc()
+    _check(lib().qswitch_down_combine_noalloc(_ptr(mid), T, k, I, ctypes.byref(d), H, _ptr(expert_offsets),
+                                              _ptr(sorted_assign), _ptr(weights), _ptr(y), int(deterministic),
+                                              _stream()))
     return y
 
 

@@ -309,6 +309,25 @@ int qswitch_down_combine(const void* mid, int32_t T, int32_t k, int32_t I, const
                   "qswitch_down_combine (combine)");
 }
 
+int qswitch_down_combine_noalloc(const void* mid, int32_t T, int32_t k, int32_t I, const qmoe_qweight* down,
+                                 int32_t H, const int32_t* expert_offsets, const int32_t* sorted_assign,
+                                 const float* weights, uint16_t* y, int32_t deterministic, hipStream_t stream) {
+  if (T <= 0 || k <= 0 || H <= 0)  // nothing to do, or rejected by the validation below
+    return qswitch_down_combine(mid, T, k, I, down, H, expert_offsets, sorted_assign, weights, y, nullptr, 0,
+                                deterministic, stream);
+  const size_t need = qswitch_down_combine_workspace(T, k, H, deterministic);
+  REQUIRE(need <= qmoe::kNoAllocScratchBytes, QMOE_ERR_UNSUPPORTED,
+          "qswitch_down_combine_noalloc: T*k*H = %lld needs %zu bytes of scratch, above the %zu the library "
+          "holds (use qswitch_down_combine with a workspace)",
+          (long long)T * k * H, need, qmoe::kNoAllocScratchBytes);
+  void* s = qmoe::noalloc_scratch();
+  REQUIRE(s != nullptr, QMOE_ERR_HIP, "qswitch_down_combine_noalloc: the library's scratch is not available");
+  // every byte of scratch the down pass hands to the combine is written first
+  // in this call (dropped rows as zeros), so nothing is cleared
+  return qswitch_down_combine(mid, T, k, I, down, H, expert_offsets, sorted_assign, weights, y, s,
+                              qmoe::kNoAllocScratchBytes, deterministic, stream);
+}
+
 size_t qmoe_tiled_weight_bytes(int32_t experts, int32_t rows, int32_t in, int32_t split) {
   if (experts <= 0 || rows <= 0 || in <= 0 || in % 64 != 0 || split < 0) return 0;
   if (split > 0 && (split % 16 != 0 || rows != 2 * split)) return 0;

@@ -71,6 +71,10 @@ struct SwitchArgs {
 constexpr int kStatusSpin = 1;
 // this device's status word (a device address), or null
 int* device_status();
+// Scratch held by the library for the entry points that allocate nothing:
+// this device's array (a device address), or null
+constexpr size_t kNoAllocScratchBytes = size_t(16) << 20;
+void* noalloc_scratch();
 hipError_t launch_gate_up_geglu(SwitchArgs a, int num_cu, hipStream_t stream);
 hipError_t launch_down(SwitchArgs a, int num_cu, hipStream_t stream);
 hipError_t launch_dense(SwitchArgs a, int num_cu, hipStream_t stream);

@@ -831,6 +831,26 @@ int* device_status() {
   return addr[dev];
 }
 
+// Device scratch of the entry points that allocate nothing: one array per
+// device (each device holds its own copy of the module's variables), kept
+// until the process ends.  Host code never uses its name as an address: the
+// address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+void* noalloc_scratch() {
+  static void* addr[kMaxDevices];
+  static std::atomic<int> ready[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  if (!ready[dev].load(std::memory_order_acquire)) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return nullptr;
+    addr[dev] = ptr;
+    ready[dev].store(1, std::memory_order_release);
+  }
+  return addr[dev];
+}
+
 namespace {
 
 // Items a launch can hold (every one of the A rows in its own bucket's

@@ -285,6 +285,28 @@ int qswitch_down_combine(const void* mid, int32_t T, int32_t k, int32_t I,
                          hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * qswitch_down_combine_noalloc -- qswitch_down_combine without a workspace
+ * argument and without any allocation, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid hipMalloc.  Same arguments, kernels and results as
+ * qswitch_down_combine (bit for bit); the workspace is a 16 MiB array the
+ * library holds on each device it runs on, until the process ends.
+ *
+ * Limit: qswitch_down_combine_workspace(T, k, H, det) <= 16 MiB, i.e.
+ * T*k*H*2 <= 16777216 (the 256-token canvas at H 2816, top-8 takes 11.5 MB);
+ * above it the call returns QMOE_ERR_UNSUPPORTED and does nothing.
+ * Every call on one device shares that device's array: calls that overlap on
+ * one device (other streams, other host threads) race and give wrong
+ * results; serialize them.  Nothing in the array needs clearing between
+ * calls (each call writes what it reads).
+ * ---------------------------------------------------------------------- */
+int qswitch_down_combine_noalloc(const void* mid, int32_t T, int32_t k, int32_t I,
+                                 const qmoe_qweight* down, int32_t H,
+                                 const int32_t* expert_offsets, const int32_t* sorted_assign,
+                                 const float* weights, uint16_t* y, int32_t deterministic,
+                                 hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Unsorted small-batch arm (model.ts page, DiffExperts.forward: below 64
  * assignments the flat indices are not sorted and the gather matmuls read
  * each assignment's expert directly; the model's decode layers use this arm

@@ -8,14 +8,25 @@ sets (1.28 GB) are rotated between steps so the 256 MB Infinity Cache cannot
 serve a layer's weights from the previous step.
 
 Prints ONE JSON line (rank 0):
-  value      tokens/s of the whole layer (wall clock over K steps, bracketed
-             by device synchronisation; no events inside)
+  value      tokens/s of the whole layer: wall clock over K steps, bracketed
+             by device synchronisation, the four calls issued from Python
+             with its garbage collector paused (no events inside).  The same
+             K steps replayed from HIP graphs (one per weight set) are
+             reported under "graph".
   roofline   the dominant kernel (qswitch_gate_up_geglu, one kernel per call):
              algorithmic bytes per launch / its mean launch time, from HIP
              events recorded between the calls on the launch stream in a
              second pass of K steps (events between kernels add a few
              microseconds of idle time per call, so they stay out of `value`)
-  cpu_baseline  the CPU oracle timed on this host on a bounded sample
+  layer_roofline  the whole layer against HBM: algorithmic bytes per step
+             (touched experts' weights, router weight, x in, y out) over the
+             wall-clock step time -- the figure the 60 % target is set on
+  cpu_baseline  the CPU oracle timed on this host: the canvas layer with the
+             BLAS pool as it comes (value, cores) and with one thread, plus one
+             full-size run each of the dense qlinear, the prefill and the
+             skewed canvas
+  qlinear_c1 the dense 4-bit linear at 2520 x 1152 -> 1152 on its own (mean
+             launch time from HIP events, TFLOP/s against the bf16 peak)
   decode_unsorted  diagnostic, not the metric: the small-batch arm (route +
              the two unsorted calls) at 1 and 7 tokens on the same weights
   lm_head    diagnostic, not the metric: the tied LM head with its softcap,
@@ -32,8 +43,9 @@ Prints ONE JSON line (rank 0):
 Two helper modes serve the committed profiles (see profiles/):
   --copy-probe        one plain 256 MiB device copy, five times (the known-size
                       kernel that calibrates rocprofv3's FETCH_SIZE/WRITE_SIZE)
-  --summarize DIR     turns the rocprofv3 output under DIR (kt/, fetch/, write/,
-                      copy_fetch/, copy_write/) into the summaries under profiles/
+  --summarize DIR     turns the rocprofv3 output under DIR (kt*/, <workload>_{kt,
+                      fetch,write,sq}/, copy_fetch/, copy_write/) into the
+                      summaries under profiles/
 roofline.traffic is read from profiles/qswitch_gate_up_canvas_traffic.txt and
 is null when the kernel sources no longer match the hash recorded there.
 """
@@ -74,7 +86,7 @@ def parse():
     ap.add_argument("--no-head", action="store_true", help="skip the LM-head diagnostic")
     ap.add_argument("--no-other", action="store_true", help="skip the prefill and skewed-canvas diagnostic")
     ap.add_argument("--no-vision", action="store_true", help="skip the vision-tower linears diagnostic")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=8.0)
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--summarize", metavar="DIR")
     return ap.parse_args()
@@ -137,6 +149,100 @@ def _kt_table(d, title, cmd, notes):
     return lines
 
 
+SIMD_NUM = 1024  # 256 compute units x 4 SIMDs
+PROFILE_RUNS = {
+    # tag: (workload, bench arguments, title)
+    "canvas": ("moe_canvas_256tok_h2816_e128_top8",
+               "--steps 20 --warmup 5 --no-cpu-baseline --no-ff-block --no-decode --no-other --no-head --no-vision",
+               "canvas workload (256 tokens, H 2816, 128 experts, top-8, I 704) and the dense qlinear at "
+               "2520 x 1152 -> 1152"),
+    "prefill": ("moe_prefill_4096tok_h2816_e128_top8", "--workload moe_prefill_4096tok_h2816_e128_top8 "
+                "--steps 10 --warmup 2 --no-cpu-baseline",
+                "prefill workload (4096 tokens, H 2816, 128 experts, top-8, I 704)"),
+    "skew": ("moe_canvas_skew_256tok_zipf1.1", "--workload moe_canvas_skew_256tok_zipf1.1 --steps 20 --warmup 5 "
+             "--no-cpu-baseline", "Zipf-skewed canvas (256 tokens, per-expert logit offset 0.1 ln p, p ~ rank^-1.1)"),
+}
+SQ_COUNTERS = ["SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES",
+               "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE"]
+KERNEL_ROLES = [("route_logits_kernel", "moe_route: logits (partial sums)"),
+                ("route_topk_kernel", "moe_route: sum, norm, top-k, softmax"),
+                ("sort_hist_kernel", "moe_sort: slice histograms"),
+                ("sort_kernel", "moe_sort"),
+                ("qmm_kernel<0,", "qswitch_gate_up_geglu"),
+                ("qmm_kernel<1,", "qswitch_down_combine: down"),
+                ("combine_kernel", "qswitch_down_combine: weighted sum over k"),
+                ("qmm_kernel<2,", "qlinear (2520 x 1152 -> 1152)")]
+
+
+def _per_dispatch(d, counters):
+    """{kernel name: {counter: [per-dispatch values]}} from a rocprofv3 counter csv
+    (the rows of one dispatch and counter are summed)."""
+    import csv
+    import glob
+    acc = {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] in counters:
+                key = (r["Kernel_Name"], r["Dispatch_Id"], r["Counter_Name"])
+                acc[key] = acc.get(key, 0.0) + float(r["Counter_Value"])
+    out = {}
+    for (k, _, c), v in acc.items():
+        out.setdefault(k, {}).setdefault(c, []).append(v)
+    return out
+
+
+def _kt_means(d):
+    import csv
+    import glob
+    f = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
+    return {r["Name"]: (float(r["AverageNs"]) / 1e3, int(r["Calls"])) for r in csv.DictReader(open(f[0]))} if f else {}
+
+
+def _counter_summary(d, tag, kf, kw):
+    """profiles/layer_kernels_<tag>_counters.md from DIR/<tag>_{kt,fetch,write,sq}."""
+    wl, args, title = PROFILE_RUNS[tag]
+    kt = _kt_means(os.path.join(d, f"{tag}_kt"))
+    fe = _per_dispatch(os.path.join(d, f"{tag}_fetch"), {"FETCH_SIZE"})
+    wr = _per_dispatch(os.path.join(d, f"{tag}_write"), {"WRITE_SIZE"})
+    sq = _per_dispatch(os.path.join(d, f"{tag}_sq"), set(SQ_COUNTERS))
+    mean = lambda m, k, c: float(np.mean(m[k][c])) if k in m and c in m[k] else float("nan")
+    cmd = "rocprofv3 {o} -d DIR/{t} -o p --output-format csv -- python3 bench.py " + args
+    lines = [f"# Per-kernel counters, {title}", "",
+             "Commands (from the repository root, TMPDIR=/tmp), one rocprofv3 run each:", "",
+             "    " + cmd.format(o="--kernel-trace --stats", t=f"{tag}_kt"),
+             "    " + cmd.format(o="--pmc FETCH_SIZE", t=f"{tag}_fetch"),
+             "    " + cmd.format(o="--pmc WRITE_SIZE", t=f"{tag}_write"),
+             "    " + cmd.format(o="--pmc " + " ".join(SQ_COUNTERS), t=f"{tag}_sq"),
+             "    rocprofv3 --pmc FETCH_SIZE -d DIR/copy_fetch -o p --output-format csv -- python3 bench.py --copy-probe",
+             "    rocprofv3 --pmc WRITE_SIZE -d DIR/copy_write -o p --output-format csv -- python3 bench.py --copy-probe",
+             "    python3 bench.py --summarize DIR", "",
+             f"HBM bytes: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) times {kf:.4f} and {kw:.4f}, what the same",
+             "counters read for a plain 256 MiB device copy.  Time: the kernel-trace mean of the same workload.",
+             "MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 1024 SIMDs), the rocprofv3 MfmaUtil",
+             "expression; bf16 TFLOP/s: SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 / time (the bias-term fp32 MFMAs",
+             "are not counted); VALU and MFMA: instructions issued per dispatch (wave instructions).", "",
+             "| kernel | role | dispatches | mean us | HBM read MB | HBM write MB | HBM GB/s | VALU instr | MFMA instr "
+             "| bf16 TFLOP/s | MFMA busy |",
+             "|---|---|---|---|---|---|---|---|---|---|---|"]
+    names = sorted(set(kt) | set(fe) | set(sq), key=lambda n: -kt.get(n, (0, 0))[0] * kt.get(n, (0, 0))[1])
+    for n in names:
+        role = next((r for pat, r in KERNEL_ROLES if pat in n), None)
+        if role is None:
+            continue
+        us, calls = kt.get(n, (float("nan"), 0))
+        rd = mean(fe, n, "FETCH_SIZE") * 1024 * kf
+        wb = mean(wr, n, "WRITE_SIZE") * 1024 * kw
+        gbs = (rd + wb) / (us * 1e-6) / 1e9
+        tf = mean(sq, n, "SQ_INSTS_VALU_MFMA_MOPS_BF16") * 512 / (us * 1e-6) / 1e12
+        busy = 100.0 * mean(sq, n, "SQ_VALU_MFMA_BUSY_CYCLES") / (mean(sq, n, "GRBM_GUI_ACTIVE") * SIMD_NUM)
+        short = n.replace("void ", "").replace("qmoe::", "").split("(")[0]
+        lines.append(f"| `{short}` | {role} | {calls} | {us:.2f} | {rd / 1e6:.2f} | {wb / 1e6:.2f} | {gbs:.0f} | "
+                     f"{mean(sq, n, 'SQ_INSTS_VALU'):.3g} | {mean(sq, n, 'SQ_INSTS_MFMA'):.3g} | {tf:.1f} | {busy:.1f}% |")
+    out = os.path.join(ROOT, "profiles", f"layer_kernels_{tag}_counters.md")
+    open(out, "w").write("\n".join(lines) + "\n")
+    return lines
+
+
 def summarize(d):
     import glob
     kt = "rocprofv3 --kernel-trace --stats -d DIR/{d} -o kt --output-format csv -- python3 bench.py {a}"
@@ -188,8 +294,8 @@ def summarize(d):
             out_name = "switch_kernels_" + ("prefill" if "prefill" in wl else "skew") + "_kernel_trace.md"
             open(os.path.join(ROOT, "profiles", out_name), "w").write("\n".join(tab) + "\n")
 
-    fetch, nf = _pmc_per_dispatch(os.path.join(d, "fetch"), "FETCH_SIZE", lambda n: "qmm_kernel<0" in n)
-    write, nw = _pmc_per_dispatch(os.path.join(d, "write"), "WRITE_SIZE", lambda n: "qmm_kernel<0" in n)
+    fetch, nf = _pmc_per_dispatch(os.path.join(d, "canvas_fetch"), "FETCH_SIZE", lambda n: "qmm_kernel<0" in n)
+    write, nw = _pmc_per_dispatch(os.path.join(d, "canvas_write"), "WRITE_SIZE", lambda n: "qmm_kernel<0" in n)
     # the copy: the dispatches of the largest kernel in the probe run
     cf, ncf = _pmc_per_dispatch(os.path.join(d, "copy_fetch"), "FETCH_SIZE", lambda n: "opy" in n)
     cw, ncw = _pmc_per_dispatch(os.path.join(d, "copy_write"), "WRITE_SIZE", lambda n: "opy" in n)
@@ -199,8 +305,8 @@ def summarize(d):
     cmd = ("rocprofv3 --pmc {c} -d DIR/{d} -o p --output-format csv -- python3 bench.py {a}")
     txt = ["# HBM traffic of qswitch_gate_up_geglu (qmm_kernel<0,...>), canvas workload",
            "# Commands (from the repository root, TMPDIR=/tmp), one counter per run:",
-           "#   " + cmd.format(c="FETCH_SIZE", d="fetch", a="--steps 20 --warmup 5 --no-cpu-baseline --no-ff-block --no-decode --no-other"),
-           "#   " + cmd.format(c="WRITE_SIZE", d="write", a="--steps 20 --warmup 5 --no-cpu-baseline --no-ff-block --no-decode --no-other"),
+           "#   " + cmd.format(c="FETCH_SIZE", d="canvas_fetch", a=PROFILE_RUNS["canvas"][1]),
+           "#   " + cmd.format(c="WRITE_SIZE", d="canvas_write", a=PROFILE_RUNS["canvas"][1]),
            "#   " + cmd.format(c="FETCH_SIZE", d="copy_fetch", a="--copy-probe"),
            "#   " + cmd.format(c="WRITE_SIZE", d="copy_write", a="--copy-probe"),
            "# FETCH_SIZE / WRITE_SIZE are KiB per dispatch; each is scaled by what the same",
@@ -213,6 +319,9 @@ def summarize(d):
            f"traffic_bytes_per_launch={traffic:.0f}"]
     open(TRAFFIC_FILE, "w").write("\n".join(txt) + "\n")
     print("\n".join(lines[-12:]))
+    for tag in PROFILE_RUNS:
+        if os.path.isdir(os.path.join(d, f"{tag}_sq")):
+            print("\n".join(_counter_summary(d, tag, kf, kw)[-10:]))
     print("\n".join(txt[-11:]))
 
 
@@ -227,29 +336,48 @@ def router_bytes(cfg):
     return cfg.E * (cfg.H // 2 + 4 * (cfg.H // 64)) + 2 * cfg.H + 2 * cfg.E
 
 
-def cpu_baseline(cfg, inp, seconds):
-    import oracle as O
-    threads = None
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads") or 0) for i in threadpool_info()) or None
-    except Exception:
-        pass
-    if threads is None:
-        threads = len(os.sched_getaffinity(0))
-    wt = inp.weights
+def _timed_runs(fn, seconds, max_runs=5):
     times = []
     t_start = time.perf_counter()
     while True:
         t0 = time.perf_counter()
-        O.moe_layer(inp.x, wt, cfg.k, cfg.I, cfg.eps, grouped=True)
+        fn()
         times.append(time.perf_counter() - t0)
-        if time.perf_counter() - t_start >= seconds or len(times) >= 5:
-            break
-    t = float(np.median(times))
+        if time.perf_counter() - t_start >= seconds or len(times) >= max_runs:
+            return float(np.median(times)), len(times)
+
+
+def cpu_baseline(cfg, inp, seconds, synth):
+    """The oracle as it stands, on this host's cores: the canvas layer with the
+    BLAS thread pool as it comes (the reported value) and with one thread, and
+    one run each of the dense qlinear (C1 geometry), the 4096-token prefill and
+    the skewed canvas, all full size (about 20-30 s of CPU work in all)."""
+    import oracle as O
+    from threadpoolctl import threadpool_info, threadpool_limits
+    threads = max((i.get("num_threads") or 0) for i in threadpool_info()) or len(os.sched_getaffinity(0))
+    wt = inp.weights
+    layer = lambda c, i: (lambda: O.moe_layer(i.x, i.weights, c.k, c.I, c.eps, grouped=True))
+    t, n = _timed_runs(layer(cfg, inp), seconds)
+    with threadpool_limits(1):
+        t1, n1 = _timed_runs(layer(cfg, inp), 0.0, 1)
+    others = {}
+    c1 = synth.make_qlinear_inputs(synth.QLINEAR_VISION)
+    tq, nq = _timed_runs(lambda: O.qlinear(c1.x, c1.W.w, c1.W.scales, c1.W.biases), 1.0)
+    others[synth.QLINEAR_VISION.name] = {"value": c1.cfg.M / tq, "unit": "rows/s", "seconds": tq, "runs": nq,
+                                         "what": "fp64 dequantize + matmul, full size"}
+    for oc in (synth.PREFILL, synth.SKEW):
+        w = wt if oc.zipf_tau is None else synth.MoEWeights(
+            wt.norm_scale, wt.router, wt.per_expert_scale, wt.gate_up, wt.down,
+            synth.zipf_logit_bias(oc.E, oc.zipf_tau, oc.zipf_perm_seed))
+        oi = synth.make_moe_inputs(oc, w)
+        to, no = _timed_runs(layer(oc, oi), 0.0, 1)
+        others[oc.name] = {"value": oc.T / to, "unit": "tokens/s", "seconds": to, "runs": no,
+                           "what": "full layer (route + grouped fp32 experts)"}
     return {"value": cfg.T / t, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"full {cfg.T}-token layer (route + grouped fp32 experts), {len(times)} run(s), "
-                      f"median {t:.2f} s; host has {os.cpu_count()} logical CPUs"}
+            "sample": f"full {cfg.T}-token layer (route + grouped fp32 experts), {n} run(s), "
+                      f"median {t:.2f} s, BLAS pool of {threads} threads; host has {os.cpu_count()} logical CPUs",
+            "single_thread": {"value": cfg.T / t1, "unit": "tokens/s", "cores": 1, "seconds": t1, "runs": n1},
+            "other_configs": others}
 
 
 LAYER_CALLS = ["moe_route", "moe_sort", "qswitch_gate_up_geglu", "qswitch_down_combine"]
@@ -291,6 +419,52 @@ def make_layer_step(q, torch, cfg, x):
     return step, buf
 
 
+class _no_gc:
+    """Python's cyclic garbage collector off inside a timed loop: a full
+    collection over the interpreter's (torch-sized) heap stalls the host for
+    milliseconds, long enough to drain the launch queue and idle the GPU."""
+
+    def __enter__(self):
+        import gc
+        gc.collect()
+        gc.freeze()
+        gc.disable()
+
+    def __exit__(self, *exc):
+        import gc
+        gc.enable()
+        gc.unfreeze()
+
+
+def time_layer_graph(torch, step, sets, K, warmup):
+    """The same K steps, each layer replayed from a HIP graph (one graph per
+    weight set, captured once): no host work between the kernels.  Returns
+    wall seconds."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for p in sets:
+            step(p)
+    torch.cuda.current_stream().wait_stream(side)
+    graphs = []
+    for p in sets:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(p)
+        graphs.append(g)
+    for i in range(warmup):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    with _no_gc():
+        t0 = time.perf_counter()
+        for i in range(K):
+            graphs[i % len(graphs)].replay()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    del graphs
+    return wall
+
+
 def time_layer(torch, step, sets, K, warmup, off):
     """Wall time of K steps (weight sets rotated, no events inside), then the
     per-call mean times (us) from a second pass of K steps with HIP events
@@ -304,11 +478,12 @@ def time_layer(torch, step, sets, K, warmup, off):
     for i in range(warmup):
         step(sets[i % len(sets)])
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        step(sets[i % len(sets)])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with _no_gc():
+        t0 = time.perf_counter()
+        for i in range(K):
+            step(sets[i % len(sets)])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(K)]
     torch.cuda.synchronize()
     for i in range(K):
@@ -575,6 +750,33 @@ def lm_head_timing(q, torch, synth, K, warmup, vocab=262144, rows=256, hidden=28
     return head
 
 
+def qlinear_c1_timing(q, torch, synth, K, warmup):
+    """The dense 4-bit linear at the vision tower's geometry on its own: x
+    [2520, 1152] bf16 against one 1152 -> 1152 weight, bf16 out, K launches
+    each bracketed by HIP events on the launch stream."""
+    cfg = synth.QLINEAR_VISION
+    dev = torch.device("cuda:0")
+    inp = synth.make_qlinear_inputs(cfg)
+    x = torch.from_numpy(inp.x).to(dev)
+    W = q.QuantWeight(*(torch.from_numpy(a).to(dev) for a in (inp.W.w, inp.W.scales, inp.W.biases))).tiled(0)
+    y = torch.empty((cfg.M, cfg.N), dtype=torch.bfloat16, device=dev)
+    for _ in range(warmup):
+        q.qlinear(x, W, y)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for a, b in ev:
+        a.record()
+        q.qlinear(x, W, y)
+        b.record()
+    torch.cuda.synchronize()
+    us = float(np.mean([a.elapsed_time(b) * 1e3 for a, b in ev]))
+    flops = 2.0 * cfg.M * cfg.N * cfg.K
+    hbm = cfg.M * cfg.K * 2 + cfg.N * (cfg.K // 2 + 4 * (cfg.K // 64)) + cfg.M * cfg.N * 2
+    return {"workload": cfg.name, "launches": K, "mean_launch_us": us, "tflops": flops / (us * 1e-6) / 1e12,
+            "mfma_frac": flops / (us * 1e-6) / (MFMA_BF16_PEAK_TFLOPS * 1e12),
+            "hbm_GBs": hbm / (us * 1e-6) / 1e9, "alg_bytes": hbm, "flops": flops}
+
+
 def vision_timing(q, torch, synth, passes=3, blocks=27, rows=2520, hidden=1152, mlp=4304):
     """Diagnostic: the vision tower's 4-bit linears at their geometry, 27
     blocks x (q, k, v, o: 1152 -> 1152; gate|up fused with GeGLU: 1152 ->
@@ -658,6 +860,7 @@ def main():
     A = T * k
     step, buf = make_layer_step(q, torch, cfg, x)
     wall, mean_us, touched = time_layer(torch, step, sets, args.steps, args.warmup, buf["off"])
+    wall_graph = time_layer_graph(torch, step, sets, args.steps, args.warmup)
     K = args.steps
 
     gu_b, dn_b = expert_bytes(cfg)
@@ -690,12 +893,19 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs_gu / HBM_PEAK_GBS,
                      "traffic": read_traffic(), "alg_bytes_per_launch": gate_up_alg,
                      "mean_launch_us": mean_us["qswitch_gate_up_geglu"]},
+        "layer_roofline": {"bound": "hbm", "achieved": layer_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                           "frac": layer_gbs / HBM_PEAK_GBS, "alg_bytes_per_step": layer_alg,
+                           "what": "the whole layer: algorithmic bytes per step / wall-clock step time"},
         "layer": {"alg_bytes": layer_alg, "achieved_GBs": layer_gbs, "hbm_frac": layer_gbs / HBM_PEAK_GBS,
                   "flops": flops, "mfma_frac": flops / (ms * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12),
                   "call_mean_us": mean_us,
                   "call_sum_us": float(sum(mean_us.values()))},
         "cpu_baseline": None,
+        "graph": {"tokens_per_s": T * K / wall_graph, "ms_per_step": wall_graph / K * 1e3,
+                  "what": "the same K steps, each layer replayed from a HIP graph (one per weight set)"},
     }
+    if cfg.name == synth.CANVAS.name:
+        out["qlinear_c1"] = qlinear_c1_timing(q, torch, synth, K, args.warmup)
     if cfg.name == synth.CANVAS.name and not args.no_decode:
         out["decode_unsorted"] = decode_timing(q, torch, synth, sets, K, args.warmup)
     if cfg.name == synth.CANVAS.name and not args.no_other:
@@ -710,7 +920,7 @@ def main():
                                           buf)
     if not args.no_cpu_baseline:
         inp = synth.MoEInputs(cfg, x_host, host_first)
-        out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_seconds, synth)
     print(json.dumps(out), flush=True)
 
 

@@ -349,6 +349,58 @@ def test_layer_all_tokens_against_grouped_oracle(cfg):
     assert err <= Y_TOL
 
 
+def test_sorted_layer_in_hip_graph():
+    """The sorted layer (route, sort, gate_up, down + combine) on the canvas
+    workload captured in a HIP graph, twice over with two token sets: every
+    replay, with eager work and synchronisations in between, gives the eager
+    result bit for bit (the calls enqueue only kernels)."""
+    import bit_quantized_moe_diffrouter_amd as q
+    cfg = synth.CANVAS
+    say(f"[graph] {cfg.name}")
+    inp = inputs(cfg)
+    p = params(cfg)
+    T, k, H, I, E = cfg.T, cfg.k, cfg.H, cfg.I, cfg.E
+    xs = [dev_tensor(inp.x), dev_tensor(synth.make_activations(T, H, 78))]
+    dev = "cuda"
+    ws_r = torch.empty(q.moe_route_workspace(T, H, E), dtype=torch.uint8, device=dev)
+    ws_d = torch.empty(q.qswitch_down_combine_workspace(T, k, H, 1), dtype=torch.uint8, device=dev)
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    wts = torch.empty((T, k), dtype=torch.float32, device=dev)
+    off = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    sa = torch.empty(T * k, dtype=torch.int32, device=dev)
+    mid = torch.empty(q.qswitch_mid_bytes(T, k, I, E), dtype=torch.uint8, device=dev)
+    ys = [torch.empty((T, H), dtype=torch.bfloat16, device=dev) for _ in xs]
+
+    def layers():
+        for x, y in zip(xs, ys):
+            q.moe_route(x, p.norm_scale, cfg.eps, p.router, p.per_expert_scale, k, None, indices=idx, weights=wts,
+                        workspace=ws_r)
+            q.moe_sort(idx, E, off, sa, workspace=None)
+            q.qswitch_gate_up_geglu(x, p.gate_up, I, k, off, sa, mid=mid)
+            q.qswitch_down_combine(mid, T, k, p.down, wts, off, sa, y=y, workspace=ws_d, deterministic=1)
+
+    layers()
+    torch.cuda.synchronize()
+    eager = [y.clone() for y in ys]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        layers()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        layers()
+    for rep in range(3):
+        for y in ys:
+            y.fill_(0)
+        q.moe_sort(idx, E)          # unrelated eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for y, e in zip(ys, eager):
+            assert torch.equal(y.view(torch.uint16), e.view(torch.uint16)), f"replay {rep} differs from eager"
+
+
 def test_layer_deterministic_bitwise():
     import bit_quantized_moe_diffrouter_amd as q
     cfg = synth.CANVAS

@@ -586,11 +586,12 @@ def ff_block_timing(q, torch, synth, ffc, h, sets, K, warmup, t, buf):
     for i in range(warmup):
         block(i)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        block(i)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with _no_gc():
+        t0 = time.perf_counter()
+        for i in range(K):
+            block(i)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(K)]
     for i in range(K):
         block(i, evs[i])
@@ -649,11 +650,12 @@ def decode_timing(q, torch, synth, sets, K, warmup, tokens=(1, 7)):
         for i in range(warmup):
             layer(i)
         torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(K):
-            layer(i)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
+        with _no_gc():
+            t0 = time.perf_counter()
+            for i in range(K):
+                layer(i)
+            torch.cuda.synchronize()
+            wall = time.perf_counter() - t0
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
         for i in range(K):
             layer(i, evs[i])
@@ -674,11 +676,12 @@ def decode_timing(q, torch, synth, sets, K, warmup, tokens=(1, 7)):
         graph.replay()
         torch.cuda.synchronize()
         reps = max(1, K // 48)
-        t0 = time.perf_counter()
-        for _ in range(reps):
-            graph.replay()
-        torch.cuda.synchronize()
-        us_graph = (time.perf_counter() - t0) / (reps * 48) * 1e6
+        with _no_gc():
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                graph.replay()
+            torch.cuda.synchronize()
+            us_graph = (time.perf_counter() - t0) / (reps * 48) * 1e6
         n_touch = float(np.mean(touched))
         alg = n_touch * (gu_b + dn_b) + router_bytes(cfg) + 2 * T * H * 2
         us = wall / K * 1e6

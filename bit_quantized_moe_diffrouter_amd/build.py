@@ -21,7 +21,7 @@ OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libqmoe.so")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["qswitch.hip", "qswitch_unsorted.hip", "route.hip", "sort.hip", "ffblock.hip", "embed_t.hip"]
+HIP_SOURCES = ["qswitch.hip", "qmm_ws.hip", "qswitch_unsorted.hip", "route.hip", "sort.hip", "ffblock.hip", "embed_t.hip"]
 HOST_SOURCES = ["abi.cpp"]
 
 # Packed-fp32 instructions are kept out of the device code.

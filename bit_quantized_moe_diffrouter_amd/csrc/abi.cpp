@@ -111,6 +111,9 @@ size_t unsorted_bytes(long long T, int k, int H, int I) {
   return (size_t)std::max(gu.partials, dn.partials) * sizeof(float);
 }
 
+// the weight-stationary kernel where the weight blocks meet many rows
+bool use_ws(int mode, long long rows, int experts) { return qmoe::ws_preferred(mode, rows, experts); }
+
 int status_ptr(int** out) {
   int* s = qmoe::device_status();
   if (s == nullptr) return fail(QMOE_ERR_HIP, "the device status word is not available");
@@ -255,6 +258,8 @@ int qswitch_gate_up_geglu(const uint16_t* x_expert, int32_t T, int32_t H, const 
   a.E = E;
   a.ktop = k;
   a.rows_total = T * k;
+  if (use_ws(qmoe::MODE_GATE_UP, a.rows_total, E))
+    return launched(qmoe::launch_ws<qmoe::MODE_GATE_UP>(a, ncu, stream), "qswitch_gate_up_geglu");
   return launched(qmoe::launch_gate_up_geglu(a, ncu, stream), "qswitch_gate_up_geglu");
 }
 
@@ -405,6 +410,8 @@ int qlinear_softcap(const uint16_t* x, int32_t M, const qmoe_qweight* W, float c
   a.ktop = 1;
   a.rows_total = M;
   a.cap = cap;
+  if (use_ws(qmoe::MODE_DENSE_SOFTCAP, M, 1))
+    return launched(qmoe::launch_ws<qmoe::MODE_DENSE_SOFTCAP>(a, ncu, stream), "qlinear_softcap");
   return launched(qmoe::launch_dense_softcap(a, ncu, stream), "qlinear_softcap");
 }
 

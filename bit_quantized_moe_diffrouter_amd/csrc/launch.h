@@ -49,6 +49,12 @@ hipError_t launch_tile_weight(const uint32_t* w, const uint16_t* s, const uint16
 constexpr int kActBlock = 2048;
 long long act_tiles_max(long long A, int E);
 
+// gate_up + GeGLU and down over sorted expert rows; the dense linear; the
+// dense linear with a fused gate|up weight and the GeGLU (the decoder's dense
+// MLP branch, first half); the dense linear as the tied LM head, its bf16
+// logits widened and softcapped to fp32
+enum : int { MODE_GATE_UP = 0, MODE_DOWN = 1, MODE_DENSE = 2, MODE_DENSE_GEGLU = 3, MODE_DENSE_SOFTCAP = 4 };
+
 struct SwitchArgs {
   const uint16_t* a;       // gate_up, dense: bf16 rows of length K; down: activation tiles
   const void* w;           // tiled weight [E, nblk, K/64] units of kTiledUnit bytes
@@ -85,6 +91,13 @@ hipError_t launch_dense_geglu(SwitchArgs a, int num_cu, hipStream_t stream);
 // cap * tanh(bf16(logit) / cap)
 hipError_t launch_dense_softcap(SwitchArgs a, int num_cu, hipStream_t stream);
 hipError_t launch_combine(const uint16_t* D, const float* w, int T, int k, int H, uint16_t* y, hipStream_t stream);
+// The weight-stationary kernel (many rows per weight block): whether it is
+// the faster one for `rows` rows (A = T*k for the switch modes) over
+// `experts` experts, and its launcher (same arguments and outputs as the
+// launchers above; the dequantized weight is rounded to bf16 once).
+bool ws_preferred(int mode, long long rows, int experts);
+template <int MODE>
+hipError_t launch_ws(SwitchArgs a, int num_cu, hipStream_t stream);
 
 // ---------------------------------------------------------------- unsorted small-batch switch linears
 enum : int { UNSORTED_GATE_UP = 0, UNSORTED_DOWN = 1 };

@@ -1,0 +1,374 @@
+// Weight-stationary 4-bit linears for gfx950, for weight blocks that meet
+// many rows: the gate_up switch linear + GeGLU at prefill-sized batches and
+// the tied LM head with its softcap.
+//
+// What is computed is the same as in qswitch.hip (diffusion-gemma model.ts
+// page, DiffExperts.forward for gate_up; logitsFromHidden for the head):
+// y = x . dequant(W)^T with W = scale * q + bias per 64-wide group.  Here the
+// dequantized weight is rounded to bf16 once, as a quantized matmul that
+// dequantizes into the activations' type does, and every product and sum is
+// done by the bf16 matrix cores with fp32 accumulation.
+//
+// Why a second kernel.  The chunked kernel streams each weight unit through
+// one wave, which unpacks it and applies the group's affine in fp32 for at
+// most 32 rows: at a few rows per expert that is the least work per weight
+// byte, but with hundreds of rows per block the unpacking and the per-group
+// epilogue are repeated for every 32-row chunk and the vector ALU, not the
+// matrix cores, sets the pace.  Here a workgroup owns a tile of BM rows x one
+// 128-row weight block over the whole contraction: per group its four waves
+// dequantize the block's 4608-byte unit once, each wave a quarter, into LDS
+// (bf16, already in matrix-core operand order), and every wave runs its
+// 16 * MT rows against all 128 columns from there.
+//
+// Pipeline per group g (one workgroup barrier each): dequantize group g + 1
+// (its codes were loaded kPD groups earlier) into the LDS buffer the previous
+// group's products have finished reading; the products of group g from the
+// other buffer; then the loads of group g + kPD into the register slot just
+// consumed.  Activations are loaded straight into operand registers: the
+// tiled weight's k order puts a lane's 16 k values of a group in 32
+// contiguous bytes of an activation row.
+#include <algorithm>
+#include <atomic>
+
+#include "common.h"
+#include "launch.h"
+
+namespace qmoe {
+
+namespace {
+
+constexpr int kWsWaves = 4;
+constexpr int kWsThreads = kWsWaves * 64;
+constexpr int kBBuf = 8 * 2 * 64 * 16;      // one group's dequantized operands: 16 KB
+constexpr int kWsLds = 2 * kBBuf;           // double buffer; the epilogue reuses it
+constexpr int kWsXcds = 8;
+constexpr int kWsMaxBuckets = 257;
+
+template <class F, int... I>
+__device__ __forceinline__ void ws_steps(F& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+
+__device__ __forceinline__ void ws_wave_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// One operand-ordered code word (code 2p at bits 4p, code 2p + 1 at bits
+// 16 + 4p) -> four dwords of bf16 pairs bf16(s q + b), codes (2p, 2p + 1) in
+// dword p.  The nibbles are spread to bytes with two masks and converted by
+// the byte-to-float conversions (v_cvt_f32_ubyte0..3).
+__device__ __forceinline__ u32x4_t dequant_word(uint32_t w, float s, float b) {
+  const uint32_t lo = w & 0x0F0F0F0Fu;         // bytes: codes 0, 4, 1, 5
+  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;  // bytes: codes 2, 6, 3, 7
+  auto f = [&](uint32_t v, int byte) __attribute__((always_inline)) {
+    return __builtin_fmaf(s, (float)((v >> (8 * byte)) & 0xFFu), b);
+  };
+  u32x4_t r;
+  r[0] = pack_bf16x2(f(lo, 0), f(lo, 2));
+  r[1] = pack_bf16x2(f(hi, 0), f(hi, 2));
+  r[2] = pack_bf16x2(f(lo, 1), f(lo, 3));
+  r[3] = pack_bf16x2(f(hi, 1), f(hi, 3));
+  return r;
+}
+
+}  // namespace
+
+template <int MODE, int MT, int kPD>
+__global__ __launch_bounds__(kWsThreads, 2) void qmm_ws_kernel(const SwitchArgs p) {
+  static_assert(MODE == MODE_GATE_UP || MODE == MODE_DENSE_SOFTCAP, "gate_up or the head");
+  constexpr bool kRows = MODE == MODE_DENSE_SOFTCAP;
+  constexpr int BM = 16 * MT * kWsWaves;  // rows of the workgroup's tile
+  static_assert(MT == 1 || MT == 2 || MT == 4, "1, 2 or 4 row tiles per wave (the epilogue stages at most 8 KB per wave)");
+  extern __shared__ __attribute__((aligned(16))) uint8_t ws_lds[];
+  __shared__ int s_lo[kWsMaxBuckets];
+  __shared__ int s_hi[kWsMaxBuckets];
+  __shared__ __attribute__((aligned(16))) int s_cpre[kWsMaxBuckets + 3];  // chunks before each expert
+  __shared__ int s_tpre[kWsMaxBuckets + 1];                              // activation tiles before each expert
+  __shared__ int s_scan[kWsWaves];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ln = lane & 15, lq = lane >> 4;
+  const int K = p.K, G = K / kGroup, A = p.rows_total, nblk = p.nblk;
+  const int grid = (int)gridDim.x, bid = (int)blockIdx.x;
+  // workgroup b runs on die b % 8: consecutive positions (the blocks of one
+  // row chunk, which read the same activations) share a die's L2
+  const int pos = (grid % kWsXcds == 0) ? (bid % kWsXcds) * (grid / kWsXcds) + bid / kWsXcds : bid;
+
+  // ---- this workgroup's item: (row chunk of BM rows, weight block)
+  int e = 0, r0 = 0, rows = 0, blk = 0, tau0 = 0;
+  if constexpr (kRows) {
+    const int nch = (A + BM - 1) / BM;
+    if (pos >= nch * nblk) return;
+    const int ch = pos / nblk;
+    blk = pos - ch * nblk;
+    r0 = ch * BM;
+    rows = min(BM, A - r0);
+  } else {
+    const int E = p.E;
+    for (int b = tid; b < E; b += kWsThreads) {
+      const int o0 = p.offsets[b], o1 = p.offsets[b + 1];
+      const int lo = min(max(o0, 0), A);
+      s_lo[b] = lo;
+      s_hi[b] = min(max(o1, lo), A);
+    }
+    __syncthreads();
+    auto scan = [&](int v) __attribute__((always_inline)) {  // exclusive prefix over experts (two per thread)
+      int all;
+      const int incl = block_inclusive_scan<kWsThreads>(v, s_scan, &all);
+      return incl - v;
+    };
+    int c0 = 0, c1 = 0, t0 = 0, t1 = 0;
+    const int b0 = 2 * tid, b1 = 2 * tid + 1;
+    if (b0 < E) {
+      const int n = s_hi[b0] - s_lo[b0];
+      c0 = (n + BM - 1) / BM;
+      t0 = (n + 15) / 16;
+    }
+    if (b1 < E) {
+      const int n = s_hi[b1] - s_lo[b1];
+      c1 = (n + BM - 1) / BM;
+      t1 = (n + 15) / 16;
+    }
+    const int cx = scan(c0 + c1);
+    const int tx = scan(t0 + t1);
+    if (b0 <= E) s_cpre[b0] = cx, s_tpre[b0] = tx;
+    if (b1 <= E) s_cpre[b1] = cx + c0, s_tpre[b1] = tx + t0;
+    if (tid == 0) s_cpre[E + 1] = s_cpre[E + 2] = 0x7fffffff;  // int4 reads past the end
+    __syncthreads();
+    const int nch = s_cpre[E];
+    if (pos >= nch * nblk) return;
+    const int ch = pos / nblk;
+    blk = pos - ch * nblk;
+    // the expert holding chunk ch: the number of experts whose first chunk is
+    // at most ch, less one, counted by the wave (lane l holds cpre[4l..4l+3])
+    {
+      const int4 c4 = ((const int4*)s_cpre)[lane];
+      const int eb = 4 * lane;
+      const int n = __popcll(__ballot(eb < E && c4.x <= ch)) + __popcll(__ballot(eb + 1 < E && c4.y <= ch)) +
+                    __popcll(__ballot(eb + 2 < E && c4.z <= ch)) + __popcll(__ballot(eb + 3 < E && c4.w <= ch));
+      e = __builtin_amdgcn_readfirstlane(n - 1);
+    }
+    r0 = s_lo[e] + (ch - s_cpre[e]) * BM;
+    rows = min(BM, s_hi[e] - r0);
+    tau0 = s_tpre[e] + (r0 - s_lo[e]) / 16;
+  }
+  e = __builtin_amdgcn_readfirstlane(e);
+  r0 = __builtin_amdgcn_readfirstlane(r0);
+  rows = __builtin_amdgcn_readfirstlane(rows);
+  blk = __builtin_amdgcn_readfirstlane(blk);
+  tau0 = __builtin_amdgcn_readfirstlane(tau0);
+
+  // ---- operand addresses
+  const uint8_t* const ubase = (const uint8_t*)p.w + ((size_t)e * nblk + blk) * (size_t)G * kTiledUnit;
+  const uint32_t c_off = (uint32_t)wave * 1024 + lane * 16;           // this wave's quarter of the codes
+  const uint32_t s_off = 4096 + ln * 16 + (uint32_t)(wave >> 1) * 256;  // (scale, bias) of its subtiles
+  const uint8_t* const abytes = (const uint8_t*)p.a;
+  uint32_t aoff[MT];
+  const int wrow = 16 * MT * wave;  // first tile row of this wave
+  const bool wave_rows = wrow < rows;
+#pragma unroll
+  for (int m = 0; m < MT; ++m) {
+    const int rl = min(wrow + 16 * m + ln, rows - 1);  // rows past the chunk read its last row
+    if constexpr (MODE == MODE_GATE_UP) {
+      const int a = p.assign[r0 + rl];
+      const int src = (a >= 0 && a < A) ? a / p.ktop : 0;
+      aoff[m] = (uint32_t)src * (uint32_t)(K * 2) + lq * 32;
+    } else {
+      aoff[m] = (uint32_t)(r0 + rl) * (uint32_t)(K * 2) + lq * 32;
+    }
+  }
+
+  // ---- the ring of register slots: codes + scales of the wave's quarter of a
+  // unit, and the activation operands of its row tiles
+  u32x4_t rc[kPD], rs[kPD];
+  u32x4_t ra[kPD][MT][2];
+  auto issue = [&](u32x4_t& c, u32x4_t& s, u32x4_t (&a)[MT][2], int g) __attribute__((always_inline)) {
+    const uint8_t* u = ubase + (size_t)g * kTiledUnit;
+    c = __builtin_nontemporal_load((const u32x4_t*)(u + c_off));
+    s = __builtin_nontemporal_load((const u32x4_t*)(u + s_off));
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const uint8_t* ab = abytes + aoff[m] + (uint32_t)g * 128;
+      a[m][0] = *(const u32x4_t*)ab;
+      a[m][1] = *(const u32x4_t*)(ab + 16);
+    }
+  };
+  // dequantize the wave's two subtiles (2 wave, 2 wave + 1) of a unit into LDS
+  // buffer `buf`: [subtile][half][lane] 16 bytes, the matrix cores' B order
+  auto dequant = [&](const u32x4_t& c, const u32x4_t& s, int buf) __attribute__((always_inline)) {
+    uint8_t* const dst = ws_lds + buf * kBBuf;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int j = 2 * wave + t;
+      const uint32_t sb = s[(2 * wave + t) & 3];
+      const float sc = __uint_as_float(sb << 16), bc = __uint_as_float(sb & 0xffff0000u);
+      const u32x4_t d0 = dequant_word(c[2 * t], sc, bc);
+      const u32x4_t d1 = dequant_word(c[2 * t + 1], sc, bc);
+      *(u32x4_t*)(dst + ((j * 2 + 0) * 64 + lane) * 16) = d0;
+      *(u32x4_t*)(dst + ((j * 2 + 1) * 64 + lane) * 16) = d1;
+    }
+  };
+
+  f32x4_t acc[MT][8];
+#pragma unroll
+  for (int m = 0; m < MT; ++m)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[m][j] = zero4();
+  auto products = [&](const u32x4_t (&a)[MT][2], int buf) __attribute__((always_inline)) {
+    const uint8_t* const src = ws_lds + buf * kBBuf;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const u32x4_t b0 = *(const u32x4_t*)(src + ((j * 2 + 0) * 64 + lane) * 16);
+      const u32x4_t b1 = *(const u32x4_t*)(src + ((j * 2 + 1) * 64 + lane) * 16);
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        acc[m][j] = mfma16x16x32(a[m][0], b0, acc[m][j]);
+        acc[m][j] = mfma16x16x32(a[m][1], b1, acc[m][j]);
+      }
+    }
+  };
+
+#pragma unroll
+  for (int d = 0; d < kPD; ++d) {
+    issue(rc[d], rs[d], ra[d], min(d, G - 1));
+    asm volatile("" ::: "memory");  // keeps the slots' loads in ring order
+  }
+  dequant(rc[0], rs[0], 0);
+  __syncthreads();
+
+  int g = 0;  // the group whose products are next
+  auto step = [&](auto d_tag) __attribute__((always_inline)) {
+    constexpr int d = decltype(d_tag)::value;
+    constexpr int dn = (d + 1) % kPD;
+    if (g >= G) return;  // uniform over the workgroup
+    if (g + 1 < G) dequant(rc[dn], rs[dn], (g + 1) & 1);
+    if (wave_rows) products(ra[d], g & 1);
+    issue(rc[d], rs[d], ra[d], min(g + kPD, G - 1));  // past the end: the last group again (never used)
+    asm volatile("" ::: "memory");
+    __syncthreads();
+    ++g;
+  };
+  do {
+    ws_steps(step, std::make_integer_sequence<int, kPD>{});
+  } while (g < G);
+  // the loads issued past the end complete before the staging below
+#pragma unroll
+  for (int d = 0; d < kPD; ++d) {
+    asm volatile("" ::"v"(rc[d]), "v"(rs[d]));
+#pragma unroll
+    for (int m = 0; m < MT; ++m) asm volatile("" ::"v"(ra[d][m][0]), "v"(ra[d][m][1]));
+  }
+  if (!wave_rows) return;  // no workgroup barrier follows
+
+  // ---- epilogue: acc[m][j][i] is row wrow + 16 m + 4 lq + i, column
+  // 16 j + ln of the block; staged per wave in its 8 KB of the LDS (the last
+  // group's operands are no longer read: every wave passed the barrier)
+  uint8_t* const wlds = ws_lds + (size_t)wave * (kWsLds / kWsWaves);
+  if constexpr (MODE == MODE_GATE_UP) {
+    // gate j and up j + 4 -> columns 16 j .. 16 j + 15 of block blk of the
+    // activation tiles: column 16 q + 8 h + i of tile row r sits at byte
+    // h * 1024 + (16 q + r) * 16 + 2 i of the tile's block
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          *(uint16_t*)(wlds + m * 2048 + (ln >> 3) * 1024 + (16 * j + 4 * lq + i) * 16 + (ln & 7) * 2) =
+              f32_to_bf16_bits(gelu_tanh(acc[m][j][i]) * acc[m][j + 4][i]);
+    ws_wave_fence();
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      if (wrow + 16 * m >= rows) continue;
+      const int tau = tau0 + MT * wave + m;
+      if (tau < 0 || tau >= p.max_tiles) continue;
+      uint8_t* const dst = (uint8_t*)p.out + ((size_t)tau * (p.Nout / 64) + blk) * kActBlock + lane * 16;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) *(u32x4_t*)(dst + h * 1024) = *(const u32x4_t*)(wlds + m * 2048 + h * 1024 + lane * 16);
+    }
+  } else {  // the head: logits rounded to bf16, widened, cap * tanh(z / cap)
+    float* const stg = (float*)wlds;
+    const int c = lane & 31;
+    const int col = blk * 128 + 4 * c;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      if (m > 0) ws_wave_fence();  // the previous tile's staging reads are done
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float z = bf16_bits_to_f32(f32_to_bf16_bits(acc[m][j][i]));
+          stg[(4 * lq + i) * 128 + 16 * j + ln] = p.cap * tanhf(z / p.cap);
+        }
+      ws_wave_fence();
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int r = 2 * q + (lane >> 5), lr = wrow + 16 * m + r;
+        if (lr < rows && col < p.Nout)
+          *(u32x4_t*)((float*)p.out + (size_t)(r0 + lr) * p.Nout + col) = *(const u32x4_t*)(stg + r * 128 + 4 * c);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ launchers
+namespace {
+
+constexpr int kWsMaxDevices = 64;
+
+template <int MODE, int MT, int PD>
+hipError_t launch_ws_cfg(const SwitchArgs& a, int grid, hipStream_t stream) {
+  static std::atomic<int> attr_done[kWsMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kWsMaxDevices) dev = 0;
+  if (!attr_done[dev].load(std::memory_order_acquire)) {
+    const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&qmm_ws_kernel<MODE, MT, PD>),
+                                                hipFuncAttributeMaxDynamicSharedMemorySize, kWsLds);
+    if (attr != hipSuccess) return attr;
+    attr_done[dev].store(1, std::memory_order_release);
+  }
+  hipLaunchKernelGGL((qmm_ws_kernel<MODE, MT, PD>), dim3((unsigned)grid), dim3(kWsThreads), kWsLds, stream, a);
+  return hipGetLastError();
+}
+
+long long round8(long long n) { return (n + kWsXcds - 1) / kWsXcds * kWsXcds; }
+
+}  // namespace
+
+// Where the weight-stationary kernel is the faster one (measured on the
+// prefill gate_up pass and the 256-row head; the down pass, the dense linear
+// and the dense GeGLU stayed on the chunked kernel, which was as fast or
+// faster there): gate_up from an average of 96 rows per expert, the head
+// from 128 rows.
+bool ws_preferred(int mode, long long rows, int experts) {
+  if (mode == MODE_GATE_UP) return experts <= 256 && rows >= 96LL * experts;
+  if (mode == MODE_DENSE_SOFTCAP) return rows >= 128;
+  return false;
+}
+
+template <int MODE>
+hipError_t launch_ws(SwitchArgs a, int num_cu, hipStream_t stream) {
+  a.ntiles = a.nblk;
+  const long long A = a.rows_total;
+  if (A <= 0) return hipSuccess;
+  if constexpr (MODE == MODE_GATE_UP) {
+    // every row in its bucket's chunks, at most one partial chunk per expert
+    const long long items = ((A + 127) / 128 + std::min<long long>(a.E, A)) * a.nblk;
+    if (items > (1LL << 30)) return hipErrorInvalidValue;
+    return launch_ws_cfg<MODE, 2, 3>(a, (int)round8(std::max<long long>(items, 1)), stream);
+  } else {
+    // 64 rows per wave where that still gives two workgroups per compute unit
+    const long long items4 = (A + 255) / 256 * a.nblk, items2 = (A + 127) / 128 * a.nblk;
+    if (items2 > (1LL << 30)) return hipErrorInvalidValue;
+    if (items4 >= 2LL * num_cu) return launch_ws_cfg<MODE, 4, 2>(a, (int)round8(items4), stream);
+    return launch_ws_cfg<MODE, 2, 3>(a, (int)round8(items2), stream);
+  }
+}
+
+template hipError_t launch_ws<MODE_GATE_UP>(SwitchArgs, int, hipStream_t);
+template hipError_t launch_ws<MODE_DENSE_SOFTCAP>(SwitchArgs, int, hipStream_t);
+
+}  // namespace qmoe

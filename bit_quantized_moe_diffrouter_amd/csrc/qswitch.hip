@@ -49,12 +49,6 @@
 
 namespace qmoe {
 
-// gate_up + GeGLU and down over sorted expert rows; the dense linear; the
-// dense linear with a fused gate|up weight and the GeGLU (the decoder's dense
-// MLP branch, first half); the dense linear as the tied LM head, its bf16
-// logits widened and softcapped to fp32
-enum : int { MODE_GATE_UP = 0, MODE_DOWN = 1, MODE_DENSE = 2, MODE_DENSE_GEGLU = 3, MODE_DENSE_SOFTCAP = 4 };
-
 namespace {
 
 constexpr int kWaves = 4;

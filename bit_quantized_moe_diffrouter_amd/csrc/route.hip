@@ -13,9 +13,8 @@
 // 1 / sqrt(mean(x^2) + eps).  A (token tile, k-range) grid fills the chip at
 // 256 tokens; the partial logits go to a workspace and kernel 2 sums them in
 // a fixed order, so the result is run-to-run reproducible.  Kernel 2 runs one
-// wave per token: each logit's rank is counted against the token's table of
-// ordering keys, the k best land in slots 0..k-1 in descending order, then the
-// softmax in fp32.
+// wave per token: a radix select finds the k-th largest ordering key, the k
+// best land in slots 0..k-1 in descending order, then the softmax in fp32.
 #include <math.h>
 
 #include "common.h"
@@ -214,10 +213,10 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 // One wave per token; NI = ceil(E / 64) logits per lane (expert lane + 64 i).
-// Top-k by rank: every lane counts, for each of its logits, how many of the
-// token's E keys beat it, reading the key table from LDS by broadcast; the
-// logits of rank < k land in slot rank, which is the descending order the
-// softmax and the outputs take.
+// Top-k by a radix select of the k-th largest key (ties to the lower
+// expert), then the k selected keys rank each other; the logit of rank r
+// lands in slot r, which is the descending order the softmax and the outputs
+// take.
 template <int NI>
 __global__ __launch_bounds__(256) void route_topk_kernel(const RouteArgs p) {
   __shared__ __align__(16) unsigned long long s_key[4][64 * NI];
@@ -282,28 +281,57 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const RouteArgs p) {
       v[i] = (s != s) ? -INFINITY : s;  // NaN never wins
       key[i] = select_key(v[i], e);
     }
-    s_key[wv][e] = key[i];
   }
-  wave_lds_sync();
 
-  int rank[NI];
+  // The k-th largest of the keys' high words (the logits in an order-keeping
+  // integer form) by a radix select, one bit per step from the top, each
+  // step counting with one ballot per key slot; then the keys above it and,
+  // among those equal to it, the lowest experts are the selected ones.
+  // Their order: each counts the selected 64-bit keys above its own.
+  uint32_t hk[NI];
 #pragma unroll
-  for (int i = 0; i < NI; ++i) rank[i] = 0;
-  const int E4 = (E + 3) & ~3;  // keys past E are 0 and beat nothing
-  const ulonglong2* tab = reinterpret_cast<const ulonglong2*>(s_key[wv]);
-  for (int c = 0; c < E4 / 2; c += 2) {
-    const ulonglong2 k01 = tab[c], k23 = tab[c + 1];
+  for (int i = 0; i < NI; ++i) hk[i] = (uint32_t)(key[i] >> 32);  // 0 past E: below every real key
+  auto count_ge = [&](uint32_t t) __attribute__((always_inline)) {
+    int n = 0;
 #pragma unroll
-    for (int i = 0; i < NI; ++i)
-      rank[i] += (int)(k01.x > key[i]) + (int)(k01.y > key[i]) + (int)(k23.x > key[i]) + (int)(k23.y > key[i]);
+    for (int i = 0; i < NI; ++i) n += __popcll(__ballot(hk[i] >= t));
+    return n;
+  };
+  uint32_t tau = 0;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t cand = tau | (1u << b);
+    if (count_ge(cand) >= p.k) tau = cand;
+  }
+  int n_gt = 0;
+#pragma unroll
+  for (int i = 0; i < NI; ++i) n_gt += __popcll(__ballot(hk[i] > tau));
+  const unsigned long long lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int eq_before = 0, sel_before = 0;  // equal keys / selected keys of lower experts (slots i' < i, then lanes)
+  bool sel[NI];
+  int slot[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const unsigned long long eqm = __ballot(hk[i] == tau && key[i] != 0);
+    const bool eq = hk[i] == tau && key[i] != 0;
+    sel[i] = key[i] != 0 && (hk[i] > tau || (eq && n_gt + eq_before + __popcll(eqm & lt) < p.k));
+    const unsigned long long sm = __ballot(sel[i]);
+    slot[i] = sel_before + __popcll(sm & lt);
+    eq_before += __popcll(eqm);
+    sel_before += __popcll(sm);
   }
 #pragma unroll
   for (int i = 0; i < NI; ++i)
-    if (key[i] != 0 && rank[i] < p.k) {
-      s_sv[wv][rank[i]] = v[i];
-      s_se[wv][rank[i]] = lane + 64 * i;
-      s_pes[wv][rank[i]] = pes_v[i];
-    }
+    if (sel[i]) s_key[wv][slot[i]] = key[i];  // the k selected keys, compacted
+  wave_lds_sync();
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    if (!sel[i]) continue;
+    int rank = 0;
+    for (int t = 0; t < p.k; ++t) rank += (int)(s_key[wv][t] > key[i]);
+    s_sv[wv][rank] = v[i];
+    s_se[wv][rank] = lane + 64 * i;
+    s_pes[wv][rank] = pes_v[i];
+  }
   wave_lds_sync();
 
   if (lane < p.k) {

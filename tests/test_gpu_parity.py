@@ -147,6 +147,37 @@ def test_route_ragged_and_degenerate(T, H, E, k):
         np.testing.assert_array_equal(idx_g[:, 0], np.argmax(lg_g, axis=1))
 
 
+@pytest.mark.parametrize("E,k,NI_case", [(40, 5, "one key per lane"), (128, 8, "two"), (256, 16, "four")])
+def test_route_ties_go_to_the_lower_expert(E, k, NI_case):
+    """Router rows repeated (expert e uses row e % 7), so every token's logits
+    come in groups of equal values, bitwise equal on the GPU too: the
+    selection must be the oracle's tie rule applied to the GPU's own logits
+    (descending, equal logits to the lower expert), exactly, with weights the
+    softmax of the selected logits times per_expert_scale."""
+    import bit_quantized_moe_diffrouter_amd as q
+    say(f"[route ties] E={E} k={k} ({NI_case})")
+    T, H = 37, 128
+    cfg = synth.MoEConfig("ties", T=T, H=H, E=E, k=k, I=64, seed_w=51, seed_x=52)
+    inp = synth.make_moe_inputs(cfg)
+    r = inp.weights.router
+    rep = np.arange(E) % 7
+    router = synth.QTensor(r.w[rep], r.scales[rep], r.biases[rep])
+    wt = synth.MoEWeights(inp.weights.norm_scale, router, inp.weights.per_expert_scale, inp.weights.gate_up,
+                          inp.weights.down)
+    p = dev_params(wt)
+    lo = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    idx, w = q.moe_route(dev_tensor(inp.x), p.norm_scale, cfg.eps, p.router, p.per_expert_scale, k, logits_out=lo)
+    torch.cuda.synchronize()
+    lg, idx_g, w_g = lo.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy()
+    for t in range(T):
+        assert len(set(lg[t].tolist())) <= 7
+    np.testing.assert_array_equal(idx_g, O.top_k(lg, k))
+    pes = O.bf16_to_f64(wt.per_expert_scale)
+    for t in range(T):
+        ref = O.precise_softmax(lg[t, idx_g[t]].astype(np.float64)) * pes[idx_g[t]]
+        np.testing.assert_allclose(w_g[t], ref, rtol=0, atol=1e-6)
+
+
 # ------------------------------------------------------------------------- sort
 def gpu_sort(idx, E, slices=True):
     import bit_quantized_moe_diffrouter_amd as q

@@ -113,11 +113,14 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(u32x4_t a, u32x4_t b, f32x4_t c)
 __device__ __forceinline__ f32x4_t zero4() { return f32x4_t{0.f, 0.f, 0.f, 0.f}; }
 
 // tanh-form GELU, written as z * sigmoid(2a), a = sqrt(2/pi) (z + 0.044715 z^3)
-// (0.5 (1 + tanh a) == 1 / (1 + exp(-2a))).
+// (0.5 (1 + tanh a) == 1 / (1 + exp(-2a))).  The reciprocal is the hardware's
+// (about 1 ulp): the product is rounded to bf16, 2^16 times coarser, and a
+// correctly rounded division costs six more instructions per element in the
+// epilogues.  exp(-2a) = inf gives 1 / inf = 0, the limit, for very negative z.
 __device__ __forceinline__ float gelu_tanh(float z) {
   const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
   const float a = k0 * (z + 0.044715f * z * z * z);
-  return z / (1.0f + __expf(-2.0f * a));
+  return z * __builtin_amdgcn_rcpf(1.0f + __expf(-2.0f * a));
 }
 
 __device__ __forceinline__ int wave_lane() { return threadIdx.x & 63; }

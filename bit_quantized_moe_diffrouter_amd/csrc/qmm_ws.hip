@@ -191,7 +191,7 @@ __global__ __launch_bounds__(kWsThreads, 2) void qmm_ws_kernel(const SwitchArgs 
     s = __builtin_nontemporal_load((const u32x4_t*)(u + s_off));
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-      const uint8_t* ab = abytes + aoff[m] + (uint32_t)g * 128;
+      const uint8_t* ab = abytes + (aoff[m] + (uint32_t)g * 128u);  // one 32-bit offset
       a[m][0] = *(const u32x4_t*)ab;
       a[m][1] = *(const u32x4_t*)(ab + 16);
     }

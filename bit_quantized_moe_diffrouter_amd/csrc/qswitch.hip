@@ -356,12 +356,12 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
       if constexpr (MODE == MODE_DOWN) {  // one coalesced kilobyte per operand register
-        const uint8_t* ab = abytes + l_aoff[m][0] + (uint32_t)lg * kActBlock;
+        const uint8_t* ab = abytes + (l_aoff[m][0] + (uint32_t)lg * kActBlock);  // one 32-bit offset
         sl.a[m][0] = *(const u32x4_t*)(ab);
         sl.a[m][1] = *(const u32x4_t*)(ab + kActBlock / 2);
       } else {  // 8 rows x 128 bytes per load; compute puts them in operand order
 #pragma unroll
-        for (int h = 0; h < 2; ++h) sl.a[m][h] = *(const u32x4_t*)(abytes + l_aoff[m][h] + (uint32_t)lg * 128);
+        for (int h = 0; h < 2; ++h) sl.a[m][h] = *(const u32x4_t*)(abytes + (l_aoff[m][h] + (uint32_t)lg * 128u));
       }
     }
   };

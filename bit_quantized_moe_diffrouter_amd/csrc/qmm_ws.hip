@@ -217,17 +217,27 @@ __global__ __launch_bounds__(kWsThreads, 2) void qmm_ws_kernel(const SwitchArgs 
   for (int m = 0; m < MT; ++m)
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[m][j] = zero4();
+  // The B operands of subtile j + 2 are read while subtile j's products run:
+  // a read waited on right before its products leaves the LDS latency exposed
+  // eight times per group.  The two halves of a subtile go to different
+  // accumulators first (m, then k), so no product waits on the one before.
   auto products = [&](const u32x4_t (&a)[MT][2], int buf) __attribute__((always_inline)) {
     const uint8_t* const src = ws_lds + buf * kBBuf;
+    auto rd = [&](int j, int h) __attribute__((always_inline)) {
+      return *(const u32x4_t*)(src + ((j * 2 + h) * 64 + lane) * 16);
+    };
+    u32x4_t b[3][2];
+    b[0][0] = rd(0, 0), b[0][1] = rd(0, 1);
+    b[1][0] = rd(1, 0), b[1][1] = rd(1, 1);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const u32x4_t b0 = *(const u32x4_t*)(src + ((j * 2 + 0) * 64 + lane) * 16);
-      const u32x4_t b1 = *(const u32x4_t*)(src + ((j * 2 + 1) * 64 + lane) * 16);
+      if (j + 2 < 8) b[(j + 2) % 3][0] = rd(j + 2, 0), b[(j + 2) % 3][1] = rd(j + 2, 1);
+      __builtin_amdgcn_sched_barrier(0);  // the scheduler would sink the reads to their first use
+      const u32x4_t b0 = b[j % 3][0], b1 = b[j % 3][1];
 #pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        acc[m][j] = mfma16x16x32(a[m][0], b0, acc[m][j]);
-        acc[m][j] = mfma16x16x32(a[m][1], b1, acc[m][j]);
-      }
+      for (int m = 0; m < MT; ++m) acc[m][j] = mfma16x16x32(a[m][0], b0, acc[m][j]);
+#pragma unroll
+      for (int m = 0; m < MT; ++m) acc[m][j] = mfma16x16x32(a[m][1], b1, acc[m][j]);
     }
   };
 
@@ -358,7 +368,7 @@ hipError_t launch_ws(SwitchArgs a, int num_cu, hipStream_t stream) {
     // every row in its bucket's chunks, at most one partial chunk per expert
     const long long items = ((A + 127) / 128 + std::min<long long>(a.E, A)) * a.nblk;
     if (items > (1LL << 30)) return hipErrorInvalidValue;
-    return launch_ws_cfg<MODE, 2, 3>(a, (int)round8(std::max<long long>(items, 1)), stream);
+    return launch_ws_cfg<MODE, 2, 2>(a, (int)round8(std::max<long long>(items, 1)), stream);
   } else {
     // 64 rows per wave where that still gives two workgroups per compute unit
     const long long items4 = (A + 255) / 256 * a.nblk, items2 = (A + 127) / 128 * a.nblk;

@@ -103,14 +103,16 @@ def test_head_with_huge_cap_is_the_bf16_qlinear():
     assert np.allclose(a, b, rtol=1e-6, atol=0)
 
 
-@pytest.mark.parametrize("M,K", [(100, 128), (17, 192), (64, 64), (129, 128), (300, 192), (520, 64)])
+@pytest.mark.parametrize("M,K", [(100, 128), (17, 192), (64, 64), (129, 128), (300, 192), (520, 64), (256, 576),
+                                 (300, 704)])
 def test_head_wide_ragged_rows_sampled(M, K):
     """A wide head (131,072 rows of weights, enough items to fill the chip
     without splitting the contraction) at ragged row counts: 100 (three full
     32-row chunks and one of 4 rows), 17 (a second tile holding one row), 64;
     from 128 rows the weight-stationary kernel: 129 (a 128-row tile and one
-    row), 300 (a 256-row tile and a ragged one), 520; sampled columns, every
-    row."""
+    row), 300 (a 256-row tile and a ragged one), 520; and at 9 and 11 groups
+    (longer than its ring of codes, which every group passes through in
+    turn); sampled columns, every row."""
     import bit_quantized_moe_diffrouter_amd as q
     N = 131072
     say(f"[head] wide M={M} K={K} N={N}")

@@ -17,7 +17,9 @@ on the ragged layer shapes of the GPU tests, that:
     stored);
   * every weight, activation, mid and output access lies inside its buffer;
   * the weight-stationary kernel covers every (row chunk, block) of every
-    expert exactly once, inside the buffers.
+    expert exactly once, inside the buffers, and its per-group pipeline
+    (register ring of codes and activations, two LDS buffers, one barrier
+    per group) feeds every group's products with that group's operands.
 No GPU is used."""
 import numpy as np
 import pytest
@@ -241,6 +243,69 @@ def emulate_ws(A, E, nblk, G, offsets, assign, T, ktop, Nout, K, MT=2):
                         assert (tau * (Nout // 64) + blk + 1) * ACT_BLOCK <= max_tiles * (Nout // 64) * ACT_BLOCK
     expect = {(e, int(lo[e] + c * BM), blk) for e in range(E) for c in range(-(-int(n[e]) // BM)) for blk in range(nblk)}
     assert seen == expect
+
+
+def emulate_ws_pipeline(G, PD, refill=None, ahead=None, prod_buf=None):
+    """The weight-stationary kernel's per-group pipeline, step by step.  A
+    ring slot holds one group's codes and scales and its activation operands;
+    the prologue loads groups 0 .. PD-1 into slots 0 .. PD-1, dequantizes
+    group 0 from slot 0 into LDS buffer 0, and reaches the barrier.  Step g
+    (its slot d = g mod PD; the loop runs blocks of PD steps) dequantizes
+    group g + 1 from slot (d + 1) mod PD into buffer (g + 1) mod 2, runs the
+    products of group g from buffer g mod 2 with slot d's activations,
+    refills slot d with group min(g + PD, G - 1), and reaches the barrier.
+    Checks that every group's products read that group's dequantized
+    weights and activations, once, in order, and that a step never writes
+    the buffer its own products read (the other one was last read before
+    the previous barrier).  refill, ahead and prod_buf override the slot the
+    step refills, how far ahead it loads and the buffer the products read
+    (for the planted-mistake tests)."""
+    refill = refill or (lambda d, dn: d)
+    ahead = PD if ahead is None else ahead
+    prod_buf = prod_buf or (lambda g: g % 2)
+    slots = [(min(d, G - 1), min(d, G - 1)) for d in range(PD)]  # (codes group, activations group)
+    buf = [None, None]
+    buf[0] = slots[0][0]
+    done = []
+    g = 0
+    while g < G:
+        for d in range(PD):
+            if g >= G:
+                break
+            dn = (d + 1) % PD
+            wrote = None
+            if g + 1 < G:
+                assert slots[dn][0] == g + 1, f"group {g + 1} dequantized from a slot holding {slots[dn][0]}"
+                wrote = (g + 1) % 2
+                buf[wrote] = g + 1
+            b = prod_buf(g)
+            assert wrote is None or wrote != b, "a step overwrites the buffer its products read"
+            assert buf[b] == g, f"group {g}'s products read the weights of group {buf[b]}"
+            assert slots[d][1] == g, f"group {g}'s products read the activations of group {slots[d][1]}"
+            done.append(g)
+            r = refill(d, dn)
+            slots[r] = (min(g + ahead, G - 1), min(g + ahead, G - 1))
+            g += 1
+    assert done == list(range(G))
+
+
+@pytest.mark.parametrize("PD", [2, 3])
+def test_ws_pipeline(PD):
+    for G in range(1, 50):
+        emulate_ws_pipeline(G, PD)
+
+
+def test_ws_pipeline_catches_planted_mistakes():
+    """Refilling the slot just dequantized (group g + 1's) instead of group
+    g's, loading one group less far ahead, and reading the products from the
+    buffer being written all fail from 4 groups on."""
+    for PD in (2, 3):
+        with pytest.raises(AssertionError, match="slot holding|activations"):
+            emulate_ws_pipeline(8, PD, refill=lambda d, dn: dn)
+        with pytest.raises(AssertionError, match="slot holding|activations"):
+            emulate_ws_pipeline(8, PD, ahead=PD - 1)
+        with pytest.raises(AssertionError, match="overwrites|weights of"):
+            emulate_ws_pipeline(8, PD, prod_buf=lambda g: (g + 1) % 2)
 
 
 # ------------------------------------------------------------------ cases

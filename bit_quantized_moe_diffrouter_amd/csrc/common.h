@@ -48,31 +48,35 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float v) {
 struct OffsetCodeConsts {
   uint32_t mask;  // 0x000F000F, uniform (SGPR)
   uint32_t expo;  // 0x43004300, in a VGPR
+  int zero;       // 0, uniform, opaque to the compiler (below)
 };
+// All of this is plain C: a vector instruction written as inline asm is
+// invisible to the compiler's hazard checks, and it once reused the unread
+// upper half of an in-flight MFMA result as the asm's output register (the
+// MFMA then overwrote the unpacked codes).  The exponent pattern comes from
+// an add to v_mbcnt_lo(0, 0) (zero, but not known to be uniform), so it lives
+// in a VGPR; the shift amounts are 4p plus a uniform zero the compiler cannot
+// fold, so each stays one 64-bit shift instead of an alignbit and a shift.
 __device__ __forceinline__ OffsetCodeConsts offset_code_consts() {
   OffsetCodeConsts k;
   k.mask = __builtin_amdgcn_readfirstlane(0x000F000Fu);
-  uint32_t e = 0x43004300u;
-  asm volatile("v_mov_b32 %0, %1" : "=v"(e) : "i"(0x43004300u));
-  k.expo = e;
+  const uint32_t lane_zero = __builtin_amdgcn_mbcnt_lo(0u, 0u);
+  k.expo = 0x43004300u + lane_zero;
+  k.zero = __builtin_amdgcn_readfirstlane((int)lane_zero);
   return k;
 }
-// (a & smask) | vor: selected as one v_and_or_b32.  Written in C, not as
-// inline asm, so that the compiler sees the VGPR it writes: an MFMA that reads
-// a VALU result needs two wait states, which the compiler inserts only for
-// instructions it knows about.
+// (a & smask) | vor: selected as one v_and_or_b32.
 __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t smask, uint32_t vor) { return (a & smask) | vor; }
 __device__ __forceinline__ void unpack_offset_code_pair(uint32_t w0, uint32_t w1, const OffsetCodeConsts& k,
                                                         u32x4_t& b0, u32x4_t& b1) {
-  const u32x2_t pr = {w0, w1};
+  const uint64_t pr = ((uint64_t)w1 << 32) | w0;
   b0[0] = and_or(w0, k.mask, k.expo);
   b1[0] = and_or(w1, k.mask, k.expo);
 #pragma unroll
   for (int p = 1; p < 4; ++p) {
-    u32x2_t sh;
-    asm("v_lshrrev_b64 %0, %1, %2" : "=v"(sh) : "i"(4 * p), "v"(pr));
-    b0[p] = and_or(sh.x, k.mask, k.expo);
-    b1[p] = and_or(sh.y, k.mask, k.expo);
+    const uint64_t sh = pr >> (k.zero + 4 * p);
+    b0[p] = and_or((uint32_t)sh, k.mask, k.expo);
+    b1[p] = and_or((uint32_t)(sh >> 32), k.mask, k.expo);
   }
 }
 

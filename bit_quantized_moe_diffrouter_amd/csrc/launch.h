@@ -66,12 +66,21 @@ struct SwitchArgs {
   int Nout;        // output columns
   int E;           // experts (1 for dense)
   int ktop;        // assignments per token
+  uint32_t ktop_inv;  // floor(2^32 / ktop) + 1, or 0 when ktop is 1 (set by the launcher; see token_of)
   int rows_total;  // dense: M; switch: A = T*k
   int ntiles;      // column tiles per row chunk (set by the launcher)
   int max_tiles;   // switch: activation tiles the input and output buffers hold
   float cap;       // softcap of the LM-head mode
   int* status;     // device status word (set by the launcher)
 };
+// The token of assignment a (a / k, with 0 <= a < 2^24 and 1 <= k <= 16) as
+// one multiply-high: a * (floor(2^32 / k) + 1) / 2^32 exceeds a / k by less
+// than 2^24 / 2^32 = 2^-8, and the fraction of a / k is 0 or at least 1/16,
+// so the floor is exact.  inv = 0 stands for k = 1.
+inline uint32_t ktop_inverse(int k) { return k > 1 ? (uint32_t)((1ull << 32) / (unsigned)k + 1) : 0u; }
+__device__ __forceinline__ int token_of(int a, uint32_t inv) {
+  return inv ? (int)(((uint64_t)(uint32_t)a * inv) >> 32) : a;  // v_mul_hi_u32
+}
 // Device status word: bits a kernel raises when a bounded wait inside a
 // workgroup gave up (its outputs are then wrong).
 constexpr int kStatusSpin = 1;

@@ -174,7 +174,7 @@ __global__ __launch_bounds__(kWsThreads, 2) void qmm_ws_kernel(const SwitchArgs 
     const int rl = min(wrow + 16 * m + ln, rows - 1);  // rows past the chunk read its last row
     if constexpr (MODE == MODE_GATE_UP) {
       const int a = p.assign[r0 + rl];
-      const int src = (a >= 0 && a < A) ? a / p.ktop : 0;
+      const int src = (a >= 0 && a < A) ? token_of(a, p.ktop_inv) : 0;
       aoff[m] = (uint32_t)src * (uint32_t)(K * 2) + lq * 32;
     } else {
       aoff[m] = (uint32_t)(r0 + rl) * (uint32_t)(K * 2) + lq * 32;
@@ -362,6 +362,7 @@ bool ws_preferred(int mode, long long rows, int experts) {
 template <int MODE>
 hipError_t launch_ws(SwitchArgs a, int num_cu, hipStream_t stream) {
   a.ntiles = a.nblk;
+  a.ktop_inv = ktop_inverse(a.ktop);
   const long long A = a.rows_total;
   if (A <= 0) return hipSuccess;
   if constexpr (MODE == MODE_GATE_UP) {

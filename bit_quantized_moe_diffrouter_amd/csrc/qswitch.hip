@@ -322,7 +322,7 @@ __global__ __launch_bounds__(kThreads, 2) void qmm_kernel(const SwitchArgs p) {
           int src;
           if constexpr (MODE == MODE_GATE_UP) {
             const int a = ids_cur[m][h];
-            src = (a >= 0 && a < A) ? a / p.ktop : 0;
+            src = (a >= 0 && a < A) ? token_of(a, p.ktop_inv) : 0;
           } else {
             src = it.r0 + row_of(it, m, h);
           }
@@ -864,6 +864,7 @@ constexpr size_t lds_bytes() {
 template <int MODE, int KS, int D>
 hipError_t launch_cfg(SwitchArgs a, int extra_buckets, int num_cu, hipStream_t stream) {
   a.ntiles = a.nblk;
+  a.ktop_inv = ktop_inverse(a.ktop);
   a.status = device_status();
   if (a.status == nullptr) return hipErrorInvalidSymbol;
   constexpr size_t lds = lds_bytes<MODE, KS>();

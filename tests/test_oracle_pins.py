@@ -522,3 +522,15 @@ def test_synth_independent_biases():
     b = synth.bf16_bits_as_f32(wt.gate_up.biases).astype(np.float64)
     ratio = b[s > 0] / s[s > 0]
     assert np.std(ratio) > 1.0 and np.mean(b == -8 * s) < 0.05
+
+
+def test_token_of_multiply_high_is_exact():
+    """The switch kernels find the token of assignment a (a // k) as the high
+    32 bits of a * (floor(2^32 / k) + 1), for every a below 2^24 (the
+    library's limit on T * k) and every k from 2 to 16 (k = 1 is passed
+    through).  Checked here on all of them."""
+    import numpy as np
+    a = np.arange(1 << 24, dtype=np.uint64)
+    for k in range(2, 17):
+        inv = np.uint64((1 << 32) // k + 1)
+        assert np.array_equal((a * inv) >> np.uint64(32), a // np.uint64(k)), k

@@ -21,13 +21,16 @@ OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libqmoe.so")
 ARCH = "gfx950"
 
-HIP_SOURCES = ["qswitch.hip", "qmm_ws.hip", "qswitch_unsorted.hip", "route.hip", "sort.hip", "ffblock.hip", "embed_t.hip"]
+HIP_SOURCES = ["qswitch.hip", "qmm_ws.hip", "qmm_tall.hip", "qswitch_unsorted.hip", "route.hip", "sort.hip", "ffblock.hip", "embed_t.hip"]
 HOST_SOURCES = ["abi.cpp"]
 
 # Packed-fp32 instructions are kept out of the device code.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-                # matrix-core results in VGPRs (no accumulation-register round trips)
-                "-mllvm", "-amdgpu-mfma-vgpr-form"]
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Matrix-core results in VGPRs (no accumulation-register round trips), except
+# in the tall-tile kernel, whose one wave per SIMD keeps its sums in the
+# accumulation registers.
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+AGPR_SOURCES = {"qmm_tall.hip"}
 COMMON_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-variable",
                 "-I", os.path.join(ROOT, "include")]
 
@@ -84,7 +87,8 @@ def build(verbose: bool = False) -> str:
     jobs = []
     for src in HIP_SOURCES:
         obj = os.path.join(OBJ, src.replace(".hip", ".o"))
-        jobs.append([hipcc, f"--offload-arch={ARCH}", *COMMON_FLAGS, *DEVICE_FLAGS, *RESOURCE_FLAGS, "-c",
+        form = [] if src in AGPR_SOURCES else VGPR_FORM
+        jobs.append([hipcc, f"--offload-arch={ARCH}", *COMMON_FLAGS, *DEVICE_FLAGS, *form, *RESOURCE_FLAGS, "-c",
                      os.path.join(CSRC, src), "-o", obj])
     for src in HOST_SOURCES:
         obj = os.path.join(OBJ, src.replace(".cpp", ".o"))

@@ -382,6 +382,8 @@ int qlinear(const uint16_t* x, int32_t M, const qmoe_qweight* W, uint16_t* y, hi
   a.E = 1;
   a.ktop = 1;
   a.rows_total = M;
+  if (qmoe::tall_preferred(qmoe::MODE_DENSE, M, 1))
+    return launched(qmoe::launch_tall<qmoe::MODE_DENSE>(a, ncu, stream), "qlinear");
   return launched(qmoe::launch_dense(a, ncu, stream), "qlinear");
 }
 

@@ -106,6 +106,42 @@ __device__ __forceinline__ u32x4_t permute_pairs(u32x4_t v) {
   return o;
 }
 
+// Two operand-ordered code words (code 2p at bits 4p, code 2p + 1 at bits
+// 16 + 4p) -> eight dwords of bf16 pairs bf16(s q + b), codes (2p, 2p + 1)
+// of word i in dword p of d_i.  The nibbles are spread to bytes with one mask
+// (low nibbles: codes 0, 4, 1, 5; after one 64-bit shift of both words by 4,
+// high nibbles: codes 2, 6, 3, 7) and each byte goes through one
+// byte-to-float conversion (v_cvt_f32_ubyte0..3), one FMA, and half a pack:
+// 47 instructions per 16 codes.  The mask and the shift amount come in as
+// values the compiler cannot fold (DequantConsts): with a known mask it
+// re-derives each code as a 4-bit field extract of the word and converts
+// from byte 0, one more instruction per code.
+struct DequantConsts {
+  uint32_t mask;  // 0x0F0F0F0F, uniform
+  int four;       // 4, uniform
+};
+__device__ __forceinline__ DequantConsts dequant_consts() {
+  const int zero = __builtin_amdgcn_readfirstlane((int)__builtin_amdgcn_mbcnt_lo(0u, 0u));
+  return DequantConsts{0x0F0F0F0Fu + (uint32_t)zero, 4 + zero};
+}
+__device__ __forceinline__ void dequant_pair_bf16(uint32_t w0, uint32_t w1, float s, float b, const DequantConsts& k,
+                                                  u32x4_t& d0, u32x4_t& d1) {
+  const uint64_t sh = (((uint64_t)w1 << 32) | w0) >> k.four;
+  const uint32_t lo0 = w0 & k.mask, lo1 = w1 & k.mask;
+  const uint32_t hi0 = (uint32_t)sh & k.mask, hi1 = (uint32_t)(sh >> 32) & k.mask;
+  auto f = [&](uint32_t v, int byte) __attribute__((always_inline)) {
+    return __builtin_fmaf(s, (float)((v >> (8 * byte)) & 0xFFu), b);
+  };
+  d0[0] = pack_bf16x2(f(lo0, 0), f(lo0, 2));
+  d0[1] = pack_bf16x2(f(hi0, 0), f(hi0, 2));
+  d0[2] = pack_bf16x2(f(lo0, 1), f(lo0, 3));
+  d0[3] = pack_bf16x2(f(hi0, 1), f(hi0, 3));
+  d1[0] = pack_bf16x2(f(lo1, 0), f(lo1, 2));
+  d1[1] = pack_bf16x2(f(hi1, 0), f(hi1, 2));
+  d1[2] = pack_bf16x2(f(lo1, 1), f(lo1, 3));
+  d1[3] = pack_bf16x2(f(hi1, 1), f(hi1, 3));
+}
+
 // D = A(16x32 bf16) * B(32x16 bf16) + C, fp32 accumulate.  Lane l holds row
 // (l%16) of A and column (l%16) of B over the k-slice of lane group l/16; the
 // result holds column l%16, rows 4*(l/16)+0..3.

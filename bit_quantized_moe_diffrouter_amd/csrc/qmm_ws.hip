@@ -55,24 +55,6 @@ __device__ __forceinline__ void ws_wave_fence() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// One operand-ordered code word (code 2p at bits 4p, code 2p + 1 at bits
-// 16 + 4p) -> four dwords of bf16 pairs bf16(s q + b), codes (2p, 2p + 1) in
-// dword p.  The nibbles are spread to bytes with two masks and converted by
-// the byte-to-float conversions (v_cvt_f32_ubyte0..3).
-__device__ __forceinline__ u32x4_t dequant_word(uint32_t w, float s, float b) {
-  const uint32_t lo = w & 0x0F0F0F0Fu;         // bytes: codes 0, 4, 1, 5
-  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;  // bytes: codes 2, 6, 3, 7
-  auto f = [&](uint32_t v, int byte) __attribute__((always_inline)) {
-    return __builtin_fmaf(s, (float)((v >> (8 * byte)) & 0xFFu), b);
-  };
-  u32x4_t r;
-  r[0] = pack_bf16x2(f(lo, 0), f(lo, 2));
-  r[1] = pack_bf16x2(f(hi, 0), f(hi, 2));
-  r[2] = pack_bf16x2(f(lo, 1), f(lo, 3));
-  r[3] = pack_bf16x2(f(hi, 1), f(hi, 3));
-  return r;
-}
-
 }  // namespace
 
 template <int MODE, int MT, int kPD>
@@ -198,6 +180,7 @@ __global__ __launch_bounds__(kWsThreads, 2) void qmm_ws_kernel(const SwitchArgs 
   };
   // dequantize the wave's two subtiles (2 wave, 2 wave + 1) of a unit into LDS
   // buffer `buf`: [subtile][half][lane] 16 bytes, the matrix cores' B order
+  const DequantConsts dk = dequant_consts();
   auto dequant = [&](const u32x4_t& c, const u32x4_t& s, int buf) __attribute__((always_inline)) {
     uint8_t* const dst = ws_lds + buf * kBBuf;
 #pragma unroll
@@ -205,8 +188,8 @@ __global__ __launch_bounds__(kWsThreads, 2) void qmm_ws_kernel(const SwitchArgs 
       const int j = 2 * wave + t;
       const uint32_t sb = s[(2 * wave + t) & 3];
       const float sc = __uint_as_float(sb << 16), bc = __uint_as_float(sb & 0xffff0000u);
-      const u32x4_t d0 = dequant_word(c[2 * t], sc, bc);
-      const u32x4_t d1 = dequant_word(c[2 * t + 1], sc, bc);
+      u32x4_t d0, d1;
+      dequant_pair_bf16(c[2 * t], c[2 * t + 1], sc, bc, dk, d0, d1);
       *(u32x4_t*)(dst + ((j * 2 + 0) * 64 + lane) * 16) = d0;
       *(u32x4_t*)(dst + ((j * 2 + 1) * 64 + lane) * 16) = d1;
     }

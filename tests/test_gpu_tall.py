@@ -1,0 +1,84 @@
+"""GPU parity of the tall-tile kernel (csrc/qmm_tall.hip), which the dense
+qlinear takes from 512 rows: every output row against the oracle's fp64
+qlinear (vision.ts page, VisionLinear.forward, quantized arm).
+
+Shapes cover both launch configurations: 128-row tiles with the whole
+contraction per wave, and 64-row tiles with the contraction split in two
+halves reduced in LDS.  They include ragged row counts (a last tile with 1,
+9 or 88 rows), a weight with a half block (N % 128 == 64), odd group counts
+(which keep the contraction whole), a single group, and affine biases drawn
+independently of the scales.  Bar: row-relative error <= 1e-2 (reading W1:
+each dequantized weight rounded to bf16 once), integer-exact inputs bit for
+bit."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synth
+from _util import bf16_host, dev_qweight, dev_tensor, ensure_built, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ensure_built()
+    torch.cuda.init()
+
+
+# (M, N, K, independent-bias seed or None)
+SHAPES = [
+    (512, 128, 128, None),      # the smallest tall launch: 4 x 1 tiles of 128 (split: 8 x 1 of 64)
+    (2520, 1152, 1152, None),   # the vision geometry: 64-row tiles, split contraction
+    (1033, 1088, 256, 201),     # ragged last tile (9 rows), half block, 4 groups
+    (600, 320, 576, None),      # 9 groups (odd): whole contraction, last tile of 88 rows
+    (4097, 256, 192, 202),      # 3 groups, last tile of 1 row
+    (700, 192, 64, None),       # a single group
+    (8192, 1152, 1152, 203),    # 128-row tiles (one wave per SIMD)
+]
+
+
+@pytest.mark.parametrize("M,N,K,bias_seed", SHAPES, ids=[f"{s[0]}x{s[2]}to{s[1]}" for s in SHAPES])
+def test_tall_qlinear_parity(M, N, K, bias_seed):
+    import bit_quantized_moe_diffrouter_amd as q
+    say(f"[tall qlinear] M={M} N={N} K={K} bias_seed={bias_seed}")
+    cfg = synth.QLinearConfig(f"tall_{M}x{K}to{N}", M=M, N=N, K=K, seed_w=M + 1, seed_x=M + 2, bias_seed=bias_seed)
+    inp = synth.make_qlinear_inputs(cfg)
+    y = q.qlinear(dev_tensor(inp.x), dev_qweight(inp.W).tiled())
+    torch.cuda.synchronize()
+    ref = O.qlinear(inp.x, inp.W.w, inp.W.scales, inp.W.biases)
+    err = O.rowwise_rel_err(bf16_host(y), ref)
+    say(f"  rel err {err:.3e}")
+    assert err <= 1e-2
+
+
+def test_tall_integer_exact_bitwise():
+    """scale 1, bias -8, x in {-2..2} at 128-row tiles: the exact integer sums
+    rounded once to bf16, bit for bit."""
+    import bit_quantized_moe_diffrouter_amd as q
+    say("[tall integer-exact] 8192x576 -> 1152")
+    rng = np.random.default_rng(77)
+    M, N, K = 8192, 1152, 576
+    w = rng.integers(0, 2**32, size=(N, K // 8), dtype=np.uint32)
+    s = synth.to_bf16_bits(np.ones((N, K // 64), dtype=np.float32))
+    b = synth.to_bf16_bits(np.full((N, K // 64), -8.0, dtype=np.float32))
+    x = synth.to_bf16_bits(rng.integers(-2, 3, size=(M, K)).astype(np.float32))
+    y = q.qlinear(dev_tensor(x), q.QuantWeight(dev_tensor(w), dev_tensor(s), dev_tensor(b)).tiled())
+    torch.cuda.synchronize()
+    ref = O.f64_to_bf16_bits(O.qlinear(x, w, s, b))
+    np.testing.assert_array_equal(y.view(torch.uint16).cpu().numpy(), ref)
+
+
+def test_tall_repeat_is_bitwise_identical():
+    """Two calls on the same inputs give the same bits (fixed summation order)."""
+    import bit_quantized_moe_diffrouter_amd as q
+    say("[tall determinism] 2520x1152 -> 1152")
+    inp = synth.make_qlinear_inputs(synth.QLINEAR_VISION)
+    x, W = dev_tensor(inp.x), dev_qweight(inp.W).tiled()
+    y0 = q.qlinear(x, W)
+    y1 = q.qlinear(x, W)
+    torch.cuda.synchronize()
+    assert torch.equal(y0.view(torch.uint16), y1.view(torch.uint16))

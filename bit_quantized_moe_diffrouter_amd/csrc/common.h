@@ -6,6 +6,7 @@
 // is scale*q + bias.
 #pragma once
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 #include <algorithm>
@@ -188,6 +189,75 @@ __device__ __forceinline__ int block_inclusive_scan(int v, int* scratch, int* to
   __syncthreads();
   *total = tot;
   return v + before;
+}
+
+// Items of the kernels that give a workgroup a chunk of BM sorted rows of one
+// expert and one weight block (the weight-stationary and tall-tile kernels on
+// the switch linears): expert e's rows [offsets[e], offsets[e+1]) (clamped to
+// [0, A)) are cut into chunks of BM rows, numbered expert by expert, blocks
+// minor.  Also gives the first 16-row activation tile of the chunk (the
+// experts' tiles numbered the same way).  Called by every thread of an
+// NT-thread workgroup (it has workgroup barriers); E <= 2 NT and E <= 256.
+// Returns false when `pos` is past the last item.
+constexpr int kChunkMaxExperts = 256;
+struct alignas(16) ExpertChunks {
+  alignas(16) int cpre[kChunkMaxExperts + 4];  // chunks before each expert (read as int4 by 64 lanes)
+  int lo[kChunkMaxExperts + 1];
+  int hi[kChunkMaxExperts + 1];
+  int tpre[kChunkMaxExperts + 1];  // activation tiles before each expert
+  int scan[16];
+};
+static_assert(offsetof(ExpertChunks, cpre) == 0, "the int4 reads need cpre 16-byte aligned");
+template <int NT, int BM>
+__device__ __forceinline__ bool expert_chunk_item(ExpertChunks& sh, const int32_t* offsets, int E, int A, int nblk,
+                                                  int pos, int& e, int& r0, int& rows, int& blk, int& tau0) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  for (int b = tid; b < E; b += NT) {
+    const int o0 = offsets[b], o1 = offsets[b + 1];
+    const int lo = min(max(o0, 0), A);
+    sh.lo[b] = lo;
+    sh.hi[b] = min(max(o1, lo), A);
+  }
+  __syncthreads();
+  auto scan = [&](int v) __attribute__((always_inline)) {  // exclusive prefix over experts (two per thread)
+    int all;
+    const int incl = block_inclusive_scan<NT>(v, sh.scan, &all);
+    return incl - v;
+  };
+  int c0 = 0, c1 = 0, t0 = 0, t1 = 0;
+  const int b0 = 2 * tid, b1 = 2 * tid + 1;
+  if (b0 < E) {
+    const int n = sh.hi[b0] - sh.lo[b0];
+    c0 = (n + BM - 1) / BM;
+    t0 = (n + 15) / 16;
+  }
+  if (b1 < E) {
+    const int n = sh.hi[b1] - sh.lo[b1];
+    c1 = (n + BM - 1) / BM;
+    t1 = (n + 15) / 16;
+  }
+  const int cx = scan(c0 + c1);
+  const int tx = scan(t0 + t1);
+  if (b0 <= E) sh.cpre[b0] = cx, sh.tpre[b0] = tx;
+  if (b1 <= E) sh.cpre[b1] = cx + c0, sh.tpre[b1] = tx + t0;
+  if (tid < 3 && E + 1 + tid < kChunkMaxExperts + 4) sh.cpre[E + 1 + tid] = 0x7fffffff;  // int4 reads past the end
+  __syncthreads();
+  const int nch = sh.cpre[E];
+  if (pos >= nch * nblk) return false;
+  const int ch = pos / nblk;
+  blk = pos - ch * nblk;
+  // the expert holding chunk ch: the number of experts whose first chunk is
+  // at most ch, less one, counted by the wave (lane l holds cpre[4l..4l+3])
+  const int4 c4 = ((const int4*)sh.cpre)[lane];
+  const int eb = 4 * lane;
+  const int n = __popcll(__ballot(eb < E && c4.x <= ch)) + __popcll(__ballot(eb + 1 < E && c4.y <= ch)) +
+                __popcll(__ballot(eb + 2 < E && c4.z <= ch)) + __popcll(__ballot(eb + 3 < E && c4.w <= ch));
+  e = __builtin_amdgcn_readfirstlane(n - 1);
+  r0 = __builtin_amdgcn_readfirstlane(sh.lo[e] + (ch - sh.cpre[e]) * BM);
+  rows = __builtin_amdgcn_readfirstlane(min(BM, sh.hi[e] - r0));
+  tau0 = __builtin_amdgcn_readfirstlane(sh.tpre[e] + (r0 - sh.lo[e]) / 16);
+  blk = __builtin_amdgcn_readfirstlane(blk);
+  return true;
 }
 
 }  // namespace qmoe

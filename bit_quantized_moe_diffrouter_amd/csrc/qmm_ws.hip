@@ -42,7 +42,6 @@ constexpr int kWsThreads = kWsWaves * 64;
 constexpr int kBBuf = 8 * 2 * 64 * 16;      // one group's dequantized operands: 16 KB
 constexpr int kWsLds = 2 * kBBuf;           // double buffer; the epilogue reuses it
 constexpr int kWsXcds = 8;
-constexpr int kWsMaxBuckets = 257;
 
 template <class F, int... I>
 __device__ __forceinline__ void ws_steps(F& f, std::integer_sequence<int, I...>) {
@@ -64,11 +63,7 @@ __global__ __launch_bounds__(kWsThreads, 2) void qmm_ws_kernel(const SwitchArgs 
   constexpr int BM = 16 * MT * kWsWaves;  // rows of the workgroup's tile
   static_assert(MT == 1 || MT == 2 || MT == 4, "1, 2 or 4 row tiles per wave (the epilogue stages at most 8 KB per wave)");
   extern __shared__ __attribute__((aligned(16))) uint8_t ws_lds[];
-  __shared__ int s_lo[kWsMaxBuckets];
-  __shared__ int s_hi[kWsMaxBuckets];
-  __shared__ __attribute__((aligned(16))) int s_cpre[kWsMaxBuckets + 3];  // chunks before each expert
-  __shared__ int s_tpre[kWsMaxBuckets + 1];                              // activation tiles before each expert
-  __shared__ int s_scan[kWsWaves];
+  __shared__ ExpertChunks s_items;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -89,53 +84,7 @@ __global__ __launch_bounds__(kWsThreads, 2) void qmm_ws_kernel(const SwitchArgs 
     r0 = ch * BM;
     rows = min(BM, A - r0);
   } else {
-    const int E = p.E;
-    for (int b = tid; b < E; b += kWsThreads) {
-      const int o0 = p.offsets[b], o1 = p.offsets[b + 1];
-      const int lo = min(max(o0, 0), A);
-      s_lo[b] = lo;
-      s_hi[b] = min(max(o1, lo), A);
-    }
-    __syncthreads();
-    auto scan = [&](int v) __attribute__((always_inline)) {  // exclusive prefix over experts (two per thread)
-      int all;
-      const int incl = block_inclusive_scan<kWsThreads>(v, s_scan, &all);
-      return incl - v;
-    };
-    int c0 = 0, c1 = 0, t0 = 0, t1 = 0;
-    const int b0 = 2 * tid, b1 = 2 * tid + 1;
-    if (b0 < E) {
-      const int n = s_hi[b0] - s_lo[b0];
-      c0 = (n + BM - 1) / BM;
-      t0 = (n + 15) / 16;
-    }
-    if (b1 < E) {
-      const int n = s_hi[b1] - s_lo[b1];
-      c1 = (n + BM - 1) / BM;
-      t1 = (n + 15) / 16;
-    }
-    const int cx = scan(c0 + c1);
-    const int tx = scan(t0 + t1);
-    if (b0 <= E) s_cpre[b0] = cx, s_tpre[b0] = tx;
-    if (b1 <= E) s_cpre[b1] = cx + c0, s_tpre[b1] = tx + t0;
-    if (tid == 0) s_cpre[E + 1] = s_cpre[E + 2] = 0x7fffffff;  // int4 reads past the end
-    __syncthreads();
-    const int nch = s_cpre[E];
-    if (pos >= nch * nblk) return;
-    const int ch = pos / nblk;
-    blk = pos - ch * nblk;
-    // the expert holding chunk ch: the number of experts whose first chunk is
-    // at most ch, less one, counted by the wave (lane l holds cpre[4l..4l+3])
-    {
-      const int4 c4 = ((const int4*)s_cpre)[lane];
-      const int eb = 4 * lane;
-      const int n = __popcll(__ballot(eb < E && c4.x <= ch)) + __popcll(__ballot(eb + 1 < E && c4.y <= ch)) +
-                    __popcll(__ballot(eb + 2 < E && c4.z <= ch)) + __popcll(__ballot(eb + 3 < E && c4.w <= ch));
-      e = __builtin_amdgcn_readfirstlane(n - 1);
-    }
-    r0 = s_lo[e] + (ch - s_cpre[e]) * BM;
-    rows = min(BM, s_hi[e] - r0);
-    tau0 = s_tpre[e] + (r0 - s_lo[e]) / 16;
+    if (!expert_chunk_item<kWsThreads, BM>(s_items, p.offsets, p.E, A, nblk, pos, e, r0, rows, blk, tau0)) return;
   }
   e = __builtin_amdgcn_readfirstlane(e);
   r0 = __builtin_amdgcn_readfirstlane(r0);

@@ -173,7 +173,8 @@ KERNEL_ROLES = [("route_logits_kernel", "moe_route: logits (partial sums)"),
                 ("qmm_ws_kernel<4,", "qlinear_softcap (weight-stationary)"),
                 ("qmm_kernel<1,", "qswitch_down_combine: down"),
                 ("combine_kernel", "qswitch_down_combine: weighted sum over k"),
-                ("qmm_kernel<2,", "qlinear (2520 x 1152 -> 1152)")]
+                ("qmm_kernel<2,", "qlinear (2520 x 1152 -> 1152)"),
+                ("qmm_tall_kernel<2,", "qlinear (2520 x 1152 -> 1152, tall-tile kernel)")]
 
 
 def _per_dispatch(d, counters):

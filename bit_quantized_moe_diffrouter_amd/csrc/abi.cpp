@@ -440,6 +440,8 @@ int qlinear_geglu(const uint16_t* x, int32_t M, const qmoe_qweight* W, uint16_t*
   a.E = 1;
   a.ktop = 1;
   a.rows_total = M;
+  if (qmoe::tall_preferred(qmoe::MODE_DENSE_GEGLU, M, 1))
+    return launched(qmoe::launch_tall<qmoe::MODE_DENSE_GEGLU>(a, ncu, stream), "qlinear_geglu");
   return launched(qmoe::launch_dense_geglu(a, ncu, stream), "qlinear_geglu");
 }
 

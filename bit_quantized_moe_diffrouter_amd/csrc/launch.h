@@ -109,9 +109,9 @@ template <int MODE>
 hipError_t launch_ws(SwitchArgs a, int num_cu, hipStream_t stream);
 
 // The tall-tile kernel (hundreds to thousands of rows per weight block; the
-// dense linear): whether it is the faster one, and its launcher (same
-// arguments and outputs as launch_dense; the dequantized weight is rounded to
-// bf16 once).
+// dense linear, plain or with the GeGLU): whether it is the faster one, and
+// its launcher (same arguments and outputs as launch_dense and
+// launch_dense_geglu; the dequantized weight is rounded to bf16 once).
 bool tall_preferred(int mode, long long rows, int experts);
 template <int MODE>
 hipError_t launch_tall(SwitchArgs a, int num_cu, hipStream_t stream);

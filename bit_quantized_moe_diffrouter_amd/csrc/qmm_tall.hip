@@ -1,9 +1,10 @@
 // Tall-tile 4-bit linears for gfx950: the matrix-core-bound shapes, where a
 // weight block meets hundreds or thousands of rows (the dense linears of the
-// vision tower and the feed-forward block).
+// vision tower: q, k, v, o and the MLP's fused gate|up with its GeGLU).
 //
 // What is computed is the same as in qswitch.hip (diffusion-gemma model.ts
-// page, the quantized linears; vision.ts page, VisionLinear.forward):
+// page, the quantized linears; vision.ts page, VisionLinear.forward and
+// DiffVisionMLP.forward for the GeGLU):
 // y = x . dequant(W)^T with W = scale * q + bias per 64-wide group.  As in the
 // weight-stationary kernel, the dequantized weight is rounded to bf16 once and
 // every product and sum is done by the bf16 matrix cores with fp32
@@ -81,7 +82,7 @@ constexpr int tall_waves_per_simd() { return MT >= 8 ? 1 : 2; }
 template <int MODE, int MT, int KS>
 __global__ __launch_bounds__(128 * KS)
 __attribute__((amdgpu_waves_per_eu(tall_waves_per_simd<MT>(), tall_waves_per_simd<MT>()))) void qmm_tall_kernel(const SwitchArgs p) {
-  static_assert(MODE == MODE_DENSE, "the dense linear");
+  static_assert(MODE == MODE_DENSE || MODE == MODE_DENSE_GEGLU, "the dense linear, plain or with the GeGLU");
   static_assert(MT == 2 || MT == 4 || MT == 8, "2, 4 or 8 row tiles");
   static_assert(KS == 1 || KS == 2, "one or two contraction parts (KS = 2: G even, so that both parts' waves pass the same barriers)");
   constexpr int BM = 16 * MT;
@@ -320,6 +321,32 @@ __attribute__((amdgpu_waves_per_eu(tall_waves_per_simd<MT>(), tall_waves_per_sim
     }
   }
 
+  if constexpr (MODE == MODE_DENSE_GEGLU) {
+    // ---- GeGLU epilogue (the weight tiled with split = Nout: block blk holds
+    // gate rows 64 blk .. + 63 as subtiles 0-3 and the matching up rows as
+    // 4-7): gate subtile 2c + t and up subtile 2c + t + 4 (t = 0, 1) give
+    // output columns 64 blk + 32 c + 16 t .. + 15.  Staged per wave and row
+    // tile as bf16 [16 rows][32 columns] (1 KB), written with 16-byte stores
+    // (lane: row lane / 4, 8-column piece lane % 4).
+    uint16_t* const stg = (uint16_t*)(tall_lds + (size_t)c * (KS == 2 ? MT * 4 * 64 * 16 : 1024));
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      if (m >= mt) continue;
+      if (m > 0) tall_wave_fence();  // the previous tile's staging reads are done
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          stg[(4 * lq + q) * 32 + 16 * t + ln] = f32_to_bf16_bits(gelu_tanh(acc[m][t][q]) * acc[m][t + 2][q]);
+      tall_wave_fence();
+      const int r = lane >> 2, lr = 16 * m + r;
+      const int col = blk * 64 + 32 * c + 8 * (lane & 3);  // the last block may be partly past the width
+      if (lr < rows && col < p.Nout)
+        *(u32x4_t*)((uint16_t*)p.out + (size_t)(r0 + lr) * p.Nout + col) = *(const u32x4_t*)(stg + r * 32 + 8 * (lane & 3));
+    }
+    return;
+  }
+
   // ---- epilogue: acc[m][t][q] is row 16 m + 4 lq + q, column 16 j + ln of
   // the block with j = 2c + (t & 1) + 4 (t >> 1).  Staged per wave and row
   // tile as bf16 [16 rows][64 columns, t-major] in 2 KB of the LDS, written
@@ -374,7 +401,7 @@ hipError_t launch_tall_cfg(const SwitchArgs& a, long long tiles, hipStream_t str
 }  // namespace
 
 bool tall_preferred(int mode, long long rows, int experts) {
-  if (mode == MODE_DENSE) return experts == 1 && rows >= 512;
+  if (mode == MODE_DENSE || mode == MODE_DENSE_GEGLU) return experts == 1 && rows >= 512;
   return false;
 }
 
@@ -393,5 +420,6 @@ hipError_t launch_tall(SwitchArgs a, int num_cu, hipStream_t stream) {
 }
 
 template hipError_t launch_tall<MODE_DENSE>(SwitchArgs, int, hipStream_t);
+template hipError_t launch_tall<MODE_DENSE_GEGLU>(SwitchArgs, int, hipStream_t);
 
 }  // namespace qmoe

@@ -10,9 +10,9 @@
 // every product and sum is done by the bf16 matrix cores with fp32
 // accumulation.
 //
-// Shape of the work.  A workgroup owns a tile of BM = 16 MT rows x one
-// 128-row weight block.  Its waves split the block's 128 columns in two
-// halves of 64 (four 16-column subtiles each) and, optionally, the
+// Shape of the work.  A workgroup owns a tile of BM = 16 MT rows x NB
+// 128-row weight blocks.  Its waves split each block's 128 columns in two
+// halves of 64 (four 16-column subtiles each) and, optionally (one block), the
 // contraction in KS parts.  Each wave runs all BM rows against its 64
 // columns, so the four subtiles it dequantizes per group (in registers,
 // bf16(s q + b)) feed 8 MT matrix-core products: the vector work per product
@@ -79,12 +79,13 @@ constexpr size_t tall_lds_bytes() { return (size_t)KS * kTallBufs * tall_tile_by
 template <int MT>
 constexpr int tall_waves_per_simd() { return MT >= 8 ? 1 : 2; }
 
-template <int MODE, int MT, int KS>
-__global__ __launch_bounds__(128 * KS)
+template <int MODE, int MT, int KS, int NB>
+__global__ __launch_bounds__(128 * KS * NB)
 __attribute__((amdgpu_waves_per_eu(tall_waves_per_simd<MT>(), tall_waves_per_simd<MT>()))) void qmm_tall_kernel(const SwitchArgs p) {
   static_assert(MODE == MODE_DENSE || MODE == MODE_DENSE_GEGLU, "the dense linear, plain or with the GeGLU");
   static_assert(MT == 2 || MT == 4 || MT == 8, "2, 4 or 8 row tiles");
   static_assert(KS == 1 || KS == 2, "one or two contraction parts (KS = 2: G even, so that both parts' waves pass the same barriers)");
+  static_assert(NB == 1 || (NB == 2 && KS == 1), "one weight block per workgroup, or two with the contraction whole");
   constexpr int BM = 16 * MT;
   constexpr int kTile = tall_tile_bytes<MT>();
   constexpr int PB = kTallPB;
@@ -92,7 +93,9 @@ __attribute__((amdgpu_waves_per_eu(tall_waves_per_simd<MT>(), tall_waves_per_sim
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int c = wave & 1, kp = wave >> 1;  // column half, contraction part
+  // column half c; with two contraction parts the part kp, with two blocks
+  // the block bsel of the workgroup's pair
+  const int c = wave & 1, kp = (KS == 2) ? wave >> 1 : 0, bsel = (NB == 2) ? wave >> 1 : 0;
   const int ln = lane & 15, lq = lane >> 4;
   const int K = p.K, G = K / kGroup, A = p.rows_total, nblk = p.nblk;
   const int grid = (int)gridDim.x, bid = (int)blockIdx.x;
@@ -100,28 +103,36 @@ __attribute__((amdgpu_waves_per_eu(tall_waves_per_simd<MT>(), tall_waves_per_sim
   // row chunk, which read the same activations) share a die's L2
   const int pos = (grid % kTallXcds == 0) ? (bid % kTallXcds) * (grid / kTallXcds) + bid / kTallXcds : bid;
 
-  // ---- this workgroup's tile: (row chunk of BM rows, weight block)
+  // ---- this workgroup's tile: (row chunk of BM rows, NB weight blocks);
+  // this wave's block blk (past the last block with an odd count: the last
+  // block's weights, results never stored)
+  const int nbp = (nblk + NB - 1) / NB;
   const int nch = (A + BM - 1) / BM;
-  if (pos >= nch * nblk) return;
-  const int ch = pos / nblk;
-  const int blk = __builtin_amdgcn_readfirstlane(pos - ch * nblk);
+  if (pos >= nch * nbp) return;
+  const int ch = pos / nbp;
+  const int blk = __builtin_amdgcn_readfirstlane((pos - ch * nbp) * NB + bsel);
+  const int wblk = min(blk, nblk - 1);
   const int r0 = __builtin_amdgcn_readfirstlane(ch * BM);
   const int rows = __builtin_amdgcn_readfirstlane(min(BM, A - r0));
   const int mt = (rows + 15) >> 4;  // row tiles holding rows (the others are skipped)
   const int g0 = kp * G / KS, g1 = (kp + 1) * G / KS, ng = g1 - g0;
 
   // ---- operand addresses
-  const uint8_t* const ubase = (const uint8_t*)p.w + (size_t)blk * (size_t)G * kTiledUnit;
+  const uint8_t* const ubase = (const uint8_t*)p.w + (size_t)wblk * (size_t)G * kTiledUnit;
   const uint32_t cofs0 = (uint32_t)c * 1024 + lane * 16, cofs1 = (uint32_t)(2 + c) * 1024 + lane * 16;
   const uint32_t sofs0 = 4096 + ln * 16 + 8 * c, sofs1 = sofs0 + 256;
   const uint8_t* const abytes = (const uint8_t*)p.a;
-  // this wave stages row tiles m = c + 2 s: lane (ln, lq) loads the 32 bytes
-  // of row 16 m + ln that operand lanes (ln, lq) of both products hold
-  constexpr int NS = MT / 2;
+  // the 2 NB waves of a contraction part share its activations: wave wl
+  // loads row tiles m = wl + 2 NB s, lane (ln, lq) the 32 bytes of row
+  // 16 m + ln that operand lanes (ln, lq) of both products hold
+  constexpr int NW = 2 * NB;
+  constexpr int NS = MT / NW;
+  static_assert(NS >= 1, "every wave loads a row tile");
+  const int wl = (KS == 2) ? c : wave;
   uint32_t aoff[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
-    const int rl = min(16 * (c + 2 * s) + ln, rows - 1);  // rows past the chunk read its last row
+    const int rl = min(16 * (wl + NW * s) + ln, rows - 1);  // rows past the chunk read its last row
     aoff[s] = (uint32_t)(r0 + rl) * (uint32_t)(K * 2) + lq * 32;
   }
   uint8_t* const abuf = tall_lds + kp * kTallBufs * kTile;
@@ -145,7 +156,7 @@ __attribute__((amdgpu_waves_per_eu(tall_waves_per_simd<MT>(), tall_waves_per_sim
   auto dma_a = [&](int buf, int g) __attribute__((always_inline)) {
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      const int m = c + 2 * s;
+      const int m = wl + NW * s;
       const uint8_t* const ag = abytes + (size_t)__builtin_amdgcn_readfirstlane(g) * 128u;
       uint32_t o[2] = {aoff[s], aoff[s] + 16u};
       asm volatile("" : "+v"(o[0]), "+v"(o[1]));  // no instruction: keeps the offsets 32-bit
@@ -328,7 +339,7 @@ __attribute__((amdgpu_waves_per_eu(tall_waves_per_simd<MT>(), tall_waves_per_sim
     // output columns 64 blk + 32 c + 16 t .. + 15.  Staged per wave and row
     // tile as bf16 [16 rows][32 columns] (1 KB), written with 16-byte stores
     // (lane: row lane / 4, 8-column piece lane % 4).
-    uint16_t* const stg = (uint16_t*)(tall_lds + (size_t)c * (KS == 2 ? MT * 4 * 64 * 16 : 1024));
+    uint16_t* const stg = (uint16_t*)(tall_lds + (KS == 2 ? (size_t)c * MT * 4 * 64 * 16 : (size_t)wave * 1024));
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
       if (m >= mt) continue;
@@ -341,7 +352,7 @@ __attribute__((amdgpu_waves_per_eu(tall_waves_per_simd<MT>(), tall_waves_per_sim
       tall_wave_fence();
       const int r = lane >> 2, lr = 16 * m + r;
       const int col = blk * 64 + 32 * c + 8 * (lane & 3);  // the last block may be partly past the width
-      if (lr < rows && col < p.Nout)
+      if (lr < rows && col < p.Nout && blk < nblk)
         *(u32x4_t*)((uint16_t*)p.out + (size_t)(r0 + lr) * p.Nout + col) = *(const u32x4_t*)(stg + r * 32 + 8 * (lane & 3));
     }
     return;
@@ -353,7 +364,7 @@ __attribute__((amdgpu_waves_per_eu(tall_waves_per_simd<MT>(), tall_waves_per_sim
   // with 16-byte stores (lane: row lane / 4, two 8-column pieces).
   // (with two contraction parts each wave stages in its own parked sums, which
   // it has read: its LDS operations run in order)
-  uint16_t* const stg_out = (uint16_t*)(tall_lds + (size_t)c * (KS == 2 ? MT * 4 * 64 * 16 : 2048));
+  uint16_t* const stg_out = (uint16_t*)(tall_lds + (KS == 2 ? (size_t)c * MT * 4 * 64 * 16 : (size_t)wave * 2048));
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
     if (m >= mt) continue;
@@ -369,7 +380,7 @@ __attribute__((amdgpu_waves_per_eu(tall_waves_per_simd<MT>(), tall_waves_per_sim
       const int piece = 2 * (lane & 3) + h;  // 8-column piece of the 64 staged columns
       const int t = piece >> 1;
       const int col = blk * 128 + 16 * (2 * c + (t & 1) + 4 * (t >> 1)) + 8 * (piece & 1);
-      if (lr < rows && col < p.Nout)
+      if (lr < rows && col < p.Nout && blk < nblk)
         *(u32x4_t*)((uint16_t*)p.out + (size_t)(r0 + lr) * p.Nout + col) = *(const u32x4_t*)(stg_out + r * 64 + 8 * piece);
     }
   }
@@ -379,22 +390,27 @@ __attribute__((amdgpu_waves_per_eu(tall_waves_per_simd<MT>(), tall_waves_per_sim
 namespace {
 
 constexpr int kTallMaxDevices = 64;
+// Weight blocks per workgroup of the 128-row configuration: the four waves of
+// a two-block workgroup share one activation tile, so each loads half as many
+// activation bytes per group as in a one-block workgroup (each kilobyte a wave
+// loads per step costs it tens of cycles; 16384 x 2816 -> 2816: 357 -> 316 us).
+constexpr int kTallPair = 2;
 
-template <int MODE, int MT, int KS>
+template <int MODE, int MT, int KS, int NB>
 hipError_t launch_tall_cfg(const SwitchArgs& a, long long tiles, hipStream_t stream) {
   static std::atomic<int> attr_done[kTallMaxDevices];
   constexpr int lds = (int)tall_lds_bytes<MT, KS>();
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kTallMaxDevices) dev = 0;
   if (!attr_done[dev].load(std::memory_order_acquire)) {
-    const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&qmm_tall_kernel<MODE, MT, KS>),
+    const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&qmm_tall_kernel<MODE, MT, KS, NB>),
                                                 hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (attr != hipSuccess) return attr;
     attr_done[dev].store(1, std::memory_order_release);
   }
   const long long grid = (std::max<long long>(tiles, 1) + kTallXcds - 1) / kTallXcds * kTallXcds;
   if (grid > (1LL << 30)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((qmm_tall_kernel<MODE, MT, KS>), dim3((unsigned)grid), dim3(128 * KS), lds, stream, a);
+  hipLaunchKernelGGL((qmm_tall_kernel<MODE, MT, KS, NB>), dim3((unsigned)grid), dim3(128 * KS * NB), lds, stream, a);
   return hipGetLastError();
 }
 
@@ -415,8 +431,9 @@ hipError_t launch_tall(SwitchArgs a, int num_cu, hipStream_t stream) {
   // tiles with the contraction split in two equal parts (both parts' waves
   // then pass the same number of workgroup barriers)
   const long long t8 = (A + 127) / 128 * a.nblk;
-  if (2 * t8 >= 4LL * num_cu || G < 4 || G % 2 != 0) return launch_tall_cfg<MODE, 8, 1>(a, t8, stream);
-  return launch_tall_cfg<MODE, 4, 2>(a, (A + 63) / 64 * a.nblk, stream);
+  if (2 * t8 >= 4LL * num_cu || G < 4 || G % 2 != 0)
+    return launch_tall_cfg<MODE, 8, 1, kTallPair>(a, (A + 127) / 128 * ((a.nblk + kTallPair - 1) / kTallPair), stream);
+  return launch_tall_cfg<MODE, 4, 2, 1>(a, (A + 63) / 64 * a.nblk, stream);
 }
 
 template hipError_t launch_tall<MODE_DENSE>(SwitchArgs, int, hipStream_t);

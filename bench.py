@@ -169,7 +169,7 @@ KERNEL_ROLES = [("route_logits_kernel", "moe_route: logits (partial sums)"),
                 ("sort_hist_kernel", "moe_sort: slice histograms"),
                 ("sort_kernel", "moe_sort"),
                 ("qmm_kernel<0,", "qswitch_gate_up_geglu"),
-                ("qmm_ws_kernel<0,", "qswitch_gate_up_geglu (weight-stationary)"),
+                ("qmm_tall_kernel<0,", "qswitch_gate_up_geglu (tall-tile)"),
                 ("qmm_ws_kernel<4,", "qlinear_softcap (weight-stationary)"),
                 ("qmm_kernel<1,", "qswitch_down_combine: down"),
                 ("combine_kernel", "qswitch_down_combine: weighted sum over k"),

@@ -258,8 +258,8 @@ int qswitch_gate_up_geglu(const uint16_t* x_expert, int32_t T, int32_t H, const 
   a.E = E;
   a.ktop = k;
   a.rows_total = T * k;
-  if (use_ws(qmoe::MODE_GATE_UP, a.rows_total, E))
-    return launched(qmoe::launch_ws<qmoe::MODE_GATE_UP>(a, ncu, stream), "qswitch_gate_up_geglu");
+  if (qmoe::tall_preferred(qmoe::MODE_GATE_UP, a.rows_total, E))
+    return launched(qmoe::launch_tall<qmoe::MODE_GATE_UP>(a, ncu, stream), "qswitch_gate_up_geglu");
   return launched(qmoe::launch_gate_up_geglu(a, ncu, stream), "qswitch_gate_up_geglu");
 }
 

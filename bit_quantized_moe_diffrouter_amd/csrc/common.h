@@ -191,14 +191,14 @@ __device__ __forceinline__ int block_inclusive_scan(int v, int* scratch, int* to
   return v + before;
 }
 
-// Items of the kernels that give a workgroup a chunk of BM sorted rows of one
-// expert and one weight block (the weight-stationary and tall-tile kernels on
-// the switch linears): expert e's rows [offsets[e], offsets[e+1]) (clamped to
+// Items of a kernel that gives a workgroup a chunk of BM sorted rows of one
+// expert and one or more weight blocks (the tall-tile kernel on the gate_up
+// switch linear): expert e's rows [offsets[e], offsets[e+1]) (clamped to
 // [0, A)) are cut into chunks of BM rows, numbered expert by expert, blocks
 // minor.  Also gives the first 16-row activation tile of the chunk (the
-// experts' tiles numbered the same way).  Called by every thread of an
-// NT-thread workgroup (it has workgroup barriers); E <= 2 NT and E <= 256.
-// Returns false when `pos` is past the last item.
+// experts' tiles numbered the same way).  The tables are built by every
+// thread of an NT-thread workgroup (workgroup barriers); E <= 2 NT and
+// E <= 256.
 constexpr int kChunkMaxExperts = 256;
 struct alignas(16) ExpertChunks {
   alignas(16) int cpre[kChunkMaxExperts + 4];  // chunks before each expert (read as int4 by 64 lanes)
@@ -208,10 +208,10 @@ struct alignas(16) ExpertChunks {
   int scan[16];
 };
 static_assert(offsetof(ExpertChunks, cpre) == 0, "the int4 reads need cpre 16-byte aligned");
+// The tables (every thread of the workgroup; ends with a barrier) ...
 template <int NT, int BM>
-__device__ __forceinline__ bool expert_chunk_item(ExpertChunks& sh, const int32_t* offsets, int E, int A, int nblk,
-                                                  int pos, int& e, int& r0, int& rows, int& blk, int& tau0) {
-  const int tid = threadIdx.x, lane = tid & 63;
+__device__ __forceinline__ void expert_chunk_tables(ExpertChunks& sh, const int32_t* offsets, int E, int A) {
+  const int tid = threadIdx.x;
   for (int b = tid; b < E; b += NT) {
     const int o0 = offsets[b], o1 = offsets[b + 1];
     const int lo = min(max(o0, 0), A);
@@ -242,6 +242,14 @@ __device__ __forceinline__ bool expert_chunk_item(ExpertChunks& sh, const int32_
   if (b1 <= E) sh.cpre[b1] = cx + c0, sh.tpre[b1] = tx + t0;
   if (tid < 3 && E + 1 + tid < kChunkMaxExperts + 4) sh.cpre[E + 1 + tid] = 0x7fffffff;  // int4 reads past the end
   __syncthreads();
+}
+// ... and the item at position pos (one wave's work, no barrier): chunk
+// pos / nblk of the experts' chunks (sh.cpre[E] of them), block pos % nblk.
+// Returns false when pos is past the last item.
+template <int BM>
+__device__ __forceinline__ bool expert_chunk_at(const ExpertChunks& sh, int E, int nblk, int pos, int& e, int& r0,
+                                                int& rows, int& blk, int& tau0) {
+  const int lane = threadIdx.x & 63;
   const int nch = sh.cpre[E];
   if (pos >= nch * nblk) return false;
   const int ch = pos / nblk;
@@ -259,5 +267,4 @@ __device__ __forceinline__ bool expert_chunk_item(ExpertChunks& sh, const int32_
   blk = __builtin_amdgcn_readfirstlane(blk);
   return true;
 }
-
 }  // namespace qmoe

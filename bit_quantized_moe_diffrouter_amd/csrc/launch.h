@@ -100,18 +100,20 @@ hipError_t launch_dense_geglu(SwitchArgs a, int num_cu, hipStream_t stream);
 // cap * tanh(bf16(logit) / cap)
 hipError_t launch_dense_softcap(SwitchArgs a, int num_cu, hipStream_t stream);
 hipError_t launch_combine(const uint16_t* D, const float* w, int T, int k, int H, uint16_t* y, hipStream_t stream);
-// The weight-stationary kernel (many rows per weight block): whether it is
-// the faster one for `rows` rows (A = T*k for the switch modes) over
-// `experts` experts, and its launcher (same arguments and outputs as the
-// launchers above; the dequantized weight is rounded to bf16 once).
+// The weight-stationary kernel (many rows per weight block; the tied head):
+// whether it is the faster one for `rows` rows, and its launcher (same
+// arguments and outputs as launch_dense_softcap; the dequantized weight is
+// rounded to bf16 once).
 bool ws_preferred(int mode, long long rows, int experts);
 template <int MODE>
 hipError_t launch_ws(SwitchArgs a, int num_cu, hipStream_t stream);
 
 // The tall-tile kernel (hundreds to thousands of rows per weight block; the
-// dense linear, plain or with the GeGLU): whether it is the faster one, and
-// its launcher (same arguments and outputs as launch_dense and
-// launch_dense_geglu; the dequantized weight is rounded to bf16 once).
+// dense linear, plain or with the GeGLU, and the gate_up switch linear):
+// whether it is the faster one for `rows` rows (A = T*k for gate_up) over
+// `experts` experts, and its launcher (same arguments and outputs as
+// launch_dense, launch_dense_geglu and launch_gate_up_geglu; the dequantized
+// weight is rounded to bf16 once).
 bool tall_preferred(int mode, long long rows, int experts);
 template <int MODE>
 hipError_t launch_tall(SwitchArgs a, int num_cu, hipStream_t stream);

@@ -82,7 +82,10 @@ constexpr int tall_waves_per_simd() { return MT >= 8 ? 1 : 2; }
 template <int MODE, int MT, int KS, int NB>
 __global__ __launch_bounds__(128 * KS * NB)
 __attribute__((amdgpu_waves_per_eu(tall_waves_per_simd<MT>(), tall_waves_per_simd<MT>()))) void qmm_tall_kernel(const SwitchArgs p) {
-  static_assert(MODE == MODE_DENSE || MODE == MODE_DENSE_GEGLU, "the dense linear, plain or with the GeGLU");
+  static_assert(MODE == MODE_DENSE || MODE == MODE_DENSE_GEGLU || MODE == MODE_GATE_UP,
+                "the dense linear (plain or with the GeGLU) or the gate_up switch linear");
+  constexpr bool kRows = MODE == MODE_DENSE || MODE == MODE_DENSE_GEGLU;  // plain rows 0..M-1; else sorted expert rows
+  static_assert(kRows || KS == 1, "the switch modes keep the contraction whole");
   static_assert(MT == 2 || MT == 4 || MT == 8, "2, 4 or 8 row tiles");
   static_assert(KS == 1 || KS == 2, "one or two contraction parts (KS = 2: G even, so that both parts' waves pass the same barriers)");
   static_assert(NB == 1 || (NB == 2 && KS == 1), "one weight block per workgroup, or two with the contraction whole");
@@ -99,26 +102,43 @@ __attribute__((amdgpu_waves_per_eu(tall_waves_per_simd<MT>(), tall_waves_per_sim
   const int ln = lane & 15, lq = lane >> 4;
   const int K = p.K, G = K / kGroup, A = p.rows_total, nblk = p.nblk;
   const int grid = (int)gridDim.x, bid = (int)blockIdx.x;
-  // workgroup b runs on die b % 8: consecutive positions (the blocks of one
-  // row chunk, which read the same activations) share a die's L2
-  const int pos = (grid % kTallXcds == 0) ? (bid % kTallXcds) * (grid / kTallXcds) + bid / kTallXcds : bid;
-
-  // ---- this workgroup's tile: (row chunk of BM rows, NB weight blocks);
-  // this wave's block blk (past the last block with an odd count: the last
-  // block's weights, results never stored)
+  // A persistent grid: workgroup b takes positions pos0, pos0 + grid, ...
+  // Workgroup b runs on die b % 8 and pos0 numbers the workgroups die by die,
+  // so consecutive positions (the blocks of one row chunk, which read the same
+  // activations) share a die's L2 in every round.
+  const int pos0 = (grid % kTallXcds == 0) ? (bid % kTallXcds) * (grid / kTallXcds) + bid / kTallXcds : bid;
+  // Items: (row chunk of BM rows, NB weight blocks); in the switch mode the
+  // chunks of each expert's sorted rows, numbered expert by expert.
   const int nbp = (nblk + NB - 1) / NB;
-  const int nch = (A + BM - 1) / BM;
-  if (pos >= nch * nbp) return;
-  const int ch = pos / nbp;
-  const int blk = __builtin_amdgcn_readfirstlane((pos - ch * nbp) * NB + bsel);
+  __shared__ ExpertChunks s_items;  // the switch mode's chunk tables, built once
+  int n_items;
+  if constexpr (kRows) {
+    n_items = (A + BM - 1) / BM * nbp;
+  } else {
+    expert_chunk_tables<128 * KS * NB, BM>(s_items, p.offsets, p.E, A);
+    n_items = s_items.cpre[p.E] * nbp;
+  }
+
+  for (int pos = pos0; pos < n_items; pos += grid) {
+  // ---- this item: this wave's block blk (past the last block with an odd
+  // count: the last block's weights, results never stored); in the switch
+  // mode the chunk of expert e, tau0 its first activation tile
+  int e = 0, r0 = 0, rows = 0, bp = 0, tau0 = 0;
+  if constexpr (kRows) {
+    const int ch = pos / nbp;
+    bp = pos - ch * nbp;
+    r0 = __builtin_amdgcn_readfirstlane(ch * BM);
+    rows = __builtin_amdgcn_readfirstlane(min(BM, A - r0));
+  } else {
+    expert_chunk_at<BM>(s_items, p.E, nbp, pos, e, r0, rows, bp, tau0);
+  }
+  const int blk = __builtin_amdgcn_readfirstlane(bp * NB + bsel);
   const int wblk = min(blk, nblk - 1);
-  const int r0 = __builtin_amdgcn_readfirstlane(ch * BM);
-  const int rows = __builtin_amdgcn_readfirstlane(min(BM, A - r0));
   const int mt = (rows + 15) >> 4;  // row tiles holding rows (the others are skipped)
   const int g0 = kp * G / KS, g1 = (kp + 1) * G / KS, ng = g1 - g0;
 
   // ---- operand addresses
-  const uint8_t* const ubase = (const uint8_t*)p.w + (size_t)wblk * (size_t)G * kTiledUnit;
+  const uint8_t* const ubase = (const uint8_t*)p.w + ((size_t)e * nblk + wblk) * (size_t)G * kTiledUnit;
   const uint32_t cofs0 = (uint32_t)c * 1024 + lane * 16, cofs1 = (uint32_t)(2 + c) * 1024 + lane * 16;
   const uint32_t sofs0 = 4096 + ln * 16 + 8 * c, sofs1 = sofs0 + 256;
   const uint8_t* const abytes = (const uint8_t*)p.a;
@@ -133,7 +153,12 @@ __attribute__((amdgpu_waves_per_eu(tall_waves_per_simd<MT>(), tall_waves_per_sim
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const int rl = min(16 * (wl + NW * s) + ln, rows - 1);  // rows past the chunk read its last row
-    aoff[s] = (uint32_t)(r0 + rl) * (uint32_t)(K * 2) + lq * 32;
+    int src = r0 + rl;
+    if constexpr (MODE == MODE_GATE_UP) {  // the token of the sorted row's assignment
+      const int a = p.assign[src];
+      src = (a >= 0 && a < A) ? token_of(a, p.ktop_inv) : 0;
+    }
+    aoff[s] = (uint32_t)src * (uint32_t)(K * 2) + lq * 32;
   }
   uint8_t* const abuf = tall_lds + kp * kTallBufs * kTile;
 
@@ -319,20 +344,48 @@ __attribute__((amdgpu_waves_per_eu(tall_waves_per_simd<MT>(), tall_waves_per_sim
       }
     }
     __syncthreads();
-    if (kp == 1) return;  // no workgroup barrier follows
+    if (kp == 0) {
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      if (m >= mt) continue;
+      for (int m = 0; m < MT; ++m) {
+        if (m >= mt) continue;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const f32x4_t o = red[(m * 4 + t) * 64 + lane];
+        for (int t = 0; t < 4; ++t) {
+          const f32x4_t o = red[(m * 4 + t) * 64 + lane];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[m][t][q] += o[q];
+          for (int q = 0; q < 4; ++q) acc[m][t][q] += o[q];
+        }
       }
     }
   }
+  // part 1's waves have no outputs (they pass the barrier below)
+  if (kp == 0) {
 
-  if constexpr (MODE == MODE_DENSE_GEGLU) {
+  if constexpr (MODE == MODE_GATE_UP) {
+    // ---- gate_up epilogue: gate subtile 2c + t and up subtile 2c + t + 4
+    // (t = 0, 1) give columns 16 (2c + t) .. + 15 of block blk's 64 mid
+    // columns; mid's activation tiles hold column 16 q + 8 h + i of tile row r
+    // at byte h * 1024 + (16 q + r) * 16 + 2 i of the (tile, group) block, so
+    // this wave's quarters q = 2c, 2c + 1 are bytes [512 c, 512 c + 512) of
+    // each 1 KB half: staged per row tile in 1 KB of the LDS as [h][512], one
+    // 16-byte store per lane
+    uint8_t* const stg1 = tall_lds + (size_t)wave * 1024;
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      if (m >= mt) continue;
+      const int tau = tau0 + m;
+      if (tau < 0 || tau >= p.max_tiles || blk >= nblk) continue;
+      tall_wave_fence();  // the previous tile's staging reads are done
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *(uint16_t*)(stg1 + (ln >> 3) * 512 + (16 * t + 4 * lq + q) * 16 + (ln & 7) * 2) =
+              f32_to_bf16_bits(gelu_tanh(acc[m][t][q]) * acc[m][t + 2][q]);
+      tall_wave_fence();
+      uint8_t* const dst = (uint8_t*)p.out + ((size_t)tau * (p.Nout / 64) + blk) * kActBlock;
+      *(u32x4_t*)(dst + (lane >> 5) * 1024 + 512 * c + (lane & 31) * 16) = *(const u32x4_t*)(stg1 + lane * 16);
+    }
+  } else if constexpr (MODE == MODE_DENSE_GEGLU) {
     // ---- GeGLU epilogue (the weight tiled with split = Nout: block blk holds
     // gate rows 64 blk .. + 63 as subtiles 0-3 and the matching up rows as
     // 4-7): gate subtile 2c + t and up subtile 2c + t + 4 (t = 0, 1) give
@@ -355,9 +408,7 @@ __attribute__((amdgpu_waves_per_eu(tall_waves_per_simd<MT>(), tall_waves_per_sim
       if (lr < rows && col < p.Nout && blk < nblk)
         *(u32x4_t*)((uint16_t*)p.out + (size_t)(r0 + lr) * p.Nout + col) = *(const u32x4_t*)(stg + r * 32 + 8 * (lane & 3));
     }
-    return;
-  }
-
+  } else {
   // ---- epilogue: acc[m][t][q] is row 16 m + 4 lq + q, column 16 j + ln of
   // the block with j = 2c + (t & 1) + 4 (t >> 1).  Staged per wave and row
   // tile as bf16 [16 rows][64 columns, t-major] in 2 KB of the LDS, written
@@ -384,6 +435,10 @@ __attribute__((amdgpu_waves_per_eu(tall_waves_per_simd<MT>(), tall_waves_per_sim
         *(u32x4_t*)((uint16_t*)p.out + (size_t)(r0 + lr) * p.Nout + col) = *(const u32x4_t*)(stg_out + r * 64 + 8 * piece);
     }
   }
+  }  // the epilogues
+  }  // outputs of contraction part 0
+  __syncthreads();  // every wave is done with the LDS before the next item's loads land there
+  }  // items
 }
 
 // ------------------------------------------------------------------ launchers
@@ -396,8 +451,10 @@ constexpr int kTallMaxDevices = 64;
 // loads per step costs it tens of cycles; 16384 x 2816 -> 2816: 357 -> 316 us).
 constexpr int kTallPair = 2;
 
+// A persistent grid: at most one workgroup per free slot (workgroups per CU at
+// the configuration's waves per SIMD), each walking its items.
 template <int MODE, int MT, int KS, int NB>
-hipError_t launch_tall_cfg(const SwitchArgs& a, long long tiles, hipStream_t stream) {
+hipError_t launch_tall_cfg(const SwitchArgs& a, long long tiles, int num_cu, hipStream_t stream) {
   static std::atomic<int> attr_done[kTallMaxDevices];
   constexpr int lds = (int)tall_lds_bytes<MT, KS>();
   int dev = 0;
@@ -408,8 +465,11 @@ hipError_t launch_tall_cfg(const SwitchArgs& a, long long tiles, hipStream_t str
     if (attr != hipSuccess) return attr;
     attr_done[dev].store(1, std::memory_order_release);
   }
-  const long long grid = (std::max<long long>(tiles, 1) + kTallXcds - 1) / kTallXcds * kTallXcds;
-  if (grid > (1LL << 30)) return hipErrorInvalidValue;
+  constexpr int kPerCu = tall_waves_per_simd<MT>() * 4 / (2 * KS * NB);
+  static_assert(kPerCu >= 1, "a workgroup fits a CU");
+  const long long slots = (long long)std::max(num_cu, 1) * kPerCu;
+  const long long grid =
+      std::min((std::max<long long>(tiles, 1) + kTallXcds - 1) / kTallXcds * kTallXcds, std::max<long long>(slots, 1));
   hipLaunchKernelGGL((qmm_tall_kernel<MODE, MT, KS, NB>), dim3((unsigned)grid), dim3(128 * KS * NB), lds, stream, a);
   return hipGetLastError();
 }
@@ -418,25 +478,36 @@ hipError_t launch_tall_cfg(const SwitchArgs& a, long long tiles, hipStream_t str
 
 bool tall_preferred(int mode, long long rows, int experts) {
   if (mode == MODE_DENSE || mode == MODE_DENSE_GEGLU) return experts == 1 && rows >= 512;
+  if (mode == MODE_GATE_UP) return experts <= kChunkMaxExperts && rows >= 96LL * experts;
   return false;
 }
 
 template <int MODE>
 hipError_t launch_tall(SwitchArgs a, int num_cu, hipStream_t stream) {
   a.ntiles = a.nblk;
+  a.ktop_inv = ktop_inverse(a.ktop);
   const long long A = a.rows_total;
   if (A <= 0) return hipSuccess;
+  if constexpr (MODE == MODE_GATE_UP) {
+    // every row in its expert's chunks, at most one partial chunk per expert
+    if (a.E > kChunkMaxExperts) return hipErrorInvalidValue;
+    const long long items = ((A + 127) / 128 + std::min<long long>(a.E, A)) * ((a.nblk + kTallPair - 1) / kTallPair);
+    return launch_tall_cfg<MODE, 8, 1, kTallPair>(a, items, num_cu, stream);
+  } else {
   const int G = a.K / kGroup;
   // 128-row tiles where they give at least one wave per SIMD; else 64-row
   // tiles with the contraction split in two equal parts (both parts' waves
   // then pass the same number of workgroup barriers)
   const long long t8 = (A + 127) / 128 * a.nblk;
   if (2 * t8 >= 4LL * num_cu || G < 4 || G % 2 != 0)
-    return launch_tall_cfg<MODE, 8, 1, kTallPair>(a, (A + 127) / 128 * ((a.nblk + kTallPair - 1) / kTallPair), stream);
-  return launch_tall_cfg<MODE, 4, 2, 1>(a, (A + 63) / 64 * a.nblk, stream);
+    return launch_tall_cfg<MODE, 8, 1, kTallPair>(a, (A + 127) / 128 * ((a.nblk + kTallPair - 1) / kTallPair), num_cu,
+                                                  stream);
+  return launch_tall_cfg<MODE, 4, 2, 1>(a, (A + 63) / 64 * a.nblk, num_cu, stream);
+  }
 }
 
 template hipError_t launch_tall<MODE_DENSE>(SwitchArgs, int, hipStream_t);
 template hipError_t launch_tall<MODE_DENSE_GEGLU>(SwitchArgs, int, hipStream_t);
+template hipError_t launch_tall<MODE_GATE_UP>(SwitchArgs, int, hipStream_t);
 
 }  // namespace qmoe

@@ -1,9 +1,8 @@
-// Weight-stationary 4-bit linears for gfx950, for weight blocks that meet
-// many rows: the gate_up switch linear + GeGLU at prefill-sized batches and
-// the tied LM head with its softcap.
+// The weight-stationary 4-bit linear for gfx950, for weight blocks that meet
+// many rows: the tied LM head with its softcap.
 //
 // What is computed is the same as in qswitch.hip (diffusion-gemma model.ts
-// page, DiffExperts.forward for gate_up; logitsFromHidden for the head):
+// page, logitsFromHidden):
 // y = x . dequant(W)^T with W = scale * q + bias per 64-wide group.  Here the
 // dequantized weight is rounded to bf16 once, as a quantized matmul that
 // dequantizes into the activations' type does, and every product and sum is
@@ -58,12 +57,10 @@ __device__ __forceinline__ void ws_wave_fence() {
 
 template <int MODE, int MT, int kPD>
 __global__ __launch_bounds__(kWsThreads, 2) void qmm_ws_kernel(const SwitchArgs p) {
-  static_assert(MODE == MODE_GATE_UP || MODE == MODE_DENSE_SOFTCAP, "gate_up or the head");
-  constexpr bool kRows = MODE == MODE_DENSE_SOFTCAP;
+  static_assert(MODE == MODE_DENSE_SOFTCAP, "the head");
   constexpr int BM = 16 * MT * kWsWaves;  // rows of the workgroup's tile
   static_assert(MT == 1 || MT == 2 || MT == 4, "1, 2 or 4 row tiles per wave (the epilogue stages at most 8 KB per wave)");
   extern __shared__ __attribute__((aligned(16))) uint8_t ws_lds[];
-  __shared__ ExpertChunks s_items;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -75,25 +72,15 @@ __global__ __launch_bounds__(kWsThreads, 2) void qmm_ws_kernel(const SwitchArgs 
   const int pos = (grid % kWsXcds == 0) ? (bid % kWsXcds) * (grid / kWsXcds) + bid / kWsXcds : bid;
 
   // ---- this workgroup's item: (row chunk of BM rows, weight block)
-  int e = 0, r0 = 0, rows = 0, blk = 0, tau0 = 0;
-  if constexpr (kRows) {
-    const int nch = (A + BM - 1) / BM;
-    if (pos >= nch * nblk) return;
-    const int ch = pos / nblk;
-    blk = pos - ch * nblk;
-    r0 = ch * BM;
-    rows = min(BM, A - r0);
-  } else {
-    if (!expert_chunk_item<kWsThreads, BM>(s_items, p.offsets, p.E, A, nblk, pos, e, r0, rows, blk, tau0)) return;
-  }
-  e = __builtin_amdgcn_readfirstlane(e);
-  r0 = __builtin_amdgcn_readfirstlane(r0);
-  rows = __builtin_amdgcn_readfirstlane(rows);
-  blk = __builtin_amdgcn_readfirstlane(blk);
-  tau0 = __builtin_amdgcn_readfirstlane(tau0);
+  const int nch = (A + BM - 1) / BM;
+  if (pos >= nch * nblk) return;
+  const int ch = pos / nblk;
+  const int blk = __builtin_amdgcn_readfirstlane(pos - ch * nblk);
+  const int r0 = __builtin_amdgcn_readfirstlane(ch * BM);
+  const int rows = __builtin_amdgcn_readfirstlane(min(BM, A - r0));
 
   // ---- operand addresses
-  const uint8_t* const ubase = (const uint8_t*)p.w + ((size_t)e * nblk + blk) * (size_t)G * kTiledUnit;
+  const uint8_t* const ubase = (const uint8_t*)p.w + (size_t)blk * (size_t)G * kTiledUnit;
   const uint32_t c_off = (uint32_t)wave * 1024 + lane * 16;           // this wave's quarter of the codes
   const uint32_t s_off = 4096 + ln * 16 + (uint32_t)(wave >> 1) * 256;  // (scale, bias) of its subtiles
   const uint8_t* const abytes = (const uint8_t*)p.a;
@@ -103,13 +90,7 @@ __global__ __launch_bounds__(kWsThreads, 2) void qmm_ws_kernel(const SwitchArgs 
 #pragma unroll
   for (int m = 0; m < MT; ++m) {
     const int rl = min(wrow + 16 * m + ln, rows - 1);  // rows past the chunk read its last row
-    if constexpr (MODE == MODE_GATE_UP) {
-      const int a = p.assign[r0 + rl];
-      const int src = (a >= 0 && a < A) ? token_of(a, p.ktop_inv) : 0;
-      aoff[m] = (uint32_t)src * (uint32_t)(K * 2) + lq * 32;
-    } else {
-      aoff[m] = (uint32_t)(r0 + rl) * (uint32_t)(K * 2) + lq * 32;
-    }
+    aoff[m] = (uint32_t)(r0 + rl) * (uint32_t)(K * 2) + lq * 32;
   }
 
   // ---- the ring of register slots: codes + scales of the wave's quarter of a
@@ -209,29 +190,7 @@ __global__ __launch_bounds__(kWsThreads, 2) void qmm_ws_kernel(const SwitchArgs 
   // 16 j + ln of the block; staged per wave in its 8 KB of the LDS (the last
   // group's operands are no longer read: every wave passed the barrier)
   uint8_t* const wlds = ws_lds + (size_t)wave * (kWsLds / kWsWaves);
-  if constexpr (MODE == MODE_GATE_UP) {
-    // gate j and up j + 4 -> columns 16 j .. 16 j + 15 of block blk of the
-    // activation tiles: column 16 q + 8 h + i of tile row r sits at byte
-    // h * 1024 + (16 q + r) * 16 + 2 i of the tile's block
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          *(uint16_t*)(wlds + m * 2048 + (ln >> 3) * 1024 + (16 * j + 4 * lq + i) * 16 + (ln & 7) * 2) =
-              f32_to_bf16_bits(gelu_tanh(acc[m][j][i]) * acc[m][j + 4][i]);
-    ws_wave_fence();
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      if (wrow + 16 * m >= rows) continue;
-      const int tau = tau0 + MT * wave + m;
-      if (tau < 0 || tau >= p.max_tiles) continue;
-      uint8_t* const dst = (uint8_t*)p.out + ((size_t)tau * (p.Nout / 64) + blk) * kActBlock + lane * 16;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) *(u32x4_t*)(dst + h * 1024) = *(const u32x4_t*)(wlds + m * 2048 + h * 1024 + lane * 16);
-    }
-  } else {  // the head: logits rounded to bf16, widened, cap * tanh(z / cap)
+  {  // the head: logits rounded to bf16, widened, cap * tanh(z / cap)
     float* const stg = (float*)wlds;
     const int c = lane & 31;
     const int col = blk * 128 + 4 * c;
@@ -281,37 +240,27 @@ long long round8(long long n) { return (n + kWsXcds - 1) / kWsXcds * kWsXcds; }
 }  // namespace
 
 // Where the weight-stationary kernel is the faster one (measured on the
-// prefill gate_up pass and the 256-row head; the down pass, the dense linear
-// and the dense GeGLU stayed on the chunked kernel, which was as fast or
-// faster there): gate_up from an average of 96 rows per expert, the head
-// from 128 rows.
+// 256-row head): the head from 128 rows.  Gate_up at prefill sizes went to
+// the tall-tile kernel, which was faster there; the down pass, the dense
+// linear and the dense GeGLU stayed off this kernel.
 bool ws_preferred(int mode, long long rows, int experts) {
-  if (mode == MODE_GATE_UP) return experts <= 256 && rows >= 96LL * experts;
-  if (mode == MODE_DENSE_SOFTCAP) return rows >= 128;
-  return false;
+  (void)experts;
+  return mode == MODE_DENSE_SOFTCAP && rows >= 128;
 }
 
 template <int MODE>
 hipError_t launch_ws(SwitchArgs a, int num_cu, hipStream_t stream) {
+  static_assert(MODE == MODE_DENSE_SOFTCAP, "the head");
   a.ntiles = a.nblk;
-  a.ktop_inv = ktop_inverse(a.ktop);
   const long long A = a.rows_total;
   if (A <= 0) return hipSuccess;
-  if constexpr (MODE == MODE_GATE_UP) {
-    // every row in its bucket's chunks, at most one partial chunk per expert
-    const long long items = ((A + 127) / 128 + std::min<long long>(a.E, A)) * a.nblk;
-    if (items > (1LL << 30)) return hipErrorInvalidValue;
-    return launch_ws_cfg<MODE, 2, 2>(a, (int)round8(std::max<long long>(items, 1)), stream);
-  } else {
-    // 64 rows per wave where that still gives two workgroups per compute unit
-    const long long items4 = (A + 255) / 256 * a.nblk, items2 = (A + 127) / 128 * a.nblk;
-    if (items2 > (1LL << 30)) return hipErrorInvalidValue;
-    if (items4 >= 2LL * num_cu) return launch_ws_cfg<MODE, 4, 2>(a, (int)round8(items4), stream);
-    return launch_ws_cfg<MODE, 2, 3>(a, (int)round8(items2), stream);
-  }
+  // 64 rows per wave where that still gives two workgroups per compute unit
+  const long long items4 = (A + 255) / 256 * a.nblk, items2 = (A + 127) / 128 * a.nblk;
+  if (items2 > (1LL << 30)) return hipErrorInvalidValue;
+  if (items4 >= 2LL * num_cu) return launch_ws_cfg<MODE, 4, 2>(a, (int)round8(items4), stream);
+  return launch_ws_cfg<MODE, 2, 3>(a, (int)round8(items2), stream);
 }
 
-template hipError_t launch_ws<MODE_GATE_UP>(SwitchArgs, int, hipStream_t);
 template hipError_t launch_ws<MODE_DENSE_SOFTCAP>(SwitchArgs, int, hipStream_t);
 
 }  // namespace qmoe

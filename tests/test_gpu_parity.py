@@ -449,8 +449,7 @@ def test_layer_deterministic_bitwise():
 # wave pair, and the down output ends in a half block (576 = 4.5 x 128);
 # (200, 512, 6, 4, 128): experts of ~130 rows, several chunks each, many items
 # per worker.
-# From 96 rows per expert on average gate_up runs on the weight-stationary
-# kernel: (200, 512, 6, 4, 128) and the three below (128-row tiles with a
+# From 96 rows per expert on average gate_up runs on the tall-tile kernel: (200, 512, 6, 4, 128) and the three below (128-row tiles with a
 # ragged last one, empty experts, a single expert with 1000 rows, and a gate
 # width of 320 = 5 blocks of 64 columns).
 @pytest.mark.parametrize("T,H,E,k,I", [(1, 64, 1, 1, 64), (37, 192, 12, 3, 192), (9, 256, 8, 8, 64),

@@ -1,6 +1,8 @@
 """GPU parity of the tall-tile kernel (csrc/qmm_tall.hip), which the dense
 qlinear takes from 512 rows: every output row against the oracle's fp64
-qlinear (vision.ts page, VisionLinear.forward, quantized arm).
+qlinear (vision.ts page, VisionLinear.forward, quantized arm).  The gate_up
+switch linear on this kernel (from 96 rows per expert) is covered by the
+layer tests and by the dropped-index case at the end.
 
 Shapes cover both launch configurations: 128-row tiles with the whole
 contraction per wave, and 64-row tiles with the contraction split in two
@@ -132,4 +134,38 @@ def test_tall_geglu_parity(M, K, N):
     err = O.rowwise_rel_err(yh, O.dense_geglu(x, gate, up))
     say(f"  rel err {err_w1:.3e} (bf16 weights), {err:.3e} (exact weights)")
     assert err_w1 <= 5e-3
+    assert err <= 2e-2
+
+
+def test_tall_down_dropped_indices():
+    """The gate_up pass on the tall-tile kernel (from 96 rows per expert)
+    with out-of-range routing indices, then the down pass: the dropped
+    assignments sit in the tail bucket that gate_up skips and down weights
+    by zero, so each token gets the weighted sum of its remaining
+    assignments (model page, DiffExperts.forward)."""
+    import bit_quantized_moe_diffrouter_amd as q
+    from _util import dev_params
+    cfg = synth.MoEConfig("tall_down_dropped", T=300, H=256, E=4, k=2, I=128, seed_w=61, seed_x=62)
+    say(f"[tall down dropped] T={cfg.T} E={cfg.E} k={cfg.k}")
+    inp = synth.make_moe_inputs(cfg)
+    r = inp.weights.router
+    idx, w, _ = O.route(inp.x, inp.weights.norm_scale, cfg.eps, r.w, r.scales, r.biases,
+                        inp.weights.per_expert_scale, cfg.k)
+    bad = idx.copy()
+    drop = [(3, 1), (10, 0), (57, 1), (120, 0), (299, 1)]
+    for t, j in drop:
+        bad[t, j] = -1 if t % 2 else cfg.E + 3
+    p = dev_params(inp.weights)
+    x = dev_tensor(inp.x)
+    off, sa = q.moe_sort(dev_tensor(bad.astype(np.int32)), cfg.E)
+    mid = q.qswitch_gate_up_geglu(x, p.gate_up, cfg.I, cfg.k, off, sa)
+    y = q.qswitch_down_combine(mid, cfg.T, cfg.k, p.down, dev_tensor(w.astype(np.float32)), off, sa)
+    torch.cuda.synchronize()
+    w0 = w.copy()
+    for t, j in drop:
+        w0[t, j] = 0.0
+    safe = np.where((bad >= 0) & (bad < cfg.E), bad, 0)
+    ref = O.experts_bruteforce(inp.x, safe, w0, inp.weights.gate_up, inp.weights.down, cfg.I)
+    err = O.rowwise_rel_err(bf16_host(y), ref)
+    say(f"  rel err {err:.3e}")
     assert err <= 2e-2

@@ -1,5 +1,6 @@
 """CPU emulation of the switch and dense kernels' schedules (qswitch.hip's
-chunked kernel and qmm_ws.hip's weight-stationary one).
+chunked kernel, qmm_tall.hip's gate_up launch and qmm_ws.hip's
+weight-stationary pipeline).
 
 The kernels' index arithmetic is restated here in Python, independently of
 the device code: buckets and their two-tile and one-tile chunks, the
@@ -16,10 +17,11 @@ on the ragged layer shapes of the GPU tests, that:
     or finished (the row table entry of c is intact when its rows are
     stored);
   * every weight, activation, mid and output access lies inside its buffer;
-  * the weight-stationary kernel covers every (row chunk, block) of every
-    expert exactly once, inside the buffers, and its per-group pipeline
-    (register ring of codes and activations, two LDS buffers, one barrier
-    per group) feeds every group's products with that group's operands.
+  * the tall-tile kernel's gate_up launch (from 96 rows per expert) covers
+    every (row chunk, block) of every expert exactly once, inside the
+    buffers, and the weight-stationary kernel's per-group pipeline (register
+    ring of codes and activations, two LDS buffers, one barrier per group)
+    feeds every group's products with that group's operands.
 No GPU is used."""
 import numpy as np
 import pytest
@@ -201,48 +203,65 @@ def emulate_chunked(mode, A, E, nblk, G, offsets=None, assign=None, T=None, ktop
     return ks, D, grid, total_items
 
 
-def emulate_ws(A, E, nblk, G, offsets, assign, T, ktop, Nout, K, MT=2):
-    """The weight-stationary gate_up launch: every (expert chunk, block)
-    exactly once, inside the buffers."""
-    BM = 64 * MT
-    items = (-(-A // BM) + min(E, A)) * nblk
-    grid = -(-items // 8) * 8
+def emulate_tall_gate_up(A, E, nblk, G, offsets, assign, T, ktop, Nout, K, num_cu=NUM_CU, MT=8, NB=2, pos0_of=None):
+    """The tall-tile gate_up launch: a persistent grid of at most one
+    workgroup per compute unit, workgroup b starting at position pos0 (the
+    workgroups numbered die by die) and stepping by the grid; position pos is
+    chunk pos // nbp of the experts' 128-row chunks and the block pair
+    pos % nbp (block 2 (pos % nbp) + wave // 2 for each wave).  Every
+    (expert chunk, block) exactly once, inside the buffers.  pos0_of
+    overrides the first position of a workgroup (for the planted-mistake
+    test)."""
+    BM = 16 * MT
+    nbp = -(-nblk // NB)
+    items = (-(-A // BM) + min(E, A)) * nbp
+    grid = min(-(-items // 8) * 8, num_cu * (4 // (2 * NB)))
     lo = np.clip(offsets[:E], 0, A)
     hi = np.maximum(np.clip(offsets[1:E + 1], 0, A), lo)
     n = hi - lo
     cpre = np.concatenate([[0], np.cumsum(-(-n // BM))])
     tpre = np.concatenate([[0], np.cumsum(-(-n // 16))])
     max_tiles = -(-A // 16) + min(E, A)
-    nch = int(cpre[E])
+    n_items = int(cpre[E]) * nbp
+    assert n_items <= items
+    NW, NS = 2 * NB, MT // (2 * NB)
     seen = set()
     for b in range(grid):
-        pos = (b % 8) * (grid // 8) + b // 8
-        if pos >= nch * nblk:
-            continue
-        ch, blk = pos // nblk, pos % nblk
-        e = int(np.count_nonzero(cpre[:E] <= ch)) - 1
-        assert cpre[e] <= ch < cpre[e + 1]
-        r0 = int(lo[e] + (ch - cpre[e]) * BM)
-        rows = int(min(BM, hi[e] - r0))
-        assert 1 <= rows and r0 + rows <= hi[e]
-        tau0 = int(tpre[e] + (r0 - lo[e]) // 16)
-        assert (e, r0, blk) not in seen
-        seen.add((e, r0, blk))
-        assert ((e * nblk + blk) * G + G - 1) < E * nblk * G
-        for w in range(4):
-            for m in range(MT):
-                wr = 16 * MT * w + 16 * m
-                for ln in range(16):
-                    rl = min(wr + ln, rows - 1)
-                    a = int(assign[r0 + rl])
-                    src = a // ktop if 0 <= a < A else 0
-                    assert src * K * 2 + (G - 1) * 128 + 3 * 32 + 32 <= T * K * 2
-                if wr < rows:
-                    tau = tau0 + MT * w + m
+        pos0 = (b % 8) * (grid // 8) + b // 8 if grid % 8 == 0 else b
+        if pos0_of is not None:
+            pos0 = pos0_of(b, grid)
+        for pos in range(pos0, n_items, grid):
+            ch, bp = pos // nbp, pos % nbp
+            e = int(np.count_nonzero(cpre[:E] <= ch)) - 1
+            assert cpre[e] <= ch < cpre[e + 1]
+            r0 = int(lo[e] + (ch - cpre[e]) * BM)
+            rows = int(min(BM, hi[e] - r0))
+            assert 1 <= rows and r0 + rows <= hi[e]
+            tau0 = int(tpre[e] + (r0 - lo[e]) // 16)
+            mt = -(-rows // 16)
+            for wave in range(2 * NB):
+                c, bsel = wave & 1, wave >> 1
+                blk = bp * NB + bsel
+                wblk = min(blk, nblk - 1)
+                assert ((e * nblk + wblk) * G + G) * UNIT <= E * nblk * G * UNIT
+                for s in range(NS):
+                    for ln in range(16):
+                        rl = min(16 * (wave + NW * s) + ln, rows - 1)
+                        a = int(assign[r0 + rl])
+                        src = a // ktop if 0 <= a < A else 0
+                        assert src < T and src * K * 2 + (G - 1) * 128 + 3 * 32 + 32 <= T * K * 2
+                if blk >= nblk:
+                    continue
+                if c == 0:
+                    assert (e, r0, blk) not in seen, "an (expert chunk, block) computed twice"
+                    seen.add((e, r0, blk))
+                for m in range(mt):
+                    tau = tau0 + m
                     if 0 <= tau < max_tiles:
-                        assert (tau * (Nout // 64) + blk + 1) * ACT_BLOCK <= max_tiles * (Nout // 64) * ACT_BLOCK
+                        last = (tau * (Nout // 64) + blk) * ACT_BLOCK + 1024 + 512 * c + 31 * 16 + 16
+                        assert last <= max_tiles * (Nout // 64) * ACT_BLOCK
     expect = {(e, int(lo[e] + c * BM), blk) for e in range(E) for c in range(-(-int(n[e]) // BM)) for blk in range(nblk)}
-    assert seen == expect
+    assert seen == expect, "an (expert chunk, block) never computed"
 
 
 def emulate_ws_pipeline(G, PD, refill=None, ahead=None, prod_buf=None):
@@ -342,7 +361,7 @@ def both_passes(idx, T, k, E, H, I):
     ks_g = emulate_chunked("gate_up", A, E, -(-I // 64), H // 64, off, order, T, k, I, H)
     ks_d = emulate_chunked("down", A, E, -(-H // 128), I // 64, off, order, T, k, H, I)
     if A >= 96 * E:
-        emulate_ws(A, E, -(-I // 64), H // 64, off, order, T, k, I, H)
+        emulate_tall_gate_up(A, E, -(-I // 64), H // 64, off, order, T, k, I, H)
     return ks_g, ks_d
 
 
@@ -388,3 +407,17 @@ def test_emulation_catches_planted_mistakes():
     emulate_chunked("dense", 40000, 1, 8, 1)
     with pytest.raises(AssertionError, match="c \\+ 4"):
         emulate_chunked("dense", 40000, 1, 8, 1, D=4)
+
+
+def test_tall_gate_up_emulation_catches_planted_mistakes():
+    """Dropping the per-die index from the first position (every workgroup of
+    a die then starts on the same item) computes some items twice and others
+    never."""
+    T, k, E, H, I = 1024, 8, 16, 256, 704
+    idx = np.random.default_rng(9).integers(0, E, size=(T, k))
+    off, _ = O.sort_assignments(idx, E)
+    order = np.argsort(idx.reshape(-1), kind="stable").astype(np.int64)
+    args = (T * k, E, -(-I // 64), H // 64, off, order, T, k, I, H)
+    emulate_tall_gate_up(*args)
+    with pytest.raises(AssertionError, match="twice|never"):
+        emulate_tall_gate_up(*args, pos0_of=lambda b, grid: (b % 8) * (grid // 8))

@@ -169,3 +169,27 @@ def test_tall_down_dropped_indices():
     err = O.rowwise_rel_err(bf16_host(y), ref)
     say(f"  rel err {err:.3e}")
     assert err <= 2e-2
+
+
+def test_tall_gate_up_at_the_largest_expert_count():
+    """The gate_up pass on the tall-tile kernel with E = 256, k = 16 (its
+    chunk tables full: 256 experts, read 4 per lane by one wave): T = 1536
+    gives A = 24576 = 96 * E rows, the smallest count that takes this kernel.
+    The whole layer against the oracle's experts with the GPU's routing
+    (model page, DiffExperts.forward)."""
+    import bit_quantized_moe_diffrouter_amd as q
+    from _util import dev_params
+    cfg = synth.MoEConfig("tall_e256", T=1536, H=128, E=256, k=16, I=64, seed_w=71, seed_x=72)
+    say(f"[tall gate_up E=256] T={cfg.T} k={cfg.k} A={cfg.T * cfg.k}")
+    inp = synth.make_moe_inputs(cfg)
+    p = dev_params(inp.weights)
+    x = dev_tensor(inp.x)
+    y, idx, w, off, sa, mid = q.moe_layer(x, x, p, cfg.k, cfg.eps)
+    torch.cuda.synchronize()
+    assert int(off[-1].item()) == cfg.T * cfg.k
+    toks = np.arange(0, cfg.T, 7)
+    ref = O.experts_bruteforce(inp.x, idx.cpu().numpy(), w.cpu().numpy(), inp.weights.gate_up, inp.weights.down,
+                               cfg.I, tokens=toks)
+    err = O.rowwise_rel_err(bf16_host(y)[toks], ref)
+    say(f"  rel err {err:.3e} over {len(toks)} tokens")
+    assert err <= 2e-2

@@ -165,7 +165,7 @@ def run_block(cfg):
     return inp, fw, bf16_host(out), idx.cpu().numpy(), w.cpu().numpy()
 
 
-@pytest.mark.parametrize("cfg,n_tok", [(synth.FF_TINY, 16), (synth.FF_CANVAS, 8)], ids=lambda v: getattr(v, "name", v))
+@pytest.mark.parametrize("cfg,n_tok", [(synth.FF_TINY, 16), (synth.FF_CANVAS, 48)], ids=lambda v: getattr(v, "name", v))
 def test_ff_block_parity(cfg, n_tok):
     """The whole block through the bindings against the oracle's block; the
     oracle's expert stage takes the GPU's routing (so that near-tied top-k

@@ -831,8 +831,8 @@ def main():
         summarize(args.summarize)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build measures one GPU only (the layer's multi-GPU split is a design "
-              "note, not built); run with --gpus 1", file=sys.stderr)
+        print("bench.py: the layer runs on one GPU only (how it would split across GPUs is "
+              "described, not built); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     if args.copy_probe:
